@@ -1,0 +1,240 @@
+"""Benchmark of one decode step (kv_append + paged decode attention) on one GPU.
+
+Prints one JSON line. A step appends one token to every sequence and runs
+paged decode attention over the cache (the decode-step listing of "KV Cache는
+왜 LLM 서빙의 핵심인가", section "KV Cache: O(T²)를 O(T)로"), on seeded
+synthetic inputs already resident in HBM.
+
+  value     KV-tokens/s: tokens attended per step (summed over sequences)
+            divided by the measured step time
+  roofline  the split attention kernel's algorithmic bytes per launch divided
+            by its average launch time (HIP events on the launch stream),
+            against 8 TB/s
+  cpu_baseline  the oracle (fp64 C, OpenMP) on the host, on the same inputs
+
+Consecutive steps rotate over pool replicas whose total size exceeds twice the
+256 MB last-level (Infinity) cache, so a step never finds its KV there.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (ctypes)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["tiny", "llama3_8b", "llama2_70b", "kvquant_int4", "long_shared"])
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import paged_kv_cache_169_amd as kv
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    name = args.workload
+    t_setup = time.time()
+    c = wl.workload(name, device=dev, poison=False)
+    int4 = c.int4
+    B, n_h, n_kv, D = c.batch, c.n_h, c.n_kv, c.d
+    es = 4 if c.dtype == "f32" else 2
+    ctx = c.ctx_lens.cpu()
+    tokens_per_step = int(ctx.sum().item())
+
+    # replicas: consecutive steps never share KV addresses in the 256 MB MALL
+    probe = kv.make_desc(c.num_blocks, n_kv, D, "int4" if int4 else c.dtype, B if int4 else 0)
+    pool_bytes = kv.kv_pool_required_bytes(probe)
+    reps = max(2, math.ceil(2 * MALL_BYTES / pool_bytes) + 1)
+    pools = []
+    src = None
+    if int4:
+        src = kv.KVPool(c.num_blocks, n_kv, D, "bf16", device=dev)
+        src.K.copy_(c.K)
+        src.V.copy_(c.V)
+    for r in range(reps):
+        if int4:
+            p = kv.KVPool(c.num_blocks, n_kv, D, "int4", max_seqs=B, device=dev)
+            kv.kv_quantize_int4(p, src, c.tables, c.seq_lens)
+        else:
+            p = kv.KVPool(c.num_blocks, n_kv, D, c.dtype, device=dev)
+            p.K.copy_(c.K)
+            p.V.copy_(c.V)
+        pools.append(p)
+    del src
+    if name == "long_shared":
+        for p in pools:
+            kv.rope_rerotate(p, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
+    max_ctx = int(ctx.max().item())
+    opts = kv.attn_opts(split_blocks=args.split, kernel=args.kernel)
+    ws_bytes = kv.paged_decode_attention_workspace_bytes(pools[0], B, n_h, max_ctx, opts)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, n_h, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: B={B} n_h={n_h} n_kv={n_kv} d={D} dtype={'int4' if int4 else c.dtype} "
+        f"tokens/step={tokens_per_step} pool={pool_bytes/1e6:.1f} MB x {reps} replicas, "
+        f"workspace={ws_bytes/1e6:.2f} MB, setup {time.time()-t_setup:.1f}s")
+
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        p = pools[i % reps]
+        if c.append:
+            kv.kv_append(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
+        o = opts
+        if events is not None:
+            o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, events=events)
+        kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    ev = [[hip.create() for _ in range(3)] for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(i, ev[i])
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e_start.elapsed_time(e_end)
+    ms_per_step = ms_total / args.steps
+    split_ms = [hip.elapsed_ms(e[0], e[1]) for e in ev]
+    merge_ms = [hip.elapsed_ms(e[1], e[2]) for e in ev]
+    for e in ev:
+        for x in e:
+            hip.destroy(x)
+    split_avg = sum(split_ms) / len(split_ms)
+    merge_avg = sum(merge_ms) / len(merge_ms)
+
+    # algorithmic bytes of one split-kernel launch: K and V of every attended
+    # (token, kv head) once, q, the output, the block-table entries and lengths
+    nblk = ((ctx + 15) // 16)
+    if int4:
+        kv_bytes = int(ctx.sum().item()) * n_kv * 164
+    else:
+        kv_bytes = int(ctx.sum().item()) * n_kv * 2 * D * es
+    alg_bytes = kv_bytes + B * n_h * D * es + B * n_h * D * 4 + int(nblk.sum().item()) * 4 + B * 4
+    achieved = alg_bytes / (split_avg * 1e-3) / 1e9
+    value = tokens_per_step / (ms_per_step * 1e-3)
+    log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
+        f"{split_avg*1e3:.1f} us, merge {merge_avg*1e3:.1f} us, {achieved:.0f} GB/s "
+        f"({100*achieved/PEAK_HBM_GBS:.1f}% of 8 TB/s), {value/1e9:.3f} G KV-tokens/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import numpy as np
+        import oracle
+        p0 = pools[0]
+        tab = c.tables.cpu().numpy()
+        ctx_np = c.ctx_lens.cpu().numpy()
+        qh = wl.to_host_bits(c.q)
+        if int4:
+            img = oracle.Q4Image(c.num_blocks, n_kv, D, B)
+            for a, t in zip(img.arrays(), [p0.KQ, p0.KS, p0.KM, p0.VQ, p0.VS, p0.VM, p0.KTAIL]):
+                h = t.detach().cpu().contiguous()
+                a[...] = h.view(torch.int16).numpy().view(np.uint16) if h.element_size() == 2 else h.numpy()
+            Kh, Vh = oracle.q4_dequant(img, tab, ctx_np)
+        else:
+            Kh, Vh = wl.to_host_bits(p0.K), wl.to_host_bits(p0.V)
+        threads = oracle.max_threads()
+        done_tokens, t_cpu, runs = 0, 0.0, 0
+        # whole-batch oracle passes until the time budget is spent (at least one)
+        while t_cpu < args.cpu_seconds or runs == 0:
+            t1 = time.perf_counter()
+            oracle.attention(Kh, Vh, qh, tab, ctx_np, c.scale)
+            t_cpu += time.perf_counter() - t1
+            done_tokens += tokens_per_step
+            runs += 1
+        cpu = {"value": done_tokens / t_cpu, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{runs} full pass(es) of the {name} attention ({tokens_per_step} tokens x {n_h} heads, "
+                         f"fp64, OpenMP over (sequence, head)), {t_cpu:.1f} s"}
+        log(f"[bench] oracle: {cpu['value']/1e6:.3f} M KV-tokens/s on {threads} threads ({runs} runs, {t_cpu:.1f}s)")
+
+    line = {
+        "metric": "paged GQA decode attention: KV-tokens/s and achieved HBM GB/s (% of peak)",
+        "value": value,
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4" if int4 else c.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "ctx": "U[512,4096]+1" if "uniform" in str(wl.WORKLOADS[name]["lens"])
+                   else int(ctx.max().item()), "tokens_per_step": tokens_per_step, "n_h": n_h, "n_kv": n_kv,
+                   "head_dim": D, "block_size": 16, "kernel": args.kernel, "split_blocks": args.split,
+                   "accumulate": "f32", "pool_replicas": reps},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "split attention kernel", "avg_launch_us": split_avg * 1e3,
+                     "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * kvcache.h -- C ABI of a paged KV-cache decode library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [KVSYS] "KV 캐시 시스템 (KV Cache System)" (TensorRT-LLM KV cache, Korean
+ *           wiki rendering): "MQA / GQA", "데이터 타입", "제한된 어텐션 윈도우 크기".
+ *   [VLLM]  "LLM 서빙과 KV Cache, vLLM": "KV Cache", "PagedAttention".
+ *   [CORE]  "KV Cache는 왜 LLM 서빙의 핵심인가": "KV Cache: O(T²)를 O(T)로"
+ *           (decode-step listing), "메모리 공식과 GQA의 동기",
+ *           "KVQuant: 마지막 4배" (quantizer equation).
+ *   [BLEND] "Research Paper Review : CACHE BLEND": "Background" (full KV reuse
+ *           and RoPE re-rotation of a precomputed chunk).
+ *
+ * Conventions for every call:
+ *   - Device pointers point to memory the caller owns (allocated with
+ *     hipMalloc or any allocator on the same device). The library never
+ *     allocates or frees device memory and never synchronizes.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Work is enqueued asynchronously on it; the caller synchronizes.
+ *   - Calls return a kv_status synchronously. Arguments the host can check
+ *     (null pointers, sizes, shapes, dtype combinations, workspace size) are
+ *     checked before anything is launched; on error nothing is launched.
+ *     A failed launch returns KV_ERR_HIP.
+ *   - Device-resident metadata (block tables, lengths, slots) is not read by
+ *     the host. Kernels bounds-check it: a block id outside [0, num_blocks)
+ *     or a length outside [0, max_blocks * 16] never causes an out-of-range
+ *     access; attention then writes NaN to the affected sequence's output
+ *     and append/quantize/rotate skip the affected rows.
+ *     kv_validate_tables checks host copies of the same arrays.
+ */
+#ifndef KVCACHE_H
+#define KVCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_ABI_VERSION 1
+/* Tokens per physical block [VLLM, "PagedAttention": fixed-size blocks]. */
+#define KV_BLOCK_TOKENS 16
+
+typedef int32_t kv_status;
+enum {
+    KV_OK = 0,
+    KV_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape             */
+    KV_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim 96) */
+    KV_ERR_WORKSPACE = -3,   /* workspace missing or too small              */
+    KV_ERR_HIP = -4,         /* a HIP launch or runtime call failed         */
+    KV_ERR_TABLE = -5        /* kv_validate_tables found a bad entry        */
+};
+
+/* Element type of the cache [KVSYS, "데이터 타입": the cache dtype]. */
+typedef enum {
+    KV_F32 = 0,  /* K, V, q, new tokens in fp32                                   */
+    KV_BF16 = 1, /* K, V, q, new tokens in bf16                                   */
+    KV_INT4 = 2  /* KVQuant INT4 storage; q and new tokens are bf16 [CORE, KVQuant] */
+} kv_dtype;
+
+/* Pool descriptor. A pool is num_blocks physical blocks of 16 tokens for
+ * num_kv_heads kv heads of head_dim channels ([VLLM, "PagedAttention"]: a
+ * block holds a fixed number of tokens and may sit anywhere in the pool;
+ * [KVSYS, "MQA / GQA"]: blocks hold the state of one query group per kv head). */
+typedef struct {
+    int32_t num_blocks;   /* >= 1                                              */
+    int32_t block_size;   /* must be 16                                        */
+    int32_t num_kv_heads; /* >= 1                                              */
+    int32_t head_dim;     /* 64 or 128                                         */
+    int32_t max_seqs;     /* KV_INT4: rows of the bf16 K tail (>= 1); else 0   */
+    int32_t dtype;        /* kv_dtype                                          */
+} kv_pool_desc;
+
+/* Opaque host-side handle: the descriptor, the bound device base pointer and
+ * region offsets. It owns no device memory. */
+typedef struct kv_pool *kv_pool_t;
+
+/* Regions of a pool's device memory. Layouts (row-major, element (p,h,t,c)
+ * of a K or V region at ((p * n_kv + h) * 16 + t) * head_dim + c):
+ *   KV_F32 / KV_BF16 pools:
+ *     K, V        elem [num_blocks][n_kv][16][head_dim]
+ *   KV_INT4 pools:
+ *     KQ, VQ      uint8 [num_blocks][n_kv][16][head_dim/2]; byte c/2 of a
+ *                 token row holds channel c (even) in bits 0-3 and channel
+ *                 c+1 in bits 4-7
+ *     KS, KM      fp16 [num_blocks][n_kv][head_dim]   K scale, min per channel
+ *     VS, VM      fp16 [num_blocks][n_kv][16]         V scale, min per token
+ *     KTAIL       bf16 [max_seqs][n_kv][16][head_dim] K rows of each sequence's
+ *                 block that is not yet full
+ * Every region starts on a 256-byte boundary. */
+enum {
+    KV_REGION_K = 0,
+    KV_REGION_V = 1,
+    KV_REGION_KQ = 2,
+    KV_REGION_KS = 3,
+    KV_REGION_KM = 4,
+    KV_REGION_VQ = 5,
+    KV_REGION_VS = 6,
+    KV_REGION_VM = 7,
+    KV_REGION_KTAIL = 8
+};
+
+/* Options of paged_decode_attention; pass NULL for the defaults (all zero). */
+typedef struct {
+    int32_t split_blocks; /* blocks per context split; 0 = chosen by the library   */
+    int32_t kernel;       /* 0 = chosen by the library, 1 = VALU dot products,
+                             2 = MFMA tiles (bf16 and INT4 pools only)              */
+    int32_t window;       /* > 0: attend only the last `window` tokens of each
+                             sequence [KVSYS, "제한된 어텐션 윈도우 크기"]; 0 = all  */
+    int32_t reserved;     /* must be 0                                            */
+    void *events[3];      /* optional hipEvent_t handles recorded on the stream
+                             before the split kernel, after it, and after the
+                             merge kernel (for timing); NULL entries are skipped  */
+} kv_attn_opts;
+
+/* Human-readable name of a status code (static storage). */
+const char *kv_status_string(kv_status s);
+
+/* KV_ABI_VERSION of the library that was loaded. */
+int32_t kv_abi_version(void);
+
+/* Device bytes a pool with this descriptor needs (regions laid out back to
+ * back, each 256-byte aligned). 0 if the descriptor is invalid. For KV_F32 /
+ * KV_BF16 the K and V regions hold exactly 2 * num_blocks * 16 * n_kv *
+ * head_dim * elem_bytes bytes ([CORE, "메모리 공식과 GQA의 동기"]: M_KV =
+ * 2 L T (d_h n_kv) b for one layer and T = 16 num_blocks). */
+size_t kv_pool_required_bytes(const kv_pool_desc *desc);
+
+/* Bind a descriptor to caller-owned device memory of at least
+ * kv_pool_required_bytes(desc) bytes, 256-byte aligned. Launches nothing and
+ * does not touch the memory. *out receives a handle to free with
+ * kv_pool_destroy. */
+kv_status kv_pool_create(const kv_pool_desc *desc, void *device_mem, size_t bytes, kv_pool_t *out);
+
+/* Free the host-side handle (the device memory stays the caller's). */
+kv_status kv_pool_destroy(kv_pool_t pool);
+
+/* Byte offset (from device_mem) and size of one region; KV_ERR_INVALID_ARG if
+ * the pool's dtype has no such region. */
+kv_status kv_pool_region(kv_pool_t pool, int32_t region, size_t *offset, size_t *bytes);
+
+/* Descriptor the pool was created with. */
+kv_status kv_pool_get_desc(kv_pool_t pool, kv_pool_desc *desc);
+
+/* Append one new token per sequence
+ * [CORE, "KV Cache: O(T²)를 O(T)로": K_{1:t} = [K_{1:t-1}; k_t], same for V].
+ *   k_new, v_new  device [batch][n_kv][head_dim], the pool's element type
+ *                 (bf16 for KV_INT4 pools)
+ *   block_tables  device int32 [batch][max_blocks]: physical block of each
+ *                 logical 16-token block of each sequence [VLLM, PagedAttention]
+ *   seq_lens      device int32 [batch]: length BEFORE the append; the token
+ *                 goes to block block_tables[b][L/16], slot L % 16, and that
+ *                 table entry must already name a block
+ *   seq_slots     KV_INT4 only: device int32 [batch] row of the K tail that
+ *                 belongs to each sequence; NULL means row b. Ignored otherwise.
+ * KV_INT4 pools: V is coded per token at once; K goes to the tail row L % 16;
+ * when that row is the 16th, the whole block's K is coded per channel into
+ * the block (KQ/KS/KM). Two sequences must not write the same slot. */
+kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new,
+                    const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens,
+                    const int32_t *seq_slots, int32_t batch, void *stream);
+
+/* Bytes of workspace paged_decode_attention needs for these sizes and
+ * options (0 is a valid answer: then workspace may be NULL). max_ctx is an
+ * upper bound of every ctx_lens[b]. Returns (size_t)-1 on invalid input. */
+size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads,
+                                              int32_t max_ctx, const kv_attn_opts *opts);
+
+/* Single-token decode attention over the paged cache
+ * [CORE, "KV Cache: O(T²)를 O(T)로": attn_t = softmax(q_t K_{1:t}^T * scale) V_{1:t}],
+ * with K, V gathered through each sequence's block table [VLLM, PagedAttention]
+ * and query head h reading kv head h / (num_q_heads / n_kv) [KVSYS, MQA / GQA].
+ *   q             device [batch][num_q_heads][head_dim], pool element type
+ *                 (bf16 for KV_INT4)
+ *   out           device fp32 [batch][num_q_heads][head_dim]
+ *   num_q_heads   multiple of n_kv, num_q_heads / n_kv <= 16
+ *   scale         softmax scale (1/sqrt(head_dim) for the usual model)
+ *   ctx_lens      device int32 [batch]: tokens to attend (the cache length
+ *                 after this step's append); 0 gives an output of 0
+ *   seq_slots     KV_INT4: K tail row of each sequence (NULL = row b)
+ *   max_ctx       host upper bound of ctx_lens (sizes the grid/workspace)
+ *   workspace     device buffer of at least ws_bytes >=
+ *                 paged_decode_attention_workspace_bytes(...) bytes
+ * KV_INT4 pools are dequantized on the fly: full blocks from their codes,
+ * the K of a sequence's partial last block from its bf16 tail row. */
+kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads,
+                                 float scale, const int32_t *block_tables, int32_t max_blocks,
+                                 const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
+                                 int32_t max_ctx, void *workspace, size_t ws_bytes,
+                                 const kv_attn_opts *opts, void *stream);
+
+/* Bulk KVQuant INT4 coding of bf16 pool contents [CORE, "KVQuant: 마지막 4배"]:
+ * code = clamp(round((x - min) / s), 0, 15) with s = (max - min) / 15, s and min
+ * stored in fp16 and the codes computed from the stored values (fp32
+ * arithmetic, rounding half away from zero; a group whose fp16 s is 0 gets
+ * codes 0). K groups: (block, kv head, channel) over the block's 16 tokens;
+ * V groups: (token, kv head) over head_dim channels.
+ * For each sequence b with lens[b] tokens in src (through block_tables, which
+ * address both pools): full blocks get K and V codes; a partial last block
+ * gets V codes for its tokens and its K rows copied to the K tail row
+ * seq_slots[b] (NULL = b). dst: KV_INT4 pool; src: KV_BF16 pool with the same
+ * num_blocks, num_kv_heads and head_dim. Nothing else in dst is written. */
+kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables,
+                           int32_t max_blocks, const int32_t *lens, const int32_t *seq_slots,
+                           int32_t batch, void *stream);
+
+/* RoPE re-rotation of a reused chunk's keys in place [BLEND, "Background":
+ * keys precomputed as if the chunk started at position 0 are moved to the
+ * real start by one extra rotation by delta = real start - 0].
+ *   chunk_blocks  device int32: physical ids of the chunk's blocks in
+ *                 logical order
+ *   first_slot    logical position of the chunk's first token within that
+ *                 block list (0 when the chunk starts a block)
+ *   num_tokens    tokens in the chunk
+ *   delta         rotation offset in positions (may be negative)
+ *   base          RoPE base (10000 for LLaMA); pair i turns by delta * base^(-2i/head_dim)
+ *   style         0: pairs (2i, 2i+1); 1: pairs (i, i + head_dim/2)
+ * Angles and cos/sin are computed on the host in fp64 and rounded to fp32;
+ * each pair (x, y) becomes (x c - y s, x s + y c) in fp32 without fused
+ * multiply-add, rounded to the pool type. Every kv head is rotated; V is not
+ * touched. KV_F32 and KV_BF16 pools only (rotate before coding to INT4). */
+kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t first_slot,
+                        int32_t num_tokens, int32_t delta, float base, int32_t style, void *stream);
+
+/* Host-side check of HOST copies of the metadata a decode step would use:
+ * every block the first lens[b] tokens (after the append when `appending`
+ * is nonzero, i.e. lens[b] + 1 tokens) need is in [0, num_blocks), lens are
+ * non-negative and fit max_blocks * 16, and no two sequences append into the
+ * same (block, slot). KV_OK, or KV_ERR_TABLE with *bad_row set to the first
+ * offending sequence (bad_row may be NULL). */
+kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
+                             const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCACHE_H */

@@ -30,7 +30,7 @@
  *   R4 INT4 is asymmetric: code = clamp(round((x - min) / s), 0, 15) with
  *      s = (max - min) / 15, rounding half away from zero, computed in fp32
  *      from the STORED fp16 s and min; a group whose fp16 s is 0 has all
- *      codes 0. A zero min of either sign is stored as +0.
+ *      codes 0. A zero min or max of either sign is taken as +0.
  *   R5 K groups are (block, kv head, channel) over the block's 16 tokens;
  *      V groups are (token, kv head) over the d_h channels. The K of a block
  *      that is not yet full stays in bf16 in a per-sequence tail.
@@ -274,7 +274,8 @@ static void q4_group(const float *x, int n, size_t xs, uint8_t *codes, size_t cs
         if (v < mn) mn = v;
         if (v > mx) mx = v;
     }
-    if (mn == 0.0f) mn = 0.0f; /* store a zero min as +0 */
+    if (mn == 0.0f) mn = 0.0f; /* a zero min or max of either sign is +0 */
+    if (mx == 0.0f) mx = 0.0f;
     float s32 = (mx - mn) / 15.0f;
     *s16 = kvo_f32_to_f16(s32);
     *m16 = kvo_f32_to_f16(mn);

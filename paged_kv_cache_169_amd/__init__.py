@@ -1,0 +1,287 @@
+"""Python binding of libkvcache.so (include/kvcache.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels. PyTorch supplies device memory (tensors) and streams; functions
+take tensors, check that they live on the GPU with the right dtype and
+shape, and pass their data pointers to the C functions of the same name.
+
+The library must have been built (``__graft_entry__.build()``); importing
+this package raises if it is missing. There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvcache.so")
+
+KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP, KV_ERR_TABLE = 0, -1, -2, -3, -4, -5
+KV_F32, KV_BF16, KV_INT4 = 0, 1, 2
+BLOCK = 16
+(KV_REGION_K, KV_REGION_V, KV_REGION_KQ, KV_REGION_KS, KV_REGION_KM, KV_REGION_VQ, KV_REGION_VS,
+ KV_REGION_VM, KV_REGION_KTAIL) = range(9)
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+
+_DTYPES = {"f32": KV_F32, "bf16": KV_BF16, "int4": KV_INT4}
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kv_status_string(status)} ({status})")
+        self.status = status
+
+
+class kv_pool_desc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class kv_attn_opts(ctypes.Structure):
+    _fields_ = [("split_blocks", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("events", ctypes.c_void_p * 3)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I32, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+
+
+def _decl(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_kv_status_string = _decl("kv_status_string", ctypes.c_char_p, [_I32])
+_kv_abi_version = _decl("kv_abi_version", _I32, [])
+_kv_pool_required_bytes = _decl("kv_pool_required_bytes", _SZ, [ctypes.POINTER(kv_pool_desc)])
+_kv_pool_create = _decl("kv_pool_create", _I32, [ctypes.POINTER(kv_pool_desc), _P, _SZ, ctypes.POINTER(_P)])
+_kv_pool_destroy = _decl("kv_pool_destroy", _I32, [_P])
+_kv_pool_region = _decl("kv_pool_region", _I32, [_P, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)])
+_kv_pool_get_desc = _decl("kv_pool_get_desc", _I32, [_P, ctypes.POINTER(kv_pool_desc)])
+_kv_append = _decl("kv_append", _I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P])
+_paged_decode_attention_workspace_bytes = _decl(
+    "paged_decode_attention_workspace_bytes", _SZ, [_P, _I32, _I32, _I32, ctypes.POINTER(kv_attn_opts)])
+_paged_decode_attention = _decl(
+    "paged_decode_attention", _I32,
+    [_P, _P, _P, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
+_kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P])
+_rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
+_kv_validate_tables = _decl("kv_validate_tables", _I32,
+                            [ctypes.POINTER(kv_pool_desc), _P, _I32, _P, _I32, _I32, ctypes.POINTER(_I32)])
+
+
+def lib_handle():
+    """The loaded ctypes library (tests check its exports)."""
+    return _lib
+
+
+def kv_status_string(status: int) -> str:
+    return _kv_status_string(int(status)).decode()
+
+
+def kv_abi_version() -> int:
+    return int(_kv_abi_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != KV_OK:
+        raise KVError(status, where)
+
+
+def make_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16",
+              max_seqs: int = 0) -> kv_pool_desc:
+    return kv_pool_desc(int(num_blocks), BLOCK, int(num_kv_heads), int(head_dim), int(max_seqs),
+                        _DTYPES[dtype] if isinstance(dtype, str) else int(dtype))
+
+
+def kv_pool_required_bytes(desc: kv_pool_desc) -> int:
+    return int(_kv_pool_required_bytes(ctypes.byref(desc)))
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev_ptr(t: torch.Tensor | None, name: str, dtype=None, numel=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+_REGION_DTYPE = {KV_REGION_KQ: torch.uint8, KV_REGION_VQ: torch.uint8, KV_REGION_KS: torch.float16,
+                 KV_REGION_KM: torch.float16, KV_REGION_VS: torch.float16, KV_REGION_VM: torch.float16,
+                 KV_REGION_KTAIL: torch.bfloat16}
+
+
+class KVPool:
+    """A pool bound to a torch-allocated device blob (kv_pool_create).
+
+    Region views (``K``, ``V`` for fp32/bf16 pools; ``KQ``, ``KS``, ``KM``,
+    ``VQ``, ``VS``, ``VM``, ``KTAIL`` for INT4 pools) are torch views of the
+    blob with the shapes documented in include/kvcache.h."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16",
+                 max_seqs: int = 0, device="cuda", memory: torch.Tensor | None = None):
+        self.desc = make_desc(num_blocks, num_kv_heads, head_dim, dtype, max_seqs)
+        self.dtype = dtype
+        need = kv_pool_required_bytes(self.desc)
+        if need == 0:
+            raise ValueError("invalid pool descriptor")
+        if memory is None:
+            memory = torch.empty(need + 256, dtype=torch.uint8, device=device)
+        base = memory.data_ptr()
+        pad = (-base) % 256
+        self.memory = memory
+        self.blob = memory[pad:pad + need]
+        self.nbytes = need
+        h = _P()
+        _check(_kv_pool_create(ctypes.byref(self.desc), self.blob.data_ptr(), need, ctypes.byref(h)),
+               "kv_pool_create")
+        self.handle = h
+        nb, nkv, d = num_blocks, num_kv_heads, head_dim
+        shapes = {KV_REGION_K: (nb, nkv, BLOCK, d), KV_REGION_V: (nb, nkv, BLOCK, d),
+                  KV_REGION_KQ: (nb, nkv, BLOCK, d // 2), KV_REGION_VQ: (nb, nkv, BLOCK, d // 2),
+                  KV_REGION_KS: (nb, nkv, d), KV_REGION_KM: (nb, nkv, d),
+                  KV_REGION_VS: (nb, nkv, BLOCK), KV_REGION_VM: (nb, nkv, BLOCK),
+                  KV_REGION_KTAIL: (max_seqs, nkv, BLOCK, d)}
+        names = ["K", "V", "KQ", "KS", "KM", "VQ", "VS", "VM", "KTAIL"]
+        elem = {"f32": torch.float32, "bf16": torch.bfloat16}.get(dtype)
+        for r, nm in enumerate(names):
+            off, size = self.region(r)
+            if off is None:
+                setattr(self, nm, None)
+                continue
+            dt = _REGION_DTYPE.get(r, elem)
+            view = self.blob[off:off + size].view(dt).view(shapes[r])
+            setattr(self, nm, view)
+
+    def region(self, region: int):
+        off, size = _SZ(), _SZ()
+        st = _kv_pool_region(self.handle, int(region), ctypes.byref(off), ctypes.byref(size))
+        if st != KV_OK:
+            return None, None
+        return int(off.value), int(size.value)
+
+    def get_desc(self) -> kv_pool_desc:
+        d = kv_pool_desc()
+        _check(_kv_pool_get_desc(self.handle, ctypes.byref(d)), "kv_pool_get_desc")
+        return d
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            _kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _i32(t, name):
+    return _dev_ptr(t, name, torch.int32)
+
+
+def kv_append(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
+              seq_lens: torch.Tensor, seq_slots: torch.Tensor | None = None, stream=None) -> None:
+    d = pool.desc
+    B = int(seq_lens.numel())
+    want = torch.float32 if d.dtype == KV_F32 else torch.bfloat16
+    n = B * d.num_kv_heads * d.head_dim
+    st = _kv_append(pool.handle, _dev_ptr(k_new, "k_new", want, n), _dev_ptr(v_new, "v_new", want, n),
+                    _i32(block_tables, "block_tables"), int(block_tables.shape[1]), _i32(seq_lens, "seq_lens"),
+                    _i32(seq_slots, "seq_slots"), B, _stream(stream))
+    _check(st, "kv_append")
+
+
+def attn_opts(split_blocks: int = 0, kernel: int = 0, window: int = 0, events=None) -> kv_attn_opts:
+    o = kv_attn_opts(int(split_blocks), int(kernel), int(window), 0)
+    if events:
+        for i, e in enumerate(events[:3]):
+            o.events[i] = e
+    return o
+
+
+def paged_decode_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int, max_ctx: int,
+                                           opts: kv_attn_opts | None = None) -> int:
+    n = _paged_decode_attention_workspace_bytes(pool.handle, int(batch), int(num_q_heads), int(max_ctx),
+                                                ctypes.byref(opts) if opts is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise KVError(KV_ERR_INVALID_ARG, "paged_decode_attention_workspace_bytes")
+    return int(n)
+
+
+def paged_decode_attention(pool: KVPool, q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                           ctx_lens: torch.Tensor, scale: float, max_ctx: int,
+                           workspace: torch.Tensor | None = None, seq_slots: torch.Tensor | None = None,
+                           opts: kv_attn_opts | None = None, stream=None) -> None:
+    d = pool.desc
+    B, n_h, hd = q.shape
+    if hd != d.head_dim or tuple(out.shape) != (B, n_h, hd):
+        raise ValueError("q / out shape does not match the pool")
+    want = torch.float32 if d.dtype == KV_F32 else torch.bfloat16
+    ws_ptr = _dev_ptr(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _paged_decode_attention(pool.handle, _dev_ptr(q, "q", want), _dev_ptr(out, "out", torch.float32), n_h,
+                                 float(scale), _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                 _i32(ctx_lens, "ctx_lens"), _i32(seq_slots, "seq_slots"), B, int(max_ctx),
+                                 ws_ptr, ws_bytes, ctypes.byref(opts) if opts is not None else None,
+                                 _stream(stream))
+    _check(st, "paged_decode_attention")
+
+
+def kv_quantize_int4(dst: KVPool, src: KVPool, block_tables: torch.Tensor, lens: torch.Tensor,
+                     seq_slots: torch.Tensor | None = None, stream=None) -> None:
+    st = _kv_quantize_int4(dst.handle, src.handle, _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
+                           _i32(lens, "lens"), _i32(seq_slots, "seq_slots"), int(lens.numel()), _stream(stream))
+    _check(st, "kv_quantize_int4")
+
+
+def rope_rerotate(pool: KVPool, chunk_blocks: torch.Tensor, first_slot: int, num_tokens: int, delta: int,
+                  base: float = 10000.0, style: int = 0, stream=None) -> None:
+    st = _rope_rerotate(pool.handle, _i32(chunk_blocks, "chunk_blocks"), int(first_slot), int(num_tokens),
+                        int(delta), float(base), int(style), _stream(stream))
+    _check(st, "rope_rerotate")
+
+
+def kv_validate_tables(desc: kv_pool_desc, block_tables, lens, appending: bool = True):
+    """Host check of host copies (numpy int32 or CPU tensors). Returns
+    (status, first bad row or -1)."""
+    import numpy as np
+    tab = np.ascontiguousarray(np.asarray(block_tables), dtype=np.int32)
+    ln = np.ascontiguousarray(np.asarray(lens), dtype=np.int32)
+    bad = _I32(-1)
+    st = _kv_validate_tables(ctypes.byref(desc), tab.ctypes.data, int(tab.shape[1]), ln.ctypes.data,
+                             int(ln.shape[0]), int(bool(appending)), ctypes.byref(bad))
+    return int(st), int(bad.value)
+
+
+# raw entry points, for tests of the C ABI itself
+raw = {
+    "kv_pool_create": _kv_pool_create, "kv_pool_destroy": _kv_pool_destroy, "kv_pool_region": _kv_pool_region,
+    "kv_append": _kv_append, "paged_decode_attention": _paged_decode_attention,
+    "paged_decode_attention_workspace_bytes": _paged_decode_attention_workspace_bytes,
+    "kv_quantize_int4": _kv_quantize_int4, "rope_rerotate": _rope_rerotate,
+}

@@ -1,0 +1,377 @@
+// api.cpp -- the C ABI declared in include/kvcache.h: pool descriptors,
+// argument validation, workspace sizing and kernel dispatch. Host code only;
+// every computation on the hot path runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <set>
+#include <utility>
+
+#include "internal.h"
+
+using namespace kvc;
+
+struct kv_pool {
+    kv_pool_desc desc;
+    char *base;
+    size_t bytes;
+    size_t off[9];  // region offsets (SIZE_MAX if absent)
+    size_t len[9];  // region sizes
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kNone = (size_t)-1;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool desc_ok(const kv_pool_desc *d) {
+    if (!d) return false;
+    if (d->num_blocks < 1 || d->block_size != KV_BLOCK_TOKENS || d->num_kv_heads < 1) return false;
+    if (d->head_dim != 64 && d->head_dim != 128) return false;
+    if (d->dtype != KV_F32 && d->dtype != KV_BF16 && d->dtype != KV_INT4) return false;
+    if (d->dtype == KV_INT4 && d->max_seqs < 1) return false;
+    if (d->dtype != KV_INT4 && d->max_seqs < 0) return false;
+    return true;
+}
+
+// Region sizes of a descriptor (0 = region absent).
+void region_sizes(const kv_pool_desc *d, size_t len[9]) {
+    for (int i = 0; i < 9; ++i) len[i] = 0;
+    const size_t tok = (size_t)d->num_blocks * KV_BLOCK_TOKENS * d->num_kv_heads;  // token rows
+    if (d->dtype == KV_INT4) {
+        len[KV_REGION_KQ] = tok * d->head_dim / 2;
+        len[KV_REGION_VQ] = tok * d->head_dim / 2;
+        len[KV_REGION_KS] = (size_t)d->num_blocks * d->num_kv_heads * d->head_dim * 2;
+        len[KV_REGION_KM] = len[KV_REGION_KS];
+        len[KV_REGION_VS] = tok * 2;
+        len[KV_REGION_VM] = tok * 2;
+        len[KV_REGION_KTAIL] = (size_t)d->max_seqs * d->num_kv_heads * KV_BLOCK_TOKENS * d->head_dim * 2;
+    } else {
+        const size_t es = d->dtype == KV_F32 ? 4 : 2;
+        len[KV_REGION_K] = tok * d->head_dim * es;
+        len[KV_REGION_V] = len[KV_REGION_K];
+    }
+}
+
+size_t layout(const kv_pool_desc *d, size_t off[9], size_t len[9]) {
+    region_sizes(d, len);
+    size_t at = 0;
+    for (int i = 0; i < 9; ++i) {
+        if (len[i] == 0) {
+            off[i] = kNone;
+            continue;
+        }
+        off[i] = at;
+        at = align_up(at + len[i]);
+    }
+    return at;
+}
+
+PoolPtrs pool_ptrs(const kv_pool *p) {
+    auto at = [&](int r) -> char * { return p->off[r] == kNone ? nullptr : p->base + p->off[r]; };
+    PoolPtrs q;
+    q.k = at(KV_REGION_K);
+    q.v = at(KV_REGION_V);
+    q.kq = reinterpret_cast<uint8_t *>(at(KV_REGION_KQ));
+    q.vq = reinterpret_cast<uint8_t *>(at(KV_REGION_VQ));
+    q.ks = reinterpret_cast<uint16_t *>(at(KV_REGION_KS));
+    q.km = reinterpret_cast<uint16_t *>(at(KV_REGION_KM));
+    q.vs = reinterpret_cast<uint16_t *>(at(KV_REGION_VS));
+    q.vm = reinterpret_cast<uint16_t *>(at(KV_REGION_VM));
+    q.ktail = reinterpret_cast<uint16_t *>(at(KV_REGION_KTAIL));
+    return q;
+}
+
+kv_status hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Attention launch geometry for a call.
+struct AttnGeom {
+    int split_blocks;
+    int max_splits;
+    size_t ws_bytes;
+};
+
+bool attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx, const kv_attn_opts *opts,
+               AttnGeom *g) {
+    if (batch < 0 || n_h < 1 || max_ctx < 0) return false;
+    const int n_kv = pool->desc.num_kv_heads;
+    if (n_h % n_kv) return false;
+    const int window = opts ? opts->window : 0;
+    if (window < 0) return false;
+    int nblk = (max_ctx + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS;
+    if (window > 0) {
+        const int wb = (window + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS + 1;
+        if (wb < nblk) nblk = wb;
+    }
+    if (nblk < 1) nblk = 1;
+    int sb = opts ? opts->split_blocks : 0;
+    if (sb < 0) return false;
+    if (sb == 0) {
+        // Aim for about 16 workgroups per compute unit (256 CUs) over the
+        // grid when the (sequence, kv head) pairs alone cannot provide them;
+        // never split below 8 blocks (the merge then costs more than it saves).
+        const long pairs = (long)batch * n_kv;
+        const long target = 256L * 16;
+        long want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
+        if (want < 1) want = 1;
+        sb = (int)((nblk + want - 1) / want);
+        if (sb < 8) sb = 8;
+    }
+    if (sb > nblk) sb = nblk;
+    g->split_blocks = sb;
+    g->max_splits = (nblk + sb - 1) / sb;
+    if (g->max_splits <= 1) {
+        g->ws_bytes = 0;
+    } else {
+        const size_t rows = (size_t)batch * n_h * g->max_splits;
+        g->ws_bytes = align_up(rows * pool->desc.head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kv_status_string(kv_status s) {
+    switch (s) {
+        case KV_OK: return "ok";
+        case KV_ERR_INVALID_ARG: return "invalid argument";
+        case KV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KV_ERR_WORKSPACE: return "workspace missing or too small";
+        case KV_ERR_HIP: return "HIP launch or runtime error";
+        case KV_ERR_TABLE: return "block table or length out of range";
+        default: return "unknown status";
+    }
+}
+
+int32_t kv_abi_version(void) { return KV_ABI_VERSION; }
+
+size_t kv_pool_required_bytes(const kv_pool_desc *desc) {
+    if (!desc_ok(desc)) return 0;
+    size_t off[9], len[9];
+    return layout(desc, off, len);
+}
+
+kv_status kv_pool_create(const kv_pool_desc *desc, void *device_mem, size_t bytes, kv_pool_t *out) {
+    if (!out) return KV_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!desc_ok(desc)) {
+        if (desc && desc->block_size == KV_BLOCK_TOKENS && desc->num_blocks >= 1 && desc->num_kv_heads >= 1 &&
+            desc->head_dim > 0 && desc->head_dim != 64 && desc->head_dim != 128)
+            return KV_ERR_UNSUPPORTED;
+        return KV_ERR_INVALID_ARG;
+    }
+    if (!device_mem || ((uintptr_t)device_mem % kAlign) != 0) return KV_ERR_INVALID_ARG;
+    kv_pool *p = new (std::nothrow) kv_pool;
+    if (!p) return KV_ERR_INVALID_ARG;
+    p->desc = *desc;
+    p->base = static_cast<char *>(device_mem);
+    const size_t need = layout(desc, p->off, p->len);
+    if (bytes < need) {
+        delete p;
+        return KV_ERR_INVALID_ARG;
+    }
+    p->bytes = bytes;
+    *out = p;
+    return KV_OK;
+}
+
+kv_status kv_pool_destroy(kv_pool_t pool) {
+    if (!pool) return KV_ERR_INVALID_ARG;
+    delete pool;
+    return KV_OK;
+}
+
+kv_status kv_pool_region(kv_pool_t pool, int32_t region, size_t *offset, size_t *bytes) {
+    if (!pool || region < 0 || region > 8 || !offset || !bytes) return KV_ERR_INVALID_ARG;
+    if (pool->off[region] == kNone) return KV_ERR_INVALID_ARG;
+    *offset = pool->off[region];
+    *bytes = pool->len[region];
+    return KV_OK;
+}
+
+kv_status kv_pool_get_desc(kv_pool_t pool, kv_pool_desc *desc) {
+    if (!pool || !desc) return KV_ERR_INVALID_ARG;
+    *desc = pool->desc;
+    return KV_OK;
+}
+
+kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                    int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                    void *stream) {
+    if (!pool || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    if (!k_new || !v_new || !block_tables || !seq_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KV_ERR_INVALID_ARG;
+    AppendParams a;
+    a.pool = pool_ptrs(pool);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.seq_slots = pool->desc.dtype == KV_INT4 ? seq_slots : nullptr;
+    a.max_blocks = max_blocks;
+    a.batch = batch;
+    a.n_kv = pool->desc.num_kv_heads;
+    a.head_dim = pool->desc.head_dim;
+    a.num_blocks = pool->desc.num_blocks;
+    a.max_seqs = pool->desc.max_seqs;
+    return hip_status(launch_append(pool->desc.dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads, int32_t max_ctx,
+                                              const kv_attn_opts *opts) {
+    AttnGeom g;
+    if (!pool || !attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g)) return (size_t)-1;
+    return g.ws_bytes;
+}
+
+kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, float scale,
+                                 const int32_t *block_tables, int32_t max_blocks, const int32_t *ctx_lens,
+                                 const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace,
+                                 size_t ws_bytes, const kv_attn_opts *opts, void *stream) {
+    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
+    if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
+    if (opts && (opts->reserved != 0 || opts->kernel < 0 || opts->kernel > 2)) return KV_ERR_INVALID_ARG;
+    const int n_kv = pool->desc.num_kv_heads;
+    if (num_q_heads % n_kv) return KV_ERR_INVALID_ARG;
+    const int group = num_q_heads / n_kv;
+    if (group > kMaxGroup) return KV_ERR_UNSUPPORTED;
+    const int dtype = pool->desc.dtype;
+    int kernel = opts ? opts->kernel : 0;
+    if (kernel == 2 && dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
+    if (kernel == 0) kernel = (dtype == KV_BF16 && group >= 2) ? 2 : 1;
+    AttnGeom g;
+    if (!attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g)) return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    if (!q || !out || !block_tables || !ctx_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return KV_ERR_INVALID_ARG;
+    if (g.ws_bytes > 0 && (!workspace || ws_bytes < g.ws_bytes || !aligned16(workspace))) return KV_ERR_WORKSPACE;
+
+    AttnParams a;
+    a.pool = pool_ptrs(pool);
+    a.q = q;
+    a.out = out;
+    a.tables = block_tables;
+    a.ctx_lens = ctx_lens;
+    a.seq_slots = dtype == KV_INT4 ? seq_slots : nullptr;
+    const size_t rows = (size_t)batch * num_q_heads * g.max_splits;
+    a.ws_o = g.ws_bytes ? static_cast<float *>(workspace) : nullptr;
+    a.ws_ml = g.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                     align_up(rows * pool->desc.head_dim * sizeof(float)))
+                         : nullptr;
+    a.max_blocks = max_blocks;
+    a.batch = batch;
+    a.n_h = num_q_heads;
+    a.n_kv = n_kv;
+    a.group = group;
+    a.head_dim = pool->desc.head_dim;
+    a.num_blocks = pool->desc.num_blocks;
+    a.max_seqs = pool->desc.max_seqs;
+    a.split_blocks = g.split_blocks;
+    a.max_splits = g.max_splits;
+    a.window = opts ? opts->window : 0;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *const *ev = opts ? opts->events : nullptr;
+    if (ev && ev[0] && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess) return KV_ERR_HIP;
+    hipError_t e = launch_attention(dtype, kernel, a, s);
+    if (e != hipSuccess) return KV_ERR_HIP;
+    if (ev && ev[1] && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess) return KV_ERR_HIP;
+    e = launch_merge(a, s);
+    if (e != hipSuccess) return KV_ERR_HIP;
+    if (ev && ev[2] && hipEventRecord(static_cast<hipEvent_t>(ev[2]), s) != hipSuccess) return KV_ERR_HIP;
+    return KV_OK;
+}
+
+kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables, int32_t max_blocks,
+                           const int32_t *lens, const int32_t *seq_slots, int32_t batch, void *stream) {
+    if (!dst || !src || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (dst->desc.dtype != KV_INT4 || src->desc.dtype != KV_BF16) return KV_ERR_INVALID_ARG;
+    if (dst->desc.num_blocks != src->desc.num_blocks || dst->desc.num_kv_heads != src->desc.num_kv_heads ||
+        dst->desc.head_dim != src->desc.head_dim)
+        return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    if (!block_tables || !lens) return KV_ERR_INVALID_ARG;
+    QuantParams a;
+    a.dst = pool_ptrs(dst);
+    a.src = pool_ptrs(src);
+    a.tables = block_tables;
+    a.lens = lens;
+    a.seq_slots = seq_slots;
+    a.max_blocks = max_blocks;
+    a.batch = batch;
+    a.n_kv = dst->desc.num_kv_heads;
+    a.head_dim = dst->desc.head_dim;
+    a.num_blocks = dst->desc.num_blocks;
+    a.max_seqs = dst->desc.max_seqs;
+    return hip_status(launch_quantize_int4(a, static_cast<hipStream_t>(stream)));
+}
+
+kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t first_slot, int32_t num_tokens,
+                        int32_t delta, float base, int32_t style, void *stream) {
+    if (!pool || first_slot < 0 || num_tokens < 0 || (style != 0 && style != 1)) return KV_ERR_INVALID_ARG;
+    if (!(base > 0.0f) || !std::isfinite(base)) return KV_ERR_INVALID_ARG;
+    if (pool->desc.dtype == KV_INT4) return KV_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return KV_OK;
+    if (!chunk_blocks) return KV_ERR_INVALID_ARG;
+    RopeParams a;
+    a.k = pool_ptrs(pool).k;
+    a.chunk_blocks = chunk_blocks;
+    a.first_slot = first_slot;
+    a.num_tokens = num_tokens;
+    a.n_kv = pool->desc.num_kv_heads;
+    a.head_dim = pool->desc.head_dim;
+    a.num_blocks = pool->desc.num_blocks;
+    a.style = style;
+    // angles in fp64: pair i turns by delta * base^(-2i / head_dim)
+    for (int i = 0; i < 64; ++i) {
+        a.cos_t[i] = 1.0f;
+        a.sin_t[i] = 0.0f;
+    }
+    for (int i = 0; i < a.head_dim / 2; ++i) {
+        const double theta = std::pow((double)base, -(2.0 * i) / a.head_dim);
+        const double phi = (double)delta * theta;
+        a.cos_t[i] = (float)std::cos(phi);
+        a.sin_t[i] = (float)std::sin(phi);
+    }
+    return hip_status(launch_rope(pool->desc.dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
+                             const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row) {
+    if (bad_row) *bad_row = -1;
+    if (!desc_ok(desc) || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (batch > 0 && (!block_tables || !lens)) return KV_ERR_INVALID_ARG;
+    std::set<std::pair<int, int>> slots;
+    for (int b = 0; b < batch; ++b) {
+        const long n = (long)lens[b] + (appending ? 1 : 0);
+        bool ok = lens[b] >= 0 && n <= (long)max_blocks * KV_BLOCK_TOKENS;
+        const int nb = ok ? (int)((n + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS) : 0;
+        for (int j = 0; ok && j < nb; ++j) {
+            const int32_t p = block_tables[(size_t)b * max_blocks + j];
+            if (p < 0 || p >= desc->num_blocks) ok = false;
+        }
+        if (ok && appending) {
+            const int32_t p = block_tables[(size_t)b * max_blocks + lens[b] / KV_BLOCK_TOKENS];
+            ok = slots.insert({p, lens[b] % KV_BLOCK_TOKENS}).second;
+        }
+        if (!ok) {
+            if (bad_row) *bad_row = b;
+            return KV_ERR_TABLE;
+        }
+    }
+    return KV_OK;
+}
+
+}  // extern "C"

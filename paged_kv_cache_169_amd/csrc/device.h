@@ -1,0 +1,72 @@
+// device.h -- small device helpers used by several kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// bf16 <-> fp32. bf16 is the upper half of an fp32, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// fp32 <-> IEEE binary16 bits. The hardware conversion rounds to nearest even
+// (default MODE) and keeps fp16 subnormals.
+__device__ __forceinline__ uint16_t f_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// KVQuant INT4 scale and min of a group whose min/max are known: s = (max -
+// min) / 15 in fp32 (correctly rounded), both stored as fp16; a zero min or
+// max of either sign is taken as +0, so the result does not depend on which
+// zero a reduction returned.
+struct Q4Params {
+    uint16_t s16, m16;
+    float s, m;  // the stored values, widened
+};
+__device__ __forceinline__ Q4Params q4_params(float mn, float mx) {
+    if (mn == 0.0f) mn = 0.0f;
+    if (mx == 0.0f) mx = 0.0f;
+    float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+    Q4Params p;
+    p.s16 = f_to_f16_bits(s32);
+    p.m16 = f_to_f16_bits(mn);
+    p.s = f16_bits_to_f(p.s16);
+    p.m = f16_bits_to_f(p.m16);
+    return p;
+}
+
+// code = clamp(round((x - m) / s), 0, 15), rounding half away from zero, from
+// the stored (fp16) m and s; every code is 0 when s is 0.
+__device__ __forceinline__ uint32_t q4_code(float x, const Q4Params &p) {
+    if (p.s == 0.0f) return 0u;
+    float v = __fdiv_rn(__fsub_rn(x, p.m), p.s);
+    if (v <= 0.0f) return 0u;
+    if (v >= 15.0f) return 15u;
+    float t = truncf(v);  // v > 0, so v - t is exact
+    return (uint32_t)t + (__fsub_rn(v, t) >= 0.5f ? 1u : 0u);
+}
+
+}  // namespace kvc

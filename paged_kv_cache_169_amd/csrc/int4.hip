@@ -1,0 +1,136 @@
+// int4.hip -- KVQuant INT4 coding: append to an INT4 pool and bulk coding of
+// bf16 pool contents.
+//
+// Quantizer ["KV Cache는 왜 LLM 서빙의 핵심인가", section "KVQuant: 마지막 4배"]:
+// s = (max - min) / 15 per group, one 4-bit code per value. K is grouped per
+// channel (over the 16 tokens of a block), V per token (over the head_dim
+// channels). Codes are clamp(round((x - min) / s), 0, 15) computed in fp32 from
+// the stored fp16 s and min, rounding half away from zero.
+//
+// Lane mapping (one wave64 per (sequence, kv head) or (sequence, block, kv
+// head)): lane l owns channel pair (2l, 2l+1), i.e. one 32-bit word of a bf16
+// row and one byte of a code row; for head_dim 64 lanes 32..63 idle. A V row's
+// min/max is a wave reduction; a K block's per-channel min/max stays in the
+// lane (its 16 tokens are 16 loads of the same word).
+//
+// Built with -ffp-contract=off: the codes must match a plain fp32 evaluation.
+#include "device.h"
+#include "internal.h"
+
+namespace kvc {
+
+// Code one bf16 token row (one word per lane) per token into code row `dst`
+// (one byte per lane) and the fp16 scale/min at *s16, *m16.
+__device__ __forceinline__ void code_v_row(uint32_t w, bool act, uint8_t *dst, uint16_t *s16, uint16_t *m16,
+                                           int lane) {
+    const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+    float mn = act ? fminf(x0, x1) : INFINITY;
+    float mx = act ? fmaxf(x0, x1) : -INFINITY;
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    const Q4Params q = q4_params(mn, mx);
+    if (act) dst[lane] = (uint8_t)(q4_code(x0, q) | (q4_code(x1, q) << 4));
+    if (lane == 0) {
+        *s16 = q.s16;
+        *m16 = q.m16;
+    }
+}
+
+// Code the K of one full block per channel. w[t] is this lane's word of token
+// row t. Writes the 16 code rows (one byte per lane each) and the per-channel
+// fp16 scale/min of channels 2*lane, 2*lane+1.
+__device__ __forceinline__ void code_k_block(const uint32_t (&w)[kBlock], bool act, uint8_t *kq_tile,
+                                             uint16_t *ks_row, uint16_t *km_row, int lane, int half_dim) {
+    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) {
+        const float a = bf16_lo(w[t]), b = bf16_hi(w[t]);
+        mn0 = fminf(mn0, a);
+        mx0 = fmaxf(mx0, a);
+        mn1 = fminf(mn1, b);
+        mx1 = fmaxf(mx1, b);
+    }
+    const Q4Params q0 = q4_params(mn0, mx0), q1 = q4_params(mn1, mx1);
+    if (!act) return;
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t)
+        kq_tile[t * half_dim + lane] = (uint8_t)(q4_code(bf16_lo(w[t]), q0) | (q4_code(bf16_hi(w[t]), q1) << 4));
+    reinterpret_cast<uint32_t *>(ks_row)[lane] = (uint32_t)q0.s16 | ((uint32_t)q1.s16 << 16);
+    reinterpret_cast<uint32_t *>(km_row)[lane] = (uint32_t)q0.m16 | ((uint32_t)q1.m16 << 16);
+}
+
+// Append to an INT4 pool. Grid (n_kv, batch), one wave each.
+__global__ __launch_bounds__(64) void append_int4_kernel(AppendParams p) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int D = p.head_dim, hd = D / 2;
+    const bool act = lane < hd;
+    const int L = p.seq_lens[b];
+    if (L < 0 || L >= p.max_blocks * kBlock) return;
+    const int pid = p.tables[(size_t)b * p.max_blocks + L / kBlock];
+    if (pid < 0 || pid >= p.num_blocks) return;
+    const int slot = p.seq_slots ? p.seq_slots[b] : b;
+    if (slot < 0 || slot >= p.max_seqs) return;
+    const int t = L % kBlock;
+    const size_t src = ((size_t)b * p.n_kv + h) * hd;  // in words
+    const uint32_t vw = act ? reinterpret_cast<const uint32_t *>(p.v_new)[src + lane] : 0u;
+    const uint32_t kw = act ? reinterpret_cast<const uint32_t *>(p.k_new)[src + lane] : 0u;
+
+    const size_t tile = (size_t)pid * p.n_kv + h;   // (block, head) tile index
+    const size_t row = tile * kBlock + t;            // token row index
+    code_v_row(vw, act, p.pool.vq + row * hd, p.pool.vs + row, p.pool.vm + row, lane);
+
+    uint32_t *tail = reinterpret_cast<uint32_t *>(p.pool.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;
+    if (act) tail[(size_t)t * hd + lane] = kw;
+    if (t == kBlock - 1) {
+        uint32_t w[kBlock];
+#pragma unroll
+        for (int tt = 0; tt < kBlock - 1; ++tt) w[tt] = act ? tail[(size_t)tt * hd + lane] : 0u;
+        w[kBlock - 1] = kw;
+        code_k_block(w, act, p.pool.kq + tile * kBlock * hd, p.pool.ks + tile * D, p.pool.km + tile * D, lane, hd);
+    }
+}
+
+// Bulk coding. Grid (max_blocks, n_kv, batch), one wave per (block, head, seq).
+__global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int D = p.head_dim, hd = D / 2;
+    const bool act = lane < hd;
+    const int n = p.lens[b];
+    if (n < 0 || n > p.max_blocks * kBlock || j * kBlock >= n) return;
+    const int pid = p.tables[(size_t)b * p.max_blocks + j];
+    if (pid < 0 || pid >= p.num_blocks) return;
+    const int r = min(kBlock, n - j * kBlock);
+    const size_t tile = (size_t)pid * p.n_kv + h;
+    const uint32_t *ks = reinterpret_cast<const uint32_t *>(p.src.k) + tile * kBlock * hd;
+    const uint32_t *vs = reinterpret_cast<const uint32_t *>(p.src.v) + tile * kBlock * hd;
+    for (int t = 0; t < r; ++t) {
+        const uint32_t vw = act ? vs[(size_t)t * hd + lane] : 0u;
+        const size_t row = tile * kBlock + t;
+        code_v_row(vw, act, p.dst.vq + row * hd, p.dst.vs + row, p.dst.vm + row, lane);
+    }
+    if (r == kBlock) {
+        uint32_t w[kBlock];
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) w[t] = act ? ks[(size_t)t * hd + lane] : 0u;
+        code_k_block(w, act, p.dst.kq + tile * kBlock * hd, p.dst.ks + tile * D, p.dst.km + tile * D, lane, hd);
+    } else {
+        const int slot = p.seq_slots ? p.seq_slots[b] : b;
+        if (slot < 0 || slot >= p.max_seqs || !act) return;
+        uint32_t *tail = reinterpret_cast<uint32_t *>(p.dst.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;
+        for (int t = 0; t < r; ++t) tail[(size_t)t * hd + lane] = ks[(size_t)t * hd + lane];
+    }
+}
+
+hipError_t launch_append_int4(const AppendParams &p, hipStream_t s) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(append_int4_kernel, dim3(p.n_kv, p.batch), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s) {
+    if (p.batch == 0 || p.max_blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_int4_kernel, dim3(p.max_blocks, p.n_kv, p.batch), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,98 @@
+// internal.h -- parameter records shared by the host API (api.cpp) and the
+// kernel launchers (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvcache.h"
+
+namespace kvc {
+
+constexpr int kBlock = KV_BLOCK_TOKENS;  // tokens per physical block
+constexpr int kMaxGroup = 16;            // largest query group (n_h / n_kv)
+
+// Device pointers of every region of a pool (null where the dtype has none).
+struct PoolPtrs {
+    void *k, *v;                 // f32 / bf16
+    uint8_t *kq, *vq;            // int4 codes
+    uint16_t *ks, *km, *vs, *vm; // fp16 scale / min
+    uint16_t *ktail;             // bf16 K tail
+};
+
+// Everything a kernel needs about one attention call. Passed by value.
+struct AttnParams {
+    PoolPtrs pool;
+    const void *q;
+    float *out;
+    const int32_t *tables;
+    const int32_t *ctx_lens;
+    const int32_t *seq_slots;
+    float *ws_o;   // [batch][n_h][max_splits][head_dim]
+    float *ws_ml;  // [batch][n_h][max_splits][2]  (running max in log2 units, sum)
+    int32_t max_blocks, batch, n_h, n_kv, group, head_dim, num_blocks, max_seqs;
+    int32_t split_blocks, max_splits, window;
+    float scale_log2;  // scale * log2(e): scores are kept in log2 units
+};
+
+struct AppendParams {
+    PoolPtrs pool;
+    const void *k_new, *v_new;
+    const int32_t *tables, *seq_lens, *seq_slots;
+    int32_t max_blocks, batch, n_kv, head_dim, num_blocks, max_seqs;
+};
+
+struct QuantParams {
+    PoolPtrs dst, src;
+    const int32_t *tables, *lens, *seq_slots;
+    int32_t max_blocks, batch, n_kv, head_dim, num_blocks, max_seqs;
+};
+
+struct RopeParams {
+    void *k;
+    const int32_t *chunk_blocks;
+    int32_t first_slot, num_tokens, n_kv, head_dim, num_blocks, style;
+    float cos_t[64], sin_t[64];  // per pair i < head_dim / 2
+};
+
+// Kernel launchers (defined in the .hip files). Each returns the launch status.
+hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
+hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);
+hipError_t launch_merge(const AttnParams &p, hipStream_t s);
+hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
+hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
+
+// The attended block range of one sequence, shared by the split kernels and
+// the merge kernel so that both agree on the number of splits.
+struct SeqRange {
+    int n;        // attended length (after validation)
+    int lo, hi;   // attended tokens [lo, hi)
+    int blk_lo;   // first attended block
+    int nblk;     // attended blocks
+    int nsplit;   // splits (>= 1)
+    bool bad;     // length outside [0, max_blocks * 16], or more splits than
+                  // the grid and workspace were sized for (ctx above max_ctx)
+};
+
+__host__ __device__ inline SeqRange seq_range(int n, int max_blocks, int window, int split_blocks,
+                                              int max_splits) {
+    SeqRange r;
+    r.bad = n < 0 || n > max_blocks * kBlock;
+    if (!r.bad) {
+        const int lo = (window > 0 && n > window) ? n - window : 0;
+        const int nb = (n + kBlock - 1) / kBlock - lo / kBlock;
+        r.bad = nb > (long)split_blocks * max_splits;
+    }
+    if (r.bad) n = 0;
+    r.n = n;
+    r.hi = n;
+    r.lo = (window > 0 && n > window) ? n - window : 0;
+    r.blk_lo = r.lo / kBlock;
+    int blk_hi = (n + kBlock - 1) / kBlock;
+    r.nblk = blk_hi - r.blk_lo;
+    r.nsplit = r.nblk == 0 ? 1 : (r.nblk + split_blocks - 1) / split_blocks;
+    return r;
+}
+
+}  // namespace kvc
