@@ -72,6 +72,7 @@ def main():
                     choices=["tiny", "llama3_8b", "llama2_70b", "kvquant_int4", "long_shared"])
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
+    ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
     args = ap.parse_args()
 
@@ -120,7 +121,7 @@ def main():
         for p in pools:
             kv.rope_rerotate(p, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
     max_ctx = int(ctx.max().item())
-    opts = kv.attn_opts(split_blocks=args.split, kernel=args.kernel)
+    opts = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule)
     ws_bytes = kv.paged_decode_attention_workspace_bytes(pools[0], B, n_h, max_ctx, opts)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, n_h, D), dtype=torch.float32, device=dev)
@@ -138,7 +139,7 @@ def main():
             kv.kv_append(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
         o = opts
         if events is not None:
-            o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, events=events)
+            o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule, events=events)
         kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
 
     for i in range(args.warmup):
@@ -226,6 +227,7 @@ def main():
         "config": {"workload": name, "batch": B, "ctx": "U[512,4096]+1" if "uniform" in str(wl.WORKLOADS[name]["lens"])
                    else int(ctx.max().item()), "tokens_per_step": tokens_per_step, "n_h": n_h, "n_kv": n_kv,
                    "head_dim": D, "block_size": 16, "kernel": args.kernel, "split_blocks": args.split,
+                   "schedule": args.schedule,
                    "accumulate": "f32", "pool_replicas": reps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,

@@ -102,14 +102,26 @@ enum {
     KV_REGION_KTAIL = 8
 };
 
+/* How the attended tiles are spread over workgroups. */
+enum {
+    KV_SCHED_AUTO = 0,     /* balanced for the MFMA kernel, fixed splits otherwise */
+    KV_SCHED_SPLIT = 1,    /* one workgroup per (split of split_blocks blocks, kv
+                              head, sequence), then a merge of the splits         */
+    KV_SCHED_BALANCED = 2  /* a persistent grid; every workgroup takes an equal
+                              share of all (sequence, kv head, block) tiles, then
+                              a merge of the cut pairs (MFMA kernel only)          */
+};
+
 /* Options of paged_decode_attention; pass NULL for the defaults (all zero). */
 typedef struct {
-    int32_t split_blocks; /* blocks per context split; 0 = chosen by the library   */
+    int32_t split_blocks; /* KV_SCHED_SPLIT: blocks per split; 0 = chosen by the
+                             library. A nonzero value selects KV_SCHED_SPLIT
+                             when schedule is KV_SCHED_AUTO.                      */
     int32_t kernel;       /* 0 = chosen by the library, 1 = VALU dot products,
-                             2 = MFMA tiles (bf16 and INT4 pools only)              */
+                             2 = MFMA tiles (bf16 pools)                          */
     int32_t window;       /* > 0: attend only the last `window` tokens of each
                              sequence [KVSYS, "제한된 어텐션 윈도우 크기"]; 0 = all  */
-    int32_t reserved;     /* must be 0                                            */
+    int32_t schedule;     /* KV_SCHED_*                                           */
     void *events[3];      /* optional hipEvent_t handles recorded on the stream
                              before the split kernel, after it, and after the
                              merge kernel (for timing); NULL entries are skipped  */
@@ -180,7 +192,8 @@ size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int
  *   ctx_lens      device int32 [batch]: tokens to attend (the cache length
  *                 after this step's append); 0 gives an output of 0
  *   seq_slots     KV_INT4: K tail row of each sequence (NULL = row b)
- *   max_ctx       host upper bound of ctx_lens (sizes the grid/workspace)
+ *   max_ctx       host upper bound of ctx_lens (sizes the grid/workspace); a
+ *                 sequence whose ctx_lens exceeds it may get a NaN output
  *   workspace     device buffer of at least ws_bytes >=
  *                 paged_decode_attention_workspace_bytes(...) bytes
  * KV_INT4 pools are dequantized on the fly: full blocks from their codes,

@@ -24,6 +24,7 @@ BLOCK = 16
 (KV_REGION_K, KV_REGION_V, KV_REGION_KQ, KV_REGION_KS, KV_REGION_KM, KV_REGION_VQ, KV_REGION_VS,
  KV_REGION_VM, KV_REGION_KTAIL) = range(9)
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+KV_SCHED_AUTO, KV_SCHED_SPLIT, KV_SCHED_BALANCED = 0, 1, 2
 
 _DTYPES = {"f32": KV_F32, "bf16": KV_BF16, "int4": KV_INT4}
 
@@ -42,7 +43,7 @@ class kv_pool_desc(ctypes.Structure):
 
 class kv_attn_opts(ctypes.Structure):
     _fields_ = [("split_blocks", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("events", ctypes.c_void_p * 3)]
 
 
@@ -216,8 +217,9 @@ def kv_append(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, block_tabl
     _check(st, "kv_append")
 
 
-def attn_opts(split_blocks: int = 0, kernel: int = 0, window: int = 0, events=None) -> kv_attn_opts:
-    o = kv_attn_opts(int(split_blocks), int(kernel), int(window), 0)
+def attn_opts(split_blocks: int = 0, kernel: int = 0, window: int = 0, schedule: int = 0,
+              events=None) -> kv_attn_opts:
+    o = kv_attn_opts(int(split_blocks), int(kernel), int(window), int(schedule))
     if events:
         for i, e in enumerate(events[:3]):
             o.events[i] = e

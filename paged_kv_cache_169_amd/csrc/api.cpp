@@ -93,26 +93,62 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Attention launch geometry for a call.
 struct AttnGeom {
+    int kernel;        // 1 VALU, 2 MFMA
+    int schedule;      // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int split_blocks;
     int max_splits;
-    size_t ws_bytes;
+    int n_wg;          // balanced: persistent grid
+    size_t ws_bytes;   // total workspace
+    size_t off_ml;     // offset of the (m, l) partials
+    size_t off_prefix; // balanced: offset of the block prefix sums
 };
 
-bool attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx, const kv_attn_opts *opts,
-               AttnGeom *g) {
-    if (batch < 0 || n_h < 1 || max_ctx < 0) return false;
+// Largest batch of the balanced schedule (its block prefix sums live in LDS).
+constexpr int kMaxBalancedBatch = 8192;
+
+kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx, const kv_attn_opts *opts,
+                    AttnGeom *g) {
+    if (batch < 0 || n_h < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
     const int n_kv = pool->desc.num_kv_heads;
-    if (n_h % n_kv) return false;
+    const int dtype = pool->desc.dtype;
+    if (n_h % n_kv) return KV_ERR_INVALID_ARG;
+    const int group = n_h / n_kv;
+    if (group > kMaxGroup) return KV_ERR_UNSUPPORTED;
+    if (opts && (opts->kernel < 0 || opts->kernel > 2 || opts->schedule < 0 || opts->schedule > 2 ||
+                 opts->window < 0 || opts->split_blocks < 0))
+        return KV_ERR_INVALID_ARG;
+    int kernel = opts ? opts->kernel : 0;
+    if (kernel == 2 && dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
+    if (kernel == 0) kernel = dtype == KV_BF16 ? 2 : 1;
+    int sb = opts ? opts->split_blocks : 0;
+    int sched = opts ? opts->schedule : 0;
+    if (sched == KV_SCHED_AUTO)
+        sched = (kernel == 2 && sb == 0 && batch <= kMaxBalancedBatch) ? KV_SCHED_BALANCED : KV_SCHED_SPLIT;
+    if (sched == KV_SCHED_BALANCED && (kernel != 2 || batch > kMaxBalancedBatch)) return KV_ERR_UNSUPPORTED;
     const int window = opts ? opts->window : 0;
-    if (window < 0) return false;
     int nblk = (max_ctx + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS;
     if (window > 0) {
         const int wb = (window + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS + 1;
         if (wb < nblk) nblk = wb;
     }
     if (nblk < 1) nblk = 1;
-    int sb = opts ? opts->split_blocks : 0;
-    if (sb < 0) return false;
+    const size_t D = pool->desc.head_dim;
+    g->kernel = kernel;
+    g->schedule = sched;
+    g->n_wg = 0;
+    g->off_prefix = 0;
+    if (sched == KV_SCHED_BALANCED) {
+        // every attended block of every sequence is one tile; a sequence
+        // longer than max_ctx does not fit the promise and reads as bad
+        g->split_blocks = nblk;
+        g->max_splits = 1;
+        g->n_wg = balanced_grid((int)D, batch);
+        const size_t rows = (size_t)g->n_wg * 2 * group;
+        g->off_ml = align_up(rows * D * sizeof(float));
+        g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));
+        g->ws_bytes = g->off_prefix + align_up(((size_t)batch + 1) * sizeof(int32_t));
+        return KV_OK;
+    }
     if (sb == 0) {
         // Aim for about 16 workgroups per compute unit (256 CUs) over the
         // grid when the (sequence, kv head) pairs alone cannot provide them;
@@ -129,11 +165,13 @@ bool attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx,
     g->max_splits = (nblk + sb - 1) / sb;
     if (g->max_splits <= 1) {
         g->ws_bytes = 0;
+        g->off_ml = 0;
     } else {
         const size_t rows = (size_t)batch * n_h * g->max_splits;
-        g->ws_bytes = align_up(rows * pool->desc.head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+        g->off_ml = align_up(rows * D * sizeof(float));
+        g->ws_bytes = g->off_ml + align_up(rows * 2 * sizeof(float));
     }
-    return true;
+    return KV_OK;
 }
 
 }  // namespace
@@ -230,7 +268,7 @@ kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new, const 
 size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads, int32_t max_ctx,
                                               const kv_attn_opts *opts) {
     AttnGeom g;
-    if (!pool || !attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g)) return (size_t)-1;
+    if (!pool || attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g) != KV_OK) return (size_t)-1;
     return g.ws_bytes;
 }
 
@@ -241,22 +279,15 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
     if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
     if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
-    if (opts && (opts->reserved != 0 || opts->kernel < 0 || opts->kernel > 2)) return KV_ERR_INVALID_ARG;
-    const int n_kv = pool->desc.num_kv_heads;
-    if (num_q_heads % n_kv) return KV_ERR_INVALID_ARG;
-    const int group = num_q_heads / n_kv;
-    if (group > kMaxGroup) return KV_ERR_UNSUPPORTED;
-    const int dtype = pool->desc.dtype;
-    int kernel = opts ? opts->kernel : 0;
-    if (kernel == 2 && dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
-    if (kernel == 0) kernel = (dtype == KV_BF16 && group >= 2) ? 2 : 1;
     AttnGeom g;
-    if (!attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g)) return KV_ERR_INVALID_ARG;
+    const kv_status gs = attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g);
+    if (gs != KV_OK) return gs;
     if (batch == 0) return KV_OK;
     if (!q || !out || !block_tables || !ctx_lens) return KV_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out)) return KV_ERR_INVALID_ARG;
     if (g.ws_bytes > 0 && (!workspace || ws_bytes < g.ws_bytes || !aligned16(workspace))) return KV_ERR_WORKSPACE;
 
+    const int dtype = pool->desc.dtype;
     AttnParams a;
     a.pool = pool_ptrs(pool);
     a.q = q;
@@ -264,28 +295,29 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
     a.tables = block_tables;
     a.ctx_lens = ctx_lens;
     a.seq_slots = dtype == KV_INT4 ? seq_slots : nullptr;
-    const size_t rows = (size_t)batch * num_q_heads * g.max_splits;
-    a.ws_o = g.ws_bytes ? static_cast<float *>(workspace) : nullptr;
-    a.ws_ml = g.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                                     align_up(rows * pool->desc.head_dim * sizeof(float)))
-                         : nullptr;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_o = g.ws_bytes ? reinterpret_cast<float *>(ws) : nullptr;
+    a.ws_ml = g.ws_bytes ? reinterpret_cast<float *>(ws + g.off_ml) : nullptr;
+    a.ws_prefix = g.off_prefix ? reinterpret_cast<int32_t *>(ws + g.off_prefix) : nullptr;
     a.max_blocks = max_blocks;
     a.batch = batch;
     a.n_h = num_q_heads;
-    a.n_kv = n_kv;
-    a.group = group;
+    a.n_kv = pool->desc.num_kv_heads;
+    a.group = num_q_heads / a.n_kv;
     a.head_dim = pool->desc.head_dim;
     a.num_blocks = pool->desc.num_blocks;
     a.max_seqs = pool->desc.max_seqs;
     a.split_blocks = g.split_blocks;
     a.max_splits = g.max_splits;
     a.window = opts ? opts->window : 0;
+    a.schedule = g.schedule;
+    a.n_wg = g.n_wg;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *const *ev = opts ? opts->events : nullptr;
     if (ev && ev[0] && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess) return KV_ERR_HIP;
-    hipError_t e = launch_attention(dtype, kernel, a, s);
+    hipError_t e = launch_attention(dtype, g.kernel, a, s);
     if (e != hipSuccess) return KV_ERR_HIP;
     if (ev && ev[1] && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess) return KV_ERR_HIP;
     e = launch_merge(a, s);

@@ -306,18 +306,130 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams p) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
 
+// One (block, kv head) tile in MFMA operand layout.
 template <int D>
-__global__ __launch_bounds__(64) void attn_mfma_bf16_kernel(AttnParams p) {
-    constexpr int KS = D / 32;  // k-steps of S^T = K . Q^T (16x16x32)
-    constexpr int MS = D / 16;  // channel tiles of O^T (16x16x16)
-    constexpr int VC = D / 16;  // value channels per lane per token row
-    const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    SplitWork w;
-    if (!split_work(p, b, split, w)) return;
-    const int g = p.group;
-    bool bad = w.r.bad;
+struct MfmaTile {
+    bf16x8_t k[D / 32];          // A operand of S^T = K . Q^T: token n16, channels s*32 + 8G .. +8
+    uint32_t v[4][D / 32];       // rows 4G + i, channels n16 * (D/16) .. + D/16 (bf16 pairs)
+};
 
+// Block ids of a split, 64 at a time: lane i holds the id of block jbase + i.
+__device__ __forceinline__ int load_block_ids(const AttnParams &p, int b, int jbase, int j1, int lane) {
+    const int j = jbase + lane;
+    return j < j1 ? p.tables[(size_t)b * p.max_blocks + j] : 0;
+}
+
+template <int D>
+__device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh, int n16, int G, MfmaTile<D> &T) {
+    constexpr int KS = D / 32, VC = D / 16;
+    const uint16_t *tile = reinterpret_cast<const uint16_t *>(p.pool.k) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        T.k[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(tile + n16 * D + s * 32 + 8 * G));
+    const uint16_t *vt = reinterpret_cast<const uint16_t *>(p.pool.v) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t *src = vt + (4 * G + i) * D + n16 * VC;
+        if constexpr (VC == 8) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            T.v[i][0] = v.x;
+            T.v[i][1] = v.y;
+            T.v[i][2] = v.z;
+            T.v[i][3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src);
+            T.v[i][0] = v.x;
+            T.v[i][1] = v.y;
+        }
+    }
+}
+
+// Online-softmax state of one lane: head n16, the lane's 4 token rows.
+template <int D>
+struct MfmaState {
+    f32x4_t o[D / 16];
+    float m, l;
+};
+
+template <int D>
+__device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D> &T, const bf16x8_t (&qB)[D / 32],
+                                           int tlo, int thi, int G, MfmaState<D> &st) {
+    constexpr int KS = D / 32, MS = D / 16, VC = D / 16;
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s], qB[s], sc, 0, 0, 0);
+    const bool partial = tlo > 0 || thi < kBlock;  // uniform
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tt = 4 * G + r;
+        sv[r] = (!partial || (tt >= tlo && tt < thi)) ? sc[r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(st.m, mx);
+    if (!__all(mn == st.m)) {
+        // the running max moved for some head: rescale (rare after the first blocks)
+        const float alpha = exp2f(st.m - mn);
+        st.l *= alpha;
+#pragma unroll
+        for (int m = 0; m < MS; ++m) st.o[m] *= alpha;
+        st.m = mn;
+    }
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        pr[r] = exp2f(sv[r] - st.m);
+        st.l += pr[r];
+    }
+    // P^T as B operand, split into bf16 hi and lo parts
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        hi[r] = f_to_bf16(pr[r]);
+        lo[r] = f_to_bf16(pr[r] - bf16_to_f((uint16_t)hi[r]));
+    }
+    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
+    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])));
+    uint32_t vr[4][VC / 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < VC / 2; ++k) vr[i][k] = T.v[i][k];
+    if (partial) {
+        // slots outside [tlo, thi) may hold anything (even NaN): zero their rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tt = 4 * G + i;
+            if (tt < tlo || tt >= thi) {
+#pragma unroll
+                for (int k = 0; k < VC / 2; ++k) vr[i][k] = 0u;
+            }
+        }
+    }
+    // V^T as A operand for channel tile m: lane (G, n16) holds channel
+    // n16*VC + m of tokens 4G .. 4G+3.
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int wi = m >> 1, sh = (m & 1) * 16;
+        const uint32_t e0 = vr[0][wi] >> sh, e1 = vr[1][wi] >> sh, e2 = vr[2][wi] >> sh, e3 = vr[3][wi] >> sh;
+        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
+    }
+}
+
+// One lane's run of the online softmax over blocks [j0, j1) of sequence b,
+// kv head kvh. On return st.l is still the lane's partial sum (the caller
+// adds the 4 token quads).
+template <int D>
+__device__ __forceinline__ void mfma_segment(const AttnParams &p, int b, int kvh, const SeqRange &r, int j0, int j1,
+                                             int lane, MfmaState<D> &st, bool &bad) {
+    constexpr int KS = D / 32, MS = D / 16;
+    const int n16 = lane & 15, G = lane >> 4;
+    const int g = p.group;
     // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of head n16.
     bf16x8_t qB[KS];
     const int head = kvh * g + n16;
@@ -329,115 +441,169 @@ __global__ __launch_bounds__(64) void attn_mfma_bf16_kernel(AttnParams p) {
                                                  ((size_t)b * p.n_h + head) * D + s * 32 + 8 * G);
         qB[s] = __builtin_bit_cast(bf16x8_t, v);
     }
-    f32x4_t o[MS];
 #pragma unroll
-    for (int m = 0; m < MS; ++m) o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int m = 0; m < MS; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
 
-    const uint16_t *Kb = reinterpret_cast<const uint16_t *>(p.pool.k);
-    const uint16_t *Vb = reinterpret_cast<const uint16_t *>(p.pool.v);
-    for (int j = w.j0; j < w.j1; ++j) {
-        int pid = p.tables[(size_t)b * p.max_blocks + j];
+    // Block ids come from a VGPR (one per lane, 64 blocks at a time); the
+    // tile of block j+1 is in flight while block j is computed.
+    int ids = load_block_ids(p, b, j0, j1, lane);
+    int ids_base = j0;
+    auto pid_of = [&](int j) {
+        if (j - ids_base >= 64) {
+            ids_base += 64;
+            ids = load_block_ids(p, b, ids_base, j1, lane);
+        }
+        int pid = __builtin_amdgcn_readlane(ids, j - ids_base);
         if (pid < 0 || pid >= p.num_blocks) {
             bad = true;
             pid = 0;
         }
-        const size_t tile = ((size_t)pid * p.n_kv + kvh) * kBlock * D;
-        // K as A operand: lane (G, n16) holds token n16, channels s*32 + 8G .. +8
-        bf16x8_t kA[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            kA[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Kb + tile + n16 * D + s * 32 + 8 * G));
-        // V rows 4G + i, channels n16*VC .. +VC
-        uint32_t vr[4][VC / 2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint16_t *src = Vb + tile + (4 * G + i) * D + n16 * VC;
-            if (VC == 8) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(src);
-                vr[i][0] = v.x;
-                vr[i][1] = v.y;
-                vr[i][VC / 2 - 2] = v.z;
-                vr[i][VC / 2 - 1] = v.w;
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                vr[i][0] = v.x;
-                vr[i][VC / 2 - 1] = v.y;
-            }
-        }
-        f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[s], qB[s], sc, 0, 0, 0);
-
+        return pid;
+    };
+    auto bounds = [&](int j, int &tlo, int &thi) {
         const int tok0 = j * kBlock;
-        const int tlo = max(w.r.lo - tok0, 0), thi = min(w.r.hi - tok0, kBlock);
-        float sv[4];
-        float mx = -INFINITY;
+        tlo = max(r.lo - tok0, 0);
+        thi = min(r.hi - tok0, kBlock);
+    };
+    MfmaTile<D> A, B;
+    if (j0 < j1) fetch_tile<D>(p, pid_of(j0), kvh, n16, G, A);
+    for (int j = j0; j < j1; j += 2) {
+        int tlo, thi;
+        if (j + 1 < j1) fetch_tile<D>(p, pid_of(j + 1), kvh, n16, G, B);
+        bounds(j, tlo, thi);
+        mfma_block<D>(p, A, qB, tlo, thi, G, st);
+        if (j + 1 >= j1) break;
+        if (j + 2 < j1) fetch_tile<D>(p, pid_of(j + 2), kvh, n16, G, A);
+        bounds(j + 1, tlo, thi);
+        mfma_block<D>(p, B, qB, tlo, thi, G, st);
+    }
+}
+
+// lane (G, n16) holds channel (4G + r) * (D/16) + m of head n16 in o[m][r]:
+// a contiguous run of D/4 channels starting at G * D/4.
+template <int D>
+__device__ __forceinline__ void mfma_gather_run(const MfmaState<D> &st, float (&res)[D / 4]) {
+    constexpr int MS = D / 16, VC = D / 16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tt = 4 * G + r;
-            sv[r] = (tt >= tlo && tt < thi) ? sc[r] * p.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[r]);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 0; m < MS; ++m) res[r * VC + m] = st.o[m][r];
+}
+
+// Fixed-split schedule: grid (max_splits, n_kv, batch).
+template <int D>
+__global__ __launch_bounds__(64) void attn_mfma_bf16_kernel(AttnParams p) {
+    const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    SplitWork w;
+    if (!split_work(p, b, split, w)) return;
+    bool bad = w.r.bad;
+    MfmaState<D> st;
+    mfma_segment<D>(p, b, kvh, w.r, w.j0, w.j1, lane, st, bad);
+    float l = st.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (n16 < p.group) {
+        float res[D / 4];
+        mfma_gather_run<D>(st, res);
+        store_result(p, b, kvh * p.group + n16, split, w.r.nsplit, G * (D / 4), res, D / 4, st.m, l, bad, G == 0);
+    }
+}
+
+// Balanced schedule. The attended (sequence, kv head, block) tiles are
+// numbered in sequence-major, kv-head, block order; workgroup w of the
+// persistent grid takes tiles [w * per, (w+1) * per), per = ceil(total /
+// grid). A workgroup walks its range one (sequence, kv head) segment at a
+// time; a segment that covers its whole pair writes the output directly.
+// Only a workgroup's first and last segments can be partial, so partials go
+// to slot 0 (first) or 1 (last) of the workgroup's two workspace slots and
+// attn_merge_balanced_kernel combines them. Workgroup 0 also stores the block
+// prefix sums for the merge.
+__device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, int lane) {
+    // pre[b] = attended blocks of sequences < b, in LDS; returns pre[batch]
+    int carry = 0;
+    if (lane == 0) pre[0] = 0;
+    for (int base = 0; base < p.batch; base += 64) {
+        const int b = base + lane;
+        int nb = 0;
+        if (b < p.batch) {
+            const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+            nb = r.nblk;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - mn);
-        m_run = mn;
-        float pr[4];
-        float psum = 0.0f;
+        // inclusive wave scan
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pr[r] = exp2f(sv[r] - mn);
-            psum += pr[r];
+        for (int o = 1; o < 64; o <<= 1) {
+            const int x = __shfl_up(nb, o);
+            if (lane >= o) nb += x;
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int m = 0; m < MS; ++m) o[m] *= alpha;
-        // P^T as B operand (hi and lo bf16 parts)
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            hi[r] = f_to_bf16(pr[r]);
-            lo[r] = f_to_bf16(pr[r] - bf16_to_f((uint16_t)hi[r]));
+        if (b < p.batch) pre[b + 1] = carry + nb;
+        carry += __shfl(nb, 63);
+    }
+    __syncthreads();
+    return carry;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_mfma_bf16_balanced_kernel(AttnParams p) {
+    extern __shared__ int pre[];  // [batch + 1]
+    const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
+    const int wg = blockIdx.x;
+    const int nblk_total = balanced_prefix(p, pre, lane);
+    if (wg == 0)
+        for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
+    const long total = (long)nblk_total * p.n_kv;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long s = (long)wg * per;
+    const long e = min(total, s + per);
+    for (long t = s; t < e;) {
+        // sequence holding tile t: largest b with n_kv * pre[b] <= t
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((long)pre[mid] * p.n_kv <= t)
+                lo = mid;
+            else
+                hi = mid - 1;
         }
-        const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
-        const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])));
-        // rows of slots outside [tlo, thi) may hold anything (even NaN): zero them
-        if (tlo > 0 || thi < kBlock) {
+        const int b = lo;
+        const int nb = pre[b + 1] - pre[b];
+        const long pair0 = (long)pre[b] * p.n_kv;
+        const int kvh = (int)((t - pair0) / nb);
+        const int jr = (int)(t - pair0 - (long)kvh * nb);
+        const long seg_end = min(e, pair0 + (long)(kvh + 1) * nb);
+        const int cnt = (int)(seg_end - t);
+        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+        bool bad = r.bad;
+        MfmaState<D> st;
+        mfma_segment<D>(p, b, kvh, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad);
+        float l = st.l;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (n16 < p.group) {
+            float res[D / 4];
+            mfma_gather_run<D>(st, res);
+            const int head = kvh * p.group + n16;
+            const float nan = __uint_as_float(0x7fc00000u);
+            if (jr == 0 && cnt == nb) {
+                float *dst = p.out + ((size_t)b * p.n_h + head) * D + G * (D / 4);
+                const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tt = 4 * G + i;
-                if (tt < tlo || tt >= thi) {
+                for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
+            } else {
+                const int slot = t == s ? 0 : 1;
+                const size_t row = ((size_t)wg * 2 + slot) * p.group + n16;
+                float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
-                    for (int k = 0; k < VC / 2; ++k) vr[i][k] = 0u;
+                for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c];
+                if (G == 0) {
+                    p.ws_ml[row * 2] = st.m;
+                    p.ws_ml[row * 2 + 1] = bad ? nan : l;
                 }
             }
         }
-        // V^T as A operand for channel tile m: lane (G, n16) holds channel
-        // n16*VC + m of tokens 4G .. 4G+3.
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int wi = m >> 1, sh = (m & 1) * 16;
-            const uint32_t e0 = vr[0][wi] >> sh, e1 = vr[1][wi] >> sh, e2 = vr[2][wi] >> sh, e3 = vr[3][wi] >> sh;
-            const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)));
-            o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, o[m], 0, 0, 0);
-            o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, o[m], 0, 0, 0);
-        }
-    }
-
-    float l = l_run;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (n16 < g) {
-        // lane (G, n16) holds channel (4G + r) * VC + m in o[m][r]: a contiguous
-        // run of 4 * VC channels starting at 4G * VC
-        float res[4 * VC];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int m = 0; m < MS; ++m) res[r * VC + m] = o[m][r];
-        store_result(p, b, head, split, w.r.nsplit, 4 * G * VC, res, 4 * VC, m_run, l, bad, G == 0);
+        t = seg_end;
     }
 }
 
@@ -464,6 +630,47 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
         for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
     }
     float *dst = p.out + ((size_t)b * p.n_h + head) * D + lane * cv;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
+}
+
+// Merge for the balanced schedule: one wave per (head, sequence). Finds the
+// workgroups whose tile ranges cut this (sequence, kv head) pair and combines
+// their partials; writes 0 (or NaN for a bad sequence) when the pair has no
+// attended block.
+__global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
+    const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int D = p.head_dim, cv = D / 64;
+    const int kvh = head / p.group, n16 = head % p.group;
+    const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
+    float *dst = p.out + ((size_t)b * p.n_h + head) * D + lane * cv;
+    if (nb == 0) {
+        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+        const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
+        for (int c = 0; c < cv; ++c) dst[c] = v;
+        return;
+    }
+    const long total = (long)p.ws_prefix[p.batch] * p.n_kv;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long start = (long)p.ws_prefix[b] * p.n_kv + (long)kvh * nb;
+    const long end = start + nb;
+    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
+    if (w0 == w1) return;  // complete inside one workgroup: already written
+    float M = -INFINITY;
+    for (int w = w0; w <= w1; ++w) {
+        const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
+        M = fmaxf(M, p.ws_ml[(((size_t)w * 2 + slot) * p.group + n16) * 2]);
+    }
+    float acc[2] = {0.0f, 0.0f};
+    float L = 0.0f;
+    for (int w = w0; w <= w1; ++w) {
+        const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
+        const size_t row = ((size_t)w * 2 + slot) * p.group + n16;
+        const float wgt = exp2f(p.ws_ml[row * 2] - M);
+        L += wgt * p.ws_ml[row * 2 + 1];
+        const float *o = p.ws_o + row * D + lane * cv;
+        for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+    }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
 }
@@ -496,6 +703,14 @@ static hipError_t launch_valu(const AttnParams &p, dim3 grid, hipStream_t s) {
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s) {
     const dim3 grid(p.max_splits, p.n_kv, p.batch);
     if (p.batch == 0) return hipSuccess;
+    if (p.schedule == KV_SCHED_BALANCED) {
+        const size_t lds = (size_t)(p.batch + 1) * sizeof(int);
+        if (p.head_dim == 64)
+            hipLaunchKernelGGL(attn_mfma_bf16_balanced_kernel<64>, dim3(p.n_wg), dim3(64), lds, s, p);
+        else
+            hipLaunchKernelGGL(attn_mfma_bf16_balanced_kernel<128>, dim3(p.n_wg), dim3(64), lds, s, p);
+        return hipGetLastError();
+    }
     if (dtype == KV_F32) return launch_valu<KIND_F32>(p, grid, s);
     if (dtype == KV_INT4) return launch_valu<KIND_INT4>(p, grid, s);
     if (kernel == 2) {
@@ -508,8 +723,28 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
     return launch_valu<KIND_BF16>(p, grid, s);
 }
 
+int balanced_grid(int head_dim, int batch) {
+    // compute units x resident workgroups per compute unit; 256 x 2 when the
+    // runtime cannot tell (no device: only the size of a workspace is asked)
+    int dev = 0, cus = 0, per_cu = 0;
+    const size_t lds = (size_t)(batch + 1) * sizeof(int);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256 * 2;
+    hipError_t e = head_dim == 64
+                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_bf16_balanced_kernel<64>, 64, lds)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_bf16_balanced_kernel<128>, 64, lds);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 2;
+    return cus * per_cu;
+}
+
 hipError_t launch_merge(const AttnParams &p, hipStream_t s) {
-    if (p.batch == 0 || p.max_splits <= 1) return hipSuccess;
+    if (p.batch == 0) return hipSuccess;
+    if (p.schedule == KV_SCHED_BALANCED) {
+        hipLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, p);
+        return hipGetLastError();
+    }
+    if (p.max_splits <= 1) return hipSuccess;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, p);
     return hipGetLastError();
 }

@@ -33,6 +33,9 @@ struct AttnParams {
     float *ws_ml;  // [batch][n_h][max_splits][2]  (running max in log2 units, sum)
     int32_t max_blocks, batch, n_h, n_kv, group, head_dim, num_blocks, max_seqs;
     int32_t split_blocks, max_splits, window;
+    int32_t schedule;  // KV_SCHED_SPLIT or KV_SCHED_BALANCED
+    int32_t n_wg;      // balanced: persistent grid size
+    int32_t *ws_prefix;  // balanced: [batch + 1] attended blocks before each sequence
     float scale_log2;  // scale * log2(e): scores are kept in log2 units
 };
 
@@ -60,6 +63,8 @@ struct RopeParams {
 hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);
 hipError_t launch_merge(const AttnParams &p, hipStream_t s);
+// Persistent grid of the balanced schedule: resident workgroups per device.
+int balanced_grid(int head_dim, int batch);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 

@@ -131,8 +131,13 @@ def test_argument_errors_before_launch(kv):
     st, h32 = make_handle(kv, kv.make_desc(16, 2, 64, "f32"))
     o2 = kv.attn_opts(kernel=2)
     assert P(h32, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o2), None) == kv.KV_ERR_UNSUPPORTED
-    bad = kv.kv_attn_opts(0, 0, 0, 1)
+    bad = kv.kv_attn_opts(0, 0, 0, 3)                  # unknown schedule
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(bad), None) == kv.KV_ERR_INVALID_ARG
+    # the balanced schedule needs the MFMA kernel (bf16 pools)
+    o3 = kv.attn_opts(schedule=kv.KV_SCHED_BALANCED)
+    assert P(h32, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o3), None) == kv.KV_ERR_UNSUPPORTED
+    # balanced schedule without its workspace
+    assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o3), None) == kv.KV_ERR_WORKSPACE
     R = kv.raw["rope_rerotate"]
     assert R(h, FAKE, 0, 10, 5, 10000.0, 2, None) == kv.KV_ERR_INVALID_ARG
     assert R(h, FAKE, 0, 10, 5, -1.0, 0, None) == kv.KV_ERR_INVALID_ARG
@@ -158,6 +163,10 @@ def test_workspace_sizes(kv):
     o_all = kv.attn_opts(split_blocks=4)
     assert W(h, 2, 4, 50, ctypes.byref(o_all)) == 0
     assert W(h, 2, 3, 50, None) == ctypes.c_size_t(-1).value
+    ob = kv.attn_opts(schedule=kv.KV_SCHED_BALANCED)
+    n_wg = 256 * 2                                 # without a device: 256 CUs x 2
+    rows = n_wg * 2 * 2
+    assert W(h, 3, 4, 50, ctypes.byref(ob)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256 + 256
     ow = kv.attn_opts(split_blocks=1, window=16)   # a 16-token window spans at most 2 blocks
     rows = 2 * 4 * 2
     assert W(h, 2, 4, 500, ctypes.byref(ow)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256

@@ -155,12 +155,12 @@ def test_attention_parity(shape, kernel, split):
     assert max_err(out, ref) <= TOL
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_permutation_and_repeat_are_bit_identical(kernel):
+@pytest.mark.parametrize("kernel,split", [(1, 2), (2, 2), (2, 0)])
+def test_permutation_and_repeat_are_bit_identical(kernel, split):
     c = wl.make_case(300, 4, [70, 15, 128, 99], 16, 4, 128, "bf16", num_blocks=40, append=False, device=DEV)
     pool = new_pool(c)
-    a = gpu_attention(pool, c, kernel=kernel, split_blocks=2)
-    b = gpu_attention(pool, c, kernel=kernel, split_blocks=2)
+    a = gpu_attention(pool, c, kernel=kernel, split_blocks=split)
+    b = gpu_attention(pool, c, kernel=kernel, split_blocks=split)
     assert np.all(np.isfinite(a)) and np.array_equal(a, b)
     perm = torch.randperm(c.num_blocks, generator=torch.Generator().manual_seed(5)).to(DEV)
     pool2 = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
@@ -168,25 +168,25 @@ def test_permutation_and_repeat_are_bit_identical(kernel):
     pool2.V[perm.long()] = c.V
     tab2 = torch.where(c.tables >= 0, perm[c.tables.clamp(min=0).long()].to(torch.int32), c.tables)
     c2 = wl.Case(**{**c.__dict__, "tables": tab2.contiguous()})
-    moved = gpu_attention(pool2, c2, kernel=kernel, split_blocks=2)
+    moved = gpu_attention(pool2, c2, kernel=kernel, split_blocks=split)
     assert np.array_equal(a, moved)
 
 
 @pytest.mark.parametrize("window", [1, 5, 16, 17, 100, 1000])
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_window(window, kernel):
+@pytest.mark.parametrize("kernel,split", [(1, 2), (2, 2), (2, 0)])
+def test_window(window, kernel, split):
     c = wl.make_case(400, 5, [0, 9, 40, 130, 333], 8, 2, 128, "bf16", device=DEV)
     pool = new_pool(c)
     kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens)
-    out = gpu_attention(pool, c, kernel=kernel, window=window, split_blocks=2)
+    out = gpu_attention(pool, c, kernel=kernel, window=window, split_blocks=split)
     K, V = oracle_step(c)
     ref = orc.attention(K, V, bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale,
                         window=window)
     assert max_err(out, ref) <= TOL
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_empty_context_and_bad_metadata(kernel):
+@pytest.mark.parametrize("kernel,split", [(1, 1), (2, 1), (2, 0)])
+def test_empty_context_and_bad_metadata(kernel, split):
     c = wl.make_case(500, 4, [0, 20, 40, 60], 8, 2, 128, "bf16", append=False, device=DEV)
     pool = new_pool(c)
     tab = c.tables.clone()
@@ -195,7 +195,7 @@ def test_empty_context_and_bad_metadata(kernel):
     ctx = c.ctx_lens.clone()
     ctx[3] = 10_000                         # seq 3 claims more tokens than its table holds
     c2 = wl.Case(**{**c.__dict__, "tables": tab.contiguous()})
-    out = gpu_attention(pool, c2, kernel=kernel, split_blocks=1, ctx=ctx, max_ctx=60)
+    out = gpu_attention(pool, c2, kernel=kernel, split_blocks=split, ctx=ctx, max_ctx=60)
     assert np.all(out[0] == 0.0)
     assert np.all(np.isnan(out[2])) and np.all(np.isnan(out[3]))
     ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
@@ -215,6 +215,21 @@ def test_error_codes_on_device_call():
     f32q = c.q.float()
     with pytest.raises(ValueError):
         kv.paged_decode_attention(pool, f32q, out, c.tables, c.ctx_lens, c.scale, 21)
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_schedules_agree(window):
+    """Balanced and fixed-split schedules cut the context differently; both
+    stay within the bound of the oracle."""
+    lens = [int(x) for x in torch.randint(0, 900, (37,), generator=torch.Generator().manual_seed(3))]
+    c = wl.make_case(901, 37, lens, 32, 8, 128, "bf16", device=DEV)
+    pool = new_pool(c)
+    kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens)
+    K, V = oracle_step(c)
+    ref = orc.attention(K, V, bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale, window=window)
+    for split in (0, 1, 5, 64):
+        out = gpu_attention(pool, c, kernel=2, split_blocks=split, window=window)
+        assert max_err(out, ref) <= TOL, split
 
 
 # ---------------------------------------------------------------------------
