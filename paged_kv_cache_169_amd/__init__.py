@@ -16,7 +16,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvcache.so")
+# KVCACHE_LIB may name another build of the library (same ABI)
+LIB_PATH = os.environ.get("KVCACHE_LIB", os.path.join(_PKG, "libkvcache.so"))
 
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP, KV_ERR_TABLE = 0, -1, -2, -3, -4, -5
 KV_F32, KV_BF16, KV_INT4 = 0, 1, 2

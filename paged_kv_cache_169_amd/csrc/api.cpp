@@ -117,9 +117,11 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
     if (opts && (opts->kernel < 0 || opts->kernel > 2 || opts->schedule < 0 || opts->schedule > 2 ||
                  opts->window < 0 || opts->split_blocks < 0))
         return KV_ERR_INVALID_ARG;
+    // MFMA kernels: bf16 pools (head_dim 64, 128) and INT4 pools (head_dim 128)
+    const bool mfma_ok = dtype == KV_BF16 || (dtype == KV_INT4 && pool->desc.head_dim == 128);
     int kernel = opts ? opts->kernel : 0;
-    if (kernel == 2 && dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
-    if (kernel == 0) kernel = dtype == KV_BF16 ? 2 : 1;
+    if (kernel == 2 && !mfma_ok) return KV_ERR_UNSUPPORTED;
+    if (kernel == 0) kernel = mfma_ok ? 2 : 1;
     int sb = opts ? opts->split_blocks : 0;
     int sched = opts ? opts->schedule : 0;
     if (sched == KV_SCHED_AUTO)
@@ -142,7 +144,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
         // longer than max_ctx does not fit the promise and reads as bad
         g->split_blocks = nblk;
         g->max_splits = 1;
-        g->n_wg = balanced_grid((int)D, batch);
+        g->n_wg = balanced_grid(dtype, (int)D, batch);
         const size_t rows = (size_t)g->n_wg * 2 * group;
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));

@@ -64,7 +64,7 @@ hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);
 hipError_t launch_merge(const AttnParams &p, hipStream_t s);
 // Persistent grid of the balanced schedule: resident workgroups per device.
-int balanced_grid(int head_dim, int batch);
+int balanced_grid(int dtype, int head_dim, int batch);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 

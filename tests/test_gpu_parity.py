@@ -371,3 +371,24 @@ def test_int4_full_size_workload():
     ref = orc.attention(Kd, Vd, bits(c.q)[rows], tab[rows], c.ctx_lens.cpu().numpy()[rows], c.scale)
     assert np.all(np.isfinite(out))
     assert max_err(out[rows], ref) <= TOL
+
+
+@pytest.mark.parametrize("kernel,split", [(1, 0), (2, 0), (2, 1), (2, 3)])
+@pytest.mark.parametrize("window", [0, 40])
+def test_int4_attention_kernels(kernel, split, window):
+    """INT4 attention (VALU and MFMA, both schedules) against the oracle on
+    the same dequantized values; lengths cover empty, partial and full blocks."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 400]
+    c = int4_case(820, lens, n_h=32, n_kv=8, d=128)
+    slots = torch.arange(len(lens) - 1, -1, -1, dtype=torch.int32, device=DEV)
+    src, dst, img = int4_pools(c, len(lens))
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens, slots)
+    kv.kv_append(dst, c.k_new, c.v_new, c.tables, c.seq_lens, slots)
+    tab, lens_np, sl = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy(), slots.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens_np, sl)
+    orc.q4_append(img, bits(c.k_new), bits(c.v_new), tab, lens_np, sl)
+    out = gpu_attention(dst, c, kernel=kernel, split_blocks=split, window=window, seq_slots=slots)
+    Kd, Vd = orc.q4_dequant(img, tab, c.ctx_lens.cpu().numpy(), sl)
+    ref = orc.attention(Kd, Vd, bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale, window=window)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref) <= TOL
