@@ -535,30 +535,23 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 
 struct Q4Tile {
     uint4 kc;        // full block: K codes of token n16, channels 32G .. 32G+31
-    uint4 kx[8];     // full block: fp16 K scale [0..3] and min [4..7] of those
-                     // channels; partial block: bf16 tail row n16 in [0..3]
+    uint2 ksm;       // full block: this lane's 8 bytes of the block's fp16 K
+                     // scales (lanes 0-31) and mins (lanes 32-63); staged in LDS
     uint32_t vc[4];  // V codes of tokens 4G+i, channels 8 n16 .. 8 n16 + 7
     uint2 vs, vm;    // fp16 V scale / min of tokens 4G .. 4G+3
 };
 
-__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int n16, int G, bool full, int slot,
+__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int lane, int n16, int G, bool full,
                                          Q4Tile &T) {
     const size_t tile = (size_t)pid * p.n_kv + kvh;
     if (full) {
         T.kc = __builtin_bit_cast(uint4, stream_load16(p.pool.kq + (tile * kBlock + n16) * 64 + 16 * G));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            T.kx[i] = __builtin_bit_cast(uint4, stream_load16(p.pool.ks + tile * 128 + 32 * G + 8 * i));
-            T.kx[4 + i] = __builtin_bit_cast(uint4, stream_load16(p.pool.km + tile * 128 + 32 * G + 8 * i));
-        }
+        const uint16_t *sm = lane < 32 ? p.pool.ks + tile * 128 + 4 * lane : p.pool.km + tile * 128 + 4 * (lane - 32);
+        const u32x2_t v = stream_load8(sm);
+        T.ksm = make_uint2(v[0], v[1]);
     } else {
         T.kc = make_uint4(0, 0, 0, 0);
-        const uint16_t *row = p.pool.ktail + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            T.kx[i] = *reinterpret_cast<const uint4 *>(row + 8 * i);
-            T.kx[4 + i] = make_uint4(0, 0, 0, 0);
-        }
+        T.ksm = make_uint2(0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -583,16 +576,25 @@ __device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f((uint
 __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f((uint16_t)(w >> 16)); }
 
 __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const float (&qf)[32], bool full,
-                                         int tlo, int thi, int G, MfmaState<128> &st) {
+                                         const uint16_t *tail_row, int tlo, int thi, int lane, int G,
+                                         uint2 *lds_sm, MfmaState<128> &st) {
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
+        // the block's 128 scales then 128 mins (fp16) through LDS: each lane
+        // reads back those of its channels 32G .. 32G+31
+        __syncthreads();
+        lds_sm[lane] = T.ksm;
+        __syncthreads();
+        const uint4 *s4 = reinterpret_cast<const uint4 *>(lds_sm) + 4 * G;       // scales of 32G..
+        const uint4 *m4 = reinterpret_cast<const uint4 *>(lds_sm) + 16 + 4 * G;  // mins of 32G..
         const uint32_t kcw[4] = {T.kc.x, T.kc.y, T.kc.z, T.kc.w};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bf16x8_t a = q4_codes_bf16(kcw[s]);
-            const uint32_t sv[4] = {T.kx[s].x, T.kx[s].y, T.kx[s].z, T.kx[s].w};
-            const uint32_t mv[4] = {T.kx[4 + s].x, T.kx[4 + s].y, T.kx[4 + s].z, T.kx[4 + s].w};
+            const uint4 sq = s4[s], mq = m4[s];
+            const uint32_t sv[4] = {sq.x, sq.y, sq.z, sq.w};
+            const uint32_t mv[4] = {mq.x, mq.y, mq.z, mq.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -609,13 +611,15 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         corr += __shfl_xor(corr, 16);
         corr += __shfl_xor(corr, 32);
     } else {
+        // partial last block of the sequence: bf16 K from the tail row
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             uint32_t qb[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)  // q is bf16-exact: its bf16 is the top half
                 qb[k] = (__float_as_uint(qf[8 * s + 2 * k]) >> 16) | (__float_as_uint(qf[8 * s + 2 * k + 1]) & 0xffff0000u);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.kx[s]),
+            const uint4 kt = *reinterpret_cast<const uint4 *>(tail_row + 8 * s);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kt),
                                                          __builtin_bit_cast(bf16x8_t, make_uint4(qb[0], qb[1], qb[2], qb[3])), sc, 0, 0, 0);
         }
     }
@@ -720,22 +724,24 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         return pid;
     };
     auto is_full = [&](int j) { return (j + 1) * kBlock <= r.n; };
+    __shared__ uint2 lds_sm[64];  // one block's fp16 K scales and mins
+    const uint16_t *tail_row = p.pool.ktail + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
     auto bounds = [&](int j, int &tlo, int &thi) {
         const int tok0 = j * kBlock;
         tlo = max(r.lo - tok0, 0);
         thi = min(r.hi - tok0, kBlock);
     };
     Q4Tile A, B;
-    if (j0 < j1) q4_fetch(p, pid_of(j0), kvh, n16, G, is_full(j0), slot, A);
+    if (j0 < j1) q4_fetch(p, pid_of(j0), kvh, lane, n16, G, is_full(j0), A);
     for (int j = j0; j < j1; j += 2) {
         int tlo, thi;
-        if (j + 1 < j1) q4_fetch(p, pid_of(j + 1), kvh, n16, G, is_full(j + 1), slot, B);
+        if (j + 1 < j1) q4_fetch(p, pid_of(j + 1), kvh, lane, n16, G, is_full(j + 1), B);
         bounds(j, tlo, thi);
-        q4_block(p, A, qf, is_full(j), tlo, thi, G, st);
+        q4_block(p, A, qf, is_full(j), tail_row, tlo, thi, lane, G, lds_sm, st);
         if (j + 1 >= j1) break;
-        if (j + 2 < j1) q4_fetch(p, pid_of(j + 2), kvh, n16, G, is_full(j + 2), slot, A);
+        if (j + 2 < j1) q4_fetch(p, pid_of(j + 2), kvh, lane, n16, G, is_full(j + 2), A);
         bounds(j + 1, tlo, thi);
-        q4_block(p, B, qf, is_full(j + 1), tlo, thi, G, st);
+        q4_block(p, B, qf, is_full(j + 1), tail_row, tlo, thi, lane, G, lds_sm, st);
     }
 }
 
@@ -749,8 +755,12 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
+// Two resident waves per SIMD: the register budget the kernels are written to
+// (no spills; the INT4 path would otherwise take 1 wave per SIMD).
+#define KV_MFMA_WAVES __attribute__((amdgpu_waves_per_eu(2)))
+
 template <int D, bool Q4>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnParams p) {
+__global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     SplitWork w;
@@ -804,7 +814,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
 }
 
 template <int D, bool Q4>
-__global__ __launch_bounds__(64) void attn_mfma_balanced_kernel(AttnParams p) {
+__global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1]
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
