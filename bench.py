@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
     ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "quantize", "rope", "copy", "offload"],
+                    help="decode: the decode step (default); the others time one secondary kernel")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,6 +117,8 @@ def main():
     import workloads as wl
 
     dev = torch.device("cuda:0")
+    if args.op != "decode":
+        return bench_op(args, torch, kv, wl, dev)
     name = args.workload
     t_setup = time.time()
     c = wl.workload(name, device=dev, poison=False)
@@ -267,6 +271,84 @@ def main():
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+
+
+def bench_op(args, torch, kv, wl, dev):
+    """Time one secondary kernel on its natural workload; one JSON line.
+
+    append    kv_append of one token per sequence, 8B-shaped decode layer
+    quantize  kv_quantize_int4 of the INT4 workload's bf16 cache
+    rope      rope_rerotate of the long workload's 4096-token chunk
+    copy      kv_copy_blocks of 4096 blocks of the 8B-shaped pool
+    offload   kv_gather_blocks of 2048 blocks into pinned host memory, then
+              kv_scatter_blocks back (host link bandwidth)
+    All rates are algorithmic bytes (every byte read or written once) per
+    second of the kernel's average duration (HIP events, launch stream)."""
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+    name = {"append": "llama3_8b", "quantize": "kvquant_int4", "rope": "long_shared", "copy": "llama3_8b",
+            "offload": "llama3_8b"}[args.op]
+    c = wl.workload(name, device=dev, poison=False)
+    D, n_kv, B = c.d, c.n_kv, c.batch
+    pool = kv.KVPool(c.num_blocks, n_kv, D, c.dtype, device=dev)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    extra = {}
+    if args.op == "append":
+        fn = lambda: kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
+        nbytes = 2 * (B * n_kv * 2 * D * 2)
+    elif args.op == "quantize":
+        dst = kv.KVPool(c.num_blocks, n_kv, D, "int4", max_seqs=B, device=dev)
+        fn = lambda: kv.kv_quantize_int4(dst, pool, c.tables, c.seq_lens, stream=stream)
+        toks = int(c.seq_lens.sum().item())
+        nbytes = toks * n_kv * (2 * D * 2) + toks * n_kv * 164
+    elif args.op == "rope":
+        fn = lambda: kv.rope_rerotate(pool, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0, stream=stream)
+        nbytes = 2 * c.chunk_tokens * n_kv * D * 2
+    elif args.op == "copy":
+        g = torch.Generator(device="cpu").manual_seed(5)
+        perm = torch.randperm(c.num_blocks, generator=g)[:8192].to(torch.int32).to(dev)
+        src, dst = perm[:4096].contiguous(), perm[4096:].contiguous()
+        fn = lambda: kv.kv_copy_blocks(pool, src, dst, stream=stream)
+        nbytes = 2 * 4096 * kv.kv_block_bytes(pool)
+    else:
+        g = torch.Generator(device="cpu").manual_seed(6)
+        blocks = torch.randperm(c.num_blocks, generator=g)[:2048].to(torch.int32).to(dev)
+        host = torch.empty(2048 * kv.kv_block_bytes(pool), dtype=torch.uint8).pin_memory()
+        fn = lambda: kv.kv_gather_blocks(pool, blocks, host, stream=stream)
+        back = lambda: kv.kv_scatter_blocks(pool, blocks, host, stream=stream)
+        nbytes = 2048 * kv.kv_block_bytes(pool)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    for a, b in evs:
+        hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hip.hipEventRecord(a, ctypes.c_void_p(stream.cuda_stream))
+        fn()
+        hip.hip.hipEventRecord(b, ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / len(evs)
+    if args.op == "offload":
+        evs2 = [(hip.create(), hip.create()) for _ in range(args.steps)]
+        for a, b in evs2:
+            hip.hip.hipEventRecord(a, ctypes.c_void_p(stream.cuda_stream))
+            back()
+            hip.hip.hipEventRecord(b, ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        ms_back = sum(hip.elapsed_ms(a, b) for a, b in evs2) / len(evs2)
+        extra = {"restore_avg_us": ms_back * 1e3, "restore_GBps": nbytes / (ms_back * 1e-3) / 1e9,
+                 "direction_of_value": "device -> pinned host"}
+    rate = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": f"{args.op}: algorithmic bytes per second", "value": rate, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "avg_us": ms * 1e3, "bytes_per_launch": nbytes,
+            "higher_is_better": True, "data": "synthetic", "config": {"workload": name, "op": args.op},
+            "roofline": {"bound": "hbm", "achieved": rate, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": rate / PEAK_HBM_GBS}}
+    line.update(extra)
+    log(f"[bench] {args.op}: {ms*1e3:.1f} us per launch, {rate:.0f} GB/s" +
+        (f", restore {extra['restore_avg_us']:.1f} us ({extra['restore_GBps']:.0f} GB/s)" if extra else ""))
     print(json.dumps(line), flush=True)
 
 

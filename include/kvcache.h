@@ -237,6 +237,36 @@ kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_ta
 kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t first_slot,
                         int32_t num_tokens, int32_t delta, float base, int32_t style, void *stream);
 
+/* Bytes of one block in packed form: its slice of every per-block region in
+ * region order (K, V for fp32/bf16 pools; KQ, KS, KM, VQ, VS, VM for INT4).
+ * The INT4 K tail belongs to a sequence, not to a block, and is not part of
+ * a packed block. 0 for a NULL pool. */
+size_t kv_block_bytes(kv_pool_t pool);
+
+/* Copy whole blocks inside a pool [KVSYS, "부분 재사용": a partially matching
+ * block is copied before a request that reuses it writes into it]:
+ * block dst_blocks[i] <- block src_blocks[i] in every per-block region, i < n.
+ *   src_blocks, dst_blocks  device int32 [n]; the two lists must be disjoint
+ *                           and dst ids distinct (else the result depends on
+ *                           the order of writes). Out-of-range ids skip the
+ *                           pair. */
+kv_status kv_copy_blocks(kv_pool_t pool, const int32_t *src_blocks, const int32_t *dst_blocks, int32_t n,
+                         void *stream);
+
+/* Offload [KVSYS, "호스트 메모리로의 오프로딩": blocks are copied to host
+ * memory and copied back before reuse]: pack blocks[0..n) into `buffer`,
+ * block i at byte i * kv_block_bytes(pool). `buffer` is device memory or
+ * pinned host memory mapped for the device (hipHostMalloc), of at least
+ * n * kv_block_bytes(pool) bytes (`bytes`), 16-byte aligned. Out-of-range ids
+ * leave their slot of the buffer unwritten. */
+kv_status kv_gather_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, void *buffer, size_t bytes,
+                           void *stream);
+
+/* Restore: unpack `buffer` (the layout kv_gather_blocks writes) into
+ * blocks[0..n); ids must be distinct. */
+kv_status kv_scatter_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, const void *buffer, size_t bytes,
+                            void *stream);
+
 /* Host-side check of HOST copies of the metadata a decode step would use:
  * every block the first lens[b] tokens (after the append when `appending`
  * is nonzero, i.e. lens[b] + 1 tokens) need is in [0, num_blocks), lens are

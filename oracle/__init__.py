@@ -81,6 +81,12 @@ def _declare(L):
     L.kvo_rope_rerotate.argtypes = [_I, _I, _I, _P, _P, _I, _I, _I, _D, _I]
     L.kvo_rope_rotate_f64.restype = None
     L.kvo_rope_rotate_f64.argtypes = [_P, _I, _D, _D, _I]
+    for f in ("kvo_copy_blocks",):
+        getattr(L, f).restype = None
+        getattr(L, f).argtypes = [_I, _P, _P, _P, _P, _I]
+    for f in ("kvo_gather_blocks", "kvo_scatter_blocks"):
+        getattr(L, f).restype = None
+        getattr(L, f).argtypes = [_I, _P, _P, _P, _I, _P]
     L.kvo_set_threads.restype = None
     L.kvo_set_threads.argtypes = [_I]
     L.kvo_max_threads.restype = _I
@@ -262,6 +268,38 @@ def rope_rotate_f64(x: np.ndarray, delta: float, base: float, style: int = 0) ->
     y = np.array(x, dtype=np.float64, copy=True)
     lib().kvo_rope_rotate_f64(_ptr(y), len(y), float(delta), float(base), int(style))
     return y
+
+
+def _regions(arrays):
+    """Per-block regions: each array's first axis is the block id."""
+    arrs = [np.ascontiguousarray(a) for a in arrays]
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    sizes = (ctypes.c_size_t * len(arrs))(*[a.nbytes // a.shape[0] for a in arrs])
+    return arrs, ptrs, sizes
+
+
+def copy_blocks(arrays, src, dst) -> None:
+    """In place on the given region arrays (all C-contiguous, block-major)."""
+    arrs, ptrs, sizes = _regions(arrays)
+    assert all(a is b for a, b in zip(arrs, arrays)), "region arrays must be C-contiguous"
+    src, dst = _i32(src), _i32(dst)
+    lib().kvo_copy_blocks(len(arrs), ptrs, sizes, _ptr(src), _ptr(dst), len(src))
+
+
+def gather_blocks(arrays, blocks) -> np.ndarray:
+    arrs, ptrs, sizes = _regions(arrays)
+    blocks = _i32(blocks)
+    out = np.zeros(len(blocks) * sum(sizes), dtype=np.uint8)
+    lib().kvo_gather_blocks(len(arrs), ptrs, sizes, _ptr(blocks), len(blocks), _ptr(out))
+    return out
+
+
+def scatter_blocks(arrays, blocks, buffer: np.ndarray) -> None:
+    arrs, ptrs, sizes = _regions(arrays)
+    assert all(a is b for a, b in zip(arrs, arrays)), "region arrays must be C-contiguous"
+    blocks = _i32(blocks)
+    buffer = np.ascontiguousarray(buffer, dtype=np.uint8)
+    lib().kvo_scatter_blocks(len(arrs), ptrs, sizes, _ptr(blocks), len(blocks), _ptr(buffer))
 
 
 def set_threads(n: int) -> None:

@@ -570,3 +570,55 @@ int kvo_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------ */
+/* block copies: copy-on-reuse and offload / restore                   */
+/* ------------------------------------------------------------------ */
+
+/* [KVSYS, "부분 재사용"]: a partially matching block may be copied before a
+ * request that reuses it writes into it; [KVSYS, "호스트 메모리로의
+ * 오프로딩"]: blocks are copied to host memory and copied back to the GPU
+ * before reuse. A block of a pool is its slice of every per-block region;
+ * region r holds block_bytes[r] bytes per block, block p at p * block_bytes[r].
+ * The packed form of one block is the concatenation of its slices in region
+ * order. */
+
+/* dst block dst[i] <- src block src[i] in every region (lists disjoint). */
+void kvo_copy_blocks(int nreg, uint8_t **regions, const size_t *block_bytes, const int32_t *src,
+                     const int32_t *dst, int n)
+{
+    for (int i = 0; i < n; ++i)
+        for (int r = 0; r < nreg; ++r)
+            memcpy(regions[r] + (size_t)dst[i] * block_bytes[r], regions[r] + (size_t)src[i] * block_bytes[r],
+                   block_bytes[r]);
+}
+
+/* buffer <- packed blocks[0..n) ; packed block i at offset i * sum(block_bytes). */
+void kvo_gather_blocks(int nreg, uint8_t **regions, const size_t *block_bytes, const int32_t *blocks, int n,
+                       uint8_t *buffer)
+{
+    size_t per = 0;
+    for (int r = 0; r < nreg; ++r) per += block_bytes[r];
+    for (int i = 0; i < n; ++i) {
+        size_t off = (size_t)i * per;
+        for (int r = 0; r < nreg; ++r) {
+            memcpy(buffer + off, regions[r] + (size_t)blocks[i] * block_bytes[r], block_bytes[r]);
+            off += block_bytes[r];
+        }
+    }
+}
+
+/* blocks[0..n) <- packed buffer (the inverse of kvo_gather_blocks). */
+void kvo_scatter_blocks(int nreg, uint8_t **regions, const size_t *block_bytes, const int32_t *blocks, int n,
+                        const uint8_t *buffer)
+{
+    size_t per = 0;
+    for (int r = 0; r < nreg; ++r) per += block_bytes[r];
+    for (int i = 0; i < n; ++i) {
+        size_t off = (size_t)i * per;
+        for (int r = 0; r < nreg; ++r) {
+            memcpy(regions[r] + (size_t)blocks[i] * block_bytes[r], buffer + off, block_bytes[r]);
+            off += block_bytes[r];
+        }
+    }
+}

@@ -77,6 +77,10 @@ _paged_decode_attention = _decl(
     [_P, _P, _P, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
 _kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P])
 _rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
+_kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
+_kv_copy_blocks = _decl("kv_copy_blocks", _I32, [_P, _P, _P, _I32, _P])
+_kv_gather_blocks = _decl("kv_gather_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
+_kv_scatter_blocks = _decl("kv_scatter_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
 _kv_validate_tables = _decl("kv_validate_tables", _I32,
                             [ctypes.POINTER(kv_pool_desc), _P, _I32, _P, _I32, _I32, ctypes.POINTER(_I32)])
 
@@ -269,6 +273,39 @@ def rope_rerotate(pool: KVPool, chunk_blocks: torch.Tensor, first_slot: int, num
     _check(st, "rope_rerotate")
 
 
+def kv_block_bytes(pool: KVPool) -> int:
+    return int(_kv_block_bytes(pool.handle))
+
+
+def kv_copy_blocks(pool: KVPool, src_blocks: torch.Tensor, dst_blocks: torch.Tensor, stream=None) -> None:
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _check(_kv_copy_blocks(pool.handle, _i32(src_blocks, "src_blocks"), _i32(dst_blocks, "dst_blocks"), n,
+                           _stream(stream)), "kv_copy_blocks")
+
+
+def _buf_ptr(buffer: torch.Tensor, name: str) -> tuple[int, int]:
+    """Device tensor, or pinned host tensor (mapped for the device)."""
+    if not buffer.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not buffer.is_cuda and not buffer.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    return buffer.data_ptr(), buffer.numel() * buffer.element_size()
+
+
+def kv_gather_blocks(pool: KVPool, blocks: torch.Tensor, buffer: torch.Tensor, stream=None) -> None:
+    ptr, nbytes = _buf_ptr(buffer, "buffer")
+    _check(_kv_gather_blocks(pool.handle, _i32(blocks, "blocks"), int(blocks.numel()), ptr, nbytes, _stream(stream)),
+           "kv_gather_blocks")
+
+
+def kv_scatter_blocks(pool: KVPool, blocks: torch.Tensor, buffer: torch.Tensor, stream=None) -> None:
+    ptr, nbytes = _buf_ptr(buffer, "buffer")
+    _check(_kv_scatter_blocks(pool.handle, _i32(blocks, "blocks"), int(blocks.numel()), ptr, nbytes,
+                              _stream(stream)), "kv_scatter_blocks")
+
+
 def kv_validate_tables(desc: kv_pool_desc, block_tables, lens, appending: bool = True):
     """Host check of host copies (numpy int32 or CPU tensors). Returns
     (status, first bad row or -1)."""
@@ -287,4 +324,6 @@ raw = {
     "kv_append": _kv_append, "paged_decode_attention": _paged_decode_attention,
     "paged_decode_attention_workspace_bytes": _paged_decode_attention_workspace_bytes,
     "kv_quantize_int4": _kv_quantize_int4, "rope_rerotate": _rope_rerotate,
+    "kv_block_bytes": _kv_block_bytes, "kv_copy_blocks": _kv_copy_blocks, "kv_gather_blocks": _kv_gather_blocks,
+    "kv_scatter_blocks": _kv_scatter_blocks,
 }

@@ -29,6 +29,7 @@ SOURCES = {
     "append.hip": ["-ffp-contract=off"],
     "int4.hip": ["-ffp-contract=off"],
     "rope.hip": ["-ffp-contract=off"],
+    "copy.hip": [],
     "attention.hip": [],
 }
 

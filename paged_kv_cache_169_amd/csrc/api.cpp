@@ -382,6 +382,73 @@ kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t fir
     return hip_status(launch_rope(pool->desc.dtype, a, static_cast<hipStream_t>(stream)));
 }
 
+static CopyParams copy_params(const kv_pool *pool) {
+    CopyParams c;
+    c.nreg = 0;
+    c.per_block = 0;
+    const int order[6] = {KV_REGION_K, KV_REGION_V, KV_REGION_KQ, KV_REGION_KS, KV_REGION_KM, KV_REGION_VQ};
+    const int order4[6] = {KV_REGION_KQ, KV_REGION_KS, KV_REGION_KM, KV_REGION_VQ, KV_REGION_VS, KV_REGION_VM};
+    const int *ord = pool->desc.dtype == KV_INT4 ? order4 : order;
+    for (int i = 0; i < 6; ++i) {
+        const int r = ord[i];
+        if (pool->off[r] == kNone) continue;
+        const size_t per = pool->len[r] / (size_t)pool->desc.num_blocks;  // a multiple of 16
+        c.region[c.nreg] = pool->base + pool->off[r];
+        c.chunks[c.nreg] = (uint32_t)(per / 16);
+        c.per_block += (uint32_t)(per / 16);
+        ++c.nreg;
+    }
+    c.num_blocks = pool->desc.num_blocks;
+    return c;
+}
+
+size_t kv_block_bytes(kv_pool_t pool) {
+    if (!pool) return 0;
+    return (size_t)copy_params(pool).per_block * 16;
+}
+
+kv_status kv_copy_blocks(kv_pool_t pool, const int32_t *src_blocks, const int32_t *dst_blocks, int32_t n,
+                         void *stream) {
+    if (!pool || n < 0) return KV_ERR_INVALID_ARG;
+    if (n == 0) return KV_OK;
+    if (!src_blocks || !dst_blocks) return KV_ERR_INVALID_ARG;
+    CopyParams c = copy_params(pool);
+    c.src = src_blocks;
+    c.dst = dst_blocks;
+    c.buffer = nullptr;
+    c.n = n;
+    c.mode = 0;
+    return hip_status(launch_copy_blocks(c, static_cast<hipStream_t>(stream)));
+}
+
+kv_status kv_gather_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, void *buffer, size_t bytes,
+                           void *stream) {
+    if (!pool || n < 0) return KV_ERR_INVALID_ARG;
+    if (n == 0) return KV_OK;
+    CopyParams c = copy_params(pool);
+    if (!blocks || !buffer || !aligned16(buffer) || bytes < (size_t)n * c.per_block * 16) return KV_ERR_INVALID_ARG;
+    c.src = blocks;
+    c.dst = nullptr;
+    c.buffer = static_cast<char *>(buffer);
+    c.n = n;
+    c.mode = 1;
+    return hip_status(launch_copy_blocks(c, static_cast<hipStream_t>(stream)));
+}
+
+kv_status kv_scatter_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, const void *buffer, size_t bytes,
+                            void *stream) {
+    if (!pool || n < 0) return KV_ERR_INVALID_ARG;
+    if (n == 0) return KV_OK;
+    CopyParams c = copy_params(pool);
+    if (!blocks || !buffer || !aligned16(buffer) || bytes < (size_t)n * c.per_block * 16) return KV_ERR_INVALID_ARG;
+    c.src = nullptr;
+    c.dst = blocks;
+    c.buffer = const_cast<char *>(static_cast<const char *>(buffer));
+    c.n = n;
+    c.mode = 2;
+    return hip_status(launch_copy_blocks(c, static_cast<hipStream_t>(stream)));
+}
+
 kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
                              const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row) {
     if (bad_row) *bad_row = -1;

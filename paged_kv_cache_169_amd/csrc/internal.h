@@ -59,7 +59,19 @@ struct RopeParams {
     float cos_t[64], sin_t[64];  // per pair i < head_dim / 2
 };
 
+// Whole-block copies between per-block regions and a packed buffer.
+struct CopyParams {
+    char *region[6];       // per-block regions, in packed order
+    uint32_t chunks[6];    // 16-byte chunks per block of each region
+    int32_t nreg;
+    uint32_t per_block;    // 16-byte chunks of one packed block
+    const int32_t *src, *dst;  // block lists (mode 0: src -> dst; 1: src -> buffer; 2: buffer -> dst)
+    char *buffer;
+    int32_t n, num_blocks, mode;
+};
+
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
+hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
 hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);
 hipError_t launch_merge(const AttnParams &p, hipStream_t s);

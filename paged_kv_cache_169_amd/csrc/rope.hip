@@ -24,6 +24,44 @@ __device__ __forceinline__ void rotate(float x, float y, float c, float s, float
     ny = __fadd_rn(__fmul_rn(x, s), __fmul_rn(y, c));
 }
 
+// bf16 pool: pairs 4gq .. 4gq+3 of one row. Style 0 takes them from one
+// 16-byte chunk (channels 8gq .. 8gq+7), style 1 from two 8-byte chunks
+// (channels 4gq .. 4gq+3 and head_dim/2 + 4gq ..).
+__device__ __forceinline__ void rope_bf16_group(const RopeParams &p, uint16_t *row, int gq) {
+    const int D = p.head_dim;
+    if (p.style == 0) {
+        uint4 *ptr = reinterpret_cast<uint4 *>(row + 8 * gq);
+        const uint4 v = *ptr;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int pi = 4 * gq + e;
+            float nx, ny;
+            rotate(bf16_lo(w[e]), bf16_hi(w[e]), p.cos_t[pi], p.sin_t[pi], nx, ny);
+            o[e] = (uint32_t)f_to_bf16(nx) | ((uint32_t)f_to_bf16(ny) << 16);
+        }
+        *ptr = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+        uint2 *px = reinterpret_cast<uint2 *>(row + 4 * gq);
+        uint2 *py = reinterpret_cast<uint2 *>(row + D / 2 + 4 * gq);
+        const uint2 vx = *px, vy = *py;
+        const uint32_t wx[2] = {vx.x, vx.y}, wy[2] = {vy.x, vy.y};
+        uint32_t ox[2], oy[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float x0, y0, x1, y1;
+            const int p0 = 4 * gq + 2 * h, p1 = p0 + 1;
+            rotate(bf16_lo(wx[h]), bf16_lo(wy[h]), p.cos_t[p0], p.sin_t[p0], x0, y0);
+            rotate(bf16_hi(wx[h]), bf16_hi(wy[h]), p.cos_t[p1], p.sin_t[p1], x1, y1);
+            ox[h] = (uint32_t)f_to_bf16(x0) | ((uint32_t)f_to_bf16(x1) << 16);
+            oy[h] = (uint32_t)f_to_bf16(y0) | ((uint32_t)f_to_bf16(y1) << 16);
+        }
+        *px = make_uint2(ox[0], ox[1]);
+        *py = make_uint2(oy[0], oy[1]);
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
     const int D = p.head_dim;
@@ -39,24 +77,20 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
     const int pid = p.chunk_blocks[pos / kBlock];
     if (pid < 0 || pid >= p.num_blocks) return;
     const size_t row = (((size_t)pid * p.n_kv + h) * kBlock + pos % kBlock) * D;
+    if (BF16) {
+        rope_bf16_group(p, reinterpret_cast<uint16_t *>(p.k) + row, gq);
+        return;
+    }
+    float *kr = reinterpret_cast<float *>(p.k) + row;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int pi = 4 * gq + e;
         const int c0 = p.style == 0 ? 2 * pi : pi;
         const int c1 = p.style == 0 ? 2 * pi + 1 : pi + D / 2;
-        const float c = p.cos_t[pi], s = p.sin_t[pi];
         float nx, ny;
-        if (BF16) {
-            uint16_t *kr = reinterpret_cast<uint16_t *>(p.k) + row;
-            rotate(bf16_to_f(kr[c0]), bf16_to_f(kr[c1]), c, s, nx, ny);
-            kr[c0] = f_to_bf16(nx);
-            kr[c1] = f_to_bf16(ny);
-        } else {
-            float *kr = reinterpret_cast<float *>(p.k) + row;
-            rotate(kr[c0], kr[c1], c, s, nx, ny);
-            kr[c0] = nx;
-            kr[c1] = ny;
-        }
+        rotate(kr[c0], kr[c1], p.cos_t[pi], p.sin_t[pi], nx, ny);
+        kr[c0] = nx;
+        kr[c1] = ny;
     }
 }
 

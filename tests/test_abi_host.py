@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -185,3 +185,22 @@ def test_validate_tables(kv):
     assert kv.kv_validate_tables(desc, t2, [20, 10], appending=False) == (kv.KV_ERR_TABLE, 0)   # id 9 >= 8
     t3 = np.array([[5, 1], [5, 3]], dtype=np.int32)
     assert kv.kv_validate_tables(desc, t3, [3, 3], appending=True) == (kv.KV_ERR_TABLE, 1)      # same slot twice
+
+
+def test_block_copy_host_checks(kv):
+    st, h = make_handle(kv, kv.make_desc(16, 2, 64, "bf16"))
+    assert kv.raw["kv_block_bytes"](h) == 2 * 2 * 16 * 64 * 2
+    st, h4 = make_handle(kv, kv.make_desc(16, 8, 128, "int4", 4))
+    # per (block, kv head): 1024 + 256 + 256 + 1024 + 32 + 32 bytes
+    assert kv.raw["kv_block_bytes"](h4) == 8 * (1024 + 256 + 256 + 1024 + 32 + 32)
+    C, Gt, Sc = kv.raw["kv_copy_blocks"], kv.raw["kv_gather_blocks"], kv.raw["kv_scatter_blocks"]
+    assert C(h, None, FAKE, 3, None) == kv.KV_ERR_INVALID_ARG
+    assert C(h, FAKE, FAKE, -1, None) == kv.KV_ERR_INVALID_ARG
+    assert C(h, None, None, 0, None) == 0
+    per = kv.raw["kv_block_bytes"](h)
+    assert Gt(h, FAKE, 3, FAKE, 3 * per - 1, None) == kv.KV_ERR_INVALID_ARG     # buffer too small
+    assert Gt(h, FAKE, 3, FAKE + 8, 3 * per, None) == kv.KV_ERR_INVALID_ARG     # misaligned buffer
+    assert Sc(h, FAKE, 3, None, 3 * per, None) == kv.KV_ERR_INVALID_ARG
+    assert kv.raw["kv_block_bytes"](None) == 0
+    for x in (h, h4):
+        kv.raw["kv_pool_destroy"](x)

@@ -392,3 +392,60 @@ def test_int4_attention_kernels(kernel, split, window):
     ref = orc.attention(Kd, Vd, bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale, window=window)
     assert np.all(np.isfinite(out))
     assert max_err(out, ref) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# block copies
+# ---------------------------------------------------------------------------
+
+def _regions_host(pool):
+    if pool.dtype == "int4":
+        ts = [pool.KQ, pool.KS, pool.KM, pool.VQ, pool.VS, pool.VM]
+    else:
+        ts = [pool.K, pool.V]
+    out = []
+    for t in ts:
+        h = t.detach().cpu().contiguous()
+        out.append(h.view(torch.uint8).numpy().reshape(h.shape[0], -1).copy())
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "int4"])
+def test_block_copy_gather_scatter(dtype):
+    nb = 40
+    pool = kv.KVPool(nb, 4, 128, dtype, max_seqs=2 if dtype == "int4" else 0, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    pool.blob.copy_(torch.randint(0, 256, (pool.blob.numel(),), generator=g, device=DEV, dtype=torch.uint8))
+    regs = _regions_host(pool)
+    src = torch.tensor([3, 17, 38, 0, 22], dtype=torch.int32, device=DEV)
+    dst = torch.tensor([5, 1, 9, 39, 30], dtype=torch.int32, device=DEV)
+    kv.kv_copy_blocks(pool, src, dst)
+    torch.cuda.synchronize()
+    orc.copy_blocks(regs, src.cpu().numpy(), dst.cpu().numpy())
+    assert all(np.array_equal(a, b) for a, b in zip(_regions_host(pool), regs))
+    per = kv.kv_block_bytes(pool)
+    blocks = torch.tensor([39, 2, 30, 11], dtype=torch.int32, device=DEV)
+    for where in ("device", "pinned"):
+        buf = (torch.zeros(4 * per, dtype=torch.uint8, device=DEV) if where == "device"
+               else torch.zeros(4 * per, dtype=torch.uint8).pin_memory())
+        kv.kv_gather_blocks(pool, blocks, buf)
+        torch.cuda.synchronize()
+        ref = orc.gather_blocks(regs, blocks.cpu().numpy())
+        assert np.array_equal(buf.cpu().numpy(), ref), where
+    # restore into other blocks from pinned host memory
+    back = torch.tensor([12, 13, 14, 15], dtype=torch.int32, device=DEV)
+    kv.kv_scatter_blocks(pool, back, buf)
+    torch.cuda.synchronize()
+    orc.scatter_blocks(regs, back.cpu().numpy(), ref)
+    assert all(np.array_equal(a, b) for a, b in zip(_regions_host(pool), regs))
+
+
+def test_block_copy_skips_out_of_range_ids():
+    pool = kv.KVPool(8, 2, 64, "bf16", device=DEV)
+    pool.blob.fill_(3)
+    regs = _regions_host(pool)
+    kv.kv_copy_blocks(pool, torch.tensor([1, 99, 2], dtype=torch.int32, device=DEV),
+                      torch.tensor([-4, 5, 6], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    orc.copy_blocks(regs, [2], [6])
+    assert all(np.array_equal(a, b) for a, b in zip(_regions_host(pool), regs))

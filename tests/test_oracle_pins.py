@@ -573,3 +573,43 @@ def test_int4_partial_block_keys_read_back_exactly(orc, n_tokens):
         assert not np.array_equal(Kd[p, :, t], as_f64(Kb[p, :, t]))   # really quantized
         assert np.max(np.abs(Kd[p, :, t] - as_f64(Kb[p, :, t]))) < 0.5
     assert np.all(img.kt[0] == 0)            # slot 0 untouched: the tail lives in slot 1
+
+
+# ---------------------------------------------------------------------------
+# block copies (copy-on-reuse, offload / restore)
+# ---------------------------------------------------------------------------
+
+def test_block_copy_gather_scatter_round_trip(orc):
+    rng = np.random.default_rng(50)
+    K = rng.integers(0, 65535, size=(12, 2, 16, 64), dtype=np.uint16)
+    V = rng.integers(0, 65535, size=(12, 2, 16, 64), dtype=np.uint16)
+    ks = rng.integers(0, 65535, size=(12, 2, 64), dtype=np.uint16)   # a region of another block size
+    K0, V0, ks0 = K.copy(), V.copy(), ks.copy()
+    blocks = np.array([7, 2, 11, 0])
+    buf = orc.gather_blocks([K, V, ks], blocks)
+    per = (2 * 16 * 64 * 2) * 2 + 2 * 64 * 2
+    assert buf.size == 4 * per
+    # packed block i: K slice, then V slice, then ks slice, each equal to the source block
+    for i, b in enumerate(blocks):
+        seg = buf[i * per:(i + 1) * per]
+        assert np.array_equal(seg[:4096].view(np.uint16).reshape(2, 16, 64), K[b])
+        assert np.array_equal(seg[4096:8192].view(np.uint16).reshape(2, 16, 64), V[b])
+        assert np.array_equal(seg[8192:].view(np.uint16).reshape(2, 64), ks[b])
+    # scatter into other blocks, then the copies equal the originals
+    dst = np.array([1, 3, 5, 9])
+    orc.scatter_blocks([K, V, ks], dst, buf)
+    for s_, d_ in zip(blocks, dst):
+        assert np.array_equal(K[d_], K0[s_]) and np.array_equal(V[d_], V0[s_]) and np.array_equal(ks[d_], ks0[s_])
+    untouched = [b for b in range(12) if b not in dst]
+    assert np.array_equal(K[untouched], K0[untouched])
+
+
+def test_block_copy_in_pool(orc):
+    rng = np.random.default_rng(51)
+    K = rng.standard_normal((10, 2, 16, 64)).astype(np.float32)
+    V = rng.standard_normal((10, 2, 16, 64)).astype(np.float32)
+    K0, V0 = K.copy(), V.copy()
+    orc.copy_blocks([K, V], [4, 8], [0, 9])
+    assert np.array_equal(K[0], K0[4]) and np.array_equal(K[9], K0[8])
+    assert np.array_equal(V[0], V0[4]) and np.array_equal(V[9], V0[8])
+    assert np.array_equal(K[1:9], K0[1:9])
