@@ -174,6 +174,17 @@ kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new,
                     const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens,
                     const int32_t *seq_slots, int32_t batch, void *stream);
 
+/* kv_append for n_new tokens per sequence at once (a chunk of a prompt, or
+ * speculated tokens to verify): token t of sequence b (t < n_new) goes to
+ * position seq_lens[b] + t, exactly as n_new kv_append calls in order would
+ * place and code it. k_new, v_new: device [batch][n_new][n_kv][head_dim]; the
+ * table entries of every position written must exist. A sequence whose
+ * positions would pass max_blocks * 16 is skipped. kv_append is this call
+ * with n_new = 1. */
+kv_status kv_append_tokens(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                           int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                           int32_t n_new, void *stream);
+
 /* Bytes of workspace paged_decode_attention needs for these sizes and
  * options (0 is a valid answer: then workspace may be NULL). max_ctx is an
  * upper bound of every ctx_lens[b]. Returns (size_t)-1 on invalid input. */
@@ -187,7 +198,7 @@ size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int
  *   q             device [batch][num_q_heads][head_dim], pool element type
  *                 (bf16 for KV_INT4)
  *   out           device fp32 [batch][num_q_heads][head_dim]
- *   num_q_heads   multiple of n_kv, num_q_heads / n_kv <= 16
+ *   num_q_heads   multiple of n_kv (num_q_heads / n_kv <= 16 for the VALU kernel)
  *   scale         softmax scale (1/sqrt(head_dim) for the usual model)
  *   ctx_lens      device int32 [batch]: tokens to attend (the cache length
  *                 after this step's append); 0 gives an output of 0
@@ -197,12 +208,37 @@ size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int
  *   workspace     device buffer of at least ws_bytes >=
  *                 paged_decode_attention_workspace_bytes(...) bytes
  * KV_INT4 pools are dequantized on the fly: full blocks from their codes,
- * the K of a sequence's partial last block from its bf16 tail row. */
+ * the K of a sequence's partial last block from its bf16 tail row.
+ * num_q_heads / n_kv may exceed 16 only with the MFMA kernel. */
 kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads,
                                  float scale, const int32_t *block_tables, int32_t max_blocks,
                                  const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
                                  int32_t max_ctx, void *workspace, size_t ws_bytes,
                                  const kv_attn_opts *opts, void *stream);
+
+/* Bytes of workspace paged_multi_token_attention needs ((size_t)-1 on invalid
+ * input). */
+size_t paged_multi_token_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads,
+                                                   int32_t q_len, int32_t max_ctx, const kv_attn_opts *opts);
+
+/* Attention of q_len new tokens per sequence over the paged cache, causal
+ * among themselves (verifying speculated tokens, or a chunk of a prompt):
+ * the cache already holds the new tokens (appended like any other), ctx_lens[b]
+ * tokens in all, and query token i < q_len sits at position P = ctx_lens[b] -
+ * q_len + i and attends tokens 0..P [CORE, "KV Cache: O(T²)를 O(T)로": each
+ * token attends to the cache up to itself], or the last `window` of them
+ * ([KVSYS, "제한된 어텐션 윈도우 크기"]). A query token with no token to
+ * attend to (P < 0) outputs 0.
+ *   q    device [batch][q_len][num_q_heads][head_dim] (bf16)
+ *   out  device fp32 [batch][q_len][num_q_heads][head_dim]
+ * The other arguments are those of paged_decode_attention, which is this call
+ * with q_len = 1. MFMA kernels only (bf16 pools, INT4 pools with head_dim
+ * 128); each kv head's group * q_len query rows are processed in tiles of 16. */
+kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, int32_t q_len,
+                                      float scale, const int32_t *block_tables, int32_t max_blocks,
+                                      const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
+                                      int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts,
+                                      void *stream);
 
 /* Bulk KVQuant INT4 coding of bf16 pool contents [CORE, "KVQuant: 마지막 4배"]:
  * code = clamp(round((x - min) / s), 0, 15) with s = (max - min) / 15, s and min

@@ -67,6 +67,8 @@ def _declare(L):
     L.kvo_append.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _I]
     L.kvo_attention.restype = _I
     L.kvo_attention.argtypes = [_I, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I, _D, _I, _P]
+    L.kvo_attention_multi.restype = _I
+    L.kvo_attention_multi.argtypes = [_I, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I, _D, _I, _P]
     L.kvo_q4_group_bf16.restype = None
     L.kvo_q4_group_bf16.argtypes = [_P, _I, _P, _P, _P]
     L.kvo_q4_group_f32.restype = None
@@ -183,6 +185,25 @@ def attention(K: np.ndarray, V: np.ndarray, q: np.ndarray, tables: np.ndarray,
                              n_h, n_kv, d, float(scale), int(window), _ptr(out))
     if rc != 0:
         raise ValueError("n_h must be a multiple of n_kv")
+    return out
+
+
+def attention_multi(K: np.ndarray, V: np.ndarray, q: np.ndarray, tables: np.ndarray,
+                    ctx_lens: np.ndarray, scale: float, window: int = 0) -> np.ndarray:
+    """Several query tokens per sequence, causal among themselves.
+    q: [B][q_len][n_h][d]; returns [B][q_len][n_h][d] f64."""
+    nb, n_kv, bs, d = K.shape
+    B, q_len, n_h, dq = q.shape
+    assert dq == d and V.shape == K.shape and V.dtype == K.dtype
+    tables = _i32(tables)
+    ctx_lens = _i32(ctx_lens)
+    q = np.ascontiguousarray(q)
+    out = np.zeros((B, q_len, n_h, d), dtype=np.float64)
+    rc = lib().kvo_attention_multi(_dtype_of(K), _ptr(K), _ptr(V), _dtype_of(q), _ptr(q), _ptr(tables),
+                                   tables.shape[1], _ptr(ctx_lens), B, q_len, n_h, n_kv, d, float(scale),
+                                   int(window), _ptr(out))
+    if rc != 0:
+        raise ValueError("n_h must be a multiple of n_kv and q_len >= 1")
     return out
 
 

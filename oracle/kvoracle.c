@@ -622,3 +622,65 @@ void kvo_scatter_blocks(int nreg, uint8_t **regions, const size_t *block_bytes, 
         }
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* several query tokens per sequence (speculative verification,        */
+/* chunked prefill)                                                    */
+/* ------------------------------------------------------------------ */
+
+/* The decode step of [CORE, "KV Cache: O(T²)를 O(T)로"] for q_len new tokens
+ * at once: the cache already holds them, ctx_lens[b] tokens in all, and query
+ * token i (i < q_len) sits at position P = ctx - q_len + i and attends to
+ * tokens 0..P (causal among the new tokens), or to the last `window` of them
+ * ([KVSYS, "제한된 어텐션 윈도우 크기"]). A query with no token (P < 0)
+ * outputs 0. q, out: [batch][q_len][n_h][d]. Returns 0, or -1 for bad heads. */
+int kvo_attention_multi(int kv_dtype, const void *K, const void *V, int q_dtype, const void *q,
+                        const int32_t *tables, int max_blocks, const int32_t *ctx_lens, int batch, int q_len,
+                        int n_h, int n_kv, int d, double scale, int window, double *out)
+{
+    if (n_kv <= 0 || n_h % n_kv || q_len < 1) return -1;
+    int g = n_h / n_kv;
+    long total = (long)batch * q_len * n_h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long idx = 0; idx < total; ++idx) {
+        int h = (int)(idx % n_h);
+        int i = (int)((idx / n_h) % q_len);
+        int b = (int)(idx / ((long)n_h * q_len));
+        int kvh = h / g;
+        int hi = ctx_lens[b] - q_len + i + 1; /* tokens 0 .. hi-1 */
+        int lo = (window > 0 && hi > window) ? hi - window : 0;
+        double *o = out + (size_t)idx * d;
+        if (hi - lo <= 0) {
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            continue;
+        }
+        int cnt = hi - lo;
+        double *w = (double *)malloc(sizeof(double) * (size_t)cnt);
+        size_t *row = (size_t *)malloc(sizeof(size_t) * (size_t)cnt);
+        size_t qoff = (size_t)idx * d;
+        double m = -INFINITY;
+        for (int j = lo; j < hi; ++j) {
+            int p = tables[(size_t)b * max_blocks + j / BLOCK];
+            size_t r = row_index(n_kv, d, p, kvh, j % BLOCK);
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c)
+                dot += load_elem(q_dtype, q, qoff + c) * load_elem(kv_dtype, K, r + c);
+            w[j - lo] = scale * dot;
+            row[j - lo] = r;
+            if (w[j - lo] > m) m = w[j - lo];
+        }
+        double l = 0.0;
+        for (int k = 0; k < cnt; ++k) {
+            w[k] = exp(w[k] - m);
+            l += w[k];
+        }
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int k = 0; k < cnt; ++k) acc += w[k] * load_elem(kv_dtype, V, row[k] + c);
+            o[c] = acc / l;
+        }
+        free(w);
+        free(row);
+    }
+    return 0;
+}

@@ -70,11 +70,17 @@ _kv_pool_destroy = _decl("kv_pool_destroy", _I32, [_P])
 _kv_pool_region = _decl("kv_pool_region", _I32, [_P, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)])
 _kv_pool_get_desc = _decl("kv_pool_get_desc", _I32, [_P, ctypes.POINTER(kv_pool_desc)])
 _kv_append = _decl("kv_append", _I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P])
+_kv_append_tokens = _decl("kv_append_tokens", _I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P])
 _paged_decode_attention_workspace_bytes = _decl(
     "paged_decode_attention_workspace_bytes", _SZ, [_P, _I32, _I32, _I32, ctypes.POINTER(kv_attn_opts)])
 _paged_decode_attention = _decl(
     "paged_decode_attention", _I32,
     [_P, _P, _P, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
+_paged_multi_token_attention_workspace_bytes = _decl(
+    "paged_multi_token_attention_workspace_bytes", _SZ, [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(kv_attn_opts)])
+_paged_multi_token_attention = _decl(
+    "paged_multi_token_attention", _I32,
+    [_P, _P, _P, _I32, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
 _kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P])
 _rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
 _kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
@@ -222,6 +228,21 @@ def kv_append(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, block_tabl
     _check(st, "kv_append")
 
 
+def kv_append_tokens(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
+                     seq_lens: torch.Tensor, seq_slots: torch.Tensor | None = None, stream=None) -> None:
+    """k_new, v_new: [batch][n_new][n_kv][head_dim]."""
+    d = pool.desc
+    B, n_new = int(k_new.shape[0]), int(k_new.shape[1])
+    want = torch.float32 if d.dtype == KV_F32 else torch.bfloat16
+    n = B * n_new * d.num_kv_heads * d.head_dim
+    if int(seq_lens.numel()) != B:
+        raise ValueError("seq_lens must have one entry per sequence")
+    st = _kv_append_tokens(pool.handle, _dev_ptr(k_new, "k_new", want, n), _dev_ptr(v_new, "v_new", want, n),
+                           _i32(block_tables, "block_tables"), int(block_tables.shape[1]), _i32(seq_lens, "seq_lens"),
+                           _i32(seq_slots, "seq_slots"), B, n_new, _stream(stream))
+    _check(st, "kv_append_tokens")
+
+
 def attn_opts(split_blocks: int = 0, kernel: int = 0, window: int = 0, schedule: int = 0,
               events=None) -> kv_attn_opts:
     o = kv_attn_opts(int(split_blocks), int(kernel), int(window), int(schedule))
@@ -257,6 +278,34 @@ def paged_decode_attention(pool: KVPool, q: torch.Tensor, out: torch.Tensor, blo
                                  ws_ptr, ws_bytes, ctypes.byref(opts) if opts is not None else None,
                                  _stream(stream))
     _check(st, "paged_decode_attention")
+
+
+def paged_multi_token_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int, q_len: int,
+                                                max_ctx: int, opts: kv_attn_opts | None = None) -> int:
+    n = _paged_multi_token_attention_workspace_bytes(pool.handle, int(batch), int(num_q_heads), int(q_len),
+                                                     int(max_ctx), ctypes.byref(opts) if opts is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise KVError(KV_ERR_INVALID_ARG, "paged_multi_token_attention_workspace_bytes")
+    return int(n)
+
+
+def paged_multi_token_attention(pool: KVPool, q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                                ctx_lens: torch.Tensor, scale: float, max_ctx: int,
+                                workspace: torch.Tensor | None = None, seq_slots: torch.Tensor | None = None,
+                                opts: kv_attn_opts | None = None, stream=None) -> None:
+    """q: [batch][q_len][num_q_heads][head_dim] bf16; out the same shape, fp32."""
+    d = pool.desc
+    B, q_len, n_h, hd = q.shape
+    if hd != d.head_dim or tuple(out.shape) != (B, q_len, n_h, hd):
+        raise ValueError("q / out shape does not match the pool")
+    ws_ptr = _dev_ptr(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _paged_multi_token_attention(pool.handle, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(out, "out", torch.float32),
+                                      n_h, q_len, float(scale), _i32(block_tables, "block_tables"),
+                                      int(block_tables.shape[1]), _i32(ctx_lens, "ctx_lens"),
+                                      _i32(seq_slots, "seq_slots"), B, int(max_ctx), ws_ptr, ws_bytes,
+                                      ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    _check(st, "paged_multi_token_attention")
 
 
 def kv_quantize_int4(dst: KVPool, src: KVPool, block_tables: torch.Tensor, lens: torch.Tensor,
@@ -321,9 +370,11 @@ def kv_validate_tables(desc: kv_pool_desc, block_tables, lens, appending: bool =
 # raw entry points, for tests of the C ABI itself
 raw = {
     "kv_pool_create": _kv_pool_create, "kv_pool_destroy": _kv_pool_destroy, "kv_pool_region": _kv_pool_region,
-    "kv_append": _kv_append, "paged_decode_attention": _paged_decode_attention,
+    "kv_append": _kv_append, "kv_append_tokens": _kv_append_tokens, "paged_decode_attention": _paged_decode_attention,
     "paged_decode_attention_workspace_bytes": _paged_decode_attention_workspace_bytes,
     "kv_quantize_int4": _kv_quantize_int4, "rope_rerotate": _rope_rerotate,
+    "paged_multi_token_attention": _paged_multi_token_attention,
+    "paged_multi_token_attention_workspace_bytes": _paged_multi_token_attention_workspace_bytes,
     "kv_block_bytes": _kv_block_bytes, "kv_copy_blocks": _kv_copy_blocks, "kv_gather_blocks": _kv_gather_blocks,
     "kv_scatter_blocks": _kv_scatter_blocks,
 }

@@ -94,6 +94,9 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // Attention launch geometry for a call.
 struct AttnGeom {
     int kernel;        // 1 VALU, 2 MFMA
+    int ncols;         // query columns per kv head
+    int ctiles;        // 16-column tiles per kv head
+    int units;         // work units per sequence
     int schedule;      // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int split_blocks;
     int max_splits;
@@ -106,14 +109,13 @@ struct AttnGeom {
 // Largest batch of the balanced schedule (its block prefix sums live in LDS).
 constexpr int kMaxBalancedBatch = 8192;
 
-kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx, const kv_attn_opts *opts,
-                    AttnGeom *g) {
-    if (batch < 0 || n_h < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
+kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
+                    const kv_attn_opts *opts, AttnGeom *g) {
+    if (batch < 0 || n_h < 1 || max_ctx < 0 || q_len < 1) return KV_ERR_INVALID_ARG;
     const int n_kv = pool->desc.num_kv_heads;
     const int dtype = pool->desc.dtype;
     if (n_h % n_kv) return KV_ERR_INVALID_ARG;
     const int group = n_h / n_kv;
-    if (group > kMaxGroup) return KV_ERR_UNSUPPORTED;
     if (opts && (opts->kernel < 0 || opts->kernel > 2 || opts->schedule < 0 || opts->schedule > 2 ||
                  opts->window < 0 || opts->split_blocks < 0))
         return KV_ERR_INVALID_ARG;
@@ -122,6 +124,12 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
     int kernel = opts ? opts->kernel : 0;
     if (kernel == 2 && !mfma_ok) return KV_ERR_UNSUPPORTED;
     if (kernel == 0) kernel = mfma_ok ? 2 : 1;
+    // the VALU kernel serves one query token and groups of up to 16 heads; the
+    // MFMA kernels tile any number of query columns (group * q_len) by 16
+    if (kernel == 1 && (q_len > 1 || group > kMaxGroup)) return KV_ERR_UNSUPPORTED;
+    g->ncols = group * q_len;
+    g->ctiles = (g->ncols + 15) / 16;
+    g->units = kernel == 2 ? n_kv * g->ctiles : n_kv;
     int sb = opts ? opts->split_blocks : 0;
     int sched = opts ? opts->schedule : 0;
     if (sched == KV_SCHED_AUTO)
@@ -130,7 +138,8 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
     const int window = opts ? opts->window : 0;
     int nblk = (max_ctx + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS;
     if (window > 0) {
-        const int wb = (window + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS + 1;
+        // the union of the query tokens' windows spans window + q_len - 1 tokens
+        const int wb = (window + q_len - 1 + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS + 1;
         if (wb < nblk) nblk = wb;
     }
     if (nblk < 1) nblk = 1;
@@ -145,7 +154,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
         g->split_blocks = nblk;
         g->max_splits = 1;
         g->n_wg = balanced_grid(dtype, (int)D, batch);
-        const size_t rows = (size_t)g->n_wg * 2 * group;
+        const size_t rows = (size_t)g->n_wg * 2 * (g->ncols < 16 ? g->ncols : 16);
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));
         g->ws_bytes = g->off_prefix + align_up(((size_t)batch + 1) * sizeof(int32_t));
@@ -155,7 +164,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
         // Aim for about 16 workgroups per compute unit (256 CUs) over the
         // grid when the (sequence, kv head) pairs alone cannot provide them;
         // never split below 8 blocks (the merge then costs more than it saves).
-        const long pairs = (long)batch * n_kv;
+        const long pairs = (long)batch * g->units;
         const long target = 256L * 16;
         long want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
         if (want < 1) want = 1;
@@ -169,7 +178,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max
         g->ws_bytes = 0;
         g->off_ml = 0;
     } else {
-        const size_t rows = (size_t)batch * n_h * g->max_splits;
+        const size_t rows = (size_t)batch * q_len * n_h * g->max_splits;
         g->off_ml = align_up(rows * D * sizeof(float));
         g->ws_bytes = g->off_ml + align_up(rows * 2 * sizeof(float));
     }
@@ -244,10 +253,10 @@ kv_status kv_pool_get_desc(kv_pool_t pool, kv_pool_desc *desc) {
     return KV_OK;
 }
 
-kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
-                    int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
-                    void *stream) {
-    if (!pool || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+kv_status kv_append_tokens(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                           int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                           int32_t n_new, void *stream) {
+    if (!pool || batch < 0 || max_blocks < 1 || n_new < 1) return KV_ERR_INVALID_ARG;
     if (batch == 0) return KV_OK;
     if (!k_new || !v_new || !block_tables || !seq_lens) return KV_ERR_INVALID_ARG;
     if (!aligned16(k_new) || !aligned16(v_new)) return KV_ERR_INVALID_ARG;
@@ -264,25 +273,39 @@ kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new, const 
     a.head_dim = pool->desc.head_dim;
     a.num_blocks = pool->desc.num_blocks;
     a.max_seqs = pool->desc.max_seqs;
+    a.n_new = n_new;
     return hip_status(launch_append(pool->desc.dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+kv_status kv_append(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                    int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                    void *stream) {
+    return kv_append_tokens(pool, k_new, v_new, block_tables, max_blocks, seq_lens, seq_slots, batch, 1, stream);
+}
+
+size_t paged_multi_token_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads,
+                                                   int32_t q_len, int32_t max_ctx, const kv_attn_opts *opts) {
+    AttnGeom g;
+    if (!pool || attn_geom(pool, batch, num_q_heads, q_len, max_ctx, opts, &g) != KV_OK) return (size_t)-1;
+    return g.ws_bytes;
 }
 
 size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads, int32_t max_ctx,
                                               const kv_attn_opts *opts) {
-    AttnGeom g;
-    if (!pool || attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g) != KV_OK) return (size_t)-1;
-    return g.ws_bytes;
+    return paged_multi_token_attention_workspace_bytes(pool, batch, num_q_heads, 1, max_ctx, opts);
 }
 
-kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, float scale,
-                                 const int32_t *block_tables, int32_t max_blocks, const int32_t *ctx_lens,
-                                 const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace,
-                                 size_t ws_bytes, const kv_attn_opts *opts, void *stream) {
-    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
+kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, int32_t q_len,
+                                      float scale, const int32_t *block_tables, int32_t max_blocks,
+                                      const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
+                                      int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts,
+                                      void *stream) {
+    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0 || q_len < 1)
+        return KV_ERR_INVALID_ARG;
     if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
     AttnGeom g;
-    const kv_status gs = attn_geom(pool, batch, num_q_heads, max_ctx, opts, &g);
+    const kv_status gs = attn_geom(pool, batch, num_q_heads, q_len, max_ctx, opts, &g);
     if (gs != KV_OK) return gs;
     if (batch == 0) return KV_OK;
     if (!q || !out || !block_tables || !ctx_lens) return KV_ERR_INVALID_ARG;
@@ -312,6 +335,11 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
     a.split_blocks = g.split_blocks;
     a.max_splits = g.max_splits;
     a.window = opts ? opts->window : 0;
+    a.q_len = q_len;
+    a.ncols = g.ncols;
+    a.ctiles = g.ctiles;
+    a.units = g.units;
+    a.slot_cols = g.ncols < 16 ? g.ncols : 16;
     a.schedule = g.schedule;
     a.n_wg = g.n_wg;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
@@ -326,6 +354,14 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
     if (e != hipSuccess) return KV_ERR_HIP;
     if (ev && ev[2] && hipEventRecord(static_cast<hipEvent_t>(ev[2]), s) != hipSuccess) return KV_ERR_HIP;
     return KV_OK;
+}
+
+kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, float scale,
+                                 const int32_t *block_tables, int32_t max_blocks, const int32_t *ctx_lens,
+                                 const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace,
+                                 size_t ws_bytes, const kv_attn_opts *opts, void *stream) {
+    return paged_multi_token_attention(pool, q, out, num_q_heads, 1, scale, block_tables, max_blocks, ctx_lens,
+                                       seq_slots, batch, max_ctx, workspace, ws_bytes, opts, stream);
 }
 
 kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables, int32_t max_blocks,

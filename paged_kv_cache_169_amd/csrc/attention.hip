@@ -61,24 +61,25 @@ struct SplitWork {
 };
 
 __device__ __forceinline__ bool split_work(const AttnParams &p, int b, int split, SplitWork &w) {
-    w.r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+    w.r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (split >= w.r.nsplit) return false;
     w.j0 = w.r.blk_lo + split * p.split_blocks;
     w.j1 = min(w.r.blk_lo + w.r.nblk, w.j0 + p.split_blocks);
     return true;
 }
 
-// Final store of one lane's run of `n` consecutive channels of one head.
-__device__ __forceinline__ void store_result(const AttnParams &p, int b, int head, int split, int nsplit,
+// Final store of one lane's run of `n` consecutive channels of output row
+// `row` ((sequence * q_len + query token) * n_h + head).
+__device__ __forceinline__ void store_result(const AttnParams &p, size_t row, int split, int nsplit,
                                              int ch0, const float *o, int n, float m, float l, bool bad,
                                              bool write_ml) {
     const float nan = __uint_as_float(0x7fc00000u);
     if (nsplit == 1) {
-        float *dst = p.out + ((size_t)b * p.n_h + head) * p.head_dim + ch0;
+        float *dst = p.out + row * p.head_dim + ch0;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         for (int c = 0; c < n; ++c) dst[c] = bad ? nan : o[c] * inv;
     } else {
-        const size_t base = ((size_t)b * p.n_h + head) * p.max_splits + split;
+        const size_t base = row * p.max_splits + split;
         float *dst = p.ws_o + base * p.head_dim + ch0;
         for (int c = 0; c < n; ++c) dst[c] = bad ? nan : o[c];
         if (write_ml) {
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams p) {
             mb = fmaxf(mb, __shfl_xor(mb, 16));
             mb = fmaxf(mb, __shfl_xor(mb, 32));
             const float mn = fmaxf(m_run[h], mb);
-            const float alpha = exp2f(m_run[h] - mn);
+            const float alpha = mn == m_run[h] ? 1.0f : exp2f(m_run[h] - mn);
             const float pe = exp2f(s[h] - mn);
             l_run[h] = l_run[h] * alpha + pe;
 #pragma unroll
@@ -307,8 +308,9 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams p) {
         l += __shfl_xor(l, 8);
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        if (h < g) store_result(p, b, kvh * g + h, split, w.r.nsplit, lane * CV, acc[h], CV, m_run[h], l, bad,
-                                lane == 0);
+        if (h < g)
+            store_result(p, (size_t)b * p.n_h + kvh * g + h, split, w.r.nsplit, lane * CV, acc[h], CV, m_run[h], l,
+                         bad, lane == 0);
     }
 }
 
@@ -364,37 +366,67 @@ struct MfmaState {
     float bv;  // INT4: numerator term common to every channel (this lane's part)
 };
 
+// The query column a lane serves: c = ct * 16 + n16 of kv head kvh's g * q_len
+// columns is query token i = c / g of head kvh * g + c % g; it attends tokens
+// [lo, hi). Padded columns (c >= ncols) get a query of 0 and the common range.
+struct Column {
+    bool valid;
+    size_t row;  // output / query row ((b * q_len + i) * n_h + head)
+    int lo, hi;
+};
+
+__device__ __forceinline__ Column column_of(const AttnParams &p, int b, int kvh, int ct, int n16, const SeqRange &r) {
+    Column c;
+    const int ci = ct * 16 + n16;
+    c.valid = ci < p.ncols;
+    const int i = c.valid ? ci / p.group : p.q_len - 1, hq = c.valid ? ci % p.group : 0;
+    c.row = ((size_t)b * p.q_len + i) * p.n_h + kvh * p.group + hq;
+    c.hi = r.n - p.q_len + i + 1;
+    c.lo = p.window > 0 ? max(c.hi - p.window, 0) : 0;
+    return c;
+}
+
+// Score masking of one block: token position tok0 + 4G + r is valid for the
+// lane's column if it lies in [col.lo, col.hi). Blocks inside the range every
+// column attends skip the test (uniform branch).
+__device__ __forceinline__ bool needs_mask(int tok0, const SeqRange &r) {
+    return tok0 < r.all_lo || tok0 + kBlock > r.all_hi;
+}
+
 template <int D>
 __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D> &T, const bf16x8_t (&qB)[D / 32],
-                                           int tlo, int thi, int G, MfmaState<D> &st) {
+                                           int tok0, int tlo, int thi, bool mask, const Column &col, int G,
+                                           MfmaState<D> &st) {
     constexpr int KS = D / 32, MS = D / 16, VC = D / 16;
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s], qB[s], sc, 0, 0, 0);
-    const bool partial = tlo > 0 || thi < kBlock;  // uniform
+    const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int tt = 4 * G + r;
-        sv[r] = (!partial || (tt >= tlo && tt < thi)) ? sc[r] * p.scale_log2 : -INFINITY;
+        const int tp = tok0 + 4 * G + r;
+        sv[r] = (!mask || (tp >= col.lo && tp < col.hi)) ? sc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(st.m, mx);
     if (!__all(mn == st.m)) {
-        // the running max moved for some head: rescale (rare after the first blocks)
-        const float alpha = exp2f(st.m - mn);
+        // the running max moved for some column: rescale (rare after the first blocks)
+        const float alpha = mn == st.m ? 1.0f : exp2f(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
 #pragma unroll
         for (int m = 0; m < MS; ++m) st.o[m] *= alpha;
         st.m = mn;
     }
+    // a column that has seen no token yet (max -inf) gets weights 0, not NaN
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        pr[r] = exp2f(sv[r] - st.m);
+        pr[r] = exp2f(sv[r] - mref);
         st.l += pr[r];
     }
     // P^T as B operand, split into bf16 hi and lo parts
@@ -438,20 +470,18 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
 // kv head kvh. On return st.l is still the lane's partial sum (the caller
 // adds the 4 token quads).
 template <int D>
-__device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const SeqRange &r, int j0, int j1,
-                                             int lane, MfmaState<D> &st, bool &bad) {
+__device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const Column &col,
+                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st,
+                                             bool &bad) {
     constexpr int KS = D / 32, MS = D / 16;
     const int n16 = lane & 15, G = lane >> 4;
-    const int g = p.group;
-    // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of head n16.
+    // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of its column.
     bf16x8_t qB[KS];
-    const int head = kvh * g + n16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n16 < g)
-            v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) +
-                                                 ((size_t)b * p.n_h + head) * D + s * 32 + 8 * G);
+        if (col.valid)
+            v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + col.row * D + s * 32 + 8 * G);
         qB[s] = __builtin_bit_cast(bf16x8_t, v);
     }
 #pragma unroll
@@ -487,11 +517,11 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
         int tlo, thi;
         if (j + 1 < j1) fetch_tile<D>(p, pid_of(j + 1), kvh, n16, G, B);
         bounds(j, tlo, thi);
-        mfma_block<D>(p, A, qB, tlo, thi, G, st);
+        mfma_block<D>(p, A, qB, j * kBlock, tlo, thi, needs_mask(j * kBlock, r), col, G, st);
         if (j + 1 >= j1) break;
         if (j + 2 < j1) fetch_tile<D>(p, pid_of(j + 2), kvh, n16, G, A);
         bounds(j + 1, tlo, thi);
-        mfma_block<D>(p, B, qB, tlo, thi, G, st);
+        mfma_block<D>(p, B, qB, (j + 1) * kBlock, tlo, thi, needs_mask((j + 1) * kBlock, r), col, G, st);
     }
 }
 
@@ -576,8 +606,8 @@ __device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f((uint
 __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f((uint16_t)(w >> 16)); }
 
 __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const float (&qf)[32], bool full,
-                                         const uint16_t *tail_row, int tlo, int thi, int lane, int G,
-                                         uint2 *lds_sm, MfmaState<128> &st) {
+                                         const uint16_t *tail_row, int tok0, int tlo, int thi, bool mask,
+                                         const Column &col, int lane, int G, uint2 *lds_sm, MfmaState<128> &st) {
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
@@ -623,14 +653,14 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
                                                          __builtin_bit_cast(bf16x8_t, make_uint4(qb[0], qb[1], qb[2], qb[3])), sc, 0, 0, 0);
         }
     }
-    const bool partial = tlo > 0 || thi < kBlock;  // uniform
+    const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
     float sv[4];
     bool valid[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int tt = 4 * G + r;
-        valid[r] = !partial || (tt >= tlo && tt < thi);
+        const int tt = 4 * G + r, tp = tok0 + tt;
+        valid[r] = (!partial || (tt >= tlo && tt < thi)) && (!mask || (tp >= col.lo && tp < col.hi));
         sv[r] = valid[r] ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
@@ -638,7 +668,7 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(st.m, mx);
     if (!__all(mn == st.m)) {
-        const float alpha = exp2f(st.m - mn);
+        const float alpha = mn == st.m ? 1.0f : exp2f(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
         st.bv *= alpha;
 #pragma unroll
@@ -646,11 +676,12 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         st.m = mn;
     }
     const uint32_t vsw[2] = {T.vs.x, T.vs.y}, vmw[2] = {T.vm.x, T.vm.y};
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;  // no token seen yet: weights 0
     float pv[4];
     float bv = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float pr = exp2f(sv[r] - st.m);  // 0 for masked slots
+        const float pr = exp2f(sv[r] - mref);  // 0 for masked slots
         st.l += pr;
         const float vsc = (r & 1) ? f16_hi(vsw[r >> 1]) : f16_lo(vsw[r >> 1]);
         const float vmn = (r & 1) ? f16_hi(vmw[r >> 1]) : f16_lo(vmw[r >> 1]);
@@ -680,8 +711,8 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
 }
 
 template <int D>
-__device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, const SeqRange &r, int j0, int j1,
-                                           int lane, MfmaState<D> &st, bool &bad) {
+__device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, const Column &col, const SeqRange &r,
+                                           int j0, int j1, int lane, MfmaState<D> &st, bool &bad) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
     const int g = p.group;
@@ -690,13 +721,13 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         bad = true;
         slot = 0;
     }
-    // q of head n16, channels 32G .. 32G+31, in fp32 (0 for padded heads)
+    // q of the lane's column, channels 32G .. 32G+31, in fp32 (0 for padded columns)
     float qf[32];
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)b * p.n_h + kvh * g + n16) * 128 + 32 * G;
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + col.row * 128 + 32 * G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n16 < g) v = *reinterpret_cast<const uint4 *>(qrow + 8 * i);
+        if (col.valid) v = *reinterpret_cast<const uint4 *>(qrow + 8 * i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -737,21 +768,23 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         int tlo, thi;
         if (j + 1 < j1) q4_fetch(p, pid_of(j + 1), kvh, lane, n16, G, is_full(j + 1), B);
         bounds(j, tlo, thi);
-        q4_block(p, A, qf, is_full(j), tail_row, tlo, thi, lane, G, lds_sm, st);
+        q4_block(p, A, qf, is_full(j), tail_row, j * kBlock, tlo, thi, needs_mask(j * kBlock, r), col, lane, G, lds_sm,
+                 st);
         if (j + 1 >= j1) break;
         if (j + 2 < j1) q4_fetch(p, pid_of(j + 2), kvh, lane, n16, G, is_full(j + 2), A);
         bounds(j + 1, tlo, thi);
-        q4_block(p, B, qf, is_full(j + 1), tail_row, tlo, thi, lane, G, lds_sm, st);
+        q4_block(p, B, qf, is_full(j + 1), tail_row, (j + 1) * kBlock, tlo, thi, needs_mask((j + 1) * kBlock, r), col,
+                 lane, G, lds_sm, st);
     }
 }
 
 template <int D, bool Q4>
-__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, const SeqRange &r, int j0, int j1,
-                                            int lane, MfmaState<D> &st, bool &bad) {
+__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, const Column &col, const SeqRange &r,
+                                            int j0, int j1, int lane, MfmaState<D> &st, bool &bad) {
     if constexpr (Q4)
-        q4_segment<D>(p, b, kvh, r, j0, j1, lane, st, bad);
+        q4_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad);
     else
-        bf16_segment<D>(p, b, kvh, r, j0, j1, lane, st, bad);
+        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad);
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
@@ -762,21 +795,23 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 template <int D, bool Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, unit = blockIdx.y, b = blockIdx.z;
+    const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
     SplitWork w;
     if (!split_work(p, b, split, w)) return;
     bool bad = w.r.bad;
+    const Column col = column_of(p, b, kvh, ct, n16, w.r);
     MfmaState<D> st;
-    run_segment<D, Q4>(p, b, kvh, w.r, w.j0, w.j1, lane, st, bad);
+    run_segment<D, Q4>(p, b, kvh, col, w.r, w.j0, w.j1, lane, st, bad);
     float l = st.l, bv = st.bv;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     bv += __shfl_xor(bv, 16);
     bv += __shfl_xor(bv, 32);
-    if (n16 < p.group) {
+    if (col.valid) {
         float res[D / 4];
         mfma_gather_run<D>(st, bv, res);
-        store_result(p, b, kvh * p.group + n16, split, w.r.nsplit, G * (D / 4), res, D / 4, st.m, l, bad, G == 0);
+        store_result(p, col.row, split, w.r.nsplit, G * (D / 4), res, D / 4, st.m, l, bad, G == 0);
     }
 }
 
@@ -797,7 +832,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
         const int b = base + lane;
         int nb = 0;
         if (b < p.batch) {
-            const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+            const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
             nb = r.nblk;
         }
         // inclusive wave scan
@@ -821,49 +856,50 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     const int nblk_total = balanced_prefix(p, pre, lane);
     if (wg == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
-    const long total = (long)nblk_total * p.n_kv;
+    const long total = (long)nblk_total * p.units;
     const long per = (total + p.n_wg - 1) / p.n_wg;
     const long s = (long)wg * per;
     const long e = min(total, s + per);
     for (long t = s; t < e;) {
-        // sequence holding tile t: largest b with n_kv * pre[b] <= t
+        // sequence holding tile t: largest b with units * pre[b] <= t
         int lo = 0, hi = p.batch - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((long)pre[mid] * p.n_kv <= t)
+            if ((long)pre[mid] * p.units <= t)
                 lo = mid;
             else
                 hi = mid - 1;
         }
         const int b = lo;
         const int nb = pre[b + 1] - pre[b];
-        const long pair0 = (long)pre[b] * p.n_kv;
-        const int kvh = (int)((t - pair0) / nb);
-        const int jr = (int)(t - pair0 - (long)kvh * nb);
-        const long seg_end = min(e, pair0 + (long)(kvh + 1) * nb);
+        const long pair0 = (long)pre[b] * p.units;
+        const int unit = (int)((t - pair0) / nb);
+        const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
+        const int jr = (int)(t - pair0 - (long)unit * nb);
+        const long seg_end = min(e, pair0 + (long)(unit + 1) * nb);
         const int cnt = (int)(seg_end - t);
-        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         bool bad = r.bad;
+        const Column col = column_of(p, b, kvh, ct, n16, r);
         MfmaState<D> st;
-        run_segment<D, Q4>(p, b, kvh, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad);
+        run_segment<D, Q4>(p, b, kvh, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad);
         float l = st.l, bv = st.bv;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         bv += __shfl_xor(bv, 16);
         bv += __shfl_xor(bv, 32);
-        if (n16 < p.group) {
+        if (col.valid) {
             float res[D / 4];
             mfma_gather_run<D>(st, bv, res);
-            const int head = kvh * p.group + n16;
             const float nan = __uint_as_float(0x7fc00000u);
             if (jr == 0 && cnt == nb) {
-                float *dst = p.out + ((size_t)b * p.n_h + head) * D + G * (D / 4);
+                float *dst = p.out + col.row * D + G * (D / 4);
                 const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
                 for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
             } else {
                 const int slot = t == s ? 0 : 1;
-                const size_t row = ((size_t)wg * 2 + slot) * p.group + n16;
+                const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + n16;
                 float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
                 for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c];
@@ -881,65 +917,73 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 // merge of split partials
 // ---------------------------------------------------------------------------
 
+// Grid (n_h * q_len, batch): one wave per output row (query token, head).
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
-    const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+    const int b = blockIdx.y, lane = threadIdx.x;
+    const size_t row = (size_t)b * p.q_len * p.n_h + blockIdx.x;
+    const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (r.nsplit <= 1) return;
-    const size_t base = ((size_t)b * p.n_h + head) * p.max_splits;
+    const size_t base = row * p.max_splits;
     const float *ml = p.ws_ml + base * 2;
     float M = -INFINITY;
     for (int s = 0; s < r.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
     const int D = p.head_dim;
     const int cv = D / 64;
+    float *dst = p.out + row * D + lane * cv;
     float acc[2] = {0.0f, 0.0f};
     float L = 0.0f;
-    for (int s = 0; s < r.nsplit; ++s) {
-        const float wgt = exp2f(ml[2 * s] - M);
-        L += wgt * ml[2 * s + 1];
-        const float *o = p.ws_o + (base + s) * D + lane * cv;
-        for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+    if (M != -INFINITY) {  // else no split saw a token for this row: output 0
+        for (int s = 0; s < r.nsplit; ++s) {
+            const float wgt = exp2f(ml[2 * s] - M);
+            L += wgt * ml[2 * s + 1];
+            const float *o = p.ws_o + (base + s) * D + lane * cv;
+            for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+        }
     }
-    float *dst = p.out + ((size_t)b * p.n_h + head) * D + lane * cv;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
 }
 
-// Merge for the balanced schedule: one wave per (head, sequence). Finds the
-// workgroups whose tile ranges cut this (sequence, kv head) pair and combines
-// their partials; writes 0 (or NaN for a bad sequence) when the pair has no
-// attended block.
+// Merge for the balanced schedule: one wave per output row (query token,
+// head) of each sequence. Finds the workgroups whose tile ranges cut the
+// row's (sequence, unit) pair and combines their partials; writes 0 (or NaN
+// for a bad sequence) when the sequence has no attended block.
 __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
-    const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int b = blockIdx.y, lane = threadIdx.x;
+    const int head = blockIdx.x % p.n_h, qi = blockIdx.x / p.n_h;
     const int D = p.head_dim, cv = D / 64;
-    const int kvh = head / p.group, n16 = head % p.group;
+    const int kvh = head / p.group, ci = qi * p.group + head % p.group;
+    const int unit = kvh * p.ctiles + ci / 16, n16 = ci % 16;
     const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
-    float *dst = p.out + ((size_t)b * p.n_h + head) * D + lane * cv;
+    float *dst = p.out + ((size_t)b * p.q_len * p.n_h + blockIdx.x) * D + lane * cv;
     if (nb == 0) {
-        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits);
+        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
         for (int c = 0; c < cv; ++c) dst[c] = v;
         return;
     }
-    const long total = (long)p.ws_prefix[p.batch] * p.n_kv;
+    const long total = (long)p.ws_prefix[p.batch] * p.units;
     const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long start = (long)p.ws_prefix[b] * p.n_kv + (long)kvh * nb;
+    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * nb;
     const long end = start + nb;
     const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
     if (w0 == w1) return;  // complete inside one workgroup: already written
     float M = -INFINITY;
     for (int w = w0; w <= w1; ++w) {
         const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
-        M = fmaxf(M, p.ws_ml[(((size_t)w * 2 + slot) * p.group + n16) * 2]);
+        M = fmaxf(M, p.ws_ml[(((size_t)w * 2 + slot) * p.slot_cols + n16) * 2]);
     }
     float acc[2] = {0.0f, 0.0f};
     float L = 0.0f;
-    for (int w = w0; w <= w1; ++w) {
-        const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
-        const size_t row = ((size_t)w * 2 + slot) * p.group + n16;
-        const float wgt = exp2f(p.ws_ml[row * 2] - M);
-        L += wgt * p.ws_ml[row * 2 + 1];
-        const float *o = p.ws_o + row * D + lane * cv;
-        for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+    if (M != -INFINITY) {  // else no segment saw a token for this row: output 0
+        for (int w = w0; w <= w1; ++w) {
+            const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
+            const size_t row = ((size_t)w * 2 + slot) * p.slot_cols + n16;
+            const float wgt = exp2f(p.ws_ml[row * 2] - M);
+            L += wgt * p.ws_ml[row * 2 + 1];
+            const float *o = p.ws_o + row * D + lane * cv;
+            for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
@@ -971,7 +1015,7 @@ static hipError_t launch_valu(const AttnParams &p, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s) {
-    const dim3 grid(p.max_splits, p.n_kv, p.batch);
+    const dim3 grid(p.max_splits, kernel == 2 ? p.units : p.n_kv, p.batch);
     if (p.batch == 0) return hipSuccess;
     if (kernel == 2) {
         const bool q4 = dtype == KV_INT4;
@@ -1020,11 +1064,11 @@ int balanced_grid(int dtype, int head_dim, int batch) {
 hipError_t launch_merge(const AttnParams &p, hipStream_t s) {
     if (p.batch == 0) return hipSuccess;
     if (p.schedule == KV_SCHED_BALANCED) {
-        hipLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, p);
+        hipLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, p);
         return hipGetLastError();
     }
     if (p.max_splits <= 1) return hipSuccess;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 

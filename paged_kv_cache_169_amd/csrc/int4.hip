@@ -59,34 +59,45 @@ __device__ __forceinline__ void code_k_block(const uint32_t (&w)[kBlock], bool a
     reinterpret_cast<uint32_t *>(km_row)[lane] = (uint32_t)q0.m16 | ((uint32_t)q1.m16 << 16);
 }
 
-// Append to an INT4 pool. Grid (n_kv, batch), one wave each.
+// Append to an INT4 pool. Grid (n_kv, batch), one wave each; the wave takes
+// the sequence's n_new tokens in order. The K rows of the block being filled
+// live in LDS (seeded from the sequence's tail row and kept in the tail too),
+// so a block completed in the middle of the chunk is coded from LDS.
 __global__ __launch_bounds__(64) void append_int4_kernel(AppendParams p) {
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int D = p.head_dim, hd = D / 2;
     const bool act = lane < hd;
-    const int L = p.seq_lens[b];
-    if (L < 0 || L >= p.max_blocks * kBlock) return;
-    const int pid = p.tables[(size_t)b * p.max_blocks + L / kBlock];
-    if (pid < 0 || pid >= p.num_blocks) return;
+    __shared__ uint32_t rows[kBlock][64];  // K rows of the open block, one word per lane
+    const int L0 = p.seq_lens[b];
+    if (L0 < 0 || L0 + p.n_new > p.max_blocks * kBlock) return;
     const int slot = p.seq_slots ? p.seq_slots[b] : b;
     if (slot < 0 || slot >= p.max_seqs) return;
-    const int t = L % kBlock;
-    const size_t src = ((size_t)b * p.n_kv + h) * hd;  // in words
-    const uint32_t vw = act ? reinterpret_cast<const uint32_t *>(p.v_new)[src + lane] : 0u;
-    const uint32_t kw = act ? reinterpret_cast<const uint32_t *>(p.k_new)[src + lane] : 0u;
-
-    const size_t tile = (size_t)pid * p.n_kv + h;   // (block, head) tile index
-    const size_t row = tile * kBlock + t;            // token row index
-    code_v_row(vw, act, p.pool.vq + row * hd, p.pool.vs + row, p.pool.vm + row, lane);
-
     uint32_t *tail = reinterpret_cast<uint32_t *>(p.pool.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;
-    if (act) tail[(size_t)t * hd + lane] = kw;
-    if (t == kBlock - 1) {
-        uint32_t w[kBlock];
+    for (int tt = 0; tt < L0 % kBlock; ++tt) rows[tt][lane] = act ? tail[(size_t)tt * hd + lane] : 0u;
+    __syncthreads();
+    for (int k = 0; k < p.n_new; ++k) {
+        const int L = L0 + k;
+        const int pid = p.tables[(size_t)b * p.max_blocks + L / kBlock];
+        if (pid < 0 || pid >= p.num_blocks) return;
+        const int t = L % kBlock;
+        const size_t src = (((size_t)b * p.n_new + k) * p.n_kv + h) * hd;  // in words
+        const uint32_t vw = act ? reinterpret_cast<const uint32_t *>(p.v_new)[src + lane] : 0u;
+        const uint32_t kw = act ? reinterpret_cast<const uint32_t *>(p.k_new)[src + lane] : 0u;
+
+        const size_t tile = (size_t)pid * p.n_kv + h;   // (block, head) tile index
+        const size_t row = tile * kBlock + t;            // token row index
+        code_v_row(vw, act, p.pool.vq + row * hd, p.pool.vs + row, p.pool.vm + row, lane);
+
+        if (act) tail[(size_t)t * hd + lane] = kw;
+        rows[t][lane] = kw;
+        __syncthreads();
+        if (t == kBlock - 1) {
+            uint32_t w[kBlock];
 #pragma unroll
-        for (int tt = 0; tt < kBlock - 1; ++tt) w[tt] = act ? tail[(size_t)tt * hd + lane] : 0u;
-        w[kBlock - 1] = kw;
-        code_k_block(w, act, p.pool.kq + tile * kBlock * hd, p.pool.ks + tile * D, p.pool.km + tile * D, lane, hd);
+            for (int tt = 0; tt < kBlock; ++tt) w[tt] = rows[tt][lane];
+            code_k_block(w, act, p.pool.kq + tile * kBlock * hd, p.pool.ks + tile * D, p.pool.km + tile * D, lane, hd);
+        }
+        __syncthreads();
     }
 }
 

@@ -33,6 +33,11 @@ struct AttnParams {
     float *ws_ml;  // [batch][n_h][max_splits][2]  (running max in log2 units, sum)
     int32_t max_blocks, batch, n_h, n_kv, group, head_dim, num_blocks, max_seqs;
     int32_t split_blocks, max_splits, window;
+    int32_t q_len;     // query tokens per sequence (1: decode)
+    int32_t ncols;     // query columns per kv head: group * q_len
+    int32_t ctiles;    // 16-column tiles per kv head
+    int32_t units;     // work units per sequence: n_kv * ctiles
+    int32_t slot_cols; // balanced: columns of one workspace slot, min(16, ncols)
     int32_t schedule;  // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int32_t n_wg;      // balanced: persistent grid size
     int32_t *ws_prefix;  // balanced: [batch + 1] attended blocks before each sequence
@@ -41,9 +46,10 @@ struct AttnParams {
 
 struct AppendParams {
     PoolPtrs pool;
-    const void *k_new, *v_new;
+    const void *k_new, *v_new;  // [batch][n_new][n_kv][head_dim]
     const int32_t *tables, *seq_lens, *seq_slots;
     int32_t max_blocks, batch, n_kv, head_dim, num_blocks, max_seqs;
+    int32_t n_new;  // tokens appended per sequence, at positions seq_lens[b] ..
 };
 
 struct QuantParams {
@@ -81,33 +87,44 @@ hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 
 // The attended block range of one sequence, shared by the split kernels and
-// the merge kernel so that both agree on the number of splits.
+// the merge kernels so that both agree on the number of splits. With q_len
+// query tokens, query i attends tokens [lo_i, hi_i) with hi_i = n - q_len +
+// i + 1 (causal among the new tokens) and lo_i = max(0, hi_i - window) for a
+// window, else 0; [lo, hi) is their union, [all_lo, all_hi) their common part.
 struct SeqRange {
-    int n;        // attended length (after validation)
-    int lo, hi;   // attended tokens [lo, hi)
-    int blk_lo;   // first attended block
-    int nblk;     // attended blocks
-    int nsplit;   // splits (>= 1)
-    bool bad;     // length outside [0, max_blocks * 16], or more splits than
-                  // the grid and workspace were sized for (ctx above max_ctx)
+    int n;              // attended length (after validation)
+    int lo, hi;         // union of the query tokens' ranges [lo, hi)
+    int all_lo, all_hi; // tokens every query token attends
+    int blk_lo;         // first attended block
+    int nblk;           // attended blocks
+    int nsplit;         // splits (>= 1)
+    bool bad;           // length outside [0, max_blocks * 16], or more splits than
+                        // the grid and workspace were sized for (ctx above max_ctx)
 };
 
 __host__ __device__ inline SeqRange seq_range(int n, int max_blocks, int window, int split_blocks,
-                                              int max_splits) {
+                                              int max_splits, int q_len) {
     SeqRange r;
     r.bad = n < 0 || n > max_blocks * kBlock;
+    auto lo_of = [&](int m) {
+        const int first_hi = m - q_len + 1;  // range end of query token 0
+        return window > 0 ? (first_hi - window > 0 ? first_hi - window : 0) : 0;
+    };
     if (!r.bad) {
-        const int lo = (window > 0 && n > window) ? n - window : 0;
-        const int nb = (n + kBlock - 1) / kBlock - lo / kBlock;
+        const int nb = (n + kBlock - 1) / kBlock - lo_of(n) / kBlock;
         r.bad = nb > (long)split_blocks * max_splits;
     }
     if (r.bad) n = 0;
     r.n = n;
     r.hi = n;
-    r.lo = (window > 0 && n > window) ? n - window : 0;
+    r.lo = n > 0 ? lo_of(n) : 0;
+    if (r.lo > r.hi) r.lo = r.hi;
+    r.all_hi = n - q_len + 1;
+    r.all_lo = window > 0 ? (n - window > 0 ? n - window : 0) : 0;
     r.blk_lo = r.lo / kBlock;
     int blk_hi = (n + kBlock - 1) / kBlock;
     r.nblk = blk_hi - r.blk_lo;
+    if (r.nblk < 0) r.nblk = 0;
     r.nsplit = r.nblk == 0 ? 1 : (r.nblk + split_blocks - 1) / split_blocks;
     return r;
 }

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -118,8 +118,13 @@ def test_argument_errors_before_launch(kv):
     o = kv.attn_opts()
     # n_h not a multiple of n_kv
     assert P(h, FAKE, FAKE, 3, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) == kv.KV_ERR_INVALID_ARG
-    # group above 16
-    assert P(h, FAKE, FAKE, 34, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) == kv.KV_ERR_UNSUPPORTED
+    # group above 16 on the VALU kernel
+    o_valu = kv.attn_opts(kernel=1)
+    assert P(h, FAKE, FAKE, 34, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o_valu), None) == kv.KV_ERR_UNSUPPORTED
+    # several query tokens need the MFMA kernel; q_len 0 is invalid
+    M = kv.raw["paged_multi_token_attention"]
+    assert M(h, FAKE, FAKE, 4, 3, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o_valu), None) == kv.KV_ERR_UNSUPPORTED
+    assert M(h, FAKE, FAKE, 4, 0, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) == kv.KV_ERR_INVALID_ARG
     # max_ctx beyond the table
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 65, None, 0, ctypes.byref(o), None) == kv.KV_ERR_INVALID_ARG
     # non-finite scale
@@ -204,3 +209,19 @@ def test_block_copy_host_checks(kv):
     assert kv.raw["kv_block_bytes"](None) == 0
     for x in (h, h4):
         kv.raw["kv_pool_destroy"](x)
+
+
+def test_multi_token_workspace_sizes(kv):
+    desc = kv.make_desc(16, 2, 64, "bf16")
+    st, h = make_handle(kv, desc)
+    W = kv.raw["paged_multi_token_attention_workspace_bytes"]
+    o1 = kv.attn_opts(split_blocks=1)
+    # 4 query tokens, 4 heads: rows = batch * q_len * n_h * splits (50 tokens: 4 splits)
+    rows = 2 * 4 * 4 * 4
+    assert W(h, 2, 4, 4, 50, ctypes.byref(o1)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256
+    # balanced: slot rows = min(16, group * q_len) = 16 for group 2 and 9 query tokens
+    ob = kv.attn_opts(schedule=kv.KV_SCHED_BALANCED)
+    rows = 512 * 2 * 16
+    assert W(h, 3, 4, 9, 50, ctypes.byref(ob)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256 + 256
+    assert W(h, 2, 4, 0, 50, None) == ctypes.c_size_t(-1).value
+    kv.raw["kv_pool_destroy"](h)

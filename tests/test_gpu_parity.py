@@ -449,3 +449,103 @@ def test_block_copy_skips_out_of_range_ids():
     torch.cuda.synchronize()
     orc.copy_blocks(regs, [2], [6])
     assert all(np.array_equal(a, b) for a, b in zip(_regions_host(pool), regs))
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per sequence (speculative verification / chunked prefill)
+# ---------------------------------------------------------------------------
+
+def gpu_multi(pool, c, q, kernel=0, split_blocks=0, window=0, seq_slots=None, schedule=0):
+    max_ctx = int(c.ctx_lens.max().item())
+    B, k, n_h, d = q.shape
+    opts = kv.attn_opts(split_blocks=split_blocks, kernel=kernel, window=window, schedule=schedule)
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(pool, B, n_h, k, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, k, n_h, d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.paged_multi_token_attention(pool, q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, seq_slots, opts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("n_h,n_kv,k", [(8, 2, 4), (32, 8, 4), (64, 8, 2), (8, 8, 16), (16, 2, 3), (64, 8, 5)])
+@pytest.mark.parametrize("split,window", [(0, 0), (2, 0), (0, 37), (3, 37)])
+def test_multi_token_parity(n_h, n_kv, k, split, window):
+    lens = [0, 2, 16, 17, 40, 100, 300]            # cache length with the k new tokens included
+    c = wl.make_case(950 + k, len(lens), lens, n_h, n_kv, 128, "bf16", append=False, device=DEV)
+    pool = new_pool(c)
+    g = torch.Generator(device=DEV).manual_seed(k)
+    q = torch.randn((c.batch, k, n_h, 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = gpu_multi(pool, c, q, split_blocks=split, window=window)
+    ref = orc.attention_multi(bits(c.K), bits(c.V), bits(q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(),
+                              c.scale, window=window)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref) <= TOL
+
+
+def test_multi_token_one_token_is_decode():
+    c = wl.make_case(960, 5, [7, 33, 64, 100, 250], 32, 8, 128, "bf16", append=False, device=DEV)
+    pool = new_pool(c)
+    a = gpu_attention(pool, c, kernel=2)
+    b = gpu_multi(pool, c, c.q.view(c.batch, 1, c.n_h, c.d), kernel=2)
+    assert np.array_equal(a, b[:, 0])
+
+
+@pytest.mark.parametrize("split", [0, 2])
+def test_multi_token_int4(split):
+    k = 4
+    lens = [3, 16, 21, 47, 200]
+    c = int4_case(970, lens, n_h=32, n_kv=8, d=128)
+    c.append = False
+    c.ctx_lens = c.seq_lens.clone()
+    src, dst, img = int4_pools(c, len(lens))
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
+    tab, lens_np = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens_np)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    q = torch.randn((c.batch, k, c.n_h, 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = gpu_multi(dst, c, q, split_blocks=split)
+    Kd, Vd = orc.q4_dequant(img, tab, lens_np)
+    ref = orc.attention_multi(Kd, Vd, bits(q), tab, lens_np, c.scale)
+    assert max_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "int4"])
+@pytest.mark.parametrize("n_new", [1, 3, 16, 20])
+def test_append_tokens_equals_sequential_appends(dtype, n_new):
+    lens = [0, 5, 15, 16, 30, 47]
+    n_kv, d = 2, 128
+    pool_dtype = "bf16" if dtype == "int4" else dtype
+    c = wl.make_case(990 + n_new, len(lens), lens, 4, n_kv, d, pool_dtype, num_blocks=40, append=False,
+                     device=DEV, max_blocks=6)
+    # tables with room for n_new more tokens: extend each row with unused ids
+    need = [(L + n_new + 15) // 16 for L in lens]
+    used = set(int(x) for x in c.tables.cpu().flatten() if x >= 0)
+    free = [i for i in range(40) if i not in used]
+    tab = c.tables.cpu().clone()
+    for b, L in enumerate(lens):
+        have = (L + 15) // 16
+        for j in range(have, need[b]):
+            tab[b, j] = free.pop()
+    c.tables = tab.to(DEV)
+    g = torch.Generator(device=DEV).manual_seed(n_new)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kn = torch.randn((len(lens), n_new, n_kv, d), generator=g, device=DEV).to(tdt)
+    vn = torch.randn((len(lens), n_new, n_kv, d), generator=g, device=DEV).to(tdt)
+    lens_np = c.seq_lens.cpu().numpy()
+    if dtype == "int4":
+        src, dst, img = int4_pools(c, len(lens))
+        kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
+        orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab.numpy(), lens_np)
+        kv.kv_append_tokens(dst, kn, vn, c.tables, c.seq_lens)
+        for t in range(n_new):
+            orc.q4_append(img, bits(kn[:, t]), bits(vn[:, t]), tab.numpy(), lens_np + t)
+        torch.cuda.synchronize()
+        assert_img_equal(dst, img)
+    else:
+        pool = new_pool(c)
+        kv.kv_append_tokens(pool, kn, vn, c.tables, c.seq_lens)
+        torch.cuda.synchronize()
+        K, V = bits(c.K), bits(c.V)
+        for t in range(n_new):
+            orc.append(K, V, bits(kn[:, t]), bits(vn[:, t]), tab.numpy(), lens_np + t)
+        assert np.array_equal(ibits(bits(pool.K)), ibits(K)) and np.array_equal(ibits(bits(pool.V)), ibits(V))

@@ -613,3 +613,70 @@ def test_block_copy_in_pool(orc):
     assert np.array_equal(K[0], K0[4]) and np.array_equal(K[9], K0[8])
     assert np.array_equal(V[0], V0[4]) and np.array_equal(V[9], V0[8])
     assert np.array_equal(K[1:9], K0[1:9])
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per sequence
+# ---------------------------------------------------------------------------
+
+def torch_attention_multi(Kp, Vp, q, tables, ctx, scale, window=0):
+    """Independent check: contiguous attention with an explicit causal mask."""
+    Kf, Vf, qf = as_f64(Kp), as_f64(Vp), as_f64(q)
+    B, k, n_h, d = qf.shape
+    g = n_h // Kf.shape[1]
+    out = np.zeros((B, k, n_h, d))
+    for b in range(B):
+        n = int(ctx[b])
+        if n == 0:
+            continue
+        kk = torch.from_numpy(logical(Kf, tables, b, n))
+        vv = torch.from_numpy(logical(Vf, tables, b, n))
+        pos = torch.arange(n)
+        for i in range(k):
+            P = n - k + i
+            allowed = (pos <= P) & ((pos > P - window) if window else torch.ones(n, dtype=torch.bool))
+            if not bool(allowed.any()):
+                continue
+            for h in range(n_h):
+                s = (kk[:, h // g, :] @ torch.from_numpy(qf[b, i, h])) * scale
+                w = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=0)
+                out[b, i, h] = (w @ vv[:, h // g, :]).numpy()
+    return out
+
+
+def _multi_q(c, k, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((c.batch, k, c.n_h, c.d)).astype(np.float32)
+    return _bf16(q) if c.dtype == "bf16" else q
+
+
+@pytest.mark.parametrize("k,window", [(1, 0), (3, 0), (4, 0), (5, 7), (16, 0)])
+def test_multi_token_matches_torch_causal(orc, k, window):
+    c = small_case(60, (3, 16, 40, 77), 8, 2, 64, "bf16", poison=False)
+    K, V, _, tab, ctx = host(c)
+    q = _multi_q(c, k, 61)
+    got = orc.attention_multi(K, V, q, tab, ctx, c.scale, window=window)
+    ref = torch_attention_multi(K, V, q, tab, ctx, c.scale, window=window)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_multi_token_last_query_is_decode_and_causality(orc):
+    c = small_case(62, (20, 33, 50), 4, 2, 64, "f32", poison=False)
+    K, V, _, tab, ctx = host(c)
+    k = 4
+    q = _multi_q(c, k, 63)
+    multi = orc.attention_multi(K, V, q, tab, ctx, c.scale)
+    # the last query token sees the whole cache: exactly the decode attention
+    dec = orc.attention(K, V, np.ascontiguousarray(q[:, -1]), tab, ctx, c.scale)
+    assert np.array_equal(multi[:, -1], dec)
+    # query i is the decode attention over the first ctx - k + i + 1 tokens
+    for i in range(k):
+        dec_i = orc.attention(K, V, np.ascontiguousarray(q[:, i]), tab, ctx - k + i + 1, c.scale)
+        assert np.array_equal(multi[:, i], dec_i)
+    # changing a later token does not change an earlier query's output
+    K2 = K.copy()
+    p_last = tab[0, (ctx[0] - 1) // 16]
+    K2[p_last, :, (ctx[0] - 1) % 16, :] += 5.0
+    multi2 = orc.attention_multi(K2, V, q, tab, ctx, c.scale)
+    assert np.array_equal(multi2[0, :k - 1], multi[0, :k - 1])
+    assert not np.array_equal(multi2[0, k - 1], multi[0, k - 1])
