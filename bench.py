@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
     ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence: 1 is decode; k > 1 appends k tokens and runs the "
+                         "multi-token (verification) attention over them")
     ap.add_argument("--op", default="decode", choices=["decode", "append", "quantize", "rope", "copy", "offload"],
                     help="decode: the decode step (default); the others time one secondary kernel")
     args = ap.parse_args()
@@ -121,7 +124,8 @@ def main():
         return bench_op(args, torch, kv, wl, dev)
     name = args.workload
     t_setup = time.time()
-    c = wl.workload(name, device=dev, poison=False)
+    k = args.q_len
+    c = wl.workload(name, device=dev, poison=False, n_new=k if k > 1 else None)
     int4 = c.int4
     B, n_h, n_kv, D = c.batch, c.n_h, c.n_kv, c.d
     es = 4 if c.dtype == "f32" else 2
@@ -153,9 +157,9 @@ def main():
             kv.rope_rerotate(p, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
     max_ctx = int(ctx.max().item())
     opts = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule)
-    ws_bytes = kv.paged_decode_attention_workspace_bytes(pools[0], B, n_h, max_ctx, opts)
+    ws_bytes = kv.paged_multi_token_attention_workspace_bytes(pools[0], B, n_h, k, max_ctx, opts)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty((B, n_h, D), dtype=torch.float32, device=dev)
+    out = torch.empty((B, n_h, D) if k == 1 else (B, k, n_h, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] {name}: B={B} n_h={n_h} n_kv={n_kv} d={D} dtype={'int4' if int4 else c.dtype} "
         f"tokens/step={tokens_per_step} pool={pool_bytes/1e6:.1f} MB x {reps} replicas, "
@@ -166,12 +170,17 @@ def main():
 
     def step(i, events=None):
         p = pools[i % reps]
-        if c.append:
-            kv.kv_append(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
         o = opts
         if events is not None:
             o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule, events=events)
-        kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
+        if k == 1:
+            if c.append:
+                kv.kv_append(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
+            kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
+        else:
+            kv.kv_append_tokens(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
+            kv.paged_multi_token_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o,
+                                           stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -205,11 +214,11 @@ def main():
         kv_bytes = int(ctx.sum().item()) * n_kv * 164
     else:
         kv_bytes = int(ctx.sum().item()) * n_kv * 2 * D * es
-    alg_bytes = kv_bytes + B * n_h * D * es + B * n_h * D * 4 + int(nblk.sum().item()) * 4 + B * 4
+    alg_bytes = kv_bytes + k * (B * n_h * D * es + B * n_h * D * 4) + int(nblk.sum().item()) * 4 + B * 4
     achieved = alg_bytes / (split_avg * 1e-3) / 1e9
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None
-    if args.kernel == 0 and args.split == 0 and args.schedule == 0:  # the configuration the counters were taken on
+    if args.kernel == 0 and args.split == 0 and args.schedule == 0 and k == 1:  # the counters' configuration
         traffic_bytes = profiled_traffic(name)
     traffic = traffic_bytes / (split_avg * 1e-3) / 1e9 if traffic_bytes else None
     log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
@@ -217,7 +226,7 @@ def main():
         f"({100*achieved/PEAK_HBM_GBS:.1f}% of 8 TB/s), {value/1e9:.3f} G KV-tokens/s")
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and k == 1:
         import numpy as np
         import oracle
         p0 = pools[0]
@@ -263,7 +272,8 @@ def main():
                    else int(ctx.max().item()), "tokens_per_step": tokens_per_step, "n_h": n_h, "n_kv": n_kv,
                    "head_dim": D, "block_size": 16, "kernel": args.kernel, "split_blocks": args.split,
                    "schedule": args.schedule,
-                   "accumulate": "f32", "pool_replicas": reps},
+                   "accumulate": "f32", "pool_replicas": reps, "q_len": k,
+                   "query_tokens_per_s": B * k / (ms_per_step * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,

@@ -89,6 +89,12 @@ def _declare(L):
     for f in ("kvo_gather_blocks", "kvo_scatter_blocks"):
         getattr(L, f).restype = None
         getattr(L, f).argtypes = [_I, _P, _P, _P, _I, _P]
+    L.kvo_deviation.restype = None
+    L.kvo_deviation.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P]
+    L.kvo_topk.restype = None
+    L.kvo_topk.argtypes = [_P, _I, _I, _P]
+    L.kvo_recompute_ratio.restype = _D
+    L.kvo_recompute_ratio.argtypes = [_D, _D, _I, _D]
     L.kvo_set_threads.restype = None
     L.kvo_set_threads.argtypes = [_I]
     L.kvo_max_threads.restype = _I
@@ -321,6 +327,32 @@ def scatter_blocks(arrays, blocks, buffer: np.ndarray) -> None:
     blocks = _i32(blocks)
     buffer = np.ascontiguousarray(buffer, dtype=np.uint8)
     lib().kvo_scatter_blocks(len(arrs), ptrs, sizes, _ptr(blocks), len(blocks), _ptr(buffer))
+
+
+def deviation(K: np.ndarray, V: np.ndarray, chunk_blocks, first_slot: int, k_re: np.ndarray,
+              v_re: np.ndarray, token_ids=None) -> np.ndarray:
+    """fp64 squared KV deviation per row of k_re / v_re ([rows][n_kv][d])."""
+    nb, n_kv, bs, d = K.shape
+    chunk_blocks = _i32(chunk_blocks)
+    tid = None if token_ids is None else _i32(token_ids)
+    k_re, v_re = np.ascontiguousarray(k_re), np.ascontiguousarray(v_re)
+    assert k_re.dtype == K.dtype == v_re.dtype == V.dtype
+    out = np.zeros(k_re.shape[0], dtype=np.float64)
+    lib().kvo_deviation(_dtype_of(K), n_kv, d, _ptr(K), _ptr(V), _ptr(chunk_blocks), int(first_slot), _ptr(tid),
+                        k_re.shape[0], _ptr(k_re), _ptr(v_re), _ptr(out))
+    return out
+
+
+def topk(values: np.ndarray, k: int) -> np.ndarray:
+    """Rows of the k largest values (ties: lower row), in ascending order."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.zeros(min(k, len(v)), dtype=np.int32)
+    lib().kvo_topk(_ptr(v), len(v), int(k), _ptr(out))
+    return out
+
+
+def recompute_ratio(load_time: float, token_time: float, num_tokens: int, floor_ratio: float = 0.15) -> float:
+    return lib().kvo_recompute_ratio(float(load_time), float(token_time), int(num_tokens), float(floor_ratio))
 
 
 def set_threads(n: int) -> None:

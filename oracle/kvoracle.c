@@ -684,3 +684,73 @@ int kvo_attention_multi(int kv_dtype, const void *K, const void *V, int q_dtype,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* CacheBlend token selection                                          */
+/* ------------------------------------------------------------------ */
+
+/* [BLEND, "Methods"]: a token's KV deviation is how far its precomputed K/V
+ * lie from the recomputed ones; tokens with the largest deviation are
+ * recomputed. Reading: the deviation of chunk token t is the squared L2
+ * distance over all kv heads and channels, sum (K_re - K_pre)^2 +
+ * (V_re - V_pre)^2. Row i of k_re / v_re ([n_rows][n_kv][d]) is the recomputed
+ * KV of chunk token token_ids[i] (token_ids NULL: token i), the chunk's
+ * token t living at logical position first_slot + t of chunk_blocks. fp64. */
+void kvo_deviation(int dtype, int n_kv, int d, const void *K, const void *V, const int32_t *chunk_blocks,
+                   int first_slot, const int32_t *token_ids, int n_rows, const void *k_re, const void *v_re,
+                   double *dev)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        int t = token_ids ? token_ids[i] : i;
+        int pos = first_slot + t;
+        int p = chunk_blocks[pos / BLOCK];
+        double acc = 0.0;
+        for (int h = 0; h < n_kv; ++h) {
+            size_t row = row_index(n_kv, d, p, h, pos % BLOCK);
+            size_t rr = ((size_t)i * n_kv + h) * d;
+            for (int c = 0; c < d; ++c) {
+                double dk = load_elem(dtype, k_re, rr + c) - load_elem(dtype, K, row + c);
+                double dv = load_elem(dtype, v_re, rr + c) - load_elem(dtype, V, row + c);
+                acc += dk * dk + dv * dv;
+            }
+        }
+        dev[i] = acc;
+    }
+}
+
+/* [BLEND, "Methods"]: keep the k rows of largest deviation; equal values go
+ * to the lower row first. The chosen rows are returned in ascending order
+ * (row ids; with a candidate list the caller maps them through it). */
+void kvo_topk(const float *values, int n, int k, int32_t *out)
+{
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) idx[i] = i;
+    /* selection by repeated scans: plain and obviously correct, O(n k) */
+    char *taken = (char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    for (int r = 0; r < k && r < n; ++r) {
+        int best = -1;
+        for (int i = 0; i < n; ++i) {
+            if (taken[i]) continue;
+            if (best < 0 || values[i] > values[best]) best = i; /* strict: ties keep the lower row */
+        }
+        taken[best] = 1;
+    }
+    int m = 0;
+    for (int i = 0; i < n; ++i)
+        if (taken[i]) out[m++] = idx[i];
+    free(taken);
+    free(idx);
+}
+
+/* [BLEND, "System Design"]: recompute ratio = max(15 %, the ratio at which
+ * recomputing the selected tokens takes as long as loading the next layer's
+ * KV). With load_time the time to load one layer's KV and token_time the time
+ * to recompute one token of one layer, that ratio is load_time /
+ * (num_tokens * token_time); the result is also capped at 1. */
+double kvo_recompute_ratio(double load_time, double token_time, int num_tokens, double floor_ratio)
+{
+    double r = (num_tokens > 0 && token_time > 0.0) ? load_time / ((double)num_tokens * token_time) : 1.0;
+    if (r < floor_ratio) r = floor_ratio;
+    if (r > 1.0) r = 1.0;
+    return r;
+}

@@ -16,7 +16,8 @@ SRC = os.path.join(ROOT, "oracle", "kvoracle.c")
 
 MUTANTS = {
     # query head -> kv head mapping interleaved instead of contiguous groups
-    "grouping": ("int kvh = h / g;", "int kvh = h % n_kv;"),
+    "grouping": ("int kvh = h / g;\n        int n = ctx_lens[b];", "int kvh = h % n_kv;\n        int n = ctx_lens[b];"),
+    "multi_grouping": ("int kvh = h / g;\n        int hi", "int kvh = h % n_kv;\n        int hi"),
     # the softmax scale dropped
     "scale": ("double s = scale * dot;", "double s = dot;"),
     # append writes the slot after the right one
@@ -47,6 +48,22 @@ MUTANTS = {
     "rope_freq": ("double theta = pow(base, -(2.0 * i) / d);", "double theta = pow(base, -(1.0 * i) / d);"),
     # half-split pairing wrong
     "rope_pair": ("*c1 = i + d / 2;", "*c1 = d - 1 - i;"),
+    # several query tokens: no causal mask among the new tokens
+    "multi_causal": ("int hi = ctx_lens[b] - q_len + i + 1;", "int hi = ctx_lens[b];"),
+    # several query tokens: a token does not see itself
+    "multi_self": ("int hi = ctx_lens[b] - q_len + i + 1;", "int hi = ctx_lens[b] - q_len + i;"),
+    # block copy in the wrong direction
+    "copy_dir": ("memcpy(regions[r] + (size_t)dst[i] * block_bytes[r], regions[r] + (size_t)src[i] * block_bytes[r],",
+                 "memcpy(regions[r] + (size_t)src[i] * block_bytes[r], regions[r] + (size_t)dst[i] * block_bytes[r],"),
+    # KV deviation without the V term
+    "dev_no_v": ("acc += dk * dk + dv * dv;", "acc += dk * dk;"),
+    # KV deviation read from the chunk's first block slot instead of its real start
+    "dev_offset": ("int pos = first_slot + t;\n        int p = chunk_blocks[pos / BLOCK];\n        double acc",
+                   "int pos = t;\n        int p = chunk_blocks[pos / BLOCK];\n        double acc"),
+    # top-k ties go to the higher row
+    "topk_tie": ("if (best < 0 || values[i] > values[best]) best = i;", "if (best < 0 || values[i] >= values[best]) best = i;"),
+    # recompute ratio without its floor
+    "ratio_floor": ("if (r < floor_ratio) r = floor_ratio;", ""),
 }
 
 

@@ -680,3 +680,53 @@ def test_multi_token_last_query_is_decode_and_causality(orc):
     multi2 = orc.attention_multi(K2, V, q, tab, ctx, c.scale)
     assert np.array_equal(multi2[0, :k - 1], multi[0, :k - 1])
     assert not np.array_equal(multi2[0, k - 1], multi[0, k - 1])
+
+
+# ---------------------------------------------------------------------------
+# CacheBlend token selection
+# ---------------------------------------------------------------------------
+
+def test_deviation_definition(orc):
+    rng = np.random.default_rng(70)
+    # quarter-integers: every offset below is exact in fp32
+    K = (rng.integers(-16, 16, (6, 2, 16, 64)) / 4).astype(np.float32)
+    V = (rng.integers(-16, 16, (6, 2, 16, 64)) / 4).astype(np.float32)
+    chunk = np.array([4, 1, 5])
+    # recomputed = precomputed: deviation 0; a known offset gives a known value
+    pos = 3 + np.arange(20)                                # chunk tokens 0..19 at positions 3..22
+    pre_k = K[chunk[pos // 16], :, pos % 16, :]
+    pre_v = V[chunk[pos // 16], :, pos % 16, :]
+    assert np.all(orc.deviation(K, V, chunk, 3, pre_k, pre_v) == 0.0)
+    k_re, v_re = pre_k.copy(), pre_v.copy()
+    k_re[7] += 0.5                                         # 2 heads x 64 channels of 0.25
+    v_re[11, 1, 3] -= 3.0                                  # one element of 9
+    dev = orc.deviation(K, V, chunk, 3, k_re, v_re)
+    assert abs(dev[7] - 2 * 64 * 0.25) < 1e-9 and abs(dev[11] - 9.0) < 1e-9
+    assert np.count_nonzero(dev) == 2
+    # candidate rows: row i is chunk token ids[i]
+    ids = np.array([11, 7, 2])
+    dev2 = orc.deviation(K, V, chunk, 3, k_re[ids], v_re[ids], token_ids=ids)
+    assert np.array_equal(dev2, dev[ids])
+
+
+def test_topk_selection(orc):
+    v = np.array([0.5, 3.0, 1.0, 3.0, -2.0, 7.0, 1.0], dtype=np.float32)
+    assert list(orc.topk(v, 3)) == [1, 3, 5]              # 7, then the two 3s
+    assert list(orc.topk(v, 2)) == [1, 5]                 # tie between rows 1 and 3: the lower wins
+    assert list(orc.topk(v, 5)) == [1, 2, 3, 5, 6]
+    assert list(orc.topk(v, 0)) == []
+    assert list(orc.topk(v, 99)) == list(range(7))
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal(1000).astype(np.float32)
+    sel = orc.topk(x, 150)
+    ref = np.sort(np.argsort(-x, kind="stable")[:150])    # numpy's stable sort as the independent check
+    assert np.array_equal(sel, ref)
+
+
+def test_recompute_ratio(orc):
+    # loading a layer takes as long as recomputing 40 % of 1000 tokens
+    assert abs(orc.recompute_ratio(400.0, 1.0, 1000) - 0.4) < 1e-15
+    # a fast load hides little: the 15 % floor applies
+    assert orc.recompute_ratio(10.0, 1.0, 1000) == 0.15
+    # a slow load could hide more than everything: capped at 1
+    assert orc.recompute_ratio(5000.0, 1.0, 1000) == 1.0

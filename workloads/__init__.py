@@ -146,14 +146,17 @@ def _poison_unused(K: torch.Tensor, V: torch.Tensor, tables: torch.Tensor, valid
 
 def make_case(seed: int, batch: int, lens, n_h: int, n_kv: int, d: int, dtype: str = "bf16",
               num_blocks: int | None = None, pool_slack: float = 1.0, device="cpu",
-              append: bool = True, max_blocks: int | None = None, poison: bool = True,
+              append: bool | int = True, max_blocks: int | None = None, poison: bool = True,
               outliers: int = 0, outlier_scale: float = 10.0, name: str = "custom") -> Case:
     """A decode step over private (unshared) blocks.
 
     lens: the per-sequence lengths before the append (list), or
     ("uniform", lo, hi) / ("fixed", n) drawn with the seed.
-    Every sequence owns ceil((len + append) / 16) blocks; physical ids come
+    append: False, True (one new token per sequence) or a number n of new
+    tokens; with n > 1, q is [B][n][n_h][d] and k_new, v_new [B][n][n_kv][d].
+    Every sequence owns ceil((len + new tokens) / 16) blocks; physical ids come
     from a seeded permutation of the pool, handed out in logical order."""
+    n_new = int(append)
     if isinstance(lens, tuple) and lens and isinstance(lens[0], str):
         if lens[0] == "uniform":
             g = _gen(seed, _S_LENS, "cpu")
@@ -163,7 +166,7 @@ def make_case(seed: int, batch: int, lens, n_h: int, n_kv: int, d: int, dtype: s
     else:
         lens_t = torch.tensor(list(lens), dtype=torch.int64)
     assert len(lens_t) == batch
-    ctx = lens_t + (1 if append else 0)
+    ctx = lens_t + n_new
     need = [(int(c) + BLOCK - 1) // BLOCK for c in ctx]
     total = sum(need)
     if num_blocks is None:
@@ -189,14 +192,21 @@ def make_case(seed: int, batch: int, lens, n_h: int, n_kv: int, d: int, dtype: s
     V = normal(shape, seed, _S_V, device, tdt)
     if poison:
         _poison_unused(K, V, tables, lens_t.tolist())
-    q = normal((batch, n_h, d), seed, _S_Q, device, tdt)
-    k_new = normal((batch, n_kv, d), seed, _S_KNEW, device, tdt, scale_channels=sc)
-    v_new = normal((batch, n_kv, d), seed, _S_VNEW, device, tdt)
+    lead = (batch,) if n_new <= 1 else (batch, n_new)
+    q = normal(lead + (n_h, d), seed, _S_Q, device, tdt)
+    if sc is not None and n_new > 1:
+        sc = (sc[0], sc[1])
+        k_new = normal(lead + (n_kv, d), seed, _S_KNEW, device, tdt)
+        for h in range(n_kv):
+            k_new[..., h, sc[0][h]] = (k_new[..., h, sc[0][h]].float() * sc[1]).to(tdt)
+    else:
+        k_new = normal(lead + (n_kv, d), seed, _S_KNEW, device, tdt, scale_channels=sc)
+    v_new = normal(lead + (n_kv, d), seed, _S_VNEW, device, tdt)
     return Case(name=name, batch=batch, n_h=n_h, n_kv=n_kv, d=d, dtype=dtype,
                 num_blocks=num_blocks, tables=tables.to(device),
                 seq_lens=lens_t.to(torch.int32).to(device), ctx_lens=ctx.to(torch.int32).to(device),
-                K=K, V=V, q=q, k_new=k_new, v_new=v_new, scale=softmax_scale(d), append=append,
-                outlier_channels=outl)
+                K=K, V=V, q=q, k_new=k_new, v_new=v_new, scale=softmax_scale(d), append=n_new > 0,
+                outlier_channels=outl, meta={"n_new": n_new})
 
 
 def make_shared_prefix_case(seed: int, batch: int, ctx: int, shared_tokens: int, n_h: int, n_kv: int,
@@ -236,8 +246,9 @@ def make_shared_prefix_case(seed: int, batch: int, ctx: int, shared_tokens: int,
                 rope_base=rope_base)
 
 
-def workload(name: str, device="cpu", poison: bool = True) -> Case:
-    """The named workload at full size."""
+def workload(name: str, device="cpu", poison: bool = True, n_new: int | None = None) -> Case:
+    """The named workload at full size. n_new overrides the number of tokens
+    appended per sequence (several: a verification step of speculated tokens)."""
     w = WORKLOADS[name]
     if name == "long_shared":
         return make_shared_prefix_case(w["seed"], w["batch"], w["lens"][1], w["shared_tokens"], w["n_h"],
@@ -245,7 +256,7 @@ def workload(name: str, device="cpu", poison: bool = True) -> Case:
                                        w["delta_range"], w["rope_base"], w["dtype"], device, name)
     c = make_case(w["seed"], w["batch"], w["lens"], w["n_h"], w["n_kv"], w["d"], w["dtype"],
                   num_blocks=w.get("num_blocks"), pool_slack=w.get("pool_slack", 1.0), device=device,
-                  append=w["append"], poison=poison, outliers=w.get("outliers", 0),
+                  append=w["append"] if n_new is None else n_new, poison=poison, outliers=w.get("outliers", 0),
                   outlier_scale=w.get("outlier_scale", 10.0), name=name)
     c.int4 = bool(w.get("int4", False))
     return c
