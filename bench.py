@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence: 1 is decode; k > 1 appends k tokens and runs the "
                          "multi-token (verification) attention over them")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "quantize", "rope", "copy", "offload"],
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "quantize", "rope", "copy", "offload", "select"],
                     help="decode: the decode step (default); the others time one secondary kernel")
     args = ap.parse_args()
 
@@ -284,6 +284,13 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def hold_queue(torch, launches: int) -> None:
+    """Keep the GPU busy while the host enqueues the timed launches, so that
+    host-side call overhead never shows up between a kernel's two events
+    (a spin kernel of about 300 us per launch to come)."""
+    torch.cuda._sleep(int(launches * 300e-6 * 2.4e9))
+
+
 def bench_op(args, torch, kv, wl, dev):
     """Time one secondary kernel on its natural workload; one JSON line.
 
@@ -293,19 +300,34 @@ def bench_op(args, torch, kv, wl, dev):
     copy      kv_copy_blocks of 4096 blocks of the 8B-shaped pool
     offload   kv_gather_blocks of 2048 blocks into pinned host memory, then
               kv_scatter_blocks back (host link bandwidth)
+    select    kv_token_deviation over every reused token of the selection
+              workload (16 requests x 8192 tokens, 8B-shaped KV); the top-k
+              of each request at the 15 % floor is timed beside it
     All rates are algorithmic bytes (every byte read or written once) per
     second of the kernel's average duration (HIP events, launch stream)."""
     hip = HipEvents()
     stream = torch.cuda.current_stream()
     name = {"append": "llama3_8b", "quantize": "kvquant_int4", "rope": "long_shared", "copy": "llama3_8b",
-            "offload": "llama3_8b"}[args.op]
-    c = wl.workload(name, device=dev, poison=False)
+            "offload": "llama3_8b", "select": "blend_select"}[args.op]
+    c = wl.blend_workload(name, dev) if args.op == "select" else wl.workload(name, device=dev, poison=False)
     D, n_kv, B = c.d, c.n_kv, c.batch
     pool = kv.KVPool(c.num_blocks, n_kv, D, c.dtype, device=dev)
     pool.K.copy_(c.K)
     pool.V.copy_(c.V)
     extra = {}
-    if args.op == "append":
+    if args.op == "select":
+        dev_out = torch.empty(c.n_rows, dtype=torch.float64, device=dev)
+        fn = lambda: kv.kv_token_deviation(pool, c.tables, c.row_seq, c.row_pos, c.k_re, c.v_re, dev_out,
+                                           stream=stream)
+        es = 2 if c.dtype == "bf16" else 4
+        # per row: recomputed K and V rows, cached K and V rows, (seq, pos), the fp64 result
+        nbytes = c.n_rows * (4 * n_kv * D * es + 8 + 8)
+        ratio = wl.BLEND_WORKLOADS[name]["ratio"]
+        lens = (c.seg_offsets[1:] - c.seg_offsets[:-1]).tolist()
+        ks = torch.tensor([kv.kv_recompute_count(ratio, n) for n in lens], dtype=torch.int32, device=dev)
+        sel = torch.empty(c.n_rows, dtype=torch.int32, device=dev)
+        back = lambda: kv.kv_topk_select(dev_out, c.seg_offsets, ks, sel, stream=stream)
+    elif args.op == "append":
         fn = lambda: kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
         nbytes = 2 * (B * n_kv * 2 * D * 2)
     elif args.op == "quantize":
@@ -333,6 +355,7 @@ def bench_op(args, torch, kv, wl, dev):
         fn()
     torch.cuda.synchronize()
     evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    hold_queue(torch, args.steps)
     for a, b in evs:
         hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         hip.hip.hipEventRecord(a, ctypes.c_void_p(stream.cuda_stream))
@@ -340,16 +363,21 @@ def bench_op(args, torch, kv, wl, dev):
         hip.hip.hipEventRecord(b, ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / len(evs)
-    if args.op == "offload":
+    if args.op in ("offload", "select"):
         evs2 = [(hip.create(), hip.create()) for _ in range(args.steps)]
+        hold_queue(torch, args.steps)
         for a, b in evs2:
             hip.hip.hipEventRecord(a, ctypes.c_void_p(stream.cuda_stream))
             back()
             hip.hip.hipEventRecord(b, ctypes.c_void_p(stream.cuda_stream))
         torch.cuda.synchronize()
         ms_back = sum(hip.elapsed_ms(a, b) for a, b in evs2) / len(evs2)
-        extra = {"restore_avg_us": ms_back * 1e3, "restore_GBps": nbytes / (ms_back * 1e-3) / 1e9,
-                 "direction_of_value": "device -> pinned host"}
+        if args.op == "offload":
+            extra = {"restore_avg_us": ms_back * 1e3, "restore_GBps": nbytes / (ms_back * 1e-3) / 1e9,
+                     "direction_of_value": "device -> pinned host"}
+        else:
+            extra = {"topk_avg_us": ms_back * 1e3, "topk_segments": len(lens), "topk_k": int(ks[0].item()),
+                     "rows": c.n_rows}
     rate = nbytes / (ms * 1e-3) / 1e9
     line = {"metric": f"{args.op}: algorithmic bytes per second", "value": rate, "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "avg_us": ms * 1e3, "bytes_per_launch": nbytes,
@@ -358,7 +386,8 @@ def bench_op(args, torch, kv, wl, dev):
                          "frac": rate / PEAK_HBM_GBS}}
     line.update(extra)
     log(f"[bench] {args.op}: {ms*1e3:.1f} us per launch, {rate:.0f} GB/s" +
-        (f", restore {extra['restore_avg_us']:.1f} us ({extra['restore_GBps']:.0f} GB/s)" if extra else ""))
+        (f", restore {extra['restore_avg_us']:.1f} us ({extra['restore_GBps']:.0f} GB/s)" if "restore_avg_us" in extra
+         else "") + (f", top-k {extra['topk_avg_us']:.1f} us" if "topk_avg_us" in extra else ""))
     print(json.dumps(line), flush=True)
 
 

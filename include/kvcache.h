@@ -10,7 +10,9 @@
  *           (decode-step listing), "메모리 공식과 GQA의 동기",
  *           "KVQuant: 마지막 4배" (quantizer equation).
  *   [BLEND] "Research Paper Review : CACHE BLEND": "Background" (full KV reuse
- *           and RoPE re-rotation of a precomputed chunk).
+ *           and RoPE re-rotation of a precomputed chunk), "Methods" (KV
+ *           deviation, selective recompute), "System Design" (recompute
+ *           ratio).
  *
  * Conventions for every call:
  *   - Device pointers point to memory the caller owns (allocated with
@@ -302,6 +304,50 @@ kv_status kv_gather_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, voi
  * blocks[0..n); ids must be distinct. */
 kv_status kv_scatter_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, const void *buffer, size_t bytes,
                             void *stream);
+
+/* KV deviation [BLEND, "Methods"]: for row i, the squared L2 distance between
+ * the recomputed K/V of one token and the cached K/V of the same token,
+ * summed over every kv head and channel of both K and V:
+ *   deviation[i] = sum_h,c (k_re[i][h][c] - K[tok][h][c])^2
+ *                        + (v_re[i][h][c] - V[tok][h][c])^2,
+ * where tok is position row_pos[i] of sequence row_seq[i], found through
+ * block_tables[row_seq[i]] (the distance ranks tokens the way the L2 norm
+ * does). Computed in fp64 from exact differences; only the summation order
+ * differs from a sequential sum.
+ *   block_tables  device int32 [batch][max_blocks]
+ *   row_seq, row_pos  device int32 [n_rows]
+ *   k_re, v_re    device [n_rows][num_kv_heads][head_dim] of the pool dtype,
+ *                 16-byte aligned
+ *   deviation     device fp64 [n_rows]
+ * A row whose sequence, position or block id is out of range gets -inf (it is
+ * never selected ahead of a valid row). KV_F32 and KV_BF16 pools only. */
+kv_status kv_token_deviation(kv_pool_t pool, const int32_t *block_tables, int32_t max_blocks, int32_t batch,
+                             const int32_t *row_seq, const int32_t *row_pos, int32_t n_rows, const void *k_re,
+                             const void *v_re, double *deviation, void *stream);
+
+/* Selective recompute [BLEND, "Methods"]: the tokens of largest deviation are
+ * recomputed. For each segment s, values[seg_offsets[s] .. seg_offsets[s+1])
+ * (device fp64), write the indices (relative to the segment) of its
+ * min(seg_k[s], length) largest values, in ascending order, to
+ * selected[seg_offsets[s] ..]; equal values are taken lowest index first.
+ * Values must not be NaN (a NaN's rank is unspecified); -0 equals +0.
+ *   seg_offsets  device int32 [n_seg + 1], non-decreasing (a segment with a
+ *                negative length is skipped); seg_k device int32 [n_seg]
+ *   selected     device int32, at least seg_offsets[n_seg] entries; entries
+ *                past a segment's count are left unwritten. */
+kv_status kv_topk_select(const double *values, const int32_t *seg_offsets, const int32_t *seg_k, int32_t n_seg,
+                         int32_t *selected, void *stream);
+
+/* [BLEND, "System Design"]: recompute ratio = max(floor_ratio, the ratio at
+ * which recomputing the chosen tokens of a layer takes as long as loading the
+ * next layer's KV), capped at 1. load_time: time to load one layer's KV;
+ * token_time: time to recompute one token of one layer (same unit). The pages
+ * put the floor at 15 % (floor_ratio 0.15). Host only. */
+double kv_recompute_ratio(double load_time, double token_time, int32_t num_tokens, double floor_ratio);
+
+/* Tokens to recompute: ceil(ratio * num_tokens) in fp64, within
+ * [0, num_tokens]. Host only. */
+int32_t kv_recompute_count(double ratio, int32_t num_tokens);
 
 /* Host-side check of HOST copies of the metadata a decode step would use:
  * every block the first lens[b] tokens (after the append when `appending`

@@ -90,11 +90,13 @@ def _declare(L):
         getattr(L, f).restype = None
         getattr(L, f).argtypes = [_I, _P, _P, _P, _I, _P]
     L.kvo_deviation.restype = None
-    L.kvo_deviation.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P]
+    L.kvo_deviation.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P]
     L.kvo_topk.restype = None
     L.kvo_topk.argtypes = [_P, _I, _I, _P]
     L.kvo_recompute_ratio.restype = _D
     L.kvo_recompute_ratio.argtypes = [_D, _D, _I, _D]
+    L.kvo_recompute_count.restype = _I
+    L.kvo_recompute_count.argtypes = [_D, _I]
     L.kvo_set_threads.restype = None
     L.kvo_set_threads.argtypes = [_I]
     L.kvo_max_threads.restype = _I
@@ -329,23 +331,25 @@ def scatter_blocks(arrays, blocks, buffer: np.ndarray) -> None:
     lib().kvo_scatter_blocks(len(arrs), ptrs, sizes, _ptr(blocks), len(blocks), _ptr(buffer))
 
 
-def deviation(K: np.ndarray, V: np.ndarray, chunk_blocks, first_slot: int, k_re: np.ndarray,
-              v_re: np.ndarray, token_ids=None) -> np.ndarray:
-    """fp64 squared KV deviation per row of k_re / v_re ([rows][n_kv][d])."""
+def deviation(K: np.ndarray, V: np.ndarray, tables, row_seq, row_pos, k_re: np.ndarray,
+              v_re: np.ndarray) -> np.ndarray:
+    """fp64 squared KV deviation of row i of k_re / v_re ([rows][n_kv][d])
+    from the cached KV of token row_pos[i] of sequence row_seq[i]."""
     nb, n_kv, bs, d = K.shape
-    chunk_blocks = _i32(chunk_blocks)
-    tid = None if token_ids is None else _i32(token_ids)
+    tables = _i32(tables)
+    rs, rp = _i32(row_seq), _i32(row_pos)
     k_re, v_re = np.ascontiguousarray(k_re), np.ascontiguousarray(v_re)
     assert k_re.dtype == K.dtype == v_re.dtype == V.dtype
+    assert len(rs) == len(rp) == k_re.shape[0] == v_re.shape[0]
     out = np.zeros(k_re.shape[0], dtype=np.float64)
-    lib().kvo_deviation(_dtype_of(K), n_kv, d, _ptr(K), _ptr(V), _ptr(chunk_blocks), int(first_slot), _ptr(tid),
+    lib().kvo_deviation(_dtype_of(K), n_kv, d, _ptr(K), _ptr(V), _ptr(tables), tables.shape[-1], _ptr(rs), _ptr(rp),
                         k_re.shape[0], _ptr(k_re), _ptr(v_re), _ptr(out))
     return out
 
 
 def topk(values: np.ndarray, k: int) -> np.ndarray:
     """Rows of the k largest values (ties: lower row), in ascending order."""
-    v = np.ascontiguousarray(values, dtype=np.float32)
+    v = np.ascontiguousarray(values, dtype=np.float64)
     out = np.zeros(min(k, len(v)), dtype=np.int32)
     lib().kvo_topk(_ptr(v), len(v), int(k), _ptr(out))
     return out
@@ -353,6 +357,10 @@ def topk(values: np.ndarray, k: int) -> np.ndarray:
 
 def recompute_ratio(load_time: float, token_time: float, num_tokens: int, floor_ratio: float = 0.15) -> float:
     return lib().kvo_recompute_ratio(float(load_time), float(token_time), int(num_tokens), float(floor_ratio))
+
+
+def recompute_count(ratio: float, num_tokens: int) -> int:
+    return lib().kvo_recompute_count(float(ratio), int(num_tokens))
 
 
 def set_threads(n: int) -> None:

@@ -691,19 +691,18 @@ int kvo_attention_multi(int kv_dtype, const void *K, const void *V, int q_dtype,
 
 /* [BLEND, "Methods"]: a token's KV deviation is how far its precomputed K/V
  * lie from the recomputed ones; tokens with the largest deviation are
- * recomputed. Reading: the deviation of chunk token t is the squared L2
- * distance over all kv heads and channels, sum (K_re - K_pre)^2 +
- * (V_re - V_pre)^2. Row i of k_re / v_re ([n_rows][n_kv][d]) is the recomputed
- * KV of chunk token token_ids[i] (token_ids NULL: token i), the chunk's
- * token t living at logical position first_slot + t of chunk_blocks. fp64. */
-void kvo_deviation(int dtype, int n_kv, int d, const void *K, const void *V, const int32_t *chunk_blocks,
-                   int first_slot, const int32_t *token_ids, int n_rows, const void *k_re, const void *v_re,
+ * recomputed. Reading: the deviation of a token is the squared L2 distance
+ * over all kv heads and channels, sum (K_re - K_pre)^2 + (V_re - V_pre)^2.
+ * Row i of k_re / v_re ([n_rows][n_kv][d], pool dtype) is the recomputed KV of
+ * the token at position row_pos[i] of sequence row_seq[i], whose cached KV is
+ * found through that sequence's block table. fp64. */
+void kvo_deviation(int dtype, int n_kv, int d, const void *K, const void *V, const int32_t *tables, int max_blocks,
+                   const int32_t *row_seq, const int32_t *row_pos, int n_rows, const void *k_re, const void *v_re,
                    double *dev)
 {
     for (int i = 0; i < n_rows; ++i) {
-        int t = token_ids ? token_ids[i] : i;
-        int pos = first_slot + t;
-        int p = chunk_blocks[pos / BLOCK];
+        int pos = row_pos[i];
+        int p = tables[(size_t)row_seq[i] * max_blocks + pos / BLOCK];
         double acc = 0.0;
         for (int h = 0; h < n_kv; ++h) {
             size_t row = row_index(n_kv, d, p, h, pos % BLOCK);
@@ -720,26 +719,41 @@ void kvo_deviation(int dtype, int n_kv, int d, const void *K, const void *V, con
 
 /* [BLEND, "Methods"]: keep the k rows of largest deviation; equal values go
  * to the lower row first. The chosen rows are returned in ascending order
- * (row ids; with a candidate list the caller maps them through it). */
-void kvo_topk(const float *values, int n, int k, int32_t *out)
+ * (row ids; with a candidate list the caller maps them through it).
+ * Plainly: sort (value, row) pairs by value descending, row ascending, keep
+ * the first k, then sort those rows ascending. -0 and +0 compare equal. */
+typedef struct {
+    double v;
+    int32_t i;
+} kvo_vi;
+
+static int kvo_vi_rank(const void *pa, const void *pb)
 {
-    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
-    for (int i = 0; i < n; ++i) idx[i] = i;
-    /* selection by repeated scans: plain and obviously correct, O(n k) */
-    char *taken = (char *)calloc((size_t)(n > 0 ? n : 1), 1);
-    for (int r = 0; r < k && r < n; ++r) {
-        int best = -1;
-        for (int i = 0; i < n; ++i) {
-            if (taken[i]) continue;
-            if (best < 0 || values[i] > values[best]) best = i; /* strict: ties keep the lower row */
-        }
-        taken[best] = 1;
+    const kvo_vi *a = (const kvo_vi *)pa, *b = (const kvo_vi *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i > b->i) - (a->i < b->i);
+}
+
+static int kvo_i32_asc(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+void kvo_topk(const double *values, int n, int k, int32_t *out)
+{
+    if (k > n) k = n;
+    if (k <= 0) return;
+    kvo_vi *all = (kvo_vi *)malloc(sizeof(kvo_vi) * (size_t)n);
+    for (int i = 0; i < n; ++i) {
+        all[i].v = values[i];
+        all[i].i = i;
     }
-    int m = 0;
-    for (int i = 0; i < n; ++i)
-        if (taken[i]) out[m++] = idx[i];
-    free(taken);
-    free(idx);
+    qsort(all, (size_t)n, sizeof(kvo_vi), kvo_vi_rank);
+    for (int r = 0; r < k; ++r) out[r] = all[r].i;
+    qsort(out, (size_t)k, sizeof(int32_t), kvo_i32_asc);
+    free(all);
 }
 
 /* [BLEND, "System Design"]: recompute ratio = max(15 %, the ratio at which
@@ -753,4 +767,14 @@ double kvo_recompute_ratio(double load_time, double token_time, int num_tokens, 
     if (r < floor_ratio) r = floor_ratio;
     if (r > 1.0) r = 1.0;
     return r;
+}
+
+/* Tokens to recompute out of num_tokens at a ratio: the smallest whole count
+ * not below ratio * num_tokens (fp64), within [0, num_tokens]. */
+int kvo_recompute_count(double ratio, int num_tokens)
+{
+    double c = ceil(ratio * (double)num_tokens);
+    if (c < 0.0) c = 0.0;
+    if (c > (double)num_tokens) c = (double)num_tokens;
+    return (int)c;
 }

@@ -52,7 +52,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
-_P, _I32, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_P, _I32, _SZ, _F, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
 
 
 def _decl(name, res, args):
@@ -87,6 +87,10 @@ _kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
 _kv_copy_blocks = _decl("kv_copy_blocks", _I32, [_P, _P, _P, _I32, _P])
 _kv_gather_blocks = _decl("kv_gather_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
 _kv_scatter_blocks = _decl("kv_scatter_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
+_kv_token_deviation = _decl("kv_token_deviation", _I32, [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P])
+_kv_topk_select = _decl("kv_topk_select", _I32, [_P, _P, _P, _I32, _P, _P])
+_kv_recompute_ratio = _decl("kv_recompute_ratio", _D, [_D, _D, _I32, _D])
+_kv_recompute_count = _decl("kv_recompute_count", _I32, [_D, _I32])
 _kv_validate_tables = _decl("kv_validate_tables", _I32,
                             [ctypes.POINTER(kv_pool_desc), _P, _I32, _P, _I32, _I32, ctypes.POINTER(_I32)])
 
@@ -355,6 +359,49 @@ def kv_scatter_blocks(pool: KVPool, blocks: torch.Tensor, buffer: torch.Tensor, 
                               _stream(stream)), "kv_scatter_blocks")
 
 
+def kv_token_deviation(pool: KVPool, block_tables: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor,
+                       k_re: torch.Tensor, v_re: torch.Tensor, deviation: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """fp64 KV deviation per row (see kv_token_deviation in kvcache.h)."""
+    n = int(row_seq.numel())
+    if int(row_pos.numel()) != n:
+        raise ValueError("row_seq and row_pos differ in length")
+    want = n * pool.desc.num_kv_heads * pool.desc.head_dim
+    kdt = torch.float32 if pool.desc.dtype == KV_F32 else torch.bfloat16
+    if deviation is None:
+        deviation = torch.empty(n, dtype=torch.float64, device=k_re.device)
+    batch, max_blocks = block_tables.shape
+    st = _kv_token_deviation(pool.handle, _i32(block_tables, "block_tables"), int(max_blocks), int(batch),
+                             _i32(row_seq, "row_seq"), _i32(row_pos, "row_pos"), n,
+                             _dev_ptr(k_re, "k_re", kdt, want), _dev_ptr(v_re, "v_re", kdt, want),
+                             _dev_ptr(deviation, "deviation", torch.float64, n), _stream(stream))
+    _check(st, "kv_token_deviation")
+    return deviation
+
+
+def kv_topk_select(values: torch.Tensor, seg_offsets: torch.Tensor, seg_k: torch.Tensor,
+                   selected: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Ascending indices of each segment's seg_k largest values (see kvcache.h)."""
+    n_seg = int(seg_k.numel())
+    if int(seg_offsets.numel()) != n_seg + 1:
+        raise ValueError("seg_offsets needs n_seg + 1 entries")
+    if selected is None:
+        selected = torch.full((int(values.numel()),), -1, dtype=torch.int32, device=values.device)
+    st = _kv_topk_select(_dev_ptr(values, "values", torch.float64), _i32(seg_offsets, "seg_offsets"),
+                         _i32(seg_k, "seg_k"), n_seg, _dev_ptr(selected, "selected", torch.int32, values.numel()),
+                         _stream(stream))
+    _check(st, "kv_topk_select")
+    return selected
+
+
+def kv_recompute_ratio(load_time: float, token_time: float, num_tokens: int, floor_ratio: float = 0.15) -> float:
+    return float(_kv_recompute_ratio(float(load_time), float(token_time), int(num_tokens), float(floor_ratio)))
+
+
+def kv_recompute_count(ratio: float, num_tokens: int) -> int:
+    return int(_kv_recompute_count(float(ratio), int(num_tokens)))
+
+
 def kv_validate_tables(desc: kv_pool_desc, block_tables, lens, appending: bool = True):
     """Host check of host copies (numpy int32 or CPU tensors). Returns
     (status, first bad row or -1)."""
@@ -376,5 +423,6 @@ raw = {
     "paged_multi_token_attention": _paged_multi_token_attention,
     "paged_multi_token_attention_workspace_bytes": _paged_multi_token_attention_workspace_bytes,
     "kv_block_bytes": _kv_block_bytes, "kv_copy_blocks": _kv_copy_blocks, "kv_gather_blocks": _kv_gather_blocks,
-    "kv_scatter_blocks": _kv_scatter_blocks,
+    "kv_scatter_blocks": _kv_scatter_blocks, "kv_token_deviation": _kv_token_deviation,
+    "kv_topk_select": _kv_topk_select,
 }

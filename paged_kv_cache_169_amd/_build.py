@@ -31,6 +31,7 @@ SOURCES = {
     "rope.hip": ["-ffp-contract=off"],
     "copy.hip": [],
     "attention.hip": [],
+    "blend.hip": [],
 }
 
 

@@ -485,6 +485,65 @@ kv_status kv_scatter_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, co
     return hip_status(launch_copy_blocks(c, static_cast<hipStream_t>(stream)));
 }
 
+kv_status kv_token_deviation(kv_pool_t pool, const int32_t *block_tables, int32_t max_blocks, int32_t batch,
+                             const int32_t *row_seq, const int32_t *row_pos, int32_t n_rows, const void *k_re,
+                             const void *v_re, double *deviation, void *stream) {
+    if (!pool || max_blocks < 1 || batch < 0 || n_rows < 0) return KV_ERR_INVALID_ARG;
+    if (pool->desc.dtype == KV_INT4) return KV_ERR_UNSUPPORTED;
+    if (n_rows == 0) return KV_OK;
+    if (!block_tables || !row_seq || !row_pos || !k_re || !v_re || !deviation) return KV_ERR_INVALID_ARG;
+    if (!aligned16(k_re) || !aligned16(v_re)) return KV_ERR_INVALID_ARG;
+    const PoolPtrs pp = pool_ptrs(pool);
+    DeviationParams a;
+    a.k = pp.k;
+    a.v = pp.v;
+    a.tables = block_tables;
+    a.row_seq = row_seq;
+    a.row_pos = row_pos;
+    a.k_re = k_re;
+    a.v_re = v_re;
+    a.out = deviation;
+    a.max_blocks = max_blocks;
+    a.batch = batch;
+    a.n_kv = pool->desc.num_kv_heads;
+    a.head_dim = pool->desc.head_dim;
+    a.num_blocks = pool->desc.num_blocks;
+    a.n_rows = n_rows;
+    const int es = pool->desc.dtype == KV_F32 ? 4 : 2;
+    const int chunks = a.n_kv * a.head_dim * es / 16;
+    int lanes = 64;
+    while (lanes > 1 && lanes / 2 >= chunks) lanes /= 2;
+    a.lanes = lanes;
+    return hip_status(launch_deviation(pool->desc.dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+kv_status kv_topk_select(const double *values, const int32_t *seg_offsets, const int32_t *seg_k, int32_t n_seg,
+                         int32_t *selected, void *stream) {
+    if (n_seg < 0) return KV_ERR_INVALID_ARG;
+    if (n_seg == 0) return KV_OK;
+    if (!values || !seg_offsets || !seg_k || !selected) return KV_ERR_INVALID_ARG;
+    TopkParams t;
+    t.values = values;
+    t.offsets = seg_offsets;
+    t.ks = seg_k;
+    t.selected = selected;
+    t.n_seg = n_seg;
+    return hip_status(launch_topk(t, static_cast<hipStream_t>(stream)));
+}
+
+double kv_recompute_ratio(double load_time, double token_time, int32_t num_tokens, double floor_ratio) {
+    double r = (num_tokens > 0 && token_time > 0.0) ? load_time / ((double)num_tokens * token_time) : 1.0;
+    if (!(r >= floor_ratio)) r = floor_ratio;  // also a NaN ratio
+    if (r > 1.0) r = 1.0;
+    return r;
+}
+
+int32_t kv_recompute_count(double ratio, int32_t num_tokens) {
+    if (num_tokens <= 0 || !(ratio > 0.0)) return 0;
+    const double c = std::ceil(ratio * (double)num_tokens);
+    return c >= (double)num_tokens ? num_tokens : (int32_t)c;
+}
+
 kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
                              const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row) {
     if (bad_row) *bad_row = -1;

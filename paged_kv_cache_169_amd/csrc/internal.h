@@ -76,7 +76,25 @@ struct CopyParams {
     int32_t n, num_blocks, mode;
 };
 
+struct DeviationParams {
+    const void *k, *v;            // pool K / V (f32 or bf16)
+    const int32_t *tables, *row_seq, *row_pos;
+    const void *k_re, *v_re;      // [n_rows][n_kv][head_dim], pool dtype
+    double *out;                  // [n_rows]
+    int32_t max_blocks, batch, n_kv, head_dim, num_blocks, n_rows;
+    int32_t lanes;                // lanes per token: 64, or a smaller power of two
+};
+
+struct TopkParams {
+    const double *values;
+    const int32_t *offsets, *ks;  // [n_seg + 1], [n_seg]
+    int32_t *selected;            // segment s writes at offsets[s] ..
+    int32_t n_seg;
+};
+
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
+hipError_t launch_deviation(int dtype, const DeviationParams &p, hipStream_t s);
+hipError_t launch_topk(const TopkParams &p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
 hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);

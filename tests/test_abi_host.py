@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 24, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -225,3 +225,31 @@ def test_multi_token_workspace_sizes(kv):
     assert W(h, 3, 4, 9, 50, ctypes.byref(ob)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256 + 256
     assert W(h, 2, 4, 0, 50, None) == ctypes.c_size_t(-1).value
     kv.raw["kv_pool_destroy"](h)
+
+
+def test_selection_host_checks(kv):
+    h = make_handle(kv, kv.make_desc(16, 2, 64, "bf16"))[1]
+    h4 = make_handle(kv, kv.make_desc(16, 2, 64, "int4", 2))[1]
+    Dv, Tk = kv.raw["kv_token_deviation"], kv.raw["kv_topk_select"]
+    assert Dv(None, FAKE, 4, 2, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert Dv(h, FAKE, 0, 2, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG    # max_blocks < 1
+    assert Dv(h, FAKE, 4, 2, FAKE, FAKE, -1, FAKE, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert Dv(h, FAKE, 4, 2, None, FAKE, 3, FAKE, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert Dv(h, FAKE, 4, 2, FAKE, FAKE, 3, FAKE + 8, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG  # misaligned
+    assert Dv(h, None, 4, 2, None, None, 0, None, None, None, None) == 0                       # nothing to do
+    assert Dv(h4, FAKE, 4, 2, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == kv.KV_ERR_UNSUPPORTED
+    assert Tk(FAKE, FAKE, FAKE, -1, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert Tk(None, None, None, 0, None, None) == 0
+    assert Tk(FAKE, None, FAKE, 2, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    for x in (h, h4):
+        kv.raw["kv_pool_destroy"](x)
+
+
+def test_recompute_ratio_matches_oracle(kv, orc):
+    for load in (0.0, 1.0, 37.5, 150.0, 400.0, 1e6):
+        for tok in (0.0, 0.01, 1.0, 3.3):
+            for n in (0, 1, 7, 1000, 4096):
+                assert kv.kv_recompute_ratio(load, tok, n) == orc.recompute_ratio(load, tok, n)
+    for r in (0.0, 0.15, 0.2, 1 / 3, 0.5, 0.999, 1.0):
+        for n in (0, 1, 2, 7, 20, 100, 1000, 4097, 131072):
+            assert kv.kv_recompute_count(r, n) == orc.recompute_count(r, n)

@@ -57,11 +57,16 @@ MUTANTS = {
                  "memcpy(regions[r] + (size_t)src[i] * block_bytes[r], regions[r] + (size_t)dst[i] * block_bytes[r],"),
     # KV deviation without the V term
     "dev_no_v": ("acc += dk * dk + dv * dv;", "acc += dk * dk;"),
-    # KV deviation read from the chunk's first block slot instead of its real start
-    "dev_offset": ("int pos = first_slot + t;\n        int p = chunk_blocks[pos / BLOCK];\n        double acc",
-                   "int pos = t;\n        int p = chunk_blocks[pos / BLOCK];\n        double acc"),
+    # KV deviation looked up in the first sequence's table for every row
+    "dev_table": ("int p = tables[(size_t)row_seq[i] * max_blocks + pos / BLOCK];",
+                  "int p = tables[pos / BLOCK];"),
+    # recompute count rounded to nearest instead of up
+    "count_round": ("double c = ceil(ratio * (double)num_tokens);", "double c = floor(ratio * (double)num_tokens + 0.5);"),
     # top-k ties go to the higher row
-    "topk_tie": ("if (best < 0 || values[i] > values[best]) best = i;", "if (best < 0 || values[i] >= values[best]) best = i;"),
+    "topk_tie": ("return (a->i > b->i) - (a->i < b->i);", "return (a->i < b->i) - (a->i > b->i);"),
+    # top-k keeps the smallest values
+    "topk_order": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;",
+                   "if (a->v < b->v) return -1;\n    if (a->v > b->v) return 1;"),
     # recompute ratio without its floor
     "ratio_floor": ("if (r < floor_ratio) r = floor_ratio;", ""),
 }

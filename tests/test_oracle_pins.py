@@ -691,36 +691,68 @@ def test_deviation_definition(orc):
     # quarter-integers: every offset below is exact in fp32
     K = (rng.integers(-16, 16, (6, 2, 16, 64)) / 4).astype(np.float32)
     V = (rng.integers(-16, 16, (6, 2, 16, 64)) / 4).astype(np.float32)
-    chunk = np.array([4, 1, 5])
-    # recomputed = precomputed: deviation 0; a known offset gives a known value
-    pos = 3 + np.arange(20)                                # chunk tokens 0..19 at positions 3..22
-    pre_k = K[chunk[pos // 16], :, pos % 16, :]
-    pre_v = V[chunk[pos // 16], :, pos % 16, :]
-    assert np.all(orc.deviation(K, V, chunk, 3, pre_k, pre_v) == 0.0)
+    tables = np.array([[4, 1, 5], [0, 2, 3]])
+    # rows: sequence 0 positions 3..22, then sequence 1 positions 40, 7
+    rs = np.array([0] * 20 + [1, 1])
+    rp = np.concatenate([3 + np.arange(20), [40, 7]])
+    blk = tables[rs, rp // 16]
+    pre_k, pre_v = K[blk, :, rp % 16, :], V[blk, :, rp % 16, :]
+    # recomputed = precomputed: deviation 0; known offsets give known values
+    assert np.all(orc.deviation(K, V, tables, rs, rp, pre_k, pre_v) == 0.0)
     k_re, v_re = pre_k.copy(), pre_v.copy()
     k_re[7] += 0.5                                         # 2 heads x 64 channels of 0.25
     v_re[11, 1, 3] -= 3.0                                  # one element of 9
-    dev = orc.deviation(K, V, chunk, 3, k_re, v_re)
-    assert abs(dev[7] - 2 * 64 * 0.25) < 1e-9 and abs(dev[11] - 9.0) < 1e-9
-    assert np.count_nonzero(dev) == 2
-    # candidate rows: row i is chunk token ids[i]
-    ids = np.array([11, 7, 2])
-    dev2 = orc.deviation(K, V, chunk, 3, k_re[ids], v_re[ids], token_ids=ids)
-    assert np.array_equal(dev2, dev[ids])
+    v_re[21, 0, 0] += 1.0                                  # sequence 1, position 7: one element of 1
+    dev = orc.deviation(K, V, tables, rs, rp, k_re, v_re)
+    assert dev[7] == 2 * 64 * 0.25 and dev[11] == 9.0 and dev[21] == 1.0
+    assert np.count_nonzero(dev) == 3
+    # a subset of the rows, in another order, gives the same values
+    ids = np.array([21, 11, 7, 2])
+    assert np.array_equal(orc.deviation(K, V, tables, rs[ids], rp[ids], k_re[ids], v_re[ids]), dev[ids])
+    # the same row compared with another token's cache entry is not zero
+    assert orc.deviation(K, V, tables, [0], [4], pre_k[:1], pre_v[:1])[0] > 0
+
+
+def test_deviation_bf16_exact_case(orc):
+    """bf16 pool: differences of small integers, squared and summed, are exact."""
+    rng = np.random.default_rng(72)
+    Kf = rng.integers(-8, 8, (3, 4, 16, 32)).astype(np.float32)
+    Vf = rng.integers(-8, 8, (3, 4, 16, 32)).astype(np.float32)
+    K, V = orc.f32_to_bf16_bits(Kf), orc.f32_to_bf16_bits(Vf)
+    tables = np.array([[2, 0, 1]])
+    rp = np.array([0, 17, 33, 47])
+    blk = tables[0, rp // 16]
+    dk = rng.integers(-3, 4, (4, 4, 32)).astype(np.float32)
+    dv = rng.integers(-3, 4, (4, 4, 32)).astype(np.float32)
+    k_re = orc.f32_to_bf16_bits(Kf[blk, :, rp % 16, :] + dk)
+    v_re = orc.f32_to_bf16_bits(Vf[blk, :, rp % 16, :] + dv)
+    dev = orc.deviation(K, V, tables, [0] * 4, rp, k_re, v_re)
+    for i in range(4):                                     # integer sum of squares, counted by hand
+        want = sum(int(x) ** 2 for x in dk[i].ravel()) + sum(int(x) ** 2 for x in dv[i].ravel())
+        assert dev[i] == want
 
 
 def test_topk_selection(orc):
-    v = np.array([0.5, 3.0, 1.0, 3.0, -2.0, 7.0, 1.0], dtype=np.float32)
+    v = np.array([0.5, 3.0, 1.0, 3.0, -2.0, 7.0, 1.0])
     assert list(orc.topk(v, 3)) == [1, 3, 5]              # 7, then the two 3s
     assert list(orc.topk(v, 2)) == [1, 5]                 # tie between rows 1 and 3: the lower wins
     assert list(orc.topk(v, 5)) == [1, 2, 3, 5, 6]
     assert list(orc.topk(v, 0)) == []
     assert list(orc.topk(v, 99)) == list(range(7))
     rng = np.random.default_rng(71)
-    x = rng.standard_normal(1000).astype(np.float32)
+    x = rng.standard_normal(1000)
     sel = orc.topk(x, 150)
     ref = np.sort(np.argsort(-x, kind="stable")[:150])    # numpy's stable sort as the independent check
     assert np.array_equal(sel, ref)
+    # ties in bulk: small integers; brute force over every k on a tiny input
+    t = rng.integers(0, 4, 40).astype(np.float64)
+    for k in range(41):
+        order = sorted(range(40), key=lambda i: (-t[i], i))
+        assert list(orc.topk(t, k)) == sorted(order[:k])
+    # signed zeros tie; infinities order at the ends
+    z = np.array([0.0, -0.0, np.inf, -np.inf, -0.0, 1.0])
+    assert list(orc.topk(z, 3)) == [0, 2, 5]
+    assert list(orc.topk(z, 5)) == [0, 1, 2, 4, 5]
 
 
 def test_recompute_ratio(orc):
@@ -730,3 +762,15 @@ def test_recompute_ratio(orc):
     assert orc.recompute_ratio(10.0, 1.0, 1000) == 0.15
     # a slow load could hide more than everything: capped at 1
     assert orc.recompute_ratio(5000.0, 1.0, 1000) == 1.0
+
+
+def test_recompute_count(orc):
+    assert orc.recompute_count(0.15, 1000) == 150
+    assert orc.recompute_count(0.15, 7) == 2              # 1.05 rounds up: never below the ratio
+    assert orc.recompute_count(0.5, 4) == 2
+    assert orc.recompute_count(1.0, 33) == 33
+    assert orc.recompute_count(0.0, 33) == 0
+    assert orc.recompute_count(0.15, 0) == 0
+    for n in range(1, 300):                                # the count never falls below ratio * n
+        c = orc.recompute_count(0.15, n)
+        assert c >= 0.15 * n - 1e-12 and c - 1 < 0.15 * n

@@ -21,6 +21,11 @@ here, so N(0,1) data stands in for them):
                   16384 tokens of every sequence share physical blocks; a
                   4096-token chunk of that prefix is re-rotated by a seeded
                   offset in [1, 16384]
+  blend_select    16 requests x 8192 reused tokens, 8 kv heads, d_h 128,
+                  bf16 (LLaMA-3-8B KV shape): recomputed K/V rows for every
+                  reused token are the cached rows plus N(0, sigma_t^2) noise
+                  with sigma_t^2 ~ U(0, 1) per token (a near-linear deviation
+                  CDF), 5 % of tokens recomputed identically (ties at 0)
 """
 from __future__ import annotations
 
@@ -47,8 +52,14 @@ WORKLOADS = {
                         rope_base=10000.0),
 }
 
+BLEND_WORKLOADS = {
+    "blend_select": dict(batch=16, ctx=8192, n_kv=8, d=128, dtype="bf16", seed=5, unchanged=0.05,
+                         ratio=0.15),
+}
+
 # sub-stream ids, one per kind of tensor
-_S_LENS, _S_PERM, _S_K, _S_V, _S_Q, _S_KNEW, _S_VNEW, _S_OUTL, _S_DELTA = range(9)
+(_S_LENS, _S_PERM, _S_K, _S_V, _S_Q, _S_KNEW, _S_VNEW, _S_OUTL, _S_DELTA, _S_SIGMA, _S_KRE, _S_VRE,
+ _S_ROWS) = range(13)
 
 
 def _gen(seed: int, stream: int, device) -> torch.Generator:
@@ -260,6 +271,87 @@ def workload(name: str, device="cpu", poison: bool = True, n_new: int | None = N
                   outlier_scale=w.get("outlier_scale", 10.0), name=name)
     c.int4 = bool(w.get("int4", False))
     return c
+
+
+@dataclass
+class BlendCase:
+    """Selection inputs: a pool holding each request's reused tokens and the
+    recomputed K/V of a set of rows (row i: token row_pos[i] of request
+    row_seq[i]); rows of request s are rows seg_offsets[s] .. seg_offsets[s+1]."""
+    name: str
+    batch: int
+    n_kv: int
+    d: int
+    dtype: str
+    num_blocks: int
+    tables: torch.Tensor       # int32 [B][max_blocks]
+    K: torch.Tensor
+    V: torch.Tensor
+    row_seq: torch.Tensor      # int32 [rows]
+    row_pos: torch.Tensor      # int32 [rows]
+    k_re: torch.Tensor         # [rows][n_kv][d]
+    v_re: torch.Tensor
+    seg_offsets: torch.Tensor  # int32 [B + 1]
+    sigma2: torch.Tensor       # fp32 [rows], the drawn noise variance per row
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.row_seq.numel())
+
+
+def make_blend_case(seed: int, batch: int, ctx: int, n_kv: int, d: int, dtype: str = "bf16",
+                    unchanged: float = 0.05, rows_per_seq: int | None = None, device="cpu",
+                    name: str = "custom") -> BlendCase:
+    """Every request owns ctx cached tokens in private blocks (seeded
+    permutation of the pool). rows_per_seq None: a row for every cached token
+    in position order (the wide first-layer candidate set); else that many
+    seeded distinct positions per request, ascending (a narrowed set).
+    Recomputed row = cached row + sigma * N(0, 1) per element, cast to the
+    pool type, with sigma^2 ~ U(0, 1) per row and sigma = 0 for a seeded
+    `unchanged` fraction of rows."""
+    base = make_case(seed, batch, [ctx] * batch, n_kv, n_kv, d, dtype, append=False, poison=False,
+                     device=device, name=name)
+    tables = base.tables.to("cpu")
+    if rows_per_seq is None:
+        pos = torch.arange(ctx, dtype=torch.int64).repeat(batch)
+        per = [ctx] * batch
+    else:
+        g = _gen(seed, _S_ROWS, "cpu")
+        pos = torch.cat([torch.randperm(ctx, generator=g)[:rows_per_seq].sort().values for _ in range(batch)])
+        per = [min(rows_per_seq, ctx)] * batch
+    seq = torch.cat([torch.full((n,), b, dtype=torch.int64) for b, n in enumerate(per)]) if batch else \
+        torch.zeros(0, dtype=torch.int64)
+    n_rows = int(seq.numel())
+    g = _gen(seed, _S_SIGMA, "cpu")
+    sigma2 = torch.rand(n_rows, generator=g)
+    sigma2[torch.rand(n_rows, generator=g) < unchanged] = 0.0
+    blk = tables[seq, pos // BLOCK].to(torch.int64).to(device)
+    slot = (pos % BLOCK).to(device)
+    tdt = torch_dtype(dtype)
+    sig = sigma2.sqrt().to(device)[:, None, None]
+    k_re = torch.empty((n_rows, n_kv, d), dtype=tdt, device=device)
+    v_re = torch.empty_like(k_re)
+    step = 1 << 15
+    gk, gv = _gen(seed, _S_KRE, device), _gen(seed, _S_VRE, device)
+    for s in range(0, n_rows, step):
+        e = min(n_rows, s + step)
+        nk = torch.randn((e - s, n_kv, d), generator=gk, device=device)
+        nv = torch.randn((e - s, n_kv, d), generator=gv, device=device)
+        k_re[s:e] = (base.K[blk[s:e], :, slot[s:e], :].float() + sig[s:e] * nk).to(tdt)
+        v_re[s:e] = (base.V[blk[s:e], :, slot[s:e], :].float() + sig[s:e] * nv).to(tdt)
+    offs = torch.zeros(batch + 1, dtype=torch.int32)
+    if batch:
+        offs[1:] = torch.tensor(per, dtype=torch.int64).cumsum(0).to(torch.int32)
+    return BlendCase(name=name, batch=batch, n_kv=n_kv, d=d, dtype=dtype, num_blocks=base.num_blocks,
+                     tables=base.tables, K=base.K, V=base.V, row_seq=seq.to(torch.int32).to(device),
+                     row_pos=pos.to(torch.int32).to(device), k_re=k_re, v_re=v_re,
+                     seg_offsets=offs.to(device), sigma2=sigma2)
+
+
+def blend_workload(name: str, device="cpu", rows_per_seq: int | None = None) -> BlendCase:
+    w = BLEND_WORKLOADS[name]
+    return make_blend_case(w["seed"], w["batch"], w["ctx"], w["n_kv"], w["d"], w["dtype"], w["unchanged"],
+                           rows_per_seq, device, name)
 
 
 def to_host_bits(t: torch.Tensor):
