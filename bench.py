@@ -1,5 +1,9 @@
 """Benchmark of one decode step (kv_append + paged decode attention) on one GPU.
 
+The step is one kv_decode_step call: on bf16 pools the append runs inside the
+attention kernel (then the merge kernel); INT4 and fp32 pools launch the
+append kernel first.
+
 Prints one JSON line. A step appends one token to every sequence and runs
 paged decode attention over the cache (the decode-step listing of "KV Cache는
 왜 LLM 서빙의 핵심인가", section "KV Cache: O(T²)를 O(T)로"), on seeded
@@ -64,19 +68,24 @@ def profiled_traffic(workload: str):
 
 
 class HipEvents:
-    """hipEvent_t handles through the HIP runtime (ctypes)."""
+    """hipEvent_t handles through the HIP runtime (ctypes). The events only
+    time work: they are created without the system-scope fence a recorded
+    event otherwise performs (a cache writeback and invalidate that would add
+    to every step they sit in)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed ({rc})")
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         return e.value
 
     def elapsed_ms(self, a, b) -> float:
@@ -173,14 +182,12 @@ def main():
         o = opts
         if events is not None:
             o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule, events=events)
-        if k == 1:
-            if c.append:
-                kv.kv_append(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
-            kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
+        if c.append:
+            # append + attention in one call (fused into the attention kernel on bf16 pools)
+            kv.kv_decode_step(p, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=o,
+                              stream=stream)
         else:
-            kv.kv_append_tokens(p, c.k_new, c.v_new, c.tables, c.seq_lens, stream=stream)
-            kv.paged_multi_token_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o,
-                                           stream=stream)
+            kv.paged_decode_attention(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, opts=o, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -215,6 +222,9 @@ def main():
     else:
         kv_bytes = int(ctx.sum().item()) * n_kv * 2 * D * es
     alg_bytes = kv_bytes + k * (B * n_h * D * es + B * n_h * D * 4) + int(nblk.sum().item()) * 4 + B * 4
+    fused = c.append and c.dtype == "bf16" and not int4 and args.kernel in (0, 2)
+    if fused:  # the kernel also writes the step's new K and V rows into the pool
+        alg_bytes += B * k * n_kv * 2 * D * es
     achieved = alg_bytes / (split_avg * 1e-3) / 1e9
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None
@@ -277,7 +287,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,
-                     "kernel": "decode attention kernel (before the merge)", "avg_launch_us": split_avg * 1e3,
+                     "kernel": "decode attention kernel (before the merge)" + (", append fused" if fused else ""),
+                     "avg_launch_us": split_avg * 1e3,
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }

@@ -124,9 +124,12 @@ typedef struct {
     int32_t window;       /* > 0: attend only the last `window` tokens of each
                              sequence [KVSYS, "제한된 어텐션 윈도우 크기"]; 0 = all  */
     int32_t schedule;     /* KV_SCHED_*                                           */
-    void *events[3];      /* optional hipEvent_t handles recorded on the stream
-                             before the split kernel, after it, and after the
-                             merge kernel (for timing); NULL entries are skipped  */
+    void *events[3];      /* optional hipEvent_t handles, for timing: [0] and
+                             [1] take the start and end time of the attention
+                             kernel (recorded by its own dispatch), [2] the end
+                             of the merge kernel (or a plain record on the
+                             stream when no merge runs); NULL entries are
+                             skipped                                             */
 } kv_attn_opts;
 
 /* Human-readable name of a status code (static storage). */
@@ -241,6 +244,30 @@ kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out,
                                       const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
                                       int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts,
                                       void *stream);
+
+/* One whole decode step [CORE, "KV Cache: O(T²)를 O(T)로", decode-step
+ * listing: append the new k, v, then attend over the cache including them]:
+ * the same result as kv_append_tokens(k_new, v_new, seq_lens, n_new = q_len)
+ * followed by paged_multi_token_attention over seq_lens[b] + q_len tokens
+ * (q_len = 1: paged_decode_attention), bit for bit, in pool contents and
+ * output.
+ *   k_new, v_new  device [batch][q_len][num_kv_heads][head_dim], pool dtype
+ *                 (bf16 for INT4 pools), 16-byte aligned
+ *   seq_lens      device int32 [batch], lengths BEFORE the append
+ *   max_ctx       largest seq_lens[b] + q_len; the workspace is
+ *                 paged_multi_token_attention_workspace_bytes(pool, batch,
+ *                 num_q_heads, q_len, max_ctx, opts)
+ * The other arguments are those of paged_multi_token_attention. On bf16
+ * pools with the MFMA kernel the append is fused into the attention kernel:
+ * tiles take the new rows from k_new / v_new and write them into the pool
+ * (one kernel fewer per step); other pools launch the append kernel first.
+ * seq_lens must not change between the two (same stream order). A sequence
+ * whose length is out of range or above max_ctx gets NaN and may be left
+ * unappended. */
+kv_status kv_decode_step(kv_pool_t pool, const void *k_new, const void *v_new, const void *q, float *out,
+                         int32_t num_q_heads, int32_t q_len, float scale, const int32_t *block_tables,
+                         int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                         int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts, void *stream);
 
 /* Bulk KVQuant INT4 coding of bf16 pool contents [CORE, "KVQuant: 마지막 4배"]:
  * code = clamp(round((x - min) / s), 0, 15) with s = (max - min) / 15, s and min

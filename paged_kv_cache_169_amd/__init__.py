@@ -81,6 +81,9 @@ _paged_multi_token_attention_workspace_bytes = _decl(
 _paged_multi_token_attention = _decl(
     "paged_multi_token_attention", _I32,
     [_P, _P, _P, _I32, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
+_kv_decode_step = _decl(
+    "kv_decode_step", _I32,
+    [_P, _P, _P, _P, _P, _I32, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
 _kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P])
 _rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
 _kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
@@ -312,6 +315,34 @@ def paged_multi_token_attention(pool: KVPool, q: torch.Tensor, out: torch.Tensor
     _check(st, "paged_multi_token_attention")
 
 
+def kv_decode_step(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_ctx: int,
+                   workspace: torch.Tensor | None = None, seq_slots: torch.Tensor | None = None,
+                   opts: kv_attn_opts | None = None, stream=None) -> None:
+    """Append q_len tokens per sequence, then attend (see kv_decode_step in
+    kvcache.h). q: [batch][num_q_heads][head_dim] (one token) or
+    [batch][q_len][num_q_heads][head_dim]; k_new / v_new: [batch][n_kv][head_dim]
+    or [batch][q_len][n_kv][head_dim]; out: fp32, the shape of q."""
+    d = pool.desc
+    if q.dim() == 3:
+        B, n_h, hd = q.shape
+        q_len = 1
+    else:
+        B, q_len, n_h, hd = q.shape
+    if hd != d.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out shape does not match the pool")
+    kdt = torch.float32 if d.dtype == KV_F32 else torch.bfloat16
+    n = B * q_len * d.num_kv_heads * d.head_dim
+    ws_ptr = _dev_ptr(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _kv_decode_step(pool.handle, _dev_ptr(k_new, "k_new", kdt, n), _dev_ptr(v_new, "v_new", kdt, n),
+                         _dev_ptr(q, "q", kdt), _dev_ptr(out, "out", torch.float32), n_h, q_len, float(scale),
+                         _i32(block_tables, "block_tables"), int(block_tables.shape[1]), _i32(seq_lens, "seq_lens"),
+                         _i32(seq_slots, "seq_slots"), B, int(max_ctx), ws_ptr, ws_bytes,
+                         ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    _check(st, "kv_decode_step")
+
+
 def kv_quantize_int4(dst: KVPool, src: KVPool, block_tables: torch.Tensor, lens: torch.Tensor,
                      seq_slots: torch.Tensor | None = None, stream=None) -> None:
     st = _kv_quantize_int4(dst.handle, src.handle, _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
@@ -424,5 +455,5 @@ raw = {
     "paged_multi_token_attention_workspace_bytes": _paged_multi_token_attention_workspace_bytes,
     "kv_block_bytes": _kv_block_bytes, "kv_copy_blocks": _kv_copy_blocks, "kv_gather_blocks": _kv_gather_blocks,
     "kv_scatter_blocks": _kv_scatter_blocks, "kv_token_deviation": _kv_token_deviation,
-    "kv_topk_select": _kv_topk_select,
+    "kv_topk_select": _kv_topk_select, "kv_decode_step": _kv_decode_step,
 }

@@ -153,7 +153,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         // longer than max_ctx does not fit the promise and reads as bad
         g->split_blocks = nblk;
         g->max_splits = 1;
-        g->n_wg = balanced_grid(dtype, (int)D, batch);
+        g->n_wg = balanced_grid(dtype, (int)D, batch, nblk);
         const size_t rows = (size_t)g->n_wg * 2 * (g->ncols < 16 ? g->ncols : 16);
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));
@@ -295,11 +295,19 @@ size_t paged_decode_attention_workspace_bytes(kv_pool_t pool, int32_t batch, int
     return paged_multi_token_attention_workspace_bytes(pool, batch, num_q_heads, 1, max_ctx, opts);
 }
 
-kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, int32_t q_len,
-                                      float scale, const int32_t *block_tables, int32_t max_blocks,
-                                      const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
-                                      int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts,
-                                      void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Attention over ctx_lens[b] + ctx_add tokens. With k_new / v_new (a decode
+// step: the q_len = ctx_add new tokens are appended first), the append is
+// fused into the attention kernel on the bf16 MFMA path and runs as its own
+// kernel before attention otherwise.
+kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, int32_t q_len, float scale,
+                         const int32_t *block_tables, int32_t max_blocks, const int32_t *ctx_lens,
+                         const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace, size_t ws_bytes,
+                         const kv_attn_opts *opts, void *stream, int32_t ctx_add, const void *k_new,
+                         const void *v_new) {
     if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0 || q_len < 1)
         return KV_ERR_INVALID_ARG;
     if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
@@ -310,10 +318,21 @@ kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out,
     if (batch == 0) return KV_OK;
     if (!q || !out || !block_tables || !ctx_lens) return KV_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out)) return KV_ERR_INVALID_ARG;
+    if (k_new && (!v_new || !aligned16(k_new) || !aligned16(v_new))) return KV_ERR_INVALID_ARG;
     if (g.ws_bytes > 0 && (!workspace || ws_bytes < g.ws_bytes || !aligned16(workspace))) return KV_ERR_WORKSPACE;
 
     const int dtype = pool->desc.dtype;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fused = k_new && g.kernel == 2 && dtype == KV_BF16;
+    if (k_new && !fused) {
+        const kv_status st = kv_append_tokens(pool, k_new, v_new, block_tables, max_blocks, ctx_lens, seq_slots,
+                                              batch, ctx_add, stream);
+        if (st != KV_OK) return st;
+    }
     AttnParams a;
+    a.ctx_add = ctx_add;
+    a.k_new = fused ? k_new : nullptr;
+    a.v_new = fused ? v_new : nullptr;
     a.pool = pool_ptrs(pool);
     a.q = q;
     a.out = out;
@@ -344,16 +363,35 @@ kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out,
     a.n_wg = g.n_wg;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     void *const *ev = opts ? opts->events : nullptr;
-    if (ev && ev[0] && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess) return KV_ERR_HIP;
-    hipError_t e = launch_attention(dtype, g.kernel, a, s);
+    auto evt = [&](int i) { return ev ? static_cast<hipEvent_t>(ev[i]) : nullptr; };
+    hipError_t e = launch_attention(dtype, g.kernel, a, s, evt(0), evt(1));
     if (e != hipSuccess) return KV_ERR_HIP;
-    if (ev && ev[1] && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess) return KV_ERR_HIP;
-    e = launch_merge(a, s);
+    e = launch_merge(a, s, evt(2));
     if (e != hipSuccess) return KV_ERR_HIP;
-    if (ev && ev[2] && hipEventRecord(static_cast<hipEvent_t>(ev[2]), s) != hipSuccess) return KV_ERR_HIP;
     return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, int32_t q_len,
+                                      float scale, const int32_t *block_tables, int32_t max_blocks,
+                                      const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
+                                      int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts,
+                                      void *stream) {
+    return attention_impl(pool, q, out, num_q_heads, q_len, scale, block_tables, max_blocks, ctx_lens, seq_slots,
+                          batch, max_ctx, workspace, ws_bytes, opts, stream, 0, nullptr, nullptr);
+}
+
+kv_status kv_decode_step(kv_pool_t pool, const void *k_new, const void *v_new, const void *q, float *out,
+                         int32_t num_q_heads, int32_t q_len, float scale, const int32_t *block_tables,
+                         int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                         int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts, void *stream) {
+    if (batch > 0 && (!k_new || !v_new)) return KV_ERR_INVALID_ARG;
+    return attention_impl(pool, q, out, num_q_heads, q_len, scale, block_tables, max_blocks, seq_lens, seq_slots,
+                          batch, max_ctx, workspace, ws_bytes, opts, stream, q_len, k_new, v_new);
 }
 
 kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, float scale,

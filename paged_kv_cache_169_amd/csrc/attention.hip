@@ -33,6 +33,10 @@
 //    token-quad) is exactly the B-operand layout the PV product needs, so P
 //    never leaves registers.
 #include "device.h"
+#include <hip/hip_ext.h>
+
+#include <climits>
+
 #include "internal.h"
 
 namespace kvc {
@@ -53,6 +57,21 @@ __device__ __forceinline__ u32x2_t stream_load8(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
 }
 
+// Pointers into global memory with the address space spelled out. A pointer
+// chosen per lane between two buffers otherwise falls back to a flat
+// (generic) load, which also counts against the LDS counter: every LDS wait
+// in the softmax would then wait for the tile prefetch as well.
+typedef const __attribute__((address_space(1))) uint16_t gu16_t;
+typedef const __attribute__((address_space(1))) u32x4_t gu32x4_t;
+typedef const __attribute__((address_space(1))) u32x2_t gu32x2_t;
+__device__ __forceinline__ gu16_t *global_u16(const void *p) { return (gu16_t *)(p); }
+__device__ __forceinline__ u32x4_t stream_load16(gu16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(p));
+}
+__device__ __forceinline__ u32x2_t stream_load8(gu16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<gu32x2_t *>(p));
+}
+
 enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_INT4 = 2 };
 
 struct SplitWork {
@@ -61,7 +80,7 @@ struct SplitWork {
 };
 
 __device__ __forceinline__ bool split_work(const AttnParams &p, int b, int split, SplitWork &w) {
-    w.r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+    w.r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (split >= w.r.nsplit) return false;
     w.j0 = w.r.blk_lo + split * p.split_blocks;
     w.j1 = min(w.r.blk_lo + w.r.nblk, w.j0 + p.split_blocks);
@@ -333,17 +352,35 @@ __device__ __forceinline__ int load_block_ids(const AttnParams &p, int b, int jb
     return j < j1 ? p.tables[(size_t)b * p.max_blocks + j] : 0;
 }
 
+// Tile of block j. Rows of positions in [L0, L0 + n_new) come from the step's
+// k_new / v_new instead of the pool (fused append); newpos = L0 - 16 j is
+// uniform, and >= 16 when the block holds no new token.
 template <int D>
-__device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh, int n16, int G, MfmaTile<D> &T) {
+__device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh, int n16, int G, MfmaTile<D> &T,
+                                           int b = 0, int newpos = kBlock) {
     constexpr int KS = D / 32, VC = D / 16;
-    const uint16_t *tile = reinterpret_cast<const uint16_t *>(p.pool.k) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+    gu16_t *tile = global_u16(p.pool.k) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+    gu16_t *vt = global_u16(p.pool.v) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+    gu16_t *krow = tile + n16 * D;
+    gu16_t *vrow[4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        T.k[s] = __builtin_bit_cast(bf16x8_t, stream_load16(tile + n16 * D + s * 32 + 8 * G));
-    const uint16_t *vt = reinterpret_cast<const uint16_t *>(p.pool.v) + ((size_t)pid * p.n_kv + kvh) * kBlock * D;
+    for (int i = 0; i < 4; ++i) vrow[i] = vt + (4 * G + i) * D;
+    if (newpos < kBlock) {
+        auto fresh = [&](const void *base, int slot) {
+            return global_u16(base) + (((size_t)b * p.ctx_add + (slot - newpos)) * p.n_kv + kvh) * D;
+        };
+        if (n16 >= newpos && n16 < newpos + p.ctx_add) krow = fresh(p.k_new, n16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = 4 * G + i;
+            if (slot >= newpos && slot < newpos + p.ctx_add) vrow[i] = fresh(p.v_new, slot);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) T.k[s] = __builtin_bit_cast(bf16x8_t, stream_load16(krow + s * 32 + 8 * G));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint16_t *src = vt + (4 * G + i) * D + n16 * VC;
+        gu16_t *src = vrow[i] + n16 * VC;
         if constexpr (VC == 8) {
             const u32x4_t v = stream_load16(src);
             T.v[i][0] = v[0];
@@ -355,6 +392,24 @@ __device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh
             T.v[i][0] = v[0];
             T.v[i][1] = v[1];
         }
+    }
+}
+
+// Fused append: write the new tokens' K and V rows that fall in block j
+// (slots [max(newpos, 0), min(newpos + n_new, hi_slot))) into the pool tile.
+template <int D>
+__device__ __forceinline__ void store_new_rows(const AttnParams &p, int b, int kvh, int pid, int newpos, int lane) {
+    constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+    const int first = max(newpos, 0), last = min(newpos + p.ctx_add, kBlock);
+    const int rows = last - first;
+    for (int idx = lane; idx < 2 * rows * CPR; idx += 64) {
+        const int which = idx / (rows * CPR), rem = idx - which * rows * CPR;
+        const int slot = first + rem / CPR, c = rem % CPR;
+        const uint4 *src = reinterpret_cast<const uint4 *>(which ? p.v_new : p.k_new) +
+                           (((size_t)b * p.ctx_add + (slot - newpos)) * p.n_kv + kvh) * CPR + c;
+        uint4 *dst = reinterpret_cast<uint4 *>(which ? p.pool.v : p.pool.k) +
+                     (((size_t)pid * p.n_kv + kvh) * kBlock + slot) * CPR + c;
+        *dst = *src;
     }
 }
 
@@ -469,10 +524,15 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
 // One lane's run of the online softmax over blocks [j0, j1) of sequence b,
 // kv head kvh. On return st.l is still the lane's partial sum (the caller
 // adds the 4 token quads).
+//
+// Every tile iteration issues the same vector-memory loads and nothing else:
+// the segment's block ids are staged in LDS (sids, at least j1 - j0 entries)
+// before the loop and the fused append's rows are written before it, so the
+// waits inside the loop cover exactly the tile's own loads.
 template <int D>
 __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const Column &col,
                                              const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st,
-                                             bool &bad) {
+                                             bool &bad, bool write_new, int *sids) {
     constexpr int KS = D / 32, MS = D / 16;
     const int n16 = lane & 15, G = lane >> 4;
     // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of its column.
@@ -489,39 +549,45 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
     st.m = -INFINITY;
     st.l = 0.0f;
     st.bv = 0.0f;
+    if (j0 >= j1) return;
 
-    // Block ids come from a VGPR (one per lane, 64 blocks at a time); the
-    // tile of block j+1 is in flight while block j is computed.
-    int ids = load_block_ids(p, b, j0, j1, lane);
-    int ids_base = j0;
+    __syncthreads();  // the previous segment's reads of sids are done
+    for (int i = lane; i < j1 - j0; i += 64) sids[i] = p.tables[(size_t)b * p.max_blocks + j0 + i];
+    __syncthreads();
     auto pid_of = [&](int j) {
-        if (j - ids_base >= 64) {
-            ids_base += 64;
-            ids = load_block_ids(p, b, ids_base, j1, lane);
-        }
-        int pid = __builtin_amdgcn_readlane(ids, j - ids_base);
+        int pid = __builtin_amdgcn_readfirstlane(sids[j - j0]);
         if (pid < 0 || pid >= p.num_blocks) {
             bad = true;
             pid = 0;
         }
         return pid;
     };
-    auto bounds = [&](int j, int &tlo, int &thi) {
-        const int tok0 = j * kBlock;
-        tlo = max(r.lo - tok0, 0);
-        thi = min(r.hi - tok0, kBlock);
+    // fused append: positions from L0 on are the step's new tokens; their rows
+    // go into the pool now (nothing in this kernel reads those slots)
+    const int L0 = p.k_new ? r.n - p.ctx_add : INT_MAX;
+    if (write_new && L0 != INT_MAX) {
+        for (int j = max(j0, L0 / kBlock); j < j1; ++j) {
+            const int id = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+            if (id >= 0 && id < p.num_blocks) store_new_rows<D>(p, b, kvh, id, L0 - j * kBlock, lane);
+        }
+    }
+    auto fetch = [&](int j, MfmaTile<D> &T) {
+        const int newpos = L0 == INT_MAX ? kBlock : min(L0 - j * kBlock, kBlock);  // may be negative
+        fetch_tile<D>(p, pid_of(j), kvh, n16, G, T, b, newpos);
     };
-    MfmaTile<D> A, B;
-    if (j0 < j1) fetch_tile<D>(p, pid_of(j0), kvh, n16, G, A);
-    for (int j = j0; j < j1; j += 2) {
-        int tlo, thi;
-        if (j + 1 < j1) fetch_tile<D>(p, pid_of(j + 1), kvh, n16, G, B);
-        bounds(j, tlo, thi);
-        mfma_block<D>(p, A, qB, j * kBlock, tlo, thi, needs_mask(j * kBlock, r), col, G, st);
-        if (j + 1 >= j1) break;
-        if (j + 2 < j1) fetch_tile<D>(p, pid_of(j + 2), kvh, n16, G, A);
-        bounds(j + 1, tlo, thi);
-        mfma_block<D>(p, B, qB, (j + 1) * kBlock, tlo, thi, needs_mask((j + 1) * kBlock, r), col, G, st);
+    auto compute = [&](const MfmaTile<D> &T, int j) {
+        const int tok0 = j * kBlock;
+        const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
+        mfma_block<D>(p, T, qB, tok0, tlo, thi, needs_mask(tok0, r), col, G, st);
+    };
+    // No software prefetch: each tile is loaded and then used. The waves that
+    // share a SIMD cover each other's compute; a deeper prefetch puts more
+    // bytes in flight and measured slower (6.8 vs 6.0-6.4 TB/s in a probe of
+    // this tile pattern with per-tile work).
+    for (int j = j0; j < j1; ++j) {
+        MfmaTile<D> T;
+        fetch(j, T);
+        compute(T, j);
     }
 }
 
@@ -778,13 +844,16 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     }
 }
 
+// write_new: this unit stores the fused append's rows (column tile 0 only, so
+// that each new row is written once).
 template <int D, bool Q4>
 __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, const Column &col, const SeqRange &r,
-                                            int j0, int j1, int lane, MfmaState<D> &st, bool &bad) {
+                                            int j0, int j1, int lane, MfmaState<D> &st, bool &bad, bool write_new,
+                                            int *sids) {
     if constexpr (Q4)
         q4_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad);
     else
-        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad);
+        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, write_new, sids);
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
@@ -794,6 +863,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 
 template <int D, bool Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
+    extern __shared__ int sids[];  // [split_blocks] block ids of the segment
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int split = blockIdx.x, unit = blockIdx.y, b = blockIdx.z;
     const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
@@ -802,7 +872,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
     bool bad = w.r.bad;
     const Column col = column_of(p, b, kvh, ct, n16, w.r);
     MfmaState<D> st;
-    run_segment<D, Q4>(p, b, kvh, col, w.r, w.j0, w.j1, lane, st, bad);
+    run_segment<D, Q4>(p, b, kvh, col, w.r, w.j0, w.j1, lane, st, bad, ct == 0, sids);
     float l = st.l, bv = st.bv;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -832,7 +902,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
         const int b = base + lane;
         int nb = 0;
         if (b < p.batch) {
-            const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+            const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
             nb = r.nblk;
         }
         // inclusive wave scan
@@ -850,7 +920,8 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
 
 template <int D, bool Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
-    extern __shared__ int pre[];  // [batch + 1]
+    extern __shared__ int pre[];  // [batch + 1] block prefix sums, then [split_blocks] block ids of a segment
+    int *sids = pre + p.batch + 1;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
     const int nblk_total = balanced_prefix(p, pre, lane);
@@ -878,11 +949,11 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         const int jr = (int)(t - pair0 - (long)unit * nb);
         const long seg_end = min(e, pair0 + (long)(unit + 1) * nb);
         const int cnt = (int)(seg_end - t);
-        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         bool bad = r.bad;
         const Column col = column_of(p, b, kvh, ct, n16, r);
         MfmaState<D> st;
-        run_segment<D, Q4>(p, b, kvh, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad);
+        run_segment<D, Q4>(p, b, kvh, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, ct == 0, sids);
         float l = st.l, bv = st.bv;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
@@ -921,7 +992,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
     const int b = blockIdx.y, lane = threadIdx.x;
     const size_t row = (size_t)b * p.q_len * p.n_h + blockIdx.x;
-    const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+    const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (r.nsplit <= 1) return;
     const size_t base = row * p.max_splits;
     const float *ml = p.ws_ml + base * 2;
@@ -957,7 +1028,7 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
     float *dst = p.out + ((size_t)b * p.q_len * p.n_h + blockIdx.x) * D + lane * cv;
     if (nb == 0) {
-        const SeqRange r = seq_range(p.ctx_lens[b], p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
         for (int c = 0; c < cv; ++c) dst[c] = v;
         return;
@@ -993,60 +1064,65 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
 // launchers
 // ---------------------------------------------------------------------------
 
+// Every launch goes through hipExtLaunchKernelGGL so that optional timing
+// events are recorded by the kernel's own dispatch (start and end of the
+// kernel), not by separate queue packets between kernels.
 template <int KIND, int D>
-static hipError_t launch_valu_d(const AttnParams &p, dim3 grid, hipStream_t s) {
+static hipError_t launch_valu_d(const AttnParams &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int g = p.group;
     if (g <= 1)
-        hipLaunchKernelGGL((attn_valu_kernel<KIND, D, 1>), grid, dim3(64), 0, s, p);
+        hipExtLaunchKernelGGL((attn_valu_kernel<KIND, D, 1>), grid, dim3(64), 0, s, e0, e1, 0, p);
     else if (g <= 2)
-        hipLaunchKernelGGL((attn_valu_kernel<KIND, D, 2>), grid, dim3(64), 0, s, p);
+        hipExtLaunchKernelGGL((attn_valu_kernel<KIND, D, 2>), grid, dim3(64), 0, s, e0, e1, 0, p);
     else if (g <= 4)
-        hipLaunchKernelGGL((attn_valu_kernel<KIND, D, 4>), grid, dim3(64), 0, s, p);
+        hipExtLaunchKernelGGL((attn_valu_kernel<KIND, D, 4>), grid, dim3(64), 0, s, e0, e1, 0, p);
     else if (g <= 8)
-        hipLaunchKernelGGL((attn_valu_kernel<KIND, D, 8>), grid, dim3(64), 0, s, p);
+        hipExtLaunchKernelGGL((attn_valu_kernel<KIND, D, 8>), grid, dim3(64), 0, s, e0, e1, 0, p);
     else
-        hipLaunchKernelGGL((attn_valu_kernel<KIND, D, 16>), grid, dim3(64), 0, s, p);
+        hipExtLaunchKernelGGL((attn_valu_kernel<KIND, D, 16>), grid, dim3(64), 0, s, e0, e1, 0, p);
     return hipGetLastError();
 }
 
 template <int KIND>
-static hipError_t launch_valu(const AttnParams &p, dim3 grid, hipStream_t s) {
-    return p.head_dim == 64 ? launch_valu_d<KIND, 64>(p, grid, s) : launch_valu_d<KIND, 128>(p, grid, s);
+static hipError_t launch_valu(const AttnParams &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    return p.head_dim == 64 ? launch_valu_d<KIND, 64>(p, grid, s, e0, e1) : launch_valu_d<KIND, 128>(p, grid, s, e0, e1);
 }
 
-hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s) {
+hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(p.max_splits, kernel == 2 ? p.units : p.n_kv, p.batch);
     if (p.batch == 0) return hipSuccess;
     if (kernel == 2) {
         const bool q4 = dtype == KV_INT4;
         if (p.schedule == KV_SCHED_BALANCED) {
-            const size_t lds = (size_t)(p.batch + 1) * sizeof(int);
+            const uint32_t lds = (uint32_t)((p.batch + 1 + p.split_blocks) * sizeof(int));
+            const dim3 bg(p.n_wg);
             if (q4)
-                hipLaunchKernelGGL((attn_mfma_balanced_kernel<128, true>), dim3(p.n_wg), dim3(64), lds, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, true>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipLaunchKernelGGL((attn_mfma_balanced_kernel<64, false>), dim3(p.n_wg), dim3(64), lds, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, false>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipLaunchKernelGGL((attn_mfma_balanced_kernel<128, false>), dim3(p.n_wg), dim3(64), lds, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, false>), bg, dim3(64), lds, s, e0, e1, 0, p);
         } else {
+            const uint32_t lds = (uint32_t)(p.split_blocks * sizeof(int));
             if (q4)
-                hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(64), 0, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(64), 0, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(64), 0, s, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(64), lds, s, e0, e1, 0, p);
         }
         return hipGetLastError();
     }
-    if (dtype == KV_F32) return launch_valu<KIND_F32>(p, grid, s);
-    if (dtype == KV_INT4) return launch_valu<KIND_INT4>(p, grid, s);
-    return launch_valu<KIND_BF16>(p, grid, s);
+    if (dtype == KV_F32) return launch_valu<KIND_F32>(p, grid, s, e0, e1);
+    if (dtype == KV_INT4) return launch_valu<KIND_INT4>(p, grid, s, e0, e1);
+    return launch_valu<KIND_BF16>(p, grid, s, e0, e1);
 }
 
-int balanced_grid(int dtype, int head_dim, int batch) {
+int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     // compute units x resident workgroups per compute unit; 256 x 2 when the
     // runtime cannot tell (no device: only the size of a workspace is asked)
     int dev = 0, cus = 0, per_cu = 0;
-    const size_t lds = (size_t)(batch + 1) * sizeof(int);
+    const size_t lds = (size_t)(batch + 1 + max_blocks) * sizeof(int);
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 256 * 2;
@@ -1058,17 +1134,21 @@ int balanced_grid(int dtype, int head_dim, int batch) {
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, false>, 64, lds);
     if (e != hipSuccess || per_cu <= 0) per_cu = 2;
+    // at most two waves per SIMD: with more, more tile bytes are in flight
+    // and the 8B- and 70B-shaped decode layers measured slower (109 vs 104 us
+    // at three waves on the 8B shape)
+    if (per_cu > 8) per_cu = 8;
     return cus * per_cu;
 }
 
-hipError_t launch_merge(const AttnParams &p, hipStream_t s) {
-    if (p.batch == 0) return hipSuccess;
-    if (p.schedule == KV_SCHED_BALANCED) {
-        hipLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, p);
-        return hipGetLastError();
-    }
-    if (p.max_splits <= 1) return hipSuccess;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, p);
+hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
+    const bool none = p.batch == 0 || (p.schedule != KV_SCHED_BALANCED && p.max_splits <= 1);
+    if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
+    const dim3 grid(p.n_h * p.q_len, p.batch);
+    if (p.schedule == KV_SCHED_BALANCED)
+        hipExtLaunchKernelGGL(attn_merge_balanced_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
+    else
+        hipExtLaunchKernelGGL(attn_merge_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
     return hipGetLastError();
 }
 

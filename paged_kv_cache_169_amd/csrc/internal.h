@@ -42,7 +42,20 @@ struct AttnParams {
     int32_t n_wg;      // balanced: persistent grid size
     int32_t *ws_prefix;  // balanced: [batch + 1] attended blocks before each sequence
     float scale_log2;  // scale * log2(e): scores are kept in log2 units
+    // Decode step: the attended length of sequence b is ctx_lens[b] + ctx_add
+    // (ctx_lens then holds the lengths before the step's append). With
+    // k_new / v_new set ([batch][ctx_add][n_kv][head_dim], bf16 MFMA path
+    // only) the append is fused: tiles take the new tokens' rows from there,
+    // and the first column tile of each kv head writes them into the pool.
+    int32_t ctx_add;
+    const void *k_new, *v_new;
 };
+
+// Attended length of sequence b (negative: invalid).
+__host__ __device__ inline int ctx_of(const AttnParams &p, int b) {
+    const int L = p.ctx_lens[b];
+    return p.ctx_add == 0 ? L : (L < 0 ? -1 : L + p.ctx_add);
+}
 
 struct AppendParams {
     PoolPtrs pool;
@@ -97,10 +110,14 @@ hipError_t launch_deviation(int dtype, const DeviationParams &p, hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
 hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
-hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s);
-hipError_t launch_merge(const AttnParams &p, hipStream_t s);
+// e0 / e1 (may be null): events recorded at the start / end of the attention
+// kernel; e_end: at the end of the merge (recorded on the stream when no merge
+// kernel runs).
+hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s, hipEvent_t e0 = nullptr,
+                            hipEvent_t e1 = nullptr);
+hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end = nullptr);
 // Persistent grid of the balanced schedule: resident workgroups per device.
-int balanced_grid(int dtype, int head_dim, int batch);
+int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 
