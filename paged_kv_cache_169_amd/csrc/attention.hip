@@ -27,11 +27,12 @@
 //  * attn_mfma_bf16_kernel (bf16): the block's scores for the whole query
 //    group are one 16x16 MFMA tile, S^T[token][head] = K_tile . Q^T (heads
 //    padded to 16), and the value update is O^T[channel][head] +=
-//    V_tile^T . P^T with 16x16x16 MFMAs. P is split into bf16 hi + lo parts
-//    so the weights keep ~16 bits (a single bf16 would cost up to 2^-9
-//    relative error per weight). The QK output layout (lane = head + 16 *
-//    token-quad) is exactly the B-operand layout the PV product needs, so P
-//    never leaves registers.
+//    V_tile^T . P^T. P is split into bf16 hi + lo parts so the weights keep
+//    ~16 bits (a single bf16 would cost up to 2^-9 relative error per
+//    weight); both parts go into one 16x16x32 MFMA per channel tile, the
+//    tile's 4 tokens repeated along k against hi then lo. The QK output
+//    layout (lane = head + 16 * token-quad) is exactly the B-operand layout
+//    the PV product needs, so P never leaves registers.
 #include "device.h"
 #include <hip/hip_ext.h>
 
@@ -42,7 +43,6 @@
 namespace kvc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -73,6 +73,12 @@ __device__ __forceinline__ u32x2_t stream_load8(gu16_t *p) {
 }
 
 enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_INT4 = 2 };
+
+// 2^x with the hardware instruction alone. Every argument here is a
+// difference from a running maximum (<= 0, or -inf for a masked slot), so a
+// result below the normal range, which the instruction flushes to 0, is a
+// weight no fp32 softmax sum can register anyway.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct SplitWork {
     SeqRange r;
@@ -298,8 +304,8 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams p) {
             mb = fmaxf(mb, __shfl_xor(mb, 16));
             mb = fmaxf(mb, __shfl_xor(mb, 32));
             const float mn = fmaxf(m_run[h], mb);
-            const float alpha = mn == m_run[h] ? 1.0f : exp2f(m_run[h] - mn);
-            const float pe = exp2f(s[h] - mn);
+            const float alpha = mn == m_run[h] ? 1.0f : fast_exp2(m_run[h] - mn);
+            const float pe = fast_exp2(s[h] - mn);
             l_run[h] = l_run[h] * alpha + pe;
 #pragma unroll
             for (int c = 0; c < CV; ++c) acc[h][c] *= alpha;
@@ -462,7 +468,9 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int tp = tok0 + 4 * G + r;
-        sv[r] = (!mask || (tp >= col.lo && tp < col.hi)) ? sc[r] * p.scale_log2 : -INFINITY;
+        bool ok = true;
+        if (mask) ok = (tp >= col.lo) & (tp < col.hi);  // mask is uniform
+        sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -470,7 +478,7 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     const float mn = fmaxf(st.m, mx);
     if (!__all(mn == st.m)) {
         // the running max moved for some column: rescale (rare after the first blocks)
-        const float alpha = mn == st.m ? 1.0f : exp2f(st.m - mn);  // unchanged (even -inf): 1
+        const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
 #pragma unroll
         for (int m = 0; m < MS; ++m) st.o[m] *= alpha;
@@ -481,7 +489,7 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        pr[r] = exp2f(sv[r] - mref);
+        pr[r] = fast_exp2(sv[r] - mref);
         st.l += pr[r];
     }
     // P^T as B operand, split into bf16 hi and lo parts
@@ -491,8 +499,12 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         hi[r] = f_to_bf16(pr[r]);
         lo[r] = f_to_bf16(pr[r] - bf16_to_f((uint16_t)hi[r]));
     }
-    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
-    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])));
+    // hi and lo parts side by side along k: one 16x16x32 product per channel
+    // tile takes both (k = 8G + i: hi of token 4G + i for i < 4, lo of token
+    // 4G + i - 4 after)
+    const bf16x8_t pB = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(lo[0], lo[1]),
+                             pack_bf16x2(lo[2], lo[3])));
     uint32_t vr[4][VC / 2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -515,9 +527,9 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     for (int m = 0; m < MS; ++m) {
         const int wi = m >> 1, sh = (m & 1) * 16;
         const uint32_t e0 = vr[0][wi] >> sh, e1 = vr[1][wi] >> sh, e2 = vr[2][wi] >> sh, e3 = vr[3][wi] >> sh;
-        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)));
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
+        const uint32_t a01 = pack_bf16x2(e0, e1), a23 = pack_bf16x2(e2, e3);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB, st.o[m], 0, 0, 0);
     }
 }
 
@@ -629,31 +641,35 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+typedef const __attribute__((address_space(1))) uint8_t gu8_t;
+typedef const __attribute__((address_space(1))) uint32_t gu32_t;
+typedef const __attribute__((address_space(1))) uint2 gu2_t;
+__device__ __forceinline__ gu8_t *global_u8(const void *p) { return (gu8_t *)(p); }
+
 struct Q4Tile {
-    uint4 kc;        // full block: K codes of token n16, channels 32G .. 32G+31
-    uint2 ksm;       // full block: this lane's 8 bytes of the block's fp16 K
-                     // scales (lanes 0-31) and mins (lanes 32-63); staged in LDS
+    uint4 kc;        // K codes of token n16, channels 32G .. 32G+31 (score A operand)
+    uint4 ks, km;    // fp16 K scales / mins of channels 8 n16 .. 8 n16 + 7
     uint32_t vc[4];  // V codes of tokens 4G+i, channels 8 n16 .. 8 n16 + 7
-    uint2 vs, vm;    // fp16 V scale / min of tokens 4G .. 4G+3
+    uint2 vs, vm;    // fp16 V scales / mins of tokens 4G .. 4G+3
 };
 
-__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int lane, int n16, int G, bool full,
-                                         Q4Tile &T) {
+// All of a block's loads, whether or not the block is full (a partial block
+// takes its K from the tail row, and its pool K bytes go unused): the same
+// loads on every path keep the compiler's waits to the tile being used.
+__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int n16, int G, Q4Tile &T) {
     const size_t tile = (size_t)pid * p.n_kv + kvh;
-    if (full) {
-        T.kc = __builtin_bit_cast(uint4, stream_load16(p.pool.kq + (tile * kBlock + n16) * 64 + 16 * G));
-        const uint16_t *sm = lane < 32 ? p.pool.ks + tile * 128 + 4 * lane : p.pool.km + tile * 128 + 4 * (lane - 32);
-        const u32x2_t v = stream_load8(sm);
-        T.ksm = make_uint2(v[0], v[1]);
-    } else {
-        T.kc = make_uint4(0, 0, 0, 0);
-        T.ksm = make_uint2(0, 0);
-    }
+    gu8_t *kq = global_u8(p.pool.kq) + tile * kBlock * 64;
+    gu8_t *vq = global_u8(p.pool.vq) + tile * kBlock * 64;
+    T.kc = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(kq + n16 * 64 + 16 * G)));
+    T.ks = __builtin_bit_cast(uint4, stream_load16(global_u16(p.pool.ks) + tile * 128 + 8 * n16));
+    T.km = __builtin_bit_cast(uint4, stream_load16(global_u16(p.pool.km) + tile * 128 + 8 * n16));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        T.vc[i] = *reinterpret_cast<const uint32_t *>(p.pool.vq + (tile * kBlock + 4 * G + i) * 64 + 4 * n16);
-    T.vs = *reinterpret_cast<const uint2 *>(p.pool.vs + tile * kBlock + 4 * G);
-    T.vm = *reinterpret_cast<const uint2 *>(p.pool.vm + tile * kBlock + 4 * G);
+        T.vc[i] = __builtin_nontemporal_load(reinterpret_cast<gu32_t *>(vq + (4 * G + i) * 64 + 4 * n16));
+    const u32x2_t s = stream_load8(global_u16(p.pool.vs) + tile * kBlock + 4 * G);
+    const u32x2_t m = stream_load8(global_u16(p.pool.vm) + tile * kBlock + 4 * G);
+    T.vs = make_uint2(s[0], s[1]);
+    T.vm = make_uint2(m[0], m[1]);
 }
 
 // 8 codes of one dword (channel 2k in the low nibble of byte k) as exact bf16.
@@ -671,52 +687,81 @@ __device__ __forceinline__ bf16x8_t q4_codes_bf16(uint32_t w) {
 __device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f((uint16_t)w); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f((uint16_t)(w >> 16)); }
 
-__device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const float (&qf)[32], bool full,
-                                         const uint16_t *tail_row, int tok0, int tlo, int thi, bool mask,
-                                         const Column &col, int lane, int G, uint2 *lds_sm, MfmaState<128> &st) {
+// Per-workgroup LDS of the INT4 path: the score product's B operand (query
+// times per-channel K scale, bf16 hi and lo parts) of the 16 columns, and the
+// per-column partial sums of query times K min. Rows are padded to 17 chunks
+// of 8 channels (272 bytes) so that the reads of 8 consecutive lanes, one row
+// each, fall in distinct banks.
+struct Q4Lds {
+    uint4 b[2][16][17];   // [hi / lo][column][channel chunk]
+    float corr[16][20];   // [column][channel chunk], padded
+};
+
+// Query of the columns this lane computes products for: column 4 pi + G,
+// channels 8 n16 .. 8 n16 + 7, pass pi < npass (fp32, bf16-exact; 0 for
+// padded columns).
+template <int NP>
+struct Q4Query {
+    float q[NP][8];
+    int npass;
+};
+
+// One (block, kv head) tile. Scores of a full block: s_t = sum_c code_tc *
+// (q_c * kscale_c) + sum_c q_c * kmin_c. The products are formed once per
+// (column, channel) by the lane that owns them (column 4 pi + G, channels
+// 8 n16 ..) and exchanged through LDS into the MFMA B layout; the min term is
+// summed per column the same way. A partial last block takes bf16 K from the
+// tail row (global, 16 x 128 per sequence and kv head) with plain q.
+template <int NP>
+__device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const Q4Query<NP> &Q, bool full,
+                                         gu16_t *tail_row, int tok0, int tlo, int thi, bool mask,
+                                         const Column &col, int n16, int G, Q4Lds &L, MfmaState<128> &st) {
+    __syncthreads();  // the previous tile's reads of L are done
+    const uint32_t sw[4] = {T.ks.x, T.ks.y, T.ks.z, T.ks.w}, mw[4] = {T.km.x, T.km.y, T.km.z, T.km.w};
+#pragma unroll
+    for (int pi = 0; pi < NP; ++pi) {
+        if (pi >= Q.npass) break;
+        const int c = 4 * pi + G;
+        uint32_t hi[4], lo[4];
+        if (full) {
+            float cp = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float q0 = Q.q[pi][2 * k], q1 = Q.q[pi][2 * k + 1];
+                const float p0 = q0 * f16_lo(sw[k]), p1 = q1 * f16_hi(sw[k]);  // exact products
+                cp = fmaf(q0, f16_lo(mw[k]), cp);
+                cp = fmaf(q1, f16_hi(mw[k]), cp);
+                hi[k] = cvt_pk_bf16(p0, p1);
+                lo[k] = cvt_pk_bf16(p0 - __uint_as_float(hi[k] << 16), p1 - __uint_as_float(hi[k] & 0xffff0000u));
+            }
+            L.b[1][c][n16] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            L.corr[c][n16] = cp;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) hi[k] = cvt_pk_bf16(Q.q[pi][2 * k], Q.q[pi][2 * k + 1]);  // exact
+        }
+        L.b[0][c][n16] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    }
+    __syncthreads();
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
-        // the block's 128 scales then 128 mins (fp16) through LDS: each lane
-        // reads back those of its channels 32G .. 32G+31
-        __syncthreads();
-        lds_sm[lane] = T.ksm;
-        __syncthreads();
-        const uint4 *s4 = reinterpret_cast<const uint4 *>(lds_sm) + 4 * G;       // scales of 32G..
-        const uint4 *m4 = reinterpret_cast<const uint4 *>(lds_sm) + 16 + 4 * G;  // mins of 32G..
+        const float4 cq = *reinterpret_cast<const float4 *>(&L.corr[n16][4 * G]);
+        corr = (cq.x + cq.y) + (cq.z + cq.w);
+        corr += __shfl_xor(corr, 16);
+        corr += __shfl_xor(corr, 32);
         const uint32_t kcw[4] = {T.kc.x, T.kc.y, T.kc.z, T.kc.w};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bf16x8_t a = q4_codes_bf16(kcw[s]);
-            const uint4 sq = s4[s], mq = m4[s];
-            const uint32_t sv[4] = {sq.x, sq.y, sq.z, sq.w};
-            const uint32_t mv[4] = {mq.x, mq.y, mq.z, mq.w};
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float q0 = qf[8 * s + 2 * k], q1 = qf[8 * s + 2 * k + 1];
-                const float p0 = q0 * f16_lo(sv[k]), p1 = q1 * f16_hi(sv[k]);  // exact products
-                corr = fmaf(q0, f16_lo(mv[k]), corr);
-                corr = fmaf(q1, f16_hi(mv[k]), corr);
-                hi[k] = cvt_pk_bf16(p0, p1);
-                lo[k] = cvt_pk_bf16(p0 - __uint_as_float(hi[k] << 16), p1 - __uint_as_float(hi[k] & 0xffff0000u));
-            }
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, L.b[1][n16][4 * G + s]), sc, 0, 0, 0);
         }
-        corr += __shfl_xor(corr, 16);
-        corr += __shfl_xor(corr, 32);
     } else {
-        // partial last block of the sequence: bf16 K from the tail row
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint32_t qb[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)  // q is bf16-exact: its bf16 is the top half
-                qb[k] = (__float_as_uint(qf[8 * s + 2 * k]) >> 16) | (__float_as_uint(qf[8 * s + 2 * k + 1]) & 0xffff0000u);
-            const uint4 kt = *reinterpret_cast<const uint4 *>(tail_row + 8 * s);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kt),
-                                                         __builtin_bit_cast(bf16x8_t, make_uint4(qb[0], qb[1], qb[2], qb[3])), sc, 0, 0, 0);
+            const bf16x8_t kt = __builtin_bit_cast(bf16x8_t, stream_load16(tail_row + 8 * s));
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
         }
     }
     const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
@@ -725,16 +770,20 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+        // partial and mask are uniform; the tests are plain bit operations
         const int tt = 4 * G + r, tp = tok0 + tt;
-        valid[r] = (!partial || (tt >= tlo && tt < thi)) && (!mask || (tp >= col.lo && tp < col.hi));
-        sv[r] = valid[r] ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
+        bool ok = true;
+        if (partial) ok = (tt >= tlo) & (tt < thi);
+        if (mask) ok = ok & (tp >= col.lo) & (tp < col.hi);
+        valid[r] = ok;
+        sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(st.m, mx);
     if (!__all(mn == st.m)) {
-        const float alpha = mn == st.m ? 1.0f : exp2f(st.m - mn);  // unchanged (even -inf): 1
+        const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
         st.bv *= alpha;
 #pragma unroll
@@ -747,7 +796,7 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     float bv = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float pr = exp2f(sv[r] - mref);  // 0 for masked slots
+        const float pr = fast_exp2(sv[r] - mref);  // 0 for masked slots
         st.l += pr;
         const float vsc = (r & 1) ? f16_hi(vsw[r >> 1]) : f16_lo(vsw[r >> 1]);
         const float vmn = (r & 1) ? f16_hi(vmw[r >> 1]) : f16_lo(vmw[r >> 1]);
@@ -763,42 +812,50 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
 #pragma unroll
     for (int r = 0; r < 4; ++r) bv = fmaf(-128.0f, hf[r] + lf[r], bv);
     st.bv += bv;
-    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(h01, h23));
-    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(l01, l23));
+    const bf16x8_t pB = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));  // hi, lo along k
+    // A operand of channel tile m: bf16(128 + code) of tokens 4G .. 4G+3,
+    // channel 8 n16 + m. Tokens (0,1) and (2,3) are paired so that one shift
+    // and one and-or give both halves of a dword: x holds channels 0-3 (xl)
+    // or 4-7 (xh) of the first token in its low half, of the second in its
+    // high half.
+    const uint32_t x01l = (T.vc[0] & 0xffffu) | (T.vc[1] << 16), x01h = (T.vc[0] >> 16) | (T.vc[1] & 0xffff0000u);
+    const uint32_t x23l = (T.vc[2] & 0xffffu) | (T.vc[3] << 16), x23h = (T.vc[2] >> 16) | (T.vc[3] & 0xffff0000u);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        uint32_t e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = 0x4300u | ((T.vc[i] >> (4 * m)) & 15u);  // bf16(128 + code)
-        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16)));
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
+        const int sh = 4 * (m & 3);
+        const uint32_t e01 = (((m < 4 ? x01l : x01h) >> sh) & 0x000f000fu) | 0x43004300u;
+        const uint32_t e23 = (((m < 4 ? x23l : x23h) >> sh) & 0x000f000fu) | 0x43004300u;
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(e01, e23, e01, e23));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB, st.o[m], 0, 0, 0);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, const Column &col, const SeqRange &r,
-                                           int j0, int j1, int lane, MfmaState<D> &st, bool &bad) {
+template <int D, int NP>
+__device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
+                                           const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
+                                           int *sids) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
-    const int g = p.group;
     int slot = p.seq_slots ? p.seq_slots[b] : b;
     if (slot < 0 || slot >= p.max_seqs) {
         bad = true;
         slot = 0;
     }
-    // q of the lane's column, channels 32G .. 32G+31, in fp32 (0 for padded columns)
-    float qf[32];
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + col.row * 128 + 32 * G;
+    // query of the product layout: column 4 pi + G of this column tile,
+    // channels 8 n16 .. 8 n16 + 7
+    Q4Query<NP> Q;
+    Q.npass = min((min(p.ncols - ct * 16, 16) + 3) / 4, NP);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int pi = 0; pi < NP; ++pi) {
+        const Column cq = column_of(p, b, kvh, ct, 4 * pi + G, r);
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (col.valid) v = *reinterpret_cast<const uint4 *>(qrow + 8 * i);
+        if (pi < Q.npass && cq.valid)
+            v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + cq.row * 128 + 8 * n16);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            qf[8 * i + 2 * k] = bf16_lo(w[k]);
-            qf[8 * i + 2 * k + 1] = bf16_hi(w[k]);
+            Q.q[pi][2 * k] = bf16_lo(w[k]);
+            Q.q[pi][2 * k + 1] = bf16_hi(w[k]);
         }
     }
 #pragma unroll
@@ -806,14 +863,20 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     st.m = -INFINITY;
     st.l = 0.0f;
     st.bv = 0.0f;
-    int ids = load_block_ids(p, b, j0, j1, lane);
-    int ids_base = j0;
+    if (j0 >= j1) return;
+    __shared__ Q4Lds L;
+    __syncthreads();  // the previous segment's reads of sids and L are done
+    for (int i = lane; i < j1 - j0; i += 64) sids[i] = p.tables[(size_t)b * p.max_blocks + j0 + i];
+    // columns past the passes are never written: zero B rows (padded columns)
+    for (int i = lane; i < (16 - 4 * Q.npass) * 17; i += 64) {
+        const int c = 4 * Q.npass + i / 17, k = i % 17;
+        L.b[0][c][k] = make_uint4(0, 0, 0, 0);
+        L.b[1][c][k] = make_uint4(0, 0, 0, 0);
+        if (k < 16) L.corr[c][k] = 0.0f;
+    }
+    __syncthreads();
     auto pid_of = [&](int j) {
-        if (j - ids_base >= 64) {
-            ids_base += 64;
-            ids = load_block_ids(p, b, ids_base, j1, lane);
-        }
-        int pid = __builtin_amdgcn_readlane(ids, j - ids_base);
+        int pid = __builtin_amdgcn_readfirstlane(sids[j - j0]);
         if (pid < 0 || pid >= p.num_blocks) {
             bad = true;
             pid = 0;
@@ -821,39 +884,36 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         return pid;
     };
     auto is_full = [&](int j) { return (j + 1) * kBlock <= r.n; };
-    __shared__ uint2 lds_sm[64];  // one block's fp16 K scales and mins
-    const uint16_t *tail_row = p.pool.ktail + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
-    auto bounds = [&](int j, int &tlo, int &thi) {
+    gu16_t *tail_row = global_u16(p.pool.ktail) + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
+    auto step = [&](const Q4Tile &T, int j) {
         const int tok0 = j * kBlock;
-        tlo = max(r.lo - tok0, 0);
-        thi = min(r.hi - tok0, kBlock);
+        const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
+        q4_block<NP>(p, T, Q, is_full(j), tail_row, tok0, tlo, thi, needs_mask(tok0, r), col, n16, G, L, st);
     };
+    // one tile in flight ahead of the one in use; the load past the end
+    // re-reads the segment's last tile (cached) instead of being skipped
+    auto fetch = [&](int j, Q4Tile &T) { q4_fetch(p, pid_of(j < j1 ? j : j1 - 1), kvh, n16, G, T); };
     Q4Tile A, B;
-    if (j0 < j1) q4_fetch(p, pid_of(j0), kvh, lane, n16, G, is_full(j0), A);
+    fetch(j0, A);
     for (int j = j0; j < j1; j += 2) {
-        int tlo, thi;
-        if (j + 1 < j1) q4_fetch(p, pid_of(j + 1), kvh, lane, n16, G, is_full(j + 1), B);
-        bounds(j, tlo, thi);
-        q4_block(p, A, qf, is_full(j), tail_row, j * kBlock, tlo, thi, needs_mask(j * kBlock, r), col, lane, G, lds_sm,
-                 st);
+        fetch(j + 1, B);
+        step(A, j);
         if (j + 1 >= j1) break;
-        if (j + 2 < j1) q4_fetch(p, pid_of(j + 2), kvh, lane, n16, G, is_full(j + 2), A);
-        bounds(j + 1, tlo, thi);
-        q4_block(p, B, qf, is_full(j + 1), tail_row, (j + 1) * kBlock, tlo, thi, needs_mask((j + 1) * kBlock, r), col,
-                 lane, G, lds_sm, st);
+        fetch(j + 2, A);
+        step(B, j + 1);
     }
 }
 
-// write_new: this unit stores the fused append's rows (column tile 0 only, so
-// that each new row is written once).
-template <int D, bool Q4>
-__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, const Column &col, const SeqRange &r,
-                                            int j0, int j1, int lane, MfmaState<D> &st, bool &bad, bool write_new,
+// Column tile ct of kv head kvh. Only column tile 0 stores the fused
+// append's rows, so that each new row is written once.
+template <int D, int Q4>
+__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
+                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
                                             int *sids) {
-    if constexpr (Q4)
-        q4_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad);
+    if constexpr (Q4 > 0)
+        q4_segment<D, Q4>(p, b, kvh, ct, col, r, j0, j1, lane, st, bad, sids);
     else
-        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, write_new, sids);
+        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, ct == 0, sids);
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
@@ -861,7 +921,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 // (no spills; the INT4 path would otherwise take 1 wave per SIMD).
 #define KV_MFMA_WAVES __attribute__((amdgpu_waves_per_eu(2)))
 
-template <int D, bool Q4>
+template <int D, int Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     extern __shared__ int sids[];  // [split_blocks] block ids of the segment
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
@@ -872,7 +932,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
     bool bad = w.r.bad;
     const Column col = column_of(p, b, kvh, ct, n16, w.r);
     MfmaState<D> st;
-    run_segment<D, Q4>(p, b, kvh, col, w.r, w.j0, w.j1, lane, st, bad, ct == 0, sids);
+    run_segment<D, Q4>(p, b, kvh, ct, col, w.r, w.j0, w.j1, lane, st, bad, sids);
     float l = st.l, bv = st.bv;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -918,7 +978,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
     return carry;
 }
 
-template <int D, bool Q4>
+template <int D, int Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] block prefix sums, then [split_blocks] block ids of a segment
     int *sids = pre + p.batch + 1;
@@ -953,7 +1013,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         bool bad = r.bad;
         const Column col = column_of(p, b, kvh, ct, n16, r);
         MfmaState<D> st;
-        run_segment<D, Q4>(p, b, kvh, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, ct == 0, sids);
+        run_segment<D, Q4>(p, b, kvh, ct, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
         float l = st.l, bv = st.bv;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
@@ -1005,7 +1065,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
     float L = 0.0f;
     if (M != -INFINITY) {  // else no split saw a token for this row: output 0
         for (int s = 0; s < r.nsplit; ++s) {
-            const float wgt = exp2f(ml[2 * s] - M);
+            const float wgt = fast_exp2(ml[2 * s] - M);
             L += wgt * ml[2 * s + 1];
             const float *o = p.ws_o + (base + s) * D + lane * cv;
             for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
@@ -1050,7 +1110,7 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
         for (int w = w0; w <= w1; ++w) {
             const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
             const size_t row = ((size_t)w * 2 + slot) * p.slot_cols + n16;
-            const float wgt = exp2f(p.ws_ml[row * 2] - M);
+            const float wgt = fast_exp2(p.ws_ml[row * 2] - M);
             L += wgt * p.ws_ml[row * 2 + 1];
             const float *o = p.ws_o + row * D + lane * cv;
             for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
@@ -1096,20 +1156,24 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
         if (p.schedule == KV_SCHED_BALANCED) {
             const uint32_t lds = (uint32_t)((p.batch + 1 + p.split_blocks) * sizeof(int));
             const dim3 bg(p.n_wg);
-            if (q4)
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, true>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            if (q4 && p.ncols <= 4)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            else if (q4)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, false>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, false>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0>), bg, dim3(64), lds, s, e0, e1, 0, p);
         } else {
             const uint32_t lds = (uint32_t)(p.split_blocks * sizeof(int));
-            if (q4)
-                hipExtLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            if (q4 && p.ncols <= 4)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (q4)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipExtLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipExtLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0>), grid, dim3(64), lds, s, e0, e1, 0, p);
         }
         return hipGetLastError();
     }
@@ -1128,11 +1192,11 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
         return 256 * 2;
     hipError_t e;
     if (dtype == KV_INT4)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, true>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 4>, 64, lds);
     else if (head_dim == 64)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<64, false>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<64, 0>, 64, lds);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, false>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 0>, 64, lds);
     if (e != hipSuccess || per_cu <= 0) per_cu = 2;
     // at most two waves per SIMD: with more, more tile bytes are in flight
     // and the 8B- and 70B-shaped decode layers measured slower (109 vs 104 us
