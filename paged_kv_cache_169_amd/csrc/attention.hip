@@ -1099,21 +1099,49 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     const long end = start + nb;
     const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
     if (w0 == w1) return;  // complete inside one workgroup: already written
-    float M = -INFINITY;
-    for (int w = w0; w <= w1; ++w) {
+    // workspace row of the partial that workgroup w holds for this pair
+    auto ws_row = [&](int w) {
         const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
-        M = fmaxf(M, p.ws_ml[(((size_t)w * 2 + slot) * p.slot_cols + n16) * 2]);
-    }
+        return ((size_t)w * 2 + slot) * p.slot_cols + n16;
+    };
+    // Partials 64 at a time: lane i reads the (m, l) of workgroup base + i, so
+    // the chunk's maxima and sums take one round trip and a wave reduction;
+    // the value rows are then loaded four at a time with their weights read
+    // from the lanes that hold them.
+    float M = -INFINITY, L = 0.0f;
     float acc[2] = {0.0f, 0.0f};
-    float L = 0.0f;
-    if (M != -INFINITY) {  // else no segment saw a token for this row: output 0
-        for (int w = w0; w <= w1; ++w) {
-            const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
-            const size_t row = ((size_t)w * 2 + slot) * p.slot_cols + n16;
-            const float wgt = fast_exp2(p.ws_ml[row * 2] - M);
-            L += wgt * p.ws_ml[row * 2 + 1];
-            const float *o = p.ws_o + row * D + lane * cv;
-            for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
+    for (int base = w0; base <= w1; base += 64) {
+        const int w = base + lane;
+        float m = -INFINITY, l = 0.0f;
+        if (w <= w1) {
+            const size_t row = ws_row(w);
+            m = p.ws_ml[row * 2];
+            l = p.ws_ml[row * 2 + 1];
+        }
+        const float Mn = fmaxf(M, wave_max(m));
+        if (Mn == -INFINITY) continue;  // no segment has seen a token yet
+        const float a = fast_exp2(M - Mn);  // 0 while M is -inf
+        L *= a;
+        acc[0] *= a;
+        acc[1] *= a;
+        M = Mn;
+        const float wgt = w <= w1 ? fast_exp2(m - M) : 0.0f;
+        L += wave_sum(wgt * l);  // a NaN l (bad sequence) makes the row NaN
+        const int cnt = min(64, w1 - base + 1);
+        for (int i0 = 0; i0 < cnt; i0 += 4) {
+            float wi[4], o[4][2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = min(i0 + k, cnt - 1);  // past the end: weight 0, row re-read
+                wi[k] = i0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i)) : 0.0f;
+                const float *src = p.ws_o + ws_row(base + i) * D + lane * cv;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) o[k][c] = c < cv ? src[c] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) acc[c] = fmaf(wi[k], o[k][c], acc[c]);
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;

@@ -37,6 +37,11 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
 
 // KVQuant INT4 scale and min of a group whose min/max are known: s = (max -
 // min) / 15 in fp32 (correctly rounded), both stored as fp16; a zero min or

@@ -73,7 +73,17 @@ __global__ __launch_bounds__(64) void append_int4_kernel(AppendParams p) {
     const int slot = p.seq_slots ? p.seq_slots[b] : b;
     if (slot < 0 || slot >= p.max_seqs) return;
     uint32_t *tail = reinterpret_cast<uint32_t *>(p.pool.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;
-    for (int tt = 0; tt < L0 % kBlock; ++tt) rows[tt][lane] = act ? tail[(size_t)tt * hd + lane] : 0u;
+    // the rows already in the open block are needed only if this call
+    // completes it; they are loaded together (independent loads)
+    const int t0 = L0 % kBlock;
+    if (t0 > 0 && t0 + p.n_new >= kBlock) {
+        uint32_t w[kBlock - 1];
+#pragma unroll
+        for (int tt = 0; tt < kBlock - 1; ++tt) w[tt] = (act && tt < t0) ? tail[(size_t)tt * hd + lane] : 0u;
+#pragma unroll
+        for (int tt = 0; tt < kBlock - 1; ++tt)
+            if (tt < t0) rows[tt][lane] = w[tt];
+    }
     __syncthreads();
     for (int k = 0; k < p.n_new; ++k) {
         const int L = L0 + k;

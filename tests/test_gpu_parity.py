@@ -51,11 +51,11 @@ def new_pool(c, dtype=None):
     return p
 
 
-def gpu_attention(pool, c, kernel=0, split_blocks=0, window=0, seq_slots=None, ctx=None, max_ctx=None):
+def gpu_attention(pool, c, kernel=0, split_blocks=0, window=0, seq_slots=None, ctx=None, max_ctx=None, schedule=0):
     ctx = c.ctx_lens if ctx is None else ctx
     if max_ctx is None:
         max_ctx = int(ctx.max().item()) if ctx.numel() else 0
-    opts = kv.attn_opts(split_blocks=split_blocks, kernel=kernel, window=window)
+    opts = kv.attn_opts(split_blocks=split_blocks, kernel=kernel, window=window, schedule=schedule)
     nbytes = kv.paged_decode_attention_workspace_bytes(pool, c.batch, c.n_h, max_ctx, opts)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
     out = torch.full((c.batch, c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
@@ -230,6 +230,21 @@ def test_schedules_agree(window):
     for split in (0, 1, 5, 64):
         out = gpu_attention(pool, c, kernel=2, split_blocks=split, window=window)
         assert max_err(out, ref) <= TOL, split
+
+
+@pytest.mark.parametrize("lens,n_h,n_kv,window", [([40000], 8, 1, 0), ([0, 17, 30000], 4, 1, 0),
+                                                   ([25000, 9], 16, 2, 20000)])
+def test_balanced_merge_many_partials(lens, n_h, n_kv, window):
+    """Few long sequences over the whole persistent grid: one (sequence, kv
+    head) pair is cut across hundreds of workgroups, so the merge combines its
+    partials in several chunks of 64."""
+    c = wl.make_case(907, len(lens), lens, n_h, n_kv, 128, "bf16", device=DEV)
+    pool = new_pool(c)
+    kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens)
+    K, V = oracle_step(c)
+    ref = orc.attention(K, V, bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale, window=window)
+    out = gpu_attention(pool, c, kernel=2, window=window, schedule=2)
+    assert max_err(out, ref) <= TOL
 
 
 # ---------------------------------------------------------------------------
