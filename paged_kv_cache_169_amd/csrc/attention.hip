@@ -43,6 +43,7 @@
 namespace kvc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -80,13 +81,20 @@ enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_INT4 = 2 };
 // weight no fp32 softmax sum can register anyway.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A value every lane of the wave reads from the same address, moved to a
+// scalar register: the loads these come from are vector loads (the kernels
+// also write global memory), and whatever is derived from them - block
+// ranges, loop counters, tile addresses - would otherwise stay in vector
+// registers and cost vector instructions on every tile.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 struct SplitWork {
     SeqRange r;
     int j0, j1;  // blocks [j0, j1) of this split
 };
 
 __device__ __forceinline__ bool split_work(const AttnParams &p, int b, int split, SplitWork &w) {
-    w.r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+    w.r = seq_range(uniform(ctx_of(p, b)), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (split >= w.r.nsplit) return false;
     w.j0 = w.r.blk_lo + split * p.split_blocks;
     w.j1 = min(w.r.blk_lo + w.r.nblk, w.j0 + p.split_blocks);
@@ -656,32 +664,50 @@ struct Q4Tile {
 // All of a block's loads, whether or not the block is full (a partial block
 // takes its K from the tail row, and its pool K bytes go unused): the same
 // loads on every path keep the compiler's waits to the tile being used.
+// Buffer resource over `bytes` bytes from base (scalar registers), for raw
+// buffer loads: the tile base stays scalar, the lane offset is a 32-bit
+// vector operand, and reads past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+enum { kLoadStream = 2 };  // cache policy of a raw buffer load: non-temporal
+
 __device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int n16, int G, Q4Tile &T) {
     const size_t tile = (size_t)pid * p.n_kv + kvh;
-    gu8_t *kq = global_u8(p.pool.kq) + tile * kBlock * 64;
-    gu8_t *vq = global_u8(p.pool.vq) + tile * kBlock * 64;
-    T.kc = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(kq + n16 * 64 + 16 * G)));
-    T.ks = __builtin_bit_cast(uint4, stream_load16(global_u16(p.pool.ks) + tile * 128 + 8 * n16));
-    T.km = __builtin_bit_cast(uint4, stream_load16(global_u16(p.pool.km) + tile * 128 + 8 * n16));
+    const auto kq = tile_rsrc(p.pool.kq + tile * (kBlock * 64), kBlock * 64);
+    const auto vq = tile_rsrc(p.pool.vq + tile * (kBlock * 64), kBlock * 64);
+    const auto ks = tile_rsrc(p.pool.ks + tile * 128, 256);
+    const auto km = tile_rsrc(p.pool.km + tile * 128, 256);
+    const auto vs = tile_rsrc(p.pool.vs + tile * kBlock, kBlock * 2);
+    const auto vm = tile_rsrc(p.pool.vm + tile * kBlock, kBlock * 2);
+    T.kc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, n16 * 64 + 16 * G, 0, kLoadStream));
+    T.ks = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ks, 16 * n16, 0, kLoadStream));
+    T.km = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(km, 16 * n16, 0, kLoadStream));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        T.vc[i] = __builtin_nontemporal_load(reinterpret_cast<gu32_t *>(vq + (4 * G + i) * 64 + 4 * n16));
-    const u32x2_t s = stream_load8(global_u16(p.pool.vs) + tile * kBlock + 4 * G);
-    const u32x2_t m = stream_load8(global_u16(p.pool.vm) + tile * kBlock + 4 * G);
+        T.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(vq, (4 * G + i) * 64 + 4 * n16, 0, kLoadStream);
+    const u32x2_t s = __builtin_amdgcn_raw_buffer_load_b64(vs, 8 * G, 0, kLoadStream);
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(vm, 8 * G, 0, kLoadStream);
     T.vs = make_uint2(s[0], s[1]);
     T.vm = make_uint2(m[0], m[1]);
 }
 
+
 // 8 codes of one dword (channel 2k in the low nibble of byte k) as exact bf16.
+// Each code goes to a byte of its own, in channel order; a byte c < 16 read
+// as an OCP E4M3 value is exactly c * 2^-9 (a subnormal for c < 8, exponent
+// field 1 for 8 <= c < 16), so the hardware fp8 -> bf16 conversion with scale
+// 2^9 gives c itself, two codes per instruction.
 __device__ __forceinline__ bf16x8_t q4_codes_bf16(uint32_t w) {
-    const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;
-    uint32_t d[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float fe = (float)((ev >> (8 * k)) & 0xffu), fo = (float)((od >> (8 * k)) & 0xffu);
-        d[k] = (__float_as_uint(fe) >> 16) | (__float_as_uint(fo) & 0xffff0000u);  // exact: small integers
-    }
-    return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+    const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes of channels 0,2,4,6 / 1,3,5,7
+    const uint32_t c03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // bytes: c0 c1 c2 c3
+    const uint32_t c47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // bytes: c4 c5 c6 c7
+    const bf16x2_t d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c03, 512.0f, false);
+    const bf16x2_t d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c03, 512.0f, true);
+    const bf16x2_t d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c47, 512.0f, false);
+    const bf16x2_t d3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c47, 512.0f, true);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
+                                                   __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)));
 }
 
 __device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f((uint16_t)w); }
@@ -812,7 +838,8 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
 #pragma unroll
     for (int r = 0; r < 4; ++r) bv = fmaf(-128.0f, hf[r] + lf[r], bv);
     st.bv += bv;
-    const bf16x8_t pB = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));  // hi, lo along k
+    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(h01, h23));
+    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(l01, l23));
     // A operand of channel tile m: bf16(128 + code) of tokens 4G .. 4G+3,
     // channel 8 n16 + m. Tokens (0,1) and (2,3) are paired so that one shift
     // and one and-or give both halves of a dword: x holds channels 0-3 (xl)
@@ -825,8 +852,11 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         const int sh = 4 * (m & 3);
         const uint32_t e01 = (((m < 4 ? x01l : x01h) >> sh) & 0x000f000fu) | 0x43004300u;
         const uint32_t e23 = (((m < 4 ? x23l : x23h) >> sh) & 0x000f000fu) | 0x43004300u;
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(e01, e23, e01, e23));
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB, st.o[m], 0, 0, 0);
+        // two 16x16x16 products: one 16x16x32 would need the A operand twice
+        // (register copies, and this path is bound by vector instructions)
+        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(e01, e23));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
     }
 }
 
@@ -836,7 +866,7 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
                                            int *sids) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
-    int slot = p.seq_slots ? p.seq_slots[b] : b;
+    int slot = uniform(p.seq_slots ? p.seq_slots[b] : b);
     if (slot < 0 || slot >= p.max_seqs) {
         bad = true;
         slot = 0;
@@ -984,7 +1014,11 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     int *sids = pre + p.batch + 1;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
-    const int nblk_total = balanced_prefix(p, pre, lane);
+    // The INT4 path is bound by vector instructions: there the sequence
+    // search and everything derived from it are moved to scalar registers.
+    // The bf16 path keeps them in vector registers (measured faster: the
+    // scalar form runs out of scalar registers there).
+    const int nblk_total = Q4 ? uniform(balanced_prefix(p, pre, lane)) : balanced_prefix(p, pre, lane);
     if (wg == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)nblk_total * p.units;
@@ -993,23 +1027,27 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     const long e = min(total, s + per);
     for (long t = s; t < e;) {
         // sequence holding tile t: largest b with units * pre[b] <= t
+        auto pre_s = [&](int i) { return Q4 ? uniform(pre[i]) : pre[i]; };
         int lo = 0, hi = p.batch - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((long)pre[mid] * p.units <= t)
+            if ((long)pre_s(mid) * p.units <= t)
                 lo = mid;
             else
                 hi = mid - 1;
         }
         const int b = lo;
-        const int nb = pre[b + 1] - pre[b];
-        const long pair0 = (long)pre[b] * p.units;
+        const int pb = pre_s(b);
+        const int nb = pre_s(b + 1) - pb;
+        const long pair0 = (long)pb * p.units;
         const int unit = (int)((t - pair0) / nb);
         const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
         const int jr = (int)(t - pair0 - (long)unit * nb);
         const long seg_end = min(e, pair0 + (long)(unit + 1) * nb);
         const int cnt = (int)(seg_end - t);
-        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const int ctx = ctx_of(p, b);
+        const SeqRange r = seq_range(Q4 ? uniform(ctx) : ctx, p.max_blocks, p.window, p.split_blocks, p.max_splits,
+                                     p.q_len);
         bool bad = r.bad;
         const Column col = column_of(p, b, kvh, ct, n16, r);
         MfmaState<D> st;
