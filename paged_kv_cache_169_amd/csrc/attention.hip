@@ -632,10 +632,9 @@ __device__ __forceinline__ void mfma_gather_run(const MfmaState<D> &st, float bv
 // integers; the min term is a per-head correction added to the scores.
 // A sequence's partial last block takes its K from the bf16 tail row with
 // plain q. Values: sum_t p_t (min_t + scale_t * code_tc) = sum_t P'_t *
-// (128 + code_tc) + sum_t (p_t * min_t - 128 * P'_t) with P'_t = p_t *
-// scale_t (bf16 hi + lo in the B operand) and bf16(128 + code) in the A
-// operand (exact, and finite whatever a masked slot holds); the second sum is
-// a per-head numerator term kept beside o.
+// code_tc + sum_t p_t * min_t with P'_t = p_t * scale_t (bf16 hi + lo in
+// the B operand) and the exact codes in the A operand; the second sum is a
+// per-head numerator term kept beside o.
 // Lane (G, n16) covers channels 32G .. 32G+31 in the score product and
 // value channels 8 n16 .. 8 n16 + 7 in the value product.
 // ---------------------------------------------------------------------------
@@ -732,6 +731,91 @@ struct Q4Query {
     int npass;
 };
 
+// Online softmax and value update of one INT4 tile, given its raw scores sc
+// (before the per-column min term corr). MASKED: some slots of the tile are
+// outside the attended range (partial block, window, causal columns); their
+// weights are 0 and their V parameters, which may be anything, are not used.
+// Values: sum_t p_t (min_t + scale_t * code_tc) = sum_t P'_t * code_tc +
+// sum_t p_t * min_t with P'_t = p_t * scale_t (bf16 hi + lo in the B
+// operand) and the exact codes in the A operand; the second sum is a
+// per-column numerator term kept beside o.
+template <bool MASKED>
+__device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const f32x4_t &sc, float corr,
+                                              int tok0, int tlo, int thi, bool partial, bool mask, const Column &col,
+                                              int G, MfmaState<128> &st) {
+    float sv[4];
+    bool valid[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tt = 4 * G + r, tp = tok0 + tt;
+        bool ok = true;
+        if (MASKED) {
+            if (partial) ok = (tt >= tlo) & (tt < thi);
+            if (mask) ok = ok & (tp >= col.lo) & (tp < col.hi);
+        }
+        valid[r] = ok;
+        sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(st.m, mx);
+    if (!__all(mn == st.m)) {
+        const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
+        st.l *= alpha;
+        st.bv *= alpha;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) st.o[m] *= alpha;
+        st.m = mn;
+    }
+    const uint32_t vsw[2] = {T.vs.x, T.vs.y}, vmw[2] = {T.vm.x, T.vm.y};
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;  // no token seen yet: weights 0
+    float pv[4];
+    float bv = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float pr = fast_exp2(sv[r] - mref);  // 0 for masked slots
+        st.l += pr;
+        const float vsc = (r & 1) ? f16_hi(vsw[r >> 1]) : f16_lo(vsw[r >> 1]);
+        const float vmn = (r & 1) ? f16_hi(vmw[r >> 1]) : f16_lo(vmw[r >> 1]);
+        pv[r] = valid[r] ? pr * vsc : 0.0f;
+        bv = valid[r] ? fmaf(pr, vmn, bv) : bv;
+    }
+    st.bv += bv;
+    const uint32_t h01 = cvt_pk_bf16(pv[0], pv[1]), h23 = cvt_pk_bf16(pv[2], pv[3]);
+    const uint32_t l01 = cvt_pk_bf16(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = cvt_pk_bf16(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(h01, h23));
+    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(l01, l23));
+    // A operand of channel tile m: the exact codes of tokens 4G .. 4G+3 at
+    // channel 8 n16 + m. Bytes of tokens (0,1) and (2,3) are interleaved so
+    // that after splitting nibbles each 16-bit half holds one channel of both
+    // tokens, which the fp8 conversion turns into a bf16 pair (see
+    // q4_codes_bf16 for why that conversion is exact).
+    uint32_t a01[8], a23[8];
+    auto spread = [](uint32_t x, uint32_t(&dst)[8], int c0) {
+        const uint32_t e = x & 0x0f0f0f0fu, o = (x >> 4) & 0x0f0f0f0fu;
+        dst[c0 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(e, 512.0f, false));
+        dst[c0 + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(e, 512.0f, true));
+        dst[c0 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(o, 512.0f, false));
+        dst[c0 + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(o, 512.0f, true));
+    };
+    spread(__builtin_amdgcn_perm(T.vc[1], T.vc[0], 0x05010400u), a01, 0);  // channels 0-3
+    spread(__builtin_amdgcn_perm(T.vc[1], T.vc[0], 0x07030602u), a01, 4);  // channels 4-7
+    spread(__builtin_amdgcn_perm(T.vc[3], T.vc[2], 0x05010400u), a23, 0);
+    spread(__builtin_amdgcn_perm(T.vc[3], T.vc[2], 0x07030602u), a23, 4);
+    // masked slots: P' is 0 there and the codes are finite, so nothing leaks
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        // two 16x16x16 products: one 16x16x32 would need the A operand twice
+        // (register copies, and this path is bound by vector instructions)
+        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(a01[m], a23[m]));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
+    }
+}
+
 // One (block, kv head) tile. Scores of a full block: s_t = sum_c code_tc *
 // (q_c * kscale_c) + sum_c q_c * kmin_c. The products are formed once per
 // (column, channel) by the lane that owns them (column 4 pi + G, channels
@@ -791,73 +875,10 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         }
     }
     const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
-    float sv[4];
-    bool valid[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        // partial and mask are uniform; the tests are plain bit operations
-        const int tt = 4 * G + r, tp = tok0 + tt;
-        bool ok = true;
-        if (partial) ok = (tt >= tlo) & (tt < thi);
-        if (mask) ok = ok & (tp >= col.lo) & (tp < col.hi);
-        valid[r] = ok;
-        sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(st.m, mx);
-    if (!__all(mn == st.m)) {
-        const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
-        st.l *= alpha;
-        st.bv *= alpha;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) st.o[m] *= alpha;
-        st.m = mn;
-    }
-    const uint32_t vsw[2] = {T.vs.x, T.vs.y}, vmw[2] = {T.vm.x, T.vm.y};
-    const float mref = st.m == -INFINITY ? 0.0f : st.m;  // no token seen yet: weights 0
-    float pv[4];
-    float bv = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float pr = fast_exp2(sv[r] - mref);  // 0 for masked slots
-        st.l += pr;
-        const float vsc = (r & 1) ? f16_hi(vsw[r >> 1]) : f16_lo(vsw[r >> 1]);
-        const float vmn = (r & 1) ? f16_hi(vmw[r >> 1]) : f16_lo(vmw[r >> 1]);
-        pv[r] = valid[r] ? pr * vsc : 0.0f;            // masked slots may hold NaN params
-        bv = valid[r] ? fmaf(pr, vmn, bv) : bv;
-    }
-    const uint32_t h01 = cvt_pk_bf16(pv[0], pv[1]), h23 = cvt_pk_bf16(pv[2], pv[3]);
-    const float hf[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u), __uint_as_float(h23 << 16),
-                         __uint_as_float(h23 & 0xffff0000u)};
-    const uint32_t l01 = cvt_pk_bf16(pv[0] - hf[0], pv[1] - hf[1]), l23 = cvt_pk_bf16(pv[2] - hf[2], pv[3] - hf[3]);
-    const float lf[4] = {__uint_as_float(l01 << 16), __uint_as_float(l01 & 0xffff0000u), __uint_as_float(l23 << 16),
-                         __uint_as_float(l23 & 0xffff0000u)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bv = fmaf(-128.0f, hf[r] + lf[r], bv);
-    st.bv += bv;
-    const bf16x4_t pHi = __builtin_bit_cast(bf16x4_t, make_uint2(h01, h23));
-    const bf16x4_t pLo = __builtin_bit_cast(bf16x4_t, make_uint2(l01, l23));
-    // A operand of channel tile m: bf16(128 + code) of tokens 4G .. 4G+3,
-    // channel 8 n16 + m. Tokens (0,1) and (2,3) are paired so that one shift
-    // and one and-or give both halves of a dword: x holds channels 0-3 (xl)
-    // or 4-7 (xh) of the first token in its low half, of the second in its
-    // high half.
-    const uint32_t x01l = (T.vc[0] & 0xffffu) | (T.vc[1] << 16), x01h = (T.vc[0] >> 16) | (T.vc[1] & 0xffff0000u);
-    const uint32_t x23l = (T.vc[2] & 0xffffu) | (T.vc[3] << 16), x23h = (T.vc[2] >> 16) | (T.vc[3] & 0xffff0000u);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int sh = 4 * (m & 3);
-        const uint32_t e01 = (((m < 4 ? x01l : x01h) >> sh) & 0x000f000fu) | 0x43004300u;
-        const uint32_t e23 = (((m < 4 ? x23l : x23h) >> sh) & 0x000f000fu) | 0x43004300u;
-        // two 16x16x16 products: one 16x16x32 would need the A operand twice
-        // (register copies, and this path is bound by vector instructions)
-        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(e01, e23));
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
-        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
-    }
+    if (partial || mask)  // uniform: the rare masked form and the common one are separate code
+        q4_softmax_pv<true>(p, T, sc, corr, tok0, tlo, thi, partial, mask, col, G, st);
+    else
+        q4_softmax_pv<false>(p, T, sc, corr, tok0, tlo, thi, partial, mask, col, G, st);
 }
 
 template <int D, int NP>
