@@ -88,6 +88,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // registers and cost vector instructions on every tile.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Max / sum over lanes l, l^16, l^32, l^48: the four lanes that hold one
+// column in the 16x16 MFMA layouts. gfx950's lane-swap instructions do both
+// butterfly steps inside the VALU (no LDS round trip); every lane of the
+// four ends with the same bits (each step adds the same two operands in the
+// same order on both lanes of a pair).
+__device__ __forceinline__ float col_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 struct SplitWork {
     SeqRange r;
     int j0, j1;  // blocks [j0, j1) of this split
@@ -481,9 +499,7 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(st.m, mx);
+    const float mn = fmaxf(st.m, col_max(mx));
     if (!__all(mn == st.m)) {
         // the running max moved for some column: rescale (rare after the first blocks)
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
@@ -758,9 +774,7 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
         sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(st.m, mx);
+    const float mn = fmaxf(st.m, col_max(mx));
     if (!__all(mn == st.m)) {
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
@@ -857,16 +871,16 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     float corr = 0.0f;
     if (full) {
         const float4 cq = *reinterpret_cast<const float4 *>(&L.corr[n16][4 * G]);
-        corr = (cq.x + cq.y) + (cq.z + cq.w);
-        corr += __shfl_xor(corr, 16);
-        corr += __shfl_xor(corr, 32);
+        corr = col_sum((cq.x + cq.y) + (cq.z + cq.w));
         const uint32_t kcw[4] = {T.kc.x, T.kc.y, T.kc.z, T.kc.w};
+        f32x4_t sl = {0.0f, 0.0f, 0.0f, 0.0f};  // hi and lo parts in two chains: half the dependent latency
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bf16x8_t a = q4_codes_bf16(kcw[s]);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, L.b[1][n16][4 * G + s]), sc, 0, 0, 0);
+            sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, L.b[1][n16][4 * G + s]), sl, 0, 0, 0);
         }
+        sc += sl;
     } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -984,11 +998,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
     const Column col = column_of(p, b, kvh, ct, n16, w.r);
     MfmaState<D> st;
     run_segment<D, Q4>(p, b, kvh, ct, col, w.r, w.j0, w.j1, lane, st, bad, sids);
-    float l = st.l, bv = st.bv;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    bv += __shfl_xor(bv, 16);
-    bv += __shfl_xor(bv, 32);
+    const float l = col_sum(st.l), bv = col_sum(st.bv);
     if (col.valid) {
         float res[D / 4];
         mfma_gather_run<D>(st, bv, res);
@@ -1073,11 +1083,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         const Column col = column_of(p, b, kvh, ct, n16, r);
         MfmaState<D> st;
         run_segment<D, Q4>(p, b, kvh, ct, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
-        float l = st.l, bv = st.bv;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        bv += __shfl_xor(bv, 16);
-        bv += __shfl_xor(bv, 32);
+        const float l = col_sum(st.l), bv = col_sum(st.bv);
         if (col.valid) {
             float res[D / 4];
             mfma_gather_run<D>(st, bv, res);
