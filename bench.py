@@ -67,6 +67,23 @@ def profiled_traffic(workload: str):
     return int(d["hbm_bytes_per_dispatch"])
 
 
+def unique_attended_tokens(tables, ctx) -> int:
+    """Attended (physical block, slot) positions counted once: every sequence
+    attends slots [0, min(16, n - 16 j)) of its logical block j, so a physical
+    block contributes the largest such count over the entries that name it."""
+    import torch
+    best = {}
+    for b in range(tables.shape[0]):
+        n = int(ctx[b])
+        nb = (n + 15) // 16
+        ids = tables[b, :nb].tolist()
+        for j, pid in enumerate(ids):
+            cnt = min(16, n - 16 * j)
+            if cnt > best.get(pid, 0):
+                best[pid] = cnt
+    return sum(best.values())
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime (ctypes). The events only
     time work: they are created without the system-scope fence a recorded
@@ -215,16 +232,21 @@ def main():
     merge_avg = sum(merge_ms) / len(merge_ms)
 
     # algorithmic bytes of one split-kernel launch: K and V of every attended
-    # (token, kv head) once, q, the output, the block-table entries and lengths
+    # (token, kv head) once, q, the output, the block-table entries and lengths.
+    # Where tables share physical blocks (the long shared-prefix workload) a
+    # shared token's K and V count once: the unique bytes are what HBM must
+    # deliver; the logical bytes (every sequence's tokens) are reported beside.
     nblk = ((ctx + 15) // 16)
-    if int4:
-        kv_bytes = int(ctx.sum().item()) * n_kv * 164
-    else:
-        kv_bytes = int(ctx.sum().item()) * n_kv * 2 * D * es
+    per_token = n_kv * (164 if int4 else 2 * D * es)
+    logical_tokens = int(ctx.sum().item())
+    unique_tokens = unique_attended_tokens(c.tables.cpu(), ctx.cpu())
+    kv_bytes = unique_tokens * per_token
     alg_bytes = kv_bytes + k * (B * n_h * D * es + B * n_h * D * 4) + int(nblk.sum().item()) * 4 + B * 4
+    logical_bytes = alg_bytes + (logical_tokens - unique_tokens) * per_token
     fused = c.append and c.dtype == "bf16" and not int4 and args.kernel in (0, 2)
     if fused:  # the kernel also writes the step's new K and V rows into the pool
         alg_bytes += B * k * n_kv * 2 * D * es
+        logical_bytes += B * k * n_kv * 2 * D * es
     achieved = alg_bytes / (split_avg * 1e-3) / 1e9
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None
@@ -289,7 +311,8 @@ def main():
                      "traffic_bytes_per_launch": traffic_bytes,
                      "kernel": "decode attention kernel (before the merge)" + (", append fused" if fused else ""),
                      "avg_launch_us": split_avg * 1e3,
-                     "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes},
+                     "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes,
+                     "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
