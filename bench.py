@@ -50,11 +50,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(workload: str):
+def profiled_traffic(workload: str, kernel: str = "attn_mfma_balanced"):
     """HBM bytes per dispatch of the decode kernel from the committed counter
-    summary (profiles/attn_mfma_balanced_<workload>_counters.md), or None when
-    there is none or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"attn_mfma_balanced_{workload}_counters.md")
+    summary (profiles/<kernel>_<workload>_counters.md), or None when there is
+    none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
@@ -65,6 +65,31 @@ def profiled_traffic(workload: str):
     if d.get("kernel_source_sha256") != kernel_source_digest():
         return None
     return int(d["hbm_bytes_per_dispatch"])
+
+
+def shared_prefix_groups(tables, ctx):
+    """(group_start, prefix_blocks) for prefix_groups(): runs of consecutive
+    sequences whose tables start with the same physical blocks as the run's
+    first sequence; prefix_blocks is the shortest such common start (whole
+    attended blocks only). A sequence that shares nothing is a group of one
+    with no prefix."""
+    B = tables.shape[0]
+    full = [int(ctx[b]) // 16 for b in range(B)]
+    group_start, prefix = [0], []
+    b = 0
+    while b < B:
+        e, common = b + 1, full[b]
+        while e < B:
+            n = min(full[b], full[e])
+            same = int((tables[b, :n] == tables[e, :n]).long().cumprod(0).sum()) if n > 0 else 0
+            if same == 0:
+                break
+            common = min(common, same)
+            e += 1
+        prefix.append(common if e - b > 1 else 0)
+        group_start.append(e)
+        b = e
+    return group_start, prefix
 
 
 def unique_attended_tokens(tables, ctx) -> int:
@@ -130,6 +155,9 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence: 1 is decode; k > 1 appends k tokens and runs the "
                          "multi-token (verification) attention over them")
+    ap.add_argument("--shared", type=int, default=-1,
+                    help="1: the shared-prefix entry point (each shared block read once per group), 0: the plain "
+                         "call; -1 (default): shared for the long shared-prefix workload, plain otherwise")
     ap.add_argument("--op", default="decode", choices=["decode", "append", "quantize", "rope", "copy", "offload", "select"],
                     help="decode: the decode step (default); the others time one secondary kernel")
     args = ap.parse_args()
@@ -183,7 +211,15 @@ def main():
             kv.rope_rerotate(p, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
     max_ctx = int(ctx.max().item())
     opts = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule)
-    ws_bytes = kv.paged_multi_token_attention_workspace_bytes(pools[0], B, n_h, k, max_ctx, opts)
+    shared = args.shared == 1 or (args.shared < 0 and name == "long_shared")
+    groups = None
+    if shared:
+        # sequences that name the same physical blocks from the start of their tables
+        starts, prefix = shared_prefix_groups(c.tables.cpu(), ctx)
+        groups = kv.prefix_groups(starts, prefix)
+        ws_bytes = kv.paged_decode_attention_shared_workspace_bytes(pools[0], B, n_h, max_ctx, groups, opts)
+    else:
+        ws_bytes = kv.paged_multi_token_attention_workspace_bytes(pools[0], B, n_h, k, max_ctx, opts)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, n_h, D) if k == 1 else (B, k, n_h, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -199,7 +235,12 @@ def main():
         o = opts
         if events is not None:
             o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule, events=events)
-        if c.append:
+        if shared:
+            o = kv.attn_opts(split_blocks=args.split, kernel=args.kernel, schedule=args.schedule,
+                             events=events) if events is not None else opts
+            kv.paged_decode_attention_shared(p, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, groups, ws, opts=o,
+                                             stream=stream)
+        elif c.append:
             # append + attention in one call (fused into the attention kernel on bf16 pools)
             kv.kv_decode_step(p, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=o,
                               stream=stream)
@@ -251,7 +292,7 @@ def main():
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None
     if args.kernel == 0 and args.split == 0 and args.schedule == 0 and k == 1:  # the counters' configuration
-        traffic_bytes = profiled_traffic(name)
+        traffic_bytes = profiled_traffic(name, "attn_mfma_shared" if shared else "attn_mfma_balanced")
     traffic = traffic_bytes / (split_avg * 1e-3) / 1e9 if traffic_bytes else None
     log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
         f"{split_avg*1e3:.1f} us, merge {merge_avg*1e3:.1f} us, {achieved:.0f} GB/s "
@@ -304,12 +345,13 @@ def main():
                    else int(ctx.max().item()), "tokens_per_step": tokens_per_step, "n_h": n_h, "n_kv": n_kv,
                    "head_dim": D, "block_size": 16, "kernel": args.kernel, "split_blocks": args.split,
                    "schedule": args.schedule,
-                   "accumulate": "f32", "pool_replicas": reps, "q_len": k,
+                   "accumulate": "f32", "pool_replicas": reps, "q_len": k, "shared_prefix_call": shared,
                    "query_tokens_per_s": B * k / (ms_per_step * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,
-                     "kernel": "decode attention kernel (before the merge)" + (", append fused" if fused else ""),
+                     "kernel": ("shared-prefix decode attention kernel (before the merge)" if shared else
+                                "decode attention kernel (before the merge)" + (", append fused" if fused else "")),
                      "avg_launch_us": split_avg * 1e3,
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes,
                      "logical_bytes_per_launch": logical_bytes},

@@ -44,6 +44,8 @@ extern "C" {
 #define KV_ABI_VERSION 1
 /* Tokens per physical block [VLLM, "PagedAttention": fixed-size blocks]. */
 #define KV_BLOCK_TOKENS 16
+/* Largest number of prefix groups in one paged_decode_attention_shared call. */
+#define KV_MAX_PREFIX_GROUPS 256
 
 typedef int32_t kv_status;
 enum {
@@ -220,6 +222,46 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
                                  const int32_t *ctx_lens, const int32_t *seq_slots, int32_t batch,
                                  int32_t max_ctx, void *workspace, size_t ws_bytes,
                                  const kv_attn_opts *opts, void *stream);
+
+/* Groups of sequences whose block tables share a prefix: several sequences'
+ * tables may name the same physical blocks [VLLM, "PagedAttention": blocks
+ * shared between sequences; KVSYS, "부분 재사용": a request reusing the
+ * blocks of a matching prefix]. Host arrays, read during the call only:
+ *   group_start    [n_groups + 1], non-decreasing, group_start[n_groups] <=
+ *                  batch; group i is sequences group_start[i] ..
+ *                  group_start[i+1] - 1
+ *   prefix_blocks  [n_groups], >= 0: the first prefix_blocks[i] entries of
+ *                  every member's block table name the same physical blocks
+ *                  (the kernels read them from the group's first member)
+ * Sequences outside every group have no shared prefix. */
+typedef struct {
+    int32_t n_groups; /* 0 .. KV_MAX_PREFIX_GROUPS */
+    const int32_t *group_start;
+    const int32_t *prefix_blocks;
+} kv_prefix_groups;
+
+/* Bytes of workspace paged_decode_attention_shared needs ((size_t)-1 on
+ * invalid input). */
+size_t paged_decode_attention_shared_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads,
+                                                     int32_t max_ctx, const kv_prefix_groups *groups,
+                                                     const kv_attn_opts *opts);
+
+/* paged_decode_attention for a batch whose sequences share block-table
+ * prefixes (`groups`): the same result within rounding, with each shared
+ * (block, kv head) tile read once for its whole group - the group's query
+ * rows are the columns of one tile product - instead of once per member.
+ * A member attends its whole shared prefix and then its own blocks; a member
+ * whose ctx_lens is below its prefix (prefix_blocks * 16 tokens) gets NaN.
+ * bf16 pools only (MFMA kernel; opts->kernel 0 or 2), no window
+ * (opts->window 0), fixed splits (opts->schedule 0 or KV_SCHED_SPLIT;
+ * opts->split_blocks 0 lets the library choose the blocks per work item).
+ * Other arguments as for paged_decode_attention. Errors: KV_ERR_UNSUPPORTED
+ * for other pools or options, KV_ERR_INVALID_ARG for malformed groups. */
+kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads,
+                                        float scale, const int32_t *block_tables, int32_t max_blocks,
+                                        const int32_t *ctx_lens, int32_t batch, int32_t max_ctx,
+                                        const kv_prefix_groups *groups, void *workspace, size_t ws_bytes,
+                                        const kv_attn_opts *opts, void *stream);
 
 /* Bytes of workspace paged_multi_token_attention needs ((size_t)-1 on invalid
  * input). */

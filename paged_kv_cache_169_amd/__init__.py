@@ -48,6 +48,24 @@ class kv_attn_opts(ctypes.Structure):
                 ("events", ctypes.c_void_p * 3)]
 
 
+KV_MAX_PREFIX_GROUPS = 256
+
+
+class kv_prefix_groups(ctypes.Structure):
+    _fields_ = [("n_groups", ctypes.c_int32), ("group_start", ctypes.POINTER(ctypes.c_int32)),
+                ("prefix_blocks", ctypes.POINTER(ctypes.c_int32))]
+
+
+def prefix_groups(group_start, prefix_blocks):
+    """kv_prefix_groups over host copies of the two lists; the arrays are kept
+    alive on the returned record (attribute _keep)."""
+    gs = (ctypes.c_int32 * len(group_start))(*[int(x) for x in group_start])
+    pb = (ctypes.c_int32 * max(1, len(prefix_blocks)))(*[int(x) for x in prefix_blocks])
+    g = kv_prefix_groups(len(prefix_blocks), gs, pb)
+    g._keep = (gs, pb)
+    return g
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
 
@@ -76,6 +94,13 @@ _paged_decode_attention_workspace_bytes = _decl(
 _paged_decode_attention = _decl(
     "paged_decode_attention", _I32,
     [_P, _P, _P, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
+_paged_decode_attention_shared_workspace_bytes = _decl(
+    "paged_decode_attention_shared_workspace_bytes", _SZ,
+    [_P, _I32, _I32, _I32, ctypes.POINTER(kv_prefix_groups), ctypes.POINTER(kv_attn_opts)])
+_paged_decode_attention_shared = _decl(
+    "paged_decode_attention_shared", _I32,
+    [_P, _P, _P, _I32, _F, _P, _I32, _P, _I32, _I32, ctypes.POINTER(kv_prefix_groups), _P, _SZ,
+     ctypes.POINTER(kv_attn_opts), _P])
 _paged_multi_token_attention_workspace_bytes = _decl(
     "paged_multi_token_attention_workspace_bytes", _SZ, [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(kv_attn_opts)])
 _paged_multi_token_attention = _decl(
@@ -287,6 +312,37 @@ def paged_decode_attention(pool: KVPool, q: torch.Tensor, out: torch.Tensor, blo
     _check(st, "paged_decode_attention")
 
 
+def paged_decode_attention_shared_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int, max_ctx: int,
+                                                  groups: kv_prefix_groups, opts: kv_attn_opts | None = None) -> int:
+    n = _paged_decode_attention_shared_workspace_bytes(pool.handle, int(batch), int(num_q_heads), int(max_ctx),
+                                                       ctypes.byref(groups),
+                                                       ctypes.byref(opts) if opts is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise KVError(KV_ERR_INVALID_ARG, "paged_decode_attention_shared_workspace_bytes")
+    return int(n)
+
+
+def paged_decode_attention_shared(pool: KVPool, q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                                  ctx_lens: torch.Tensor, scale: float, max_ctx: int, groups: kv_prefix_groups,
+                                  workspace: torch.Tensor | None = None, opts: kv_attn_opts | None = None,
+                                  stream=None) -> None:
+    """paged_decode_attention with the shared prefixes of `groups`
+    (prefix_groups(group_start, prefix_blocks)) read once per group."""
+    d = pool.desc
+    B, n_h, hd = q.shape
+    if hd != d.head_dim or tuple(out.shape) != (B, n_h, hd):
+        raise ValueError("q / out shape does not match the pool")
+    ws_ptr = _dev_ptr(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _paged_decode_attention_shared(pool.handle, _dev_ptr(q, "q", torch.bfloat16),
+                                        _dev_ptr(out, "out", torch.float32), n_h, float(scale),
+                                        _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                        _i32(ctx_lens, "ctx_lens"), B, int(max_ctx), ctypes.byref(groups),
+                                        ws_ptr, ws_bytes, ctypes.byref(opts) if opts is not None else None,
+                                        _stream(stream))
+    _check(st, "paged_decode_attention_shared")
+
+
 def paged_multi_token_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int, q_len: int,
                                                 max_ctx: int, opts: kv_attn_opts | None = None) -> int:
     n = _paged_multi_token_attention_workspace_bytes(pool.handle, int(batch), int(num_q_heads), int(q_len),
@@ -456,4 +512,6 @@ raw = {
     "kv_block_bytes": _kv_block_bytes, "kv_copy_blocks": _kv_copy_blocks, "kv_gather_blocks": _kv_gather_blocks,
     "kv_scatter_blocks": _kv_scatter_blocks, "kv_token_deviation": _kv_token_deviation,
     "kv_topk_select": _kv_topk_select, "kv_decode_step": _kv_decode_step,
+    "paged_decode_attention_shared": _paged_decode_attention_shared,
+    "paged_decode_attention_shared_workspace_bytes": _paged_decode_attention_shared_workspace_bytes,
 }

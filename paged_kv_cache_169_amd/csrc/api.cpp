@@ -3,6 +3,7 @@
 // every computation on the hot path runs in the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -182,6 +183,74 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         g->off_ml = align_up(rows * D * sizeof(float));
         g->ws_bytes = g->off_ml + align_up(rows * 2 * sizeof(float));
     }
+    return KV_OK;
+}
+
+
+// Geometry of paged_decode_attention_shared: blocks per work item, the
+// prefix group record the kernels get by value, and the workspace.
+struct SharedGeom {
+    int split_blocks, max_splits, ncols, ctiles, units;
+    size_t ws_bytes, off_ml;
+};
+
+kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx,
+                      const kv_prefix_groups *groups, const kv_attn_opts *opts, SharedGeom *g, PrefixArgs *pa) {
+    if (batch < 0 || n_h < 1 || max_ctx < 0 || !groups) return KV_ERR_INVALID_ARG;
+    const int n_kv = pool->desc.num_kv_heads;
+    if (n_h % n_kv) return KV_ERR_INVALID_ARG;
+    if (opts && (opts->kernel < 0 || opts->kernel > 2 || opts->schedule < 0 || opts->schedule > 2 ||
+                 opts->window < 0 || opts->split_blocks < 0))
+        return KV_ERR_INVALID_ARG;
+    if (pool->desc.dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
+    if (opts && (opts->kernel == 1 || opts->window > 0 || opts->schedule == KV_SCHED_BALANCED))
+        return KV_ERR_UNSUPPORTED;
+    const int ng = groups->n_groups;
+    if (ng < 0 || ng > KV_MAX_PREFIX_GROUPS) return KV_ERR_INVALID_ARG;
+    if (ng > 0 && (!groups->group_start || !groups->prefix_blocks)) return KV_ERR_INVALID_ARG;
+    const int group = n_h / n_kv;
+    int nblk = (max_ctx + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS;
+    if (nblk < 1) nblk = 1;
+    pa->n_groups = ng;
+    int max_members = 0, max_prefix = 0;
+    long prefix_tiles = 0, member_prefix = 0;  // shared tile loads; prefix blocks summed over members
+    for (int i = 0; i < ng; ++i) {
+        const int a = groups->group_start[i], b = groups->group_start[i + 1], P = groups->prefix_blocks[i];
+        if (a < 0 || b < a || b > batch || (i > 0 && a < groups->group_start[i - 1]) || P < 0 || P > nblk)
+            return KV_ERR_INVALID_ARG;
+        pa->start[i] = a;
+        pa->blocks[i] = P;
+        max_members = std::max(max_members, b - a);
+        max_prefix = std::max(max_prefix, P);
+        member_prefix += (long)P * (b - a);
+        prefix_tiles += (long)P * (((long)(b - a) * group + 15) / 16);
+    }
+    if (ng > 0) pa->start[ng] = groups->group_start[ng];
+    g->ncols = group;
+    g->ctiles = (group + 15) / 16;
+    g->units = n_kv * g->ctiles;
+    pa->ctiles_p = std::max(1, (max_members * group + 15) / 16);
+    pa->units_p = n_kv * pa->ctiles_p;
+    int sb = opts ? opts->split_blocks : 0;
+    if (sb == 0) {
+        // about 4.5 work items per resident workgroup: fewer, longer items
+        // leave a larger last round idle, more and shorter ones pay the
+        // per-item start (block ids, first tile) more often (measured on the
+        // long shared-prefix workload: 32 blocks per item, 4.5 rounds, beat
+        // 18 to 86 blocks)
+        const long tiles = (long)n_kv * (prefix_tiles + g->ctiles * ((long)batch * nblk - member_prefix));
+        const long target = (long)balanced_grid(KV_BF16, (int)pool->desc.head_dim, batch, nblk) * 9 / 2;
+        sb = (int)std::max(16L, (tiles + target - 1) / target);
+    }
+    if (sb > nblk) sb = nblk;
+    g->split_blocks = sb;
+    pa->max_chunks = std::max(1, (max_prefix + sb - 1) / sb);
+    pa->suffix_splits = (nblk + sb - 1) / sb;
+    g->max_splits = pa->max_chunks + pa->suffix_splits;
+    const size_t D = pool->desc.head_dim;
+    const size_t rows = (size_t)batch * n_h * g->max_splits;
+    g->off_ml = align_up(rows * D * sizeof(float));
+    g->ws_bytes = g->off_ml + align_up(rows * 2 * sizeof(float));
     return KV_OK;
 }
 
@@ -400,6 +469,68 @@ kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int3
                                  size_t ws_bytes, const kv_attn_opts *opts, void *stream) {
     return paged_multi_token_attention(pool, q, out, num_q_heads, 1, scale, block_tables, max_blocks, ctx_lens,
                                        seq_slots, batch, max_ctx, workspace, ws_bytes, opts, stream);
+}
+
+size_t paged_decode_attention_shared_workspace_bytes(kv_pool_t pool, int32_t batch, int32_t num_q_heads,
+                                                     int32_t max_ctx, const kv_prefix_groups *groups,
+                                                     const kv_attn_opts *opts) {
+    SharedGeom g;
+    PrefixArgs pa;
+    if (!pool || shared_geom(pool, batch, num_q_heads, max_ctx, groups, opts, &g, &pa) != KV_OK) return (size_t)-1;
+    return g.ws_bytes;
+}
+
+kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads,
+                                        float scale, const int32_t *block_tables, int32_t max_blocks,
+                                        const int32_t *ctx_lens, int32_t batch, int32_t max_ctx,
+                                        const kv_prefix_groups *groups, void *workspace, size_t ws_bytes,
+                                        const kv_attn_opts *opts, void *stream) {
+    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
+    if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
+    SharedGeom g;
+    PrefixArgs pa;
+    const kv_status gs = shared_geom(pool, batch, num_q_heads, max_ctx, groups, opts, &g, &pa);
+    if (gs != KV_OK) return gs;
+    if (batch == 0) return KV_OK;
+    if (!q || !out || !block_tables || !ctx_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return KV_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < g.ws_bytes || !aligned16(workspace)) return KV_ERR_WORKSPACE;
+    AttnParams a{};
+    a.ctx_add = 0;
+    a.k_new = a.v_new = nullptr;
+    a.pool = pool_ptrs(pool);
+    a.q = q;
+    a.out = out;
+    a.tables = block_tables;
+    a.ctx_lens = ctx_lens;
+    a.seq_slots = nullptr;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_o = reinterpret_cast<float *>(ws);
+    a.ws_ml = reinterpret_cast<float *>(ws + g.off_ml);
+    a.ws_prefix = nullptr;
+    a.max_blocks = max_blocks;
+    a.batch = batch;
+    a.n_h = num_q_heads;
+    a.n_kv = pool->desc.num_kv_heads;
+    a.group = num_q_heads / a.n_kv;
+    a.head_dim = pool->desc.head_dim;
+    a.num_blocks = pool->desc.num_blocks;
+    a.max_seqs = pool->desc.max_seqs;
+    a.split_blocks = g.split_blocks;
+    a.max_splits = g.max_splits;
+    a.window = 0;
+    a.q_len = 1;
+    a.ncols = g.ncols;
+    a.ctiles = g.ctiles;
+    a.units = g.units;
+    a.slot_cols = g.ncols < 16 ? g.ncols : 16;
+    a.schedule = KV_SCHED_SPLIT;
+    a.n_wg = 0;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    void *const *ev = opts ? opts->events : nullptr;
+    auto evt = [&](int i) { return ev ? static_cast<hipEvent_t>(ev[i]) : nullptr; };
+    return hip_status(launch_attention_shared(a, pa, static_cast<hipStream_t>(stream), evt(0), evt(1), evt(2)));
 }
 
 kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables, int32_t max_blocks,

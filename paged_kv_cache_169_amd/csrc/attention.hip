@@ -1110,8 +1110,204 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 }
 
 // ---------------------------------------------------------------------------
+// shared-prefix decode attention (bf16 MFMA path)
+//
+// Sequences of a prefix group name the same physical blocks for their first
+// blocks[i] logical blocks. A prefix work item streams a chunk of those
+// shared tiles once for the whole group: its columns are the group members'
+// query rows (member k, head hq -> column k * group + hq), so one tile
+// product serves every member. Suffix work items are the ordinary split work
+// on each sequence's own blocks after its prefix. Every row that has a prefix
+// keeps its results as partials (slots: the group's prefix chunks first, then
+// the sequence's suffix splits) and attn_merge_shared_kernel combines them.
+// ---------------------------------------------------------------------------
+
+// Group holding sequence b, or -1.
+__device__ __forceinline__ int prefix_group_of(const PrefixArgs &g, int b) {
+    if (g.n_groups == 0 || b < g.start[0]) return -1;
+    int lo = 0, hi = g.n_groups - 1;  // largest i with start[i] <= b
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.start[mid] <= b)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return b < g.start[lo + 1] ? lo : -1;
+}
+
+// Slots of one row: prefix chunks and suffix splits of sequence b with n
+// attended tokens and P shared blocks (bad: the length is out of range or
+// shorter than the prefix).
+struct SharedRow {
+    int nchunk, nsplit, blk_hi;
+    bool bad;
+};
+__device__ __forceinline__ SharedRow shared_row(const AttnParams &p, int n, int P) {
+    SharedRow w;
+    w.bad = n < 0 || n > p.max_blocks * kBlock || n < P * kBlock;
+    w.blk_hi = w.bad ? P : (n + kBlock - 1) / kBlock;
+    w.nchunk = (P + p.split_blocks - 1) / p.split_blocks;
+    w.nsplit = (w.blk_hi - P + p.split_blocks - 1) / p.split_blocks;
+    return w;
+}
+
+// Partial (o, m, l) of one column into slot `slot` of row `row`.
+template <int D>
+__device__ __forceinline__ void store_partial(const AttnParams &p, size_t row, int slot, int G, const float *res,
+                                              float m, float l, bool bad) {
+    const float nan = __uint_as_float(0x7fc00000u);
+    const size_t base = row * p.max_splits + slot;
+    float *dst = p.ws_o + base * D + G * (D / 4);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c];
+    if (G == 0) {
+        p.ws_ml[base * 2] = m;
+        p.ws_ml[base * 2 + 1] = bad ? nan : l;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(AttnParams p, PrefixArgs g) {
+    extern __shared__ int sids[];  // [split_blocks] block ids of the work item
+    const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
+    const int n_pref = g.n_groups * g.units_p * g.max_chunks;
+    const int item = blockIdx.x;
+    MfmaState<D> st;
+    if (item < n_pref) {
+        // prefix chunk c of group gi, kv head kvh, column tile ct
+        const int gi = item / (g.units_p * g.max_chunks), rem = item % (g.units_p * g.max_chunks);
+        const int unit = rem / g.max_chunks, c = rem % g.max_chunks;
+        const int kvh = unit / g.ctiles_p, ct = unit % g.ctiles_p;
+        const int first = g.start[gi], members = g.start[gi + 1] - first, P = g.blocks[gi];
+        const int j0 = c * p.split_blocks, j1 = min(P, j0 + p.split_blocks);
+        if (members <= 0 || j0 >= j1 || ct * 16 >= members * p.group) return;
+        const int ci = ct * 16 + n16, k = ci / p.group, hq = ci % p.group;
+        Column col;
+        col.valid = k < members;
+        col.row = (size_t)(first + (col.valid ? k : 0)) * p.n_h + kvh * p.group + hq;
+        col.lo = 0;
+        col.hi = P * kBlock;
+        const SharedRow w = shared_row(p, col.valid ? ctx_of(p, first + k) : P * kBlock, P);
+        SeqRange r;  // the prefix: P full blocks, attended whole by every member
+        r.n = r.hi = r.all_hi = P * kBlock;
+        r.lo = r.all_lo = 0;
+        r.blk_lo = 0;
+        r.nblk = P;
+        r.nsplit = w.nchunk;
+        r.bad = false;
+        bool bad = false;  // a bad block id in the shared table
+        bf16_segment<D>(p, first, kvh, col, r, j0, j1, lane, st, bad, false, sids);
+        const float l = col_sum(st.l);
+        if (col.valid) {
+            float res[D / 4];
+            mfma_gather_run<D>(st, 0.0f, res);
+            store_partial<D>(p, col.row, c, G, res, st.m, l, bad || w.bad);
+        }
+        return;
+    }
+    // suffix split `split` of sequence b, kv head kvh, column tile ct
+    const int it = item - n_pref;
+    const int b = it / (p.units * g.suffix_splits), rem = it % (p.units * g.suffix_splits);
+    const int unit = rem / g.suffix_splits, split = rem % g.suffix_splits;
+    const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
+    const int gi = prefix_group_of(g, b);
+    const int P = gi < 0 ? 0 : g.blocks[gi];
+    const int n = uniform(ctx_of(p, b));
+    const SharedRow w = shared_row(p, n, P);
+    SeqRange r;
+    r.n = r.hi = r.all_hi = w.bad ? 0 : n;
+    r.lo = r.all_lo = 0;
+    r.blk_lo = 0;
+    r.nblk = w.blk_hi;
+    r.nsplit = w.nsplit;
+    r.bad = w.bad;
+    const Column col = column_of(p, b, kvh, ct, n16, r);
+    if (split >= w.nsplit) {
+        // no suffix block here; a sequence with neither prefix nor blocks
+        // (length 0, or out of range) still gets its output
+        if (split == 0 && P == 0 && col.valid) {
+            const float v = w.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
+            float *dst = p.out + col.row * D + G * (D / 4);
+#pragma unroll
+            for (int c = 0; c < D / 4; ++c) dst[c] = v;
+        }
+        return;
+    }
+    const int j0 = P + split * p.split_blocks, j1 = min(w.blk_hi, j0 + p.split_blocks);
+    bool bad = w.bad;
+    bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, false, sids);
+    const float l = col_sum(st.l);
+    if (col.valid) {
+        float res[D / 4];
+        mfma_gather_run<D>(st, 0.0f, res);
+        if (P == 0 && w.nsplit == 1) {  // the row's only part: the output itself
+            const float nan = __uint_as_float(0x7fc00000u);
+            float *dst = p.out + col.row * D + G * (D / 4);
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
+        } else {
+            store_partial<D>(p, col.row, w.nchunk + split, G, res, st.m, l, bad);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // merge of split partials
 // ---------------------------------------------------------------------------
+
+// Combines n partials (o, m, l) of one output row into dst (this lane's cv
+// channels): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M the
+// largest m_i. row_of(i) is the workspace row of partial i. Partials 64 at a
+// time: lane i reads the (m, l) of partial base + i, so a chunk's maxima and
+// sums take one round trip and a wave reduction; the value rows follow four
+// at a time, their weights read from the lanes that hold them. A NaN l (bad
+// sequence or table) makes the row NaN; a row no partial saw a token for
+// gets 0.
+template <class RowOf>
+__device__ __forceinline__ void merge_partials(const AttnParams &p, int n, RowOf row_of, int lane, int cv,
+                                               float *dst) {
+    const int D = p.head_dim;
+    float M = -INFINITY, L = 0.0f;
+    float acc[2] = {0.0f, 0.0f};
+    for (int base = 0; base < n; base += 64) {
+        const int w = base + lane;
+        float m = -INFINITY, l = 0.0f;
+        if (w < n) {
+            const size_t row = row_of(w);
+            m = p.ws_ml[row * 2];
+            l = p.ws_ml[row * 2 + 1];
+        }
+        const float Mn = fmaxf(M, wave_max(m));
+        if (Mn == -INFINITY) continue;  // no partial has seen a token yet
+        const float a = fast_exp2(M - Mn);  // 0 while M is -inf
+        L *= a;
+        acc[0] *= a;
+        acc[1] *= a;
+        M = Mn;
+        const float wgt = w < n ? fast_exp2(m - M) : 0.0f;
+        L += wave_sum(wgt * l);
+        const int cnt = min(64, n - base);
+        for (int i0 = 0; i0 < cnt; i0 += 4) {
+            float wi[4], o[4][2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = min(i0 + k, cnt - 1);  // past the end: weight 0, row re-read
+                wi[k] = i0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i)) : 0.0f;
+                const float *src = p.ws_o + row_of(base + i) * D + lane * cv;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) o[k][c] = c < cv ? src[c] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) acc[c] = fmaf(wi[k], o[k][c], acc[c]);
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
+}
 
 // Grid (n_h * q_len, batch): one wave per output row (query token, head).
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
@@ -1120,24 +1316,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
     const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
     if (r.nsplit <= 1) return;
     const size_t base = row * p.max_splits;
-    const float *ml = p.ws_ml + base * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < r.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-    const int D = p.head_dim;
-    const int cv = D / 64;
-    float *dst = p.out + row * D + lane * cv;
-    float acc[2] = {0.0f, 0.0f};
-    float L = 0.0f;
-    if (M != -INFINITY) {  // else no split saw a token for this row: output 0
-        for (int s = 0; s < r.nsplit; ++s) {
-            const float wgt = fast_exp2(ml[2 * s] - M);
-            L += wgt * ml[2 * s + 1];
-            const float *o = p.ws_o + (base + s) * D + lane * cv;
-            for (int c = 0; c < cv; ++c) acc[c] = fmaf(wgt, o[c], acc[c]);
-        }
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
+    const int cv = p.head_dim / 64;
+    merge_partials(p, r.nsplit, [&](int s) { return base + s; }, lane, cv, p.out + row * p.head_dim + lane * cv);
 }
 
 // Merge for the balanced schedule: one wave per output row (query token,
@@ -1169,48 +1349,28 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
         const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
         return ((size_t)w * 2 + slot) * p.slot_cols + n16;
     };
-    // Partials 64 at a time: lane i reads the (m, l) of workgroup base + i, so
-    // the chunk's maxima and sums take one round trip and a wave reduction;
-    // the value rows are then loaded four at a time with their weights read
-    // from the lanes that hold them.
-    float M = -INFINITY, L = 0.0f;
-    float acc[2] = {0.0f, 0.0f};
-    for (int base = w0; base <= w1; base += 64) {
-        const int w = base + lane;
-        float m = -INFINITY, l = 0.0f;
-        if (w <= w1) {
-            const size_t row = ws_row(w);
-            m = p.ws_ml[row * 2];
-            l = p.ws_ml[row * 2 + 1];
-        }
-        const float Mn = fmaxf(M, wave_max(m));
-        if (Mn == -INFINITY) continue;  // no segment has seen a token yet
-        const float a = fast_exp2(M - Mn);  // 0 while M is -inf
-        L *= a;
-        acc[0] *= a;
-        acc[1] *= a;
-        M = Mn;
-        const float wgt = w <= w1 ? fast_exp2(m - M) : 0.0f;
-        L += wave_sum(wgt * l);  // a NaN l (bad sequence) makes the row NaN
-        const int cnt = min(64, w1 - base + 1);
-        for (int i0 = 0; i0 < cnt; i0 += 4) {
-            float wi[4], o[4][2];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = min(i0 + k, cnt - 1);  // past the end: weight 0, row re-read
-                wi[k] = i0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i)) : 0.0f;
-                const float *src = p.ws_o + ws_row(base + i) * D + lane * cv;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) o[k][c] = c < cv ? src[c] : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) acc[c] = fmaf(wi[k], o[k][c], acc[c]);
-        }
+    merge_partials(p, w1 - w0 + 1, [&](int i) { return ws_row(w0 + i); }, lane, cv, dst);
+}
+
+
+// Merge of the shared-prefix call: one wave per (sequence, head) row with
+// more than one part (a prefix, or several suffix splits).
+__global__ __launch_bounds__(64) void attn_merge_shared_kernel(AttnParams p, PrefixArgs g) {
+    const int b = blockIdx.y, lane = threadIdx.x;
+    const size_t row = (size_t)b * p.n_h + blockIdx.x;
+    const int gi = prefix_group_of(g, b);
+    const int P = gi < 0 ? 0 : g.blocks[gi];
+    const SharedRow w = shared_row(p, ctx_of(p, b), P);
+    const int total = (P > 0 ? w.nchunk : 0) + w.nsplit;
+    if (P == 0 && total <= 1) return;  // written by the attention kernel
+    const int cv = p.head_dim / 64;
+    float *dst = p.out + row * p.head_dim + lane * cv;
+    if (w.bad) {
+        for (int c = 0; c < cv; ++c) dst[c] = __uint_as_float(0x7fc00000u);
+        return;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
+    const size_t base = row * p.max_splits;
+    merge_partials(p, total, [&](int s) { return base + s; }, lane, cv, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -1306,6 +1466,23 @@ hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
         hipExtLaunchKernelGGL(attn_merge_balanced_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
     else
         hipExtLaunchKernelGGL(attn_merge_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hipStream_t s, hipEvent_t e0,
+                                   hipEvent_t e1, hipEvent_t e_end) {
+    if (p.batch == 0) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
+    const long items = (long)g.n_groups * g.units_p * g.max_chunks + (long)p.batch * p.units * g.suffix_splits;
+    const uint32_t lds = (uint32_t)(p.split_blocks * sizeof(int));
+    if (p.head_dim == 64)
+        hipExtLaunchKernelGGL((attn_mfma_shared_kernel<64>), dim3((uint32_t)items), dim3(64), lds, s, e0, e1, 0, p, g);
+    else
+        hipExtLaunchKernelGGL((attn_mfma_shared_kernel<128>), dim3((uint32_t)items), dim3(64), lds, s, e0, e1, 0, p,
+                              g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipExtLaunchKernelGGL(attn_merge_shared_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, nullptr, e_end, 0, p, g);
     return hipGetLastError();
 }
 

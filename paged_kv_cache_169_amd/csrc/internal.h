@@ -105,6 +105,23 @@ struct TopkParams {
     int32_t n_seg;
 };
 
+// Groups of sequences whose tables share a prefix of physical blocks
+// (paged_decode_attention_shared). Passed by value beside AttnParams.
+// Group i is sequences start[i] .. start[i+1]-1; their first blocks[i]
+// logical blocks name the same physical blocks. Work items of the shared
+// kernel: first the prefix items (group, unit, chunk), then the suffix items
+// (sequence, unit, split); partial slots of a row: the group's prefix chunks
+// first, then the sequence's suffix splits.
+struct PrefixArgs {
+    int32_t n_groups;
+    int32_t units_p;      // prefix units per group: n_kv * column tiles of the largest group
+    int32_t ctiles_p;     // column tiles of a prefix unit
+    int32_t max_chunks;   // prefix chunks of the longest prefix
+    int32_t suffix_splits;// suffix splits of the longest sequence
+    int32_t start[KV_MAX_PREFIX_GROUPS + 1];
+    int32_t blocks[KV_MAX_PREFIX_GROUPS];
+};
+
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
 hipError_t launch_deviation(int dtype, const DeviationParams &p, hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, hipStream_t s);
@@ -116,6 +133,10 @@ hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStream_t s, hipEvent_t e0 = nullptr,
                             hipEvent_t e1 = nullptr);
 hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end = nullptr);
+// Shared-prefix decode attention: one kernel over prefix and suffix items,
+// then the merge of every row's partials (events as for launch_attention).
+hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hipStream_t s, hipEvent_t e0,
+                                   hipEvent_t e1, hipEvent_t e_end);
 // Persistent grid of the balanced schedule: resident workgroups per device.
 int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -253,3 +253,48 @@ def test_recompute_ratio_matches_oracle(kv, orc):
     for r in (0.0, 0.15, 0.2, 1 / 3, 0.5, 0.999, 1.0):
         for n in (0, 1, 2, 7, 20, 100, 1000, 4097, 131072):
             assert kv.kv_recompute_count(r, n) == orc.recompute_count(r, n)
+
+
+def test_shared_prefix_host_checks(kv):
+    """Workspace size and argument errors of the shared-prefix entry point
+    (rows: batch * n_h * (prefix chunks of the longest prefix + suffix splits
+    of the longest sequence))."""
+    st, h = make_handle(kv, kv.make_desc(16, 2, 64, "bf16"))
+    W = kv.raw["paged_decode_attention_shared_workspace_bytes"]
+    A = kv.raw["paged_decode_attention_shared"]
+    o1 = kv.attn_opts(split_blocks=1)
+    g = kv.prefix_groups([0, 3], [2])                    # sequences 0-2 share 2 blocks
+    # 50 tokens -> 4 blocks: 2 prefix chunks + 4 suffix splits of 1 block
+    rows = 4 * 4 * (2 + 4)
+    want = (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256
+    assert W(h, 4, 4, 50, ctypes.byref(g), ctypes.byref(o1)) == want
+    bad = ctypes.c_size_t(-1).value
+    assert W(h, 4, 4, 50, ctypes.byref(kv.prefix_groups([0, 5], [2])), ctypes.byref(o1)) == bad   # beyond batch
+    assert W(h, 4, 4, 50, ctypes.byref(kv.prefix_groups([2, 1], [2])), ctypes.byref(o1)) == bad   # decreasing
+    assert W(h, 4, 4, 50, ctypes.byref(kv.prefix_groups([0, 2], [-1])), ctypes.byref(o1)) == bad  # negative prefix
+    assert W(h, 4, 4, 50, ctypes.byref(kv.prefix_groups([0, 2], [5])), ctypes.byref(o1)) == bad   # beyond max_ctx
+    assert W(h, 4, 3, 50, ctypes.byref(g), None) == bad                                            # 3 heads, 2 kv heads
+    assert W(h, 4, 4, 50, None, None) == bad
+    # no groups at all is a plain split call
+    assert W(h, 4, 4, 50, ctypes.byref(kv.prefix_groups([0], [])), ctypes.byref(o1)) != bad
+    # unsupported options and pools, checked before any launch
+    ow = kv.attn_opts(window=8)
+    assert A(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, 4, 50, ctypes.byref(g), FAKE, 1 << 20, ctypes.byref(ow), None) \
+        == kv.KV_ERR_UNSUPPORTED
+    ov = kv.attn_opts(kernel=1)
+    assert A(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, 4, 50, ctypes.byref(g), FAKE, 1 << 20, ctypes.byref(ov), None) \
+        == kv.KV_ERR_UNSUPPORTED
+    st, h32 = make_handle(kv, kv.make_desc(16, 2, 64, "f32"))
+    assert A(h32, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, 4, 50, ctypes.byref(g), FAKE, 1 << 20, None, None) \
+        == kv.KV_ERR_UNSUPPORTED
+    # workspace missing or too small
+    assert A(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, 4, 50, ctypes.byref(g), None, 0, ctypes.byref(o1), None) \
+        == kv.KV_ERR_WORKSPACE
+    assert A(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, 4, 50, ctypes.byref(g), FAKE, want - 1, ctypes.byref(o1), None) \
+        == kv.KV_ERR_WORKSPACE
+    g0 = kv.prefix_groups([0], [])
+    assert A(h, None, None, 4, 0.125, None, 4, None, 0, 50, ctypes.byref(g0), None, 0, None, None) == 0  # empty batch
+    assert A(h, None, None, 4, 0.125, None, 4, None, 0, 50, ctypes.byref(g), None, 0, None, None) \
+        == kv.KV_ERR_INVALID_ARG                                                  # a group beyond the empty batch
+    for x in (h, h32):
+        kv.raw["kv_pool_destroy"](x)

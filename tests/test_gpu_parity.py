@@ -286,6 +286,83 @@ def test_long_shared_prefix_with_rerotation():
 
 
 # ---------------------------------------------------------------------------
+# shared-prefix decode attention
+# ---------------------------------------------------------------------------
+
+def shared_case(seed, lens, n_h, n_kv, d, groups):
+    """A case whose group members' tables name their first member's physical
+    blocks for the group's prefix (the members' own first blocks go unused)."""
+    c = wl.make_case(seed, len(lens), lens, n_h, n_kv, d, "bf16", append=False, device=DEV)
+    t = c.tables.clone()
+    for (a, b), P in zip(zip(groups[0][:-1], groups[0][1:]), groups[1]):
+        for m in range(a + 1, b):
+            t[m, :P] = t[a, :P]
+    c.tables = t
+    return c
+
+
+def gpu_shared(pool, c, group_start, prefix_blocks, split_blocks=0):
+    g = kv.prefix_groups(group_start, prefix_blocks)
+    opts = kv.attn_opts(split_blocks=split_blocks)
+    max_ctx = int(c.ctx_lens.max().item())
+    nbytes = kv.paged_decode_attention_shared_workspace_bytes(pool, c.batch, c.n_h, max_ctx, g, opts)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    out = torch.full((c.batch, c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.paged_decode_attention_shared(pool, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, g, ws, opts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+SHARED_CASES = [
+    # lens, n_h, n_kv, d, (group_start, prefix_blocks)
+    ([300, 700, 520, 1000, 64], 8, 2, 128, ([0, 3, 4], [10, 5])),      # a group of 3, a group of 1, one outside
+    ([260, 250, 400, 210, 390, 300, 90], 8, 2, 128, ([0, 6], [12])),     # 6 members x 4 heads: 2 column tiles
+    ([400, 320, 330, 1000], 4, 4, 128, ([0, 4], [20])),                 # MHA; a member with no own block
+    ([180, 90, 400, 64, 100], 4, 1, 64, ([0, 0, 2, 4], [3, 4, 2])),    # MQA, d 64, an empty group
+    ([17, 33, 48, 1], 2, 2, 128, ([1, 3], [1])),                        # ragged tails, tiny prefix
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHARED_CASES)))
+@pytest.mark.parametrize("split", [0, 1, 5])
+def test_shared_prefix_parity(case, split):
+    lens, n_h, n_kv, d, groups = SHARED_CASES[case]
+    c = shared_case(60 + case, lens, n_h, n_kv, d, groups)
+    pool = new_pool(c)
+    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=split)
+    ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
+    assert max_err(out, ref) <= TOL
+
+
+def test_shared_prefix_member_shorter_than_prefix_is_nan():
+    c = shared_case(71, [300, 100, 250], 4, 2, 128, ([0, 2], [10]))   # member 1 has 100 < 160 prefix tokens
+    pool = new_pool(c)
+    out = gpu_shared(pool, c, [0, 2], [10])
+    assert np.isnan(out[1]).all()
+    keep = [0, 2]
+    ref = orc.attention(bits(c.K), bits(c.V), bits(c.q)[keep], c.tables.cpu().numpy()[keep],
+                        c.ctx_lens.cpu().numpy()[keep], c.scale)
+    assert max_err(out[keep], ref) <= TOL
+
+
+def test_shared_prefix_long_workload_matches_plain_call():
+    """The long shared-prefix workload (8 x 32768 tokens, 16384 shared, chunk
+    re-rotated) through the shared entry point: sampled rows against the oracle
+    and every row against the plain call."""
+    c = wl.workload("long_shared", device=DEV)
+    pool = new_pool(c)
+    kv.rope_rerotate(pool, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
+    out = gpu_shared(pool, c, [0, c.batch], [1024])
+    plain = gpu_attention(pool, c)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, plain) <= TOL
+    K, V = bits(pool.K), bits(pool.V)
+    rows = [0, 3, 7]
+    ref = orc.attention(K, V, bits(c.q)[rows], c.tables.cpu().numpy()[rows], c.ctx_lens.cpu().numpy()[rows], c.scale)
+    assert max_err(out[rows], ref) <= TOL
+
+
+# ---------------------------------------------------------------------------
 # RoPE re-rotation
 # ---------------------------------------------------------------------------
 
