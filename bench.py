@@ -284,10 +284,19 @@ def main():
     kv_bytes = unique_tokens * per_token
     alg_bytes = kv_bytes + k * (B * n_h * D * es + B * n_h * D * 4) + int(nblk.sum().item()) * 4 + B * 4
     logical_bytes = alg_bytes + (logical_tokens - unique_tokens) * per_token
-    fused = c.append and c.dtype == "bf16" and not int4 and args.kernel in (0, 2)
-    if fused:  # the kernel also writes the step's new K and V rows into the pool
+    fused = c.append and not shared and args.kernel in (0, 2) and c.dtype == "bf16" and (not int4 or k == 1)
+    if fused and not int4:  # the kernel also writes the step's new K and V rows into the pool
         alg_bytes += B * k * n_kv * 2 * D * es
         logical_bytes += B * k * n_kv * 2 * D * es
+    elif fused:
+        # INT4: per (sequence, kv head) the new K and V rows are read (2 x 2 d_h B)
+        # and the V code row, its scale/min and the K tail row written; a token
+        # that fills its block also reads the 15 other tail rows and writes the
+        # block's K codes and per-channel scale/min
+        fills = int(((c.seq_lens.cpu() % 16) == 15).sum().item())
+        extra = B * n_kv * (2 * 2 * D + D // 2 + 4 + 2 * D) + fills * n_kv * (15 * 2 * D + 16 * D // 2 + 2 * 2 * D)
+        alg_bytes += extra
+        logical_bytes += extra
     achieved = alg_bytes / (split_avg * 1e-3) / 1e9
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None

@@ -299,10 +299,12 @@ kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out,
  *   max_ctx       largest seq_lens[b] + q_len; the workspace is
  *                 paged_multi_token_attention_workspace_bytes(pool, batch,
  *                 num_q_heads, q_len, max_ctx, opts)
- * The other arguments are those of paged_multi_token_attention. On bf16
- * pools with the MFMA kernel the append is fused into the attention kernel:
- * tiles take the new rows from k_new / v_new and write them into the pool
- * (one kernel fewer per step); other pools launch the append kernel first.
+ * The other arguments are those of paged_multi_token_attention. With the
+ * MFMA kernel the append is fused into the attention kernel (one kernel
+ * fewer per step): on bf16 pools tiles take the new rows from k_new / v_new
+ * and write them into the pool; on INT4 pools with q_len 1 the workgroup
+ * that reads a sequence's last block codes the new token into the pool
+ * first. Other pools and INT4 with q_len > 1 launch the append kernel first.
  * seq_lens must not change between the two (same stream order). A sequence
  * whose length is out of range or above max_ctx gets NaN and may be left
  * unappended. */

@@ -392,7 +392,9 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
 
     const int dtype = pool->desc.dtype;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool fused = k_new && g.kernel == 2 && dtype == KV_BF16;
+    // the append runs inside the attention kernel on the MFMA path: bf16
+    // pools for any q_len, INT4 pools for one new token per sequence
+    const bool fused = k_new && g.kernel == 2 && (dtype == KV_BF16 || (dtype == KV_INT4 && q_len == 1));
     if (k_new && !fused) {
         const kv_status st = kv_append_tokens(pool, k_new, v_new, block_tables, max_blocks, ctx_lens, seq_slots,
                                               batch, ctx_add, stream);

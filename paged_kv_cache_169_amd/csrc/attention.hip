@@ -895,6 +895,31 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         q4_softmax_pv<false>(p, T, sc, corr, tok0, tlo, thi, partial, mask, col, G, st);
 }
 
+// Fused append of a decode step with one new token per sequence, INT4 pool
+// (head_dim 128): the same coding as the append kernel. The token's V row
+// is coded per token; its K row goes to slot t of the sequence's bf16 tail,
+// and when it is the block's 16th token the block's K is coded per channel
+// from the tail rows. pid: the block that receives the token.
+__device__ __forceinline__ void q4_append_token(const AttnParams &p, int b, int kvh, int slot, int pid, int t,
+                                                int lane) {
+    constexpr int hd = 64;  // 32-bit words of a 128-channel bf16 row
+    const size_t src = ((size_t)b * p.n_kv + kvh) * hd;
+    const uint32_t vw = reinterpret_cast<const uint32_t *>(p.v_new)[src + lane];
+    const uint32_t kw = reinterpret_cast<const uint32_t *>(p.k_new)[src + lane];
+    const size_t tile = (size_t)pid * p.n_kv + kvh, row = tile * kBlock + t;
+    code_v_row(vw, true, p.pool.vq + row * hd, p.pool.vs + row, p.pool.vm + row, lane);
+    uint32_t *tail = reinterpret_cast<uint32_t *>(p.pool.ktail) + ((size_t)slot * p.n_kv + kvh) * kBlock * hd;
+    tail[t * hd + lane] = kw;
+    if (t == kBlock - 1) {
+        uint32_t w[kBlock];
+#pragma unroll
+        for (int tt = 0; tt < kBlock - 1; ++tt) w[tt] = tail[tt * hd + lane];
+        w[kBlock - 1] = kw;
+        code_k_block(w, true, p.pool.kq + tile * kBlock * hd, p.pool.ks + tile * 128, p.pool.km + tile * 128, lane,
+                     hd);
+    }
+}
+
 template <int D, int NP>
 __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
@@ -955,11 +980,27 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
         q4_block<NP>(p, T, Q, is_full(j), tail_row, tok0, tlo, thi, needs_mask(tok0, r), col, n16, G, L, st);
     };
-    // one tile in flight ahead of the one in use; the load past the end
-    // re-reads the segment's last tile (cached) instead of being skipped
-    auto fetch = [&](int j, Q4Tile &T) { q4_fetch(p, pid_of(j < j1 ? j : j1 - 1), kvh, n16, G, T); };
+    // Fused append (decode step, one new token at position r.n - 1): the
+    // segment that ends with the sequence's last block codes the token into
+    // the pool. The first tile's loads are issued before that work (unless
+    // the first tile is the last block), and every load of the last block's
+    // tile waits for the coded token's stores.
+    const bool append = p.k_new && ct == 0 && j1 == r.blk_lo + r.nblk && !bad;
+    bool appended = false;
+    auto fetch = [&](int j, Q4Tile &T) {
+        const int jc = j < j1 ? j : j1 - 1;  // past the end: re-read the last tile (cached)
+        if (appended && jc == j1 - 1) __builtin_amdgcn_s_waitcnt(0);
+        q4_fetch(p, pid_of(jc), kvh, n16, G, T);
+    };
     Q4Tile A, B;
-    fetch(j0, A);
+    if (!append || j0 < j1 - 1) fetch(j0, A);
+    if (append) {
+        const int pid = pid_of(j1 - 1);
+        if (!bad) q4_append_token(p, b, kvh, slot, pid, (r.n - 1) % kBlock, lane);
+        appended = true;
+        if (j0 == j1 - 1) fetch(j0, A);
+    }
+    // one tile in flight ahead of the one in use
     for (int j = j0; j < j1; j += 2) {
         fetch(j + 1, B);
         step(A, j);

@@ -19,46 +19,6 @@
 
 namespace kvc {
 
-// Code one bf16 token row (one word per lane) per token into code row `dst`
-// (one byte per lane) and the fp16 scale/min at *s16, *m16.
-__device__ __forceinline__ void code_v_row(uint32_t w, bool act, uint8_t *dst, uint16_t *s16, uint16_t *m16,
-                                           int lane) {
-    const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-    float mn = act ? fminf(x0, x1) : INFINITY;
-    float mx = act ? fmaxf(x0, x1) : -INFINITY;
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    const Q4Params q = q4_params(mn, mx);
-    if (act) dst[lane] = (uint8_t)(q4_code(x0, q) | (q4_code(x1, q) << 4));
-    if (lane == 0) {
-        *s16 = q.s16;
-        *m16 = q.m16;
-    }
-}
-
-// Code the K of one full block per channel. w[t] is this lane's word of token
-// row t. Writes the 16 code rows (one byte per lane each) and the per-channel
-// fp16 scale/min of channels 2*lane, 2*lane+1.
-__device__ __forceinline__ void code_k_block(const uint32_t (&w)[kBlock], bool act, uint8_t *kq_tile,
-                                             uint16_t *ks_row, uint16_t *km_row, int lane, int half_dim) {
-    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kBlock; ++t) {
-        const float a = bf16_lo(w[t]), b = bf16_hi(w[t]);
-        mn0 = fminf(mn0, a);
-        mx0 = fmaxf(mx0, a);
-        mn1 = fminf(mn1, b);
-        mx1 = fmaxf(mx1, b);
-    }
-    const Q4Params q0 = q4_params(mn0, mx0), q1 = q4_params(mn1, mx1);
-    if (!act) return;
-#pragma unroll
-    for (int t = 0; t < kBlock; ++t)
-        kq_tile[t * half_dim + lane] = (uint8_t)(q4_code(bf16_lo(w[t]), q0) | (q4_code(bf16_hi(w[t]), q1) << 4));
-    reinterpret_cast<uint32_t *>(ks_row)[lane] = (uint32_t)q0.s16 | ((uint32_t)q1.s16 << 16);
-    reinterpret_cast<uint32_t *>(km_row)[lane] = (uint32_t)q0.m16 | ((uint32_t)q1.m16 << 16);
-}
-
 // Append to an INT4 pool. Grid (n_kv, batch), one wave each; the wave takes
 // the sequence's n_new tokens in order. The K rows of the block being filled
 // live in LDS (seeded from the sequence's tail row and kept in the tail too),

@@ -44,9 +44,11 @@ struct AttnParams {
     float scale_log2;  // scale * log2(e): scores are kept in log2 units
     // Decode step: the attended length of sequence b is ctx_lens[b] + ctx_add
     // (ctx_lens then holds the lengths before the step's append). With
-    // k_new / v_new set ([batch][ctx_add][n_kv][head_dim], bf16 MFMA path
-    // only) the append is fused: tiles take the new tokens' rows from there,
-    // and the first column tile of each kv head writes them into the pool.
+    // k_new / v_new set ([batch][ctx_add][n_kv][head_dim]; MFMA path: bf16
+    // pools, or INT4 pools with ctx_add 1) the append is fused: bf16 tiles
+    // take the new tokens' rows from there and the first column tile of each
+    // kv head writes them into the pool; on INT4 the segment that ends with a
+    // sequence's last block codes the new token into the pool first.
     int32_t ctx_add;
     const void *k_new, *v_new;
 };

@@ -110,13 +110,42 @@ def test_step_bf16_fused_matches_separate_calls(case, q_len, split, window):
     assert_same(*run_both(c, "bf16", q_len, split, window))
 
 
+INT4_LENS = [  # lengths before the step: the new token starts a block, fills one (slot 15), or lands inside
+    [100, 16, 47, 400, 3],
+    [15, 31, 0, 255, 1023, 64, 17, 2047],
+]
+
+
+@pytest.mark.parametrize("lens", range(len(INT4_LENS)))
 @pytest.mark.parametrize("q_len", [1, 5])
-@pytest.mark.parametrize("split", [0, 2])
-def test_step_int4_composed_matches_separate_calls(q_len, split):
-    print(f"step int4 q_len={q_len} split={split}", flush=True)
-    c = wl.make_case(50, 5, [100, 16, 47, 400, 3], 32, 8, 128, "bf16", pool_slack=1.2, device=DEV, append=q_len,
+@pytest.mark.parametrize("split,window", [(0, 0), (2, 0), (0, 40)])
+def test_step_int4_matches_separate_calls(lens, q_len, split, window):
+    """INT4 with one new token: the append is fused into the attention kernel
+    (coding in the workgroup that reads the last block); with 5 the append
+    kernel runs first. Pools and outputs bit-identical to the separate calls."""
+    print(f"step int4 lens={lens} q_len={q_len} split={split} window={window}", flush=True)
+    ls = INT4_LENS[lens]
+    c = wl.make_case(50 + lens, len(ls), ls, 32, 8, 128, "bf16", pool_slack=1.2, device=DEV, append=q_len,
                      outliers=4)
-    assert_same(*run_both(c, "int4", q_len, split))
+    assert_same(*run_both(c, "int4", q_len, split, window))
+
+
+def test_step_int4_bad_rows():
+    """INT4 fused step: a negative length and an out-of-range block id give NaN
+    rows and leave the pool as the separate calls leave it."""
+    lens = [100, 60, 200, 31]
+    c = wl.make_case(54, 4, lens, 32, 8, 128, "bf16", pool_slack=1.2, device=DEV, append=True)
+    seq_lens = c.seq_lens.clone()
+    seq_lens[1] = -1
+    tables = c.tables.clone()
+    tables[2, 200 // 16] = -7
+    pa, pb, out_a, out_b = run_both(c, "int4", 1, seq_lens=seq_lens, tables=tables)
+    assert np.array_equal(region_bytes(pa), region_bytes(pb)), "pool contents differ"
+    o = out_b.cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
+    a = out_a.cpu().numpy()
+    keep = [0, 3]
+    assert np.array_equal(a[keep].view(np.uint32), o[keep].view(np.uint32))
 
 
 @pytest.mark.parametrize("split", [0, 1])
