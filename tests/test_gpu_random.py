@@ -1,0 +1,207 @@
+"""Seeded random sweep of the decode-attention configurations against the
+oracle (GPU): batch, lengths (including 0 and block-edge lengths), head
+grouping, head_dim, pool dtype, window, kernel and schedule drawn from a
+fixed seed, so every run checks the same cases. Each case also runs the
+decode step (append fused where the library fuses it) against the oracle's
+append + attention. Bound: max |error| <= 2e-3, pools bit-exact."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-3
+N_CASES = 40
+
+kv = None
+orc = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    global kv, orc
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import oracle
+    import paged_kv_cache_169_amd as k
+    kv, orc = k, oracle
+    yield
+
+
+def draw(i):
+    r = random.Random(1000 + i)
+    batch = r.randint(1, 12)
+    edge = [0, 1, 15, 16, 17, 31, 32, 255, 256]
+    lens = [r.choice(edge) if r.random() < 0.3 else r.randint(0, 700) for _ in range(batch)]
+    n_kv = r.choice([1, 2, 4, 8])
+    g = r.choice([1, 2, 3, 4, 6, 8, 16])
+    d = r.choice([64, 128])
+    dtype = r.choice(["bf16", "bf16", "bf16", "f32"])
+    kernel = 1 if dtype == "f32" else r.choice([0, 1, 2])
+    schedule = 0 if kernel == 1 else r.choice([0, 1, 2])
+    split = r.choice([0, 0, 1, 2, 5]) if schedule != 2 else 0
+    window = r.choice([0, 0, 0, 1, 16, 40, 300])
+    return dict(lens=lens, n_kv=n_kv, n_h=n_kv * g, d=d, dtype=dtype, kernel=kernel, schedule=schedule,
+                split=split, window=window)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_decode_step(i):
+    cfg = draw(i)
+    print(f"random case {i}: {cfg}", flush=True)
+    c = wl.make_case(2000 + i, len(cfg["lens"]), cfg["lens"], cfg["n_h"], cfg["n_kv"], cfg["d"], cfg["dtype"],
+                     pool_slack=1.3, device=DEV, append=True)
+    pool = kv.KVPool(c.num_blocks, c.n_kv, c.d, c.dtype, device=DEV)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    opts = kv.attn_opts(split_blocks=cfg["split"], kernel=cfg["kernel"], window=cfg["window"],
+                        schedule=cfg["schedule"])
+    max_ctx = int(c.ctx_lens.max().item())
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(pool, c.batch, c.n_h, 1, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full((c.batch, c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kv_decode_step(pool, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=opts)
+    torch.cuda.synchronize()
+    K, V = wl.to_host_bits(c.K), wl.to_host_bits(c.V)
+    tab = c.tables.cpu().numpy()
+    orc.append(K, V, wl.to_host_bits(c.k_new), wl.to_host_bits(c.v_new), tab, c.seq_lens.cpu().numpy())
+    ints = (lambda a: a.view(np.uint32)) if c.dtype == "f32" else (lambda a: a)
+    assert np.array_equal(ints(wl.to_host_bits(pool.K)), ints(K)) and \
+        np.array_equal(ints(wl.to_host_bits(pool.V)), ints(V)), "pool after the step"
+    ref = orc.attention(K, V, wl.to_host_bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale, window=cfg["window"])
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= TOL
+    pool.close()
+
+
+def draw_int4(i):
+    r = random.Random(5000 + i)
+    batch = r.randint(1, 10)
+    edge = [0, 1, 14, 15, 16, 17, 31, 255]
+    lens = [r.choice(edge) if r.random() < 0.35 else r.randint(0, 600) for _ in range(batch)]
+    kernel = r.choice([0, 1, 2])
+    d = 128 if kernel != 1 else r.choice([64, 128])
+    n_kv = r.choice([1, 2, 4, 8])
+    g = r.choice([1, 2, 4, 4, 6, 8, 16])
+    schedule = 0 if kernel == 1 else r.choice([0, 1, 2])
+    split = r.choice([0, 1, 3]) if schedule != 2 else 0
+    window = r.choice([0, 0, 1, 20, 150])
+    return dict(lens=lens, n_kv=n_kv, n_h=n_kv * g, d=d, kernel=kernel, schedule=schedule, split=split,
+                window=window)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_int4_decode_step(i):
+    """INT4 pool coded from bf16, then one decode step (the append fused into
+    the MFMA kernel): the pool image bit-exact against the oracle's coding and
+    append, the output against the oracle on the same dequantized values."""
+    cfg = draw_int4(i)
+    print(f"random int4 case {i}: {cfg}", flush=True)
+    B = len(cfg["lens"])
+    c = wl.make_case(6000 + i, B, cfg["lens"], cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", pool_slack=1.3,
+                     device=DEV, append=True, outliers=min(4, cfg["d"] // 32))
+    slots = torch.tensor(random.Random(i).sample(range(B + 2), B), dtype=torch.int32, device=DEV)
+    src = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
+    src.K.copy_(c.K)
+    src.V.copy_(c.V)
+    dst = kv.KVPool(c.num_blocks, c.n_kv, c.d, "int4", max_seqs=B + 2, device=DEV)
+    dst.blob.fill_(0x5A)
+    img = orc.Q4Image(c.num_blocks, c.n_kv, c.d, B + 2)
+    for a in img.arrays():
+        a.view(np.uint8)[...] = 0x5A
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens, slots)
+    opts = kv.attn_opts(split_blocks=cfg["split"], kernel=cfg["kernel"], window=cfg["window"],
+                        schedule=cfg["schedule"])
+    max_ctx = int(c.ctx_lens.max().item())
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(dst, B, c.n_h, 1, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kv_decode_step(dst, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws,
+                      seq_slots=slots, opts=opts)
+    torch.cuda.synchronize()
+    tab, lens, sl = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy(), slots.cpu().numpy()
+    orc.q4_quantize_pool(img, wl.to_host_bits(c.K), wl.to_host_bits(c.V), tab, lens, sl)
+    orc.q4_append(img, wl.to_host_bits(c.k_new), wl.to_host_bits(c.v_new), tab, lens, sl)
+    pairs = [(dst.KQ, img.kq), (dst.KS, img.ks), (dst.KM, img.km), (dst.VQ, img.vq), (dst.VS, img.vs),
+             (dst.VM, img.vm), (dst.KTAIL, img.kt)]
+    for t, a in pairs:
+        h = t.detach().cpu().contiguous()
+        h = h.view(torch.int16).numpy().view(np.uint16) if h.element_size() == 2 else h.numpy()
+        assert np.array_equal(h, a), "INT4 pool image after the step"
+    Kd, Vd = orc.q4_dequant(img, tab, c.ctx_lens.cpu().numpy(), sl)
+    ref = orc.attention(Kd, Vd, wl.to_host_bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale, window=cfg["window"])
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= TOL
+    src.close()
+    dst.close()
+
+
+def draw_shared(i):
+    r = random.Random(7000 + i)
+    n_kv = r.choice([1, 2, 4, 8])
+    g = r.choice([1, 2, 4, 8])
+    d = r.choice([64, 128])
+    # consecutive groups with random sizes and prefixes; a sequence that
+    # shares nothing sits before the groups, after them, or between two
+    # groups as a group of its own with no prefix
+    starts, prefix, lens = [], [], []
+    b = 0
+    for k in range(r.randint(1, 4)):
+        if r.random() < 0.3:
+            lens.append(r.randint(0, 300))
+            if k > 0:
+                starts.append(b)
+                prefix.append(0)
+            b += 1
+        m = r.randint(1, 7)
+        P = r.randint(0, 12)
+        starts.append(b)
+        prefix.append(P)
+        for _ in range(m):
+            lens.append(P * 16 + r.randint(0, 200))
+        b += m
+    starts.append(b)
+    if r.random() < 0.5:
+        lens.append(r.randint(0, 300))
+    return dict(lens=lens, n_kv=n_kv, n_h=n_kv * g, d=d, starts=starts, prefix=prefix,
+                split=r.choice([0, 1, 4, 9]))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shared_prefix(i):
+    cfg = draw_shared(i)
+    print(f"random shared case {i}: {cfg}", flush=True)
+    lens = cfg["lens"]
+    c = wl.make_case(8000 + i, len(lens), lens, cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", append=False,
+                     device=DEV)
+    t = c.tables.clone()
+    for a, b2, P in zip(cfg["starts"][:-1], cfg["starts"][1:], cfg["prefix"]):
+        for m in range(a + 1, b2):
+            t[m, :P] = t[a, :P]
+    c.tables = t
+    pool = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    g = kv.prefix_groups(cfg["starts"], cfg["prefix"])
+    opts = kv.attn_opts(split_blocks=cfg["split"])
+    max_ctx = max(int(c.ctx_lens.max().item()), 1)
+    nbytes = kv.paged_decode_attention_shared_workspace_bytes(pool, c.batch, c.n_h, max_ctx, g, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full((c.batch, c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.paged_decode_attention_shared(pool, c.q, out, c.tables, c.ctx_lens, c.scale, max_ctx, g, ws, opts)
+    torch.cuda.synchronize()
+    ref = orc.attention(wl.to_host_bits(c.K), wl.to_host_bits(c.V), wl.to_host_bits(c.q), c.tables.cpu().numpy(),
+                        c.ctx_lens.cpu().numpy(), c.scale)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= TOL
+    pool.close()
