@@ -52,6 +52,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct Q4Params {
     uint16_t s16, m16;
     float s, m;  // the stored values, widened
+    float r;     // hardware reciprocal of s (1 ulp), for q4_code's fast quotient
 };
 __device__ __forceinline__ Q4Params q4_params(float mn, float mx) {
     if (mn == 0.0f) mn = 0.0f;
@@ -62,18 +63,31 @@ __device__ __forceinline__ Q4Params q4_params(float mn, float mx) {
     p.m16 = f_to_f16_bits(mn);
     p.s = f16_bits_to_f(p.s16);
     p.m = f16_bits_to_f(p.m16);
+    p.r = p.s != 0.0f ? __builtin_amdgcn_rcpf(p.s) : 0.0f;
     return p;
 }
 
 // code = clamp(round((x - m) / s), 0, 15), rounding half away from zero, from
 // the stored (fp16) m and s; every code is 0 when s is 0.
+// The quotient is first taken through the hardware reciprocal: with a 1-ulp
+// reciprocal and a rounded product it lies within 2^-18 of the exact
+// (x - m) / s for quotients below 16, and f1 = quotient + 0.5 (rounded)
+// within 2^-17 of the exact value plus one half. When f1's fraction is more
+// than 2^-16 from an integer, floor(f1) is therefore the code itself; the
+// few quotients that close to a half-integer take the correctly rounded
+// division and the exact half-away rounding.
 __device__ __forceinline__ uint32_t q4_code(float x, const Q4Params &p) {
-    if (p.s == 0.0f) return 0u;
-    float v = __fdiv_rn(__fsub_rn(x, p.m), p.s);
-    if (v <= 0.0f) return 0u;
-    if (v >= 15.0f) return 15u;
-    float t = truncf(v);  // v > 0, so v - t is exact
-    return (uint32_t)t + (__fsub_rn(v, t) >= 0.5f ? 1u : 0u);
+    // s = 0: r = 0 makes every quotient 0 (NaN for a non-finite x), code 0
+    const float d = __fsub_rn(x, p.m);
+    const float f1 = __fadd_rn(__fmul_rn(d, p.r), 0.5f);
+    float c = floorf(f1);
+    const float fr = __fsub_rn(f1, c);
+    if (fr <= 0x1p-16f || fr >= 1.0f - 0x1p-16f) {  // near a tie (rare)
+        const float v = __fdiv_rn(d, p.s);
+        const float t = truncf(v);  // v - t is exact
+        c = t + (__fsub_rn(v, t) >= 0.5f ? 1.0f : 0.0f);
+    }
+    return (uint32_t)fminf(fmaxf(c, 0.0f), 15.0f);  // clamp; a NaN quotient gives 0
 }
 
 // Lane mapping of the two coders below (one wave64 per row or block): lane l

@@ -84,21 +84,82 @@ __global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
     const size_t tile = (size_t)pid * p.n_kv + h;
     const uint32_t *ks = reinterpret_cast<const uint32_t *>(p.src.k) + tile * kBlock * hd;
     const uint32_t *vs = reinterpret_cast<const uint32_t *>(p.src.v) + tile * kBlock * hd;
-    for (int t = 0; t < r; ++t) {
-        const uint32_t vw = act ? vs[(size_t)t * hd + lane] : 0u;
+    // Every row of the block is loaded before any is coded (one round trip).
+    // V rows are coded several at a time: lpt = head_dim / 8 lanes per row,
+    // 8 channels each, so a row's min / max is a reduction over lpt lanes
+    // and 64 / lpt rows go through each pass (4 passes at head_dim 128).
+    const int lpt = D / 8, rows_per = 64 / lpt, gi = lane / lpt, cc = lane % lpt;
+    uint4 vrow[4];
+    uint32_t w[kBlock];
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int t = ps * rows_per + gi;
+        vrow[ps] = ps * rows_per < kBlock && t < r
+                       ? reinterpret_cast<const uint4 *>(vs + (size_t)t * hd)[cc]
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) w[t] = act && t < r ? ks[(size_t)t * hd + lane] : 0u;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        if (ps * rows_per >= kBlock) break;
+        const int t = ps * rows_per + gi;
+        const uint32_t x[4] = {vrow[ps].x, vrow[ps].y, vrow[ps].z, vrow[ps].w};
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mn = fminf(mn, fminf(bf16_lo(x[k]), bf16_hi(x[k])));
+            mx = fmaxf(mx, fmaxf(bf16_lo(x[k]), bf16_hi(x[k])));
+        }
+        for (int o = lpt / 2; o >= 1; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        if (t >= r) continue;
+        const Q4Params q = q4_params(mn, mx);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            packed |= (q4_code(bf16_lo(x[k]), q) | (q4_code(bf16_hi(x[k]), q) << 4)) << (8 * k);
         const size_t row = tile * kBlock + t;
-        code_v_row(vw, act, p.dst.vq + row * hd, p.dst.vs + row, p.dst.vm + row, lane);
+        reinterpret_cast<uint32_t *>(p.dst.vq + row * hd)[cc] = packed;
+        if (cc == 0) {
+            p.dst.vs[row] = q.s16;
+            p.dst.vm[row] = q.m16;
+        }
     }
     if (r == kBlock) {
-        uint32_t w[kBlock];
+        // per-channel K coding, lane = channel pair; the code bytes go through
+        // LDS so that each lane stores 16 contiguous bytes of the code tile
+        __shared__ uint8_t kc[kBlock * 64];
+        float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) w[t] = act ? ks[(size_t)t * hd + lane] : 0u;
-        code_k_block(w, act, p.dst.kq + tile * kBlock * hd, p.dst.ks + tile * D, p.dst.km + tile * D, lane, hd);
+        for (int t = 0; t < kBlock; ++t) {
+            mn0 = fminf(mn0, bf16_lo(w[t]));
+            mx0 = fmaxf(mx0, bf16_lo(w[t]));
+            mn1 = fminf(mn1, bf16_hi(w[t]));
+            mx1 = fmaxf(mx1, bf16_hi(w[t]));
+        }
+        const Q4Params q0 = q4_params(mn0, mx0), q1 = q4_params(mn1, mx1);
+        if (act) {
+#pragma unroll
+            for (int t = 0; t < kBlock; ++t)
+                kc[t * hd + lane] = (uint8_t)(q4_code(bf16_lo(w[t]), q0) | (q4_code(bf16_hi(w[t]), q1) << 4));
+            reinterpret_cast<uint32_t *>(p.dst.ks + tile * D)[lane] = (uint32_t)q0.s16 | ((uint32_t)q1.s16 << 16);
+            reinterpret_cast<uint32_t *>(p.dst.km + tile * D)[lane] = (uint32_t)q0.m16 | ((uint32_t)q1.m16 << 16);
+        }
+        __syncthreads();
+        if (lane < hd)  // the tile's 16 * hd code bytes, 16 per lane
+            reinterpret_cast<uint4 *>(p.dst.kq + tile * kBlock * hd)[lane] = reinterpret_cast<const uint4 *>(kc)[lane];
     } else {
         const int slot = p.seq_slots ? p.seq_slots[b] : b;
         if (slot < 0 || slot >= p.max_seqs || !act) return;
         uint32_t *tail = reinterpret_cast<uint32_t *>(p.dst.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;
-        for (int t = 0; t < r; ++t) tail[(size_t)t * hd + lane] = ks[(size_t)t * hd + lane];
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) {
+            if (t >= r) break;
+            tail[(size_t)t * hd + lane] = w[t];
+        }
     }
 }
 

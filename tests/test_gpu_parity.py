@@ -407,6 +407,74 @@ def int4_case(seed, lens, n_h=8, n_kv=2, d=128, outliers=4):
     return wl.make_case(seed, len(lens), lens, n_h, n_kv, d, "bf16", device=DEV, outliers=outliers)
 
 
+def tie_values(shape_rows, n, which):
+    """Rows of n values whose INT4 quotients (x - min) / s are exact
+    half-integers: row i uses (min, s) = PAIRS[i % 3]; element 0 is the min,
+    element 1 the max (min + 15 s), element j the min + ((j + i) % 15 + 0.5) s.
+    All values are exact in bf16 and fp16, and s = (max - min) / 15 exactly."""
+    pairs = [(0.0, 0.25), (-1.0, 0.125), (2.0, 0.5)]
+    out = np.empty(shape_rows + (n,), dtype=np.float32)
+    idx = np.arange(n)
+    flat = out.reshape(-1, n)
+    for i in range(flat.shape[0]):
+        m, sc = pairs[(i + which) % 3]
+        v = m + (((idx + i) % 15) + 0.5) * sc
+        v[0], v[1] = m, m + 15 * sc
+        flat[i] = v
+    return out
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_int4_exact_ties_round_half_away(fused):
+    """Groups whose quotients are exact half-integers (the rounding rule's
+    hard case): bulk coding, then an append that completes a block, bit-exact
+    against the oracle; with fused=True the append is the decode step's."""
+    lens = [31, 20]
+    c = int4_case(830, lens, n_h=4, n_kv=2, d=128, outliers=0)
+    nb, nkv, d = c.num_blocks, c.n_kv, c.d
+    # V: per token row over channels; K: per channel over a block's 16 tokens
+    v = tie_values((nb, nkv, 16), d, 0)
+    k = np.swapaxes(tie_values((nb, nkv, d), 16, 1), -1, -2).copy()
+    c.V.copy_(torch.from_numpy(v).to(DEV, torch.bfloat16))
+    c.K.copy_(torch.from_numpy(k).to(DEV, torch.bfloat16))
+    # the new tokens continue the patterns at their slots
+    knew = np.empty((2, nkv, d), dtype=np.float32)
+    vnew = tie_values((2, nkv), d, 2)
+    for b, L in enumerate(lens):
+        t = L % 16
+        knew[b] = k[0, :, t, :]
+    c.k_new.copy_(torch.from_numpy(knew).to(DEV, torch.bfloat16))
+    c.v_new.copy_(torch.from_numpy(vnew).to(DEV, torch.bfloat16))
+    slots = torch.tensor([1, 0], dtype=torch.int32, device=DEV)
+    src, dst, img = int4_pools(c, 2)
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens, slots)
+    tab, ln, sl = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy(), slots.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, ln, sl)
+    torch.cuda.synchronize()
+    assert_img_equal(dst, img)
+    if fused:
+        max_ctx = int(c.ctx_lens.max().item())
+        ws = torch.empty(max(kv.paged_decode_attention_workspace_bytes(dst, 2, c.n_h, max_ctx), 256),
+                         dtype=torch.uint8, device=DEV)
+        out = torch.empty((2, c.n_h, d), dtype=torch.float32, device=DEV)
+        kv.kv_decode_step(dst, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws,
+                          seq_slots=slots)
+    else:
+        kv.kv_append(dst, c.k_new, c.v_new, c.tables, c.seq_lens, slots)
+    torch.cuda.synchronize()
+    orc.q4_append(img, bits(c.k_new), bits(c.v_new), tab, ln, sl)
+    assert_img_equal(dst, img)
+    # the codes really are the half-away-from-zero roundings: V row i (token 0
+    # of the first block of sequence 0, kv head 0) holds codes 0, 15 and
+    # ((j + i) % 15) + 1 for its ties
+    pid = int(tab[0, 0])
+    i = pid * nkv * 16
+    row = img.vq[pid, 0, 0]
+    codes = np.stack([row & 15, row >> 4], axis=1).reshape(-1)
+    want = np.array([0, 15] + [((j + i) % 15) + 1 for j in range(2, d)])
+    assert np.array_equal(codes, want)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_int4_bulk_then_append_bit_exact(d):
     c = int4_case(800, [0, 14, 15, 16, 17, 31, 47, 100], d=d)
