@@ -11,42 +11,43 @@
 
 namespace kvc {
 
+// One workgroup per listed block: region by region, 256 threads move the
+// region's 16-byte chunks, four loads in flight per thread before the
+// stores; all index arithmetic in 32 bits within a block.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long total = (long)p.n * p.per_block;
-    if (i >= total) return;
-    const int k = (int)(i / p.per_block);
-    uint32_t c = (uint32_t)(i % p.per_block);  // chunk within the packed block
-    int r = 0;
-    while (r < p.nreg - 1 && c >= p.chunks[r]) {
-        c -= p.chunks[r];
-        ++r;
-    }
-    const size_t in_region = (size_t)c * 16;
-    if (p.mode == 2) {  // buffer -> block
-        const int d = p.dst[k];
-        if (d < 0 || d >= p.num_blocks) return;
-        const uint4 v = reinterpret_cast<const uint4 *>(p.buffer)[i];
-        *reinterpret_cast<uint4 *>(p.region[r] + (size_t)d * p.chunks[r] * 16 + in_region) = v;
-        return;
-    }
-    const int sblk = p.src[k];
-    if (sblk < 0 || sblk >= p.num_blocks) return;
-    const uint4 v = *reinterpret_cast<const uint4 *>(p.region[r] + (size_t)sblk * p.chunks[r] * 16 + in_region);
-    if (p.mode == 1) {  // block -> buffer
-        reinterpret_cast<uint4 *>(p.buffer)[i] = v;
-    } else {            // block -> block
-        const int d = p.dst[k];
-        if (d < 0 || d >= p.num_blocks) return;
-        *reinterpret_cast<uint4 *>(p.region[r] + (size_t)d * p.chunks[r] * 16 + in_region) = v;
+    const int k = blockIdx.x;
+    const int sblk = p.mode == 2 ? 0 : p.src[k];
+    const int dblk = p.mode == 1 ? 0 : p.dst[k];
+    if (p.mode != 2 && (sblk < 0 || sblk >= p.num_blocks)) return;
+    if (p.mode != 1 && (dblk < 0 || dblk >= p.num_blocks)) return;
+    const uint4 *buf_in = reinterpret_cast<const uint4 *>(p.buffer) + (size_t)k * p.per_block;
+    uint4 *buf_out = reinterpret_cast<uint4 *>(p.buffer) + (size_t)k * p.per_block;
+    uint32_t packed = 0;  // chunks of the packed block before region r
+    for (int r = 0; r < p.nreg; ++r) {
+        const uint32_t n = p.chunks[r];
+        const uint4 *src = p.mode == 2 ? buf_in + packed
+                                       : reinterpret_cast<const uint4 *>(p.region[r]) + (size_t)sblk * n;
+        uint4 *dst = p.mode == 1 ? buf_out + packed : reinterpret_cast<uint4 *>(p.region[r]) + (size_t)dblk * n;
+        for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 4 * blockDim.x) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t c = c0 + u * blockDim.x;
+                if (c < n) v[u] = src[c];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t c = c0 + u * blockDim.x;
+                if (c < n) dst[c] = v[u];
+            }
+        }
+        packed += n;
     }
 }
 
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s) {
-    const long total = (long)p.n * p.per_block;
-    if (total == 0) return hipSuccess;
-    const int threads = 256;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s, p);
+    if (p.n <= 0 || p.per_block == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)p.n), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@
 // rounded fp32 products (no fused multiply-add; file built with
 // -ffp-contract=off), rounded to the pool type.
 //
-// Work: one thread per (token, kv head, group of 4 pairs): a pure streaming
-// kernel (read and write each key element once).
+// Work: one thread per (token, kv head, group of 4 pairs), one workgroup
+// per (block, kv head) tile: a pure streaming kernel (read and write each key
+// element once).
 #include "device.h"
 #include "internal.h"
 
@@ -62,21 +63,20 @@ __device__ __forceinline__ void rope_bf16_group(const RopeParams &p, uint16_t *r
     }
 }
 
+// One workgroup per (chunk block, kv head): thread (slot t, group gq) of
+// the block's 16 x head_dim / 8 groups, so consecutive threads touch
+// consecutive bytes of the (block, kv head) tile.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
     const int D = p.head_dim;
     const int groups = D / 8;  // groups of 4 pairs per row
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long total = (long)p.num_tokens * p.n_kv * groups;
-    if (i >= total) return;
-    const int gq = (int)(i % groups);
-    long r = i / groups;
-    const int h = (int)(r % p.n_kv);
-    const int k = (int)(r / p.n_kv);
-    const int pos = p.first_slot + k;
-    const int pid = p.chunk_blocks[pos / kBlock];
+    const int kb = p.first_slot / kBlock + (int)blockIdx.x, h = blockIdx.y;
+    const int t = (int)threadIdx.x / groups, gq = (int)threadIdx.x % groups;
+    const int pos = kb * kBlock + t;  // position in the block list
+    if (pos < p.first_slot || pos >= p.first_slot + p.num_tokens) return;
+    const int pid = p.chunk_blocks[kb];
     if (pid < 0 || pid >= p.num_blocks) return;
-    const size_t row = (((size_t)pid * p.n_kv + h) * kBlock + pos % kBlock) * D;
+    const size_t row = (((size_t)pid * p.n_kv + h) * kBlock + t) * D;
     if (BF16) {
         rope_bf16_group(p, reinterpret_cast<uint16_t *>(p.k) + row, gq);
         return;
@@ -95,14 +95,14 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
 }
 
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s) {
-    const long total = (long)p.num_tokens * p.n_kv * (p.head_dim / 8);
-    if (total == 0) return hipSuccess;
-    const int threads = 256;
-    const unsigned blocks = (unsigned)((total + threads - 1) / threads);
+    if (p.num_tokens <= 0) return hipSuccess;
+    const int first = p.first_slot / kBlock, last = (p.first_slot + p.num_tokens - 1) / kBlock;
+    const dim3 grid((unsigned)(last - first + 1), (unsigned)p.n_kv);
+    const dim3 block((unsigned)(kBlock * (p.head_dim / 8)));
     if (dtype == KV_BF16)
-        hipLaunchKernelGGL(rope_kernel<true>, dim3(blocks), dim3(threads), 0, s, p);
+        hipLaunchKernelGGL(rope_kernel<true>, grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL(rope_kernel<false>, dim3(blocks), dim3(threads), 0, s, p);
+        hipLaunchKernelGGL(rope_kernel<false>, grid, block, 0, s, p);
     return hipGetLastError();
 }
 
