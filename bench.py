@@ -271,6 +271,9 @@ def main():
             hip.destroy(x)
     split_avg = sum(split_ms) / len(split_ms)
     merge_avg = sum(merge_ms) / len(merge_ms)
+    split_sorted = sorted(split_ms)
+    pct = lambda f: split_sorted[min(len(split_sorted) - 1, int(f * len(split_sorted)))] * 1e3
+    copy_rate = streaming_copy_rate(torch, stream)
 
     # algorithmic bytes of one split-kernel launch: K and V of every attended
     # (token, kv head) once, q, the output, the block-table entries and lengths.
@@ -306,6 +309,9 @@ def main():
     log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
         f"{split_avg*1e3:.1f} us, merge {merge_avg*1e3:.1f} us, {achieved:.0f} GB/s "
         f"({100*achieved/PEAK_HBM_GBS:.1f}% of 8 TB/s), {value/1e9:.3f} G KV-tokens/s")
+    log(f"[bench] achievable on this device: streaming copy {copy_rate:.0f} GB/s "
+        f"(kernel at {100*achieved/copy_rate:.1f}% of it); kernel p10/p50/p90 "
+        f"{pct(0.1):.1f}/{pct(0.5):.1f}/{pct(0.9):.1f} us")
 
     cpu = None
     if args.cpu_seconds > 0 and k == 1:
@@ -362,11 +368,34 @@ def main():
                      "kernel": ("shared-prefix decode attention kernel (before the merge)" if shared else
                                 "decode attention kernel (before the merge)" + (", append fused" if fused else "")),
                      "avg_launch_us": split_avg * 1e3,
+                     "launch_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes,
-                     "logical_bytes_per_launch": logical_bytes},
+                     "logical_bytes_per_launch": logical_bytes,
+                     "achievable": {"copy_GBps": copy_rate, "frac_of_copy": achieved / copy_rate,
+                                    "how": "torch copy_ of a 1 GiB buffer on the same device, "
+                                           "bytes read + written per second"}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def streaming_copy_rate(torch, stream, nbytes: int = 1 << 30, iters: int = 10) -> float:
+    """Achievable HBM rate on this device: torch's copy between two buffers far
+    larger than the caches, as bytes read + written per second."""
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return rate
 
 
 def hold_queue(torch, launches: int) -> None:

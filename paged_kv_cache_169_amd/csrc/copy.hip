@@ -11,34 +11,37 @@
 
 namespace kvc {
 
+typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
 // One workgroup per listed block: region by region, 256 threads move the
 // region's 16-byte chunks, four loads in flight per thread before the
-// stores; all index arithmetic in 32 bits within a block.
+// stores; all index arithmetic in 32 bits within a block. Loads and stores
+// are non-temporal: no byte is touched twice, so none is kept in the caches.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
     const int k = blockIdx.x;
     const int sblk = p.mode == 2 ? 0 : p.src[k];
     const int dblk = p.mode == 1 ? 0 : p.dst[k];
     if (p.mode != 2 && (sblk < 0 || sblk >= p.num_blocks)) return;
     if (p.mode != 1 && (dblk < 0 || dblk >= p.num_blocks)) return;
-    const uint4 *buf_in = reinterpret_cast<const uint4 *>(p.buffer) + (size_t)k * p.per_block;
-    uint4 *buf_out = reinterpret_cast<uint4 *>(p.buffer) + (size_t)k * p.per_block;
+    const chunk_t *buf_in = reinterpret_cast<const chunk_t *>(p.buffer) + (size_t)k * p.per_block;
+    chunk_t *buf_out = reinterpret_cast<chunk_t *>(p.buffer) + (size_t)k * p.per_block;
     uint32_t packed = 0;  // chunks of the packed block before region r
     for (int r = 0; r < p.nreg; ++r) {
         const uint32_t n = p.chunks[r];
-        const uint4 *src = p.mode == 2 ? buf_in + packed
-                                       : reinterpret_cast<const uint4 *>(p.region[r]) + (size_t)sblk * n;
-        uint4 *dst = p.mode == 1 ? buf_out + packed : reinterpret_cast<uint4 *>(p.region[r]) + (size_t)dblk * n;
+        const chunk_t *src = p.mode == 2 ? buf_in + packed
+                                          : reinterpret_cast<const chunk_t *>(p.region[r]) + (size_t)sblk * n;
+        chunk_t *dst = p.mode == 1 ? buf_out + packed : reinterpret_cast<chunk_t *>(p.region[r]) + (size_t)dblk * n;
         for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 4 * blockDim.x) {
-            uint4 v[4];
+            chunk_t v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t c = c0 + u * blockDim.x;
-                if (c < n) v[u] = src[c];
+                if (c < n) v[u] = __builtin_nontemporal_load(src + c);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t c = c0 + u * blockDim.x;
-                if (c < n) dst[c] = v[u];
+                if (c < n) __builtin_nontemporal_store(v[u], dst + c);
             }
         }
         packed += n;
