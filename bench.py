@@ -1,8 +1,8 @@
 """Benchmark of one decode step (kv_append + paged decode attention) on one GPU.
 
-The step is one kv_decode_step call: on bf16 pools the append runs inside the
-attention kernel (then the merge kernel); INT4 and fp32 pools launch the
-append kernel first.
+The step is one kv_decode_step call: on bf16 pools, and on INT4 pools with one
+new token per sequence, the append runs inside the attention kernel (then the
+merge kernel); fp32 pools launch the append kernel first.
 
 Prints one JSON line. A step appends one token to every sequence and runs
 paged decode attention over the cache (the decode-step listing of "KV Cache는
@@ -12,8 +12,9 @@ synthetic inputs already resident in HBM.
   value     KV-tokens/s: tokens attended per step (summed over sequences)
             divided by the measured step time
   roofline  the split attention kernel's algorithmic bytes per launch divided
-            by its average launch time (HIP events on the launch stream),
-            against 8 TB/s
+            by its average launch time (HIP events on the launch stream,
+            recorded around the kernel on every --event-every-th timed step:
+            a record costs the stream a few microseconds), against 8 TB/s
   cpu_baseline  the oracle (fp64 C, OpenMP) on the host, on the same inputs
 
 Consecutive steps rotate over pool replicas whose total size exceeds twice the
@@ -151,6 +152,9 @@ def main():
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
     ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the kernel-boundary events on every E-th timed step (each record costs the "
+                         "stream a few microseconds); 1 = every step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence: 1 is decode; k > 1 appends k tokens and runs the "
@@ -252,7 +256,8 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronized on both sides
-    ev = [[hip.create() for _ in range(3)] for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    ev = [[hip.create() for _ in range(3)] if i % every == 0 else None for i in range(args.steps)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -264,6 +269,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = e_start.elapsed_time(e_end)
     ms_per_step = ms_total / args.steps
+    ev = [e for e in ev if e is not None]
     split_ms = [hip.elapsed_ms(e[0], e[1]) for e in ev]
     merge_ms = [hip.elapsed_ms(e[1], e[2]) for e in ev]
     for e in ev:
@@ -369,6 +375,7 @@ def main():
                                 "decode attention kernel (before the merge)" + (", append fused" if fused else "")),
                      "avg_launch_us": split_avg * 1e3,
                      "launch_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+                     "timed_launches": len(split_ms),
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes,
                      "logical_bytes_per_launch": logical_bytes,
                      "achievable": {"copy_GBps": copy_rate, "frac_of_copy": achieved / copy_rate,

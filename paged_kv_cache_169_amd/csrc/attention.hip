@@ -76,10 +76,17 @@ __device__ __forceinline__ u32x2_t stream_load8(gu16_t *p) {
 enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_INT4 = 2 };
 
 // 2^x with the hardware instruction alone. Every argument here is a
-// difference from a running maximum (<= 0, or -inf for a masked slot), so a
-// result below the normal range, which the instruction flushes to 0, is a
-// weight no fp32 softmax sum can register anyway.
+// difference from a reference maximum (at most kLazyLog2, or -inf for a
+// masked slot), so a result below the normal range, which the instruction
+// flushes to 0, is a weight no fp32 softmax sum can register anyway.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lazy rescaling of the MFMA paths' online softmax: a column's reference
+// maximum m moves only when a tile's score exceeds it by more than kLazyLog2
+// (log2 units), so weights 2^(s - m) stay below 2^kLazyLog2 and the
+// accumulators are rescaled a few times per segment instead of at every new
+// maximum. (m, l, o) stay consistent for any m, so the merge is unchanged.
+constexpr float kLazyLog2 = 8.0f;
 
 // A value every lane of the wave reads from the same address, moved to a
 // scalar register: the loads these come from are vector loads (the kernels
@@ -499,9 +506,11 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
-    const float mn = fmaxf(st.m, col_max(mx));
-    if (!__all(mn == st.m)) {
-        // the running max moved for some column: rescale (rare after the first blocks)
+    const float cm = col_max(mx);
+    if (__any(cm > st.m + kLazyLog2)) {
+        // some column's maximum moved past its reference by more than the
+        // slack: move every column's reference to its maximum and rescale
+        const float mn = fmaxf(st.m, cm);
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
 #pragma unroll
@@ -774,8 +783,9 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
         sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
-    const float mn = fmaxf(st.m, col_max(mx));
-    if (!__all(mn == st.m)) {
+    const float cm = col_max(mx);
+    if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
+        const float mn = fmaxf(st.m, cm);
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
         st.bv *= alpha;

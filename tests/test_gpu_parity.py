@@ -155,6 +155,52 @@ def test_attention_parity(shape, kernel, split):
     assert max_err(out, ref) <= TOL
 
 
+def add_score_ramp(c, amp):
+    """Adds to every attended key row a multiple of its query group's mean
+    direction that grows with the token position: the scores then rise by
+    about 0.7 * amp log2 units over each sequence, so the running maximum keeps
+    moving, in steps both above and below the MFMA paths' rescaling slack."""
+    K = c.K.float().cpu()
+    q = c.q.float().cpu()
+    g = c.n_h // c.n_kv
+    u = q.view(c.batch, c.n_kv, g, c.d).mean(2)
+    u = u / u.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    tab = c.tables.cpu()
+    for b in range(c.batch):
+        n = int(c.ctx_lens[b])
+        for j in range(n):
+            K[int(tab[b, j // 16]), :, j % 16, :] += amp * (j / max(n - 1, 1)) * u[b]
+    c.K.copy_(K.to(c.K.dtype))
+
+
+@pytest.mark.parametrize("n_h", [32, 64])
+@pytest.mark.parametrize("amp", [12.0, 60.0])
+@pytest.mark.parametrize("dtype", ["bf16", "int4"])
+@pytest.mark.parametrize("split", [0, 3])
+def test_rising_scores(n_h, amp, dtype, split):
+    """Scores that climb along the sequence (the running maximum moves on most
+    tiles): the MFMA paths against the oracle, both schedules."""
+    lens = [300, 1000, 17, 2000, 40]
+    c = wl.make_case(260 + n_h + int(amp), len(lens), lens, n_h, 8, 128, "bf16", append=False, device=DEV)
+    add_score_ramp(c, amp)
+    tab, ctx = c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy()
+    if dtype == "bf16":
+        pool = new_pool(c)
+        out = gpu_attention(pool, c, kernel=2, split_blocks=split)
+        Kr, Vr = bits(c.K), bits(c.V)
+    else:
+        slots = torch.arange(len(lens), dtype=torch.int32, device=DEV)
+        src, dst, img = int4_pools(c, len(lens))
+        kv.kv_quantize_int4(dst, src, c.tables, c.ctx_lens, slots)
+        orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, ctx, slots.cpu().numpy())
+        assert_img_equal(dst, img)
+        out = gpu_attention(dst, c, kernel=2, split_blocks=split, seq_slots=slots)
+        Kr, Vr = orc.q4_dequant(img, tab, ctx, slots.cpu().numpy())
+    ref = orc.attention(Kr, Vr, bits(c.q), tab, ctx, c.scale)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref) <= TOL
+
+
 @pytest.mark.parametrize("kernel,split", [(1, 2), (2, 2), (2, 0)])
 def test_permutation_and_repeat_are_bit_identical(kernel, split):
     c = wl.make_case(300, 4, [70, 15, 128, 99], 16, 4, 128, "bf16", num_blocks=40, append=False, device=DEV)
