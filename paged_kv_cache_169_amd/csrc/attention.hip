@@ -1312,49 +1312,68 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(Attn
 // channels): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M the
 // largest m_i. row_of(i) is the workspace row of partial i. Partials 64 at a
 // time: lane i reads the (m, l) of partial base + i, so a chunk's maxima and
-// sums take one round trip and a wave reduction; the value rows follow four
-// at a time, their weights read from the lanes that hold them. A NaN l (bad
-// sequence or table) makes the row NaN; a row no partial saw a token for
-// gets 0.
+// sums take one round trip and a wave reduction. The value rows are read NB
+// at a time (NB = 4 for a short chunk, else 16), the first batch issued with
+// the (m, l) loads (the rows do not depend on the weights), so a row with few
+// partials costs one round trip; their weights are read from the lanes that
+// hold them. A NaN l (bad sequence or table) makes the row NaN; a row no
+// partial saw a token for gets 0.
+template <int NB, class RowOf>
+__device__ __forceinline__ void merge_batch(const AttnParams &p, int base, int i0, int cnt, RowOf row_of, int lane,
+                                            int cv, float (&o)[NB][2]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const int i = min(i0 + k, cnt - 1);  // past the end: row re-read, weight 0
+        const float *src = p.ws_o + row_of(base + i) * p.head_dim + lane * cv;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) o[k][c] = c < cv ? src[c] : 0.0f;
+    }
+}
+
+template <int NB, class RowOf>
+__device__ __forceinline__ void merge_chunk(const AttnParams &p, int base, int cnt, RowOf row_of, int lane, int cv,
+                                            float &M, float &L, float (&acc)[2]) {
+    const int w = base + lane;
+    float m = -INFINITY, l = 0.0f;
+    if (w < base + cnt) {
+        const size_t row = row_of(w);
+        m = p.ws_ml[row * 2];
+        l = p.ws_ml[row * 2 + 1];
+    }
+    float o[NB][2];
+    merge_batch<NB>(p, base, 0, cnt, row_of, lane, cv, o);
+    const float Mn = fmaxf(M, wave_max(m));
+    if (Mn == -INFINITY) return;  // no partial has seen a token yet
+    const float a = fast_exp2(M - Mn);  // 0 while M is -inf
+    L *= a;
+    acc[0] *= a;
+    acc[1] *= a;
+    M = Mn;
+    const float wgt = w < base + cnt ? fast_exp2(m - M) : 0.0f;
+    L += wave_sum(wgt * l);
+    for (int i0 = 0; i0 < cnt; i0 += NB) {
+        if (i0 > 0) merge_batch<NB>(p, base, i0, cnt, row_of, lane, cv, o);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const float wi = i0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i0 + k))
+                                          : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) acc[c] = fmaf(wi, o[k][c], acc[c]);
+        }
+    }
+}
+
 template <class RowOf>
 __device__ __forceinline__ void merge_partials(const AttnParams &p, int n, RowOf row_of, int lane, int cv,
                                                float *dst) {
-    const int D = p.head_dim;
     float M = -INFINITY, L = 0.0f;
     float acc[2] = {0.0f, 0.0f};
     for (int base = 0; base < n; base += 64) {
-        const int w = base + lane;
-        float m = -INFINITY, l = 0.0f;
-        if (w < n) {
-            const size_t row = row_of(w);
-            m = p.ws_ml[row * 2];
-            l = p.ws_ml[row * 2 + 1];
-        }
-        const float Mn = fmaxf(M, wave_max(m));
-        if (Mn == -INFINITY) continue;  // no partial has seen a token yet
-        const float a = fast_exp2(M - Mn);  // 0 while M is -inf
-        L *= a;
-        acc[0] *= a;
-        acc[1] *= a;
-        M = Mn;
-        const float wgt = w < n ? fast_exp2(m - M) : 0.0f;
-        L += wave_sum(wgt * l);
         const int cnt = min(64, n - base);
-        for (int i0 = 0; i0 < cnt; i0 += 4) {
-            float wi[4], o[4][2];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = min(i0 + k, cnt - 1);  // past the end: weight 0, row re-read
-                wi[k] = i0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i)) : 0.0f;
-                const float *src = p.ws_o + row_of(base + i) * D + lane * cv;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) o[k][c] = c < cv ? src[c] : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) acc[c] = fmaf(wi[k], o[k][c], acc[c]);
-        }
+        if (cnt <= 4)
+            merge_chunk<4>(p, base, cnt, row_of, lane, cv, M, L, acc);
+        else
+            merge_chunk<16>(p, base, cnt, row_of, lane, cv, M, L, acc);
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int c = 0; c < cv; ++c) dst[c] = acc[c] * inv;
