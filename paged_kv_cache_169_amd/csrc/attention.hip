@@ -376,7 +376,15 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams p) {
 // MFMA kernel (bf16 pools)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
+// (hardware conversion)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // One (block, kv head) tile in MFMA operand layout.
 template <int D>
@@ -525,19 +533,15 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         pr[r] = fast_exp2(sv[r] - mref);
         st.l += pr[r];
     }
-    // P^T as B operand, split into bf16 hi and lo parts
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        hi[r] = f_to_bf16(pr[r]);
-        lo[r] = f_to_bf16(pr[r] - bf16_to_f((uint16_t)hi[r]));
-    }
+    // P^T as B operand, split into bf16 hi and lo parts (the lo part rounds
+    // the exact fp32 remainder)
+    const uint32_t h01 = cvt_pk_bf16(pr[0], pr[1]), h23 = cvt_pk_bf16(pr[2], pr[3]);
+    const uint32_t l01 = cvt_pk_bf16(pr[0] - __uint_as_float(h01 << 16), pr[1] - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = cvt_pk_bf16(pr[2] - __uint_as_float(h23 << 16), pr[3] - __uint_as_float(h23 & 0xffff0000u));
     // hi and lo parts side by side along k: one 16x16x32 product per channel
     // tile takes both (k = 8G + i: hi of token 4G + i for i < 4, lo of token
     // 4G + i - 4 after)
-    const bf16x8_t pB = __builtin_bit_cast(
-        bf16x8_t, make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(lo[0], lo[1]),
-                             pack_bf16x2(lo[2], lo[3])));
+    const bf16x8_t pB = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));
     uint32_t vr[4][VC / 2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -558,9 +562,11 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     // n16*VC + m of tokens 4G .. 4G+3.
 #pragma unroll
     for (int m = 0; m < MS; ++m) {
-        const int wi = m >> 1, sh = (m & 1) * 16;
-        const uint32_t e0 = vr[0][wi] >> sh, e1 = vr[1][wi] >> sh, e2 = vr[2][wi] >> sh, e3 = vr[3][wi] >> sh;
-        const uint32_t a01 = pack_bf16x2(e0, e1), a23 = pack_bf16x2(e2, e3);
+        // the 16-bit half m & 1 of word m >> 1 of tokens (0, 1) and (2, 3)
+        const int wi = m >> 1;
+        const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t a01 = __builtin_amdgcn_perm(vr[1][wi], vr[0][wi], sel);
+        const uint32_t a23 = __builtin_amdgcn_perm(vr[3][wi], vr[2][wi], sel);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
         st.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB, st.o[m], 0, 0, 0);
     }
@@ -664,14 +670,6 @@ __device__ __forceinline__ void mfma_gather_run(const MfmaState<D> &st, float bv
 // value channels 8 n16 .. 8 n16 + 7 in the value product.
 // ---------------------------------------------------------------------------
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16 pair, round to nearest even (hardware conversion)
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 typedef const __attribute__((address_space(1))) uint8_t gu8_t;
 typedef const __attribute__((address_space(1))) uint32_t gu32_t;
@@ -756,21 +754,14 @@ struct Q4Query {
     int npass;
 };
 
-// Online softmax and value update of one INT4 tile, given its raw scores sc
-// (before the per-column min term corr). MASKED: some slots of the tile are
-// outside the attended range (partial block, window, causal columns); their
-// weights are 0 and their V parameters, which may be anything, are not used.
-// Values: sum_t p_t (min_t + scale_t * code_tc) = sum_t P'_t * code_tc +
-// sum_t p_t * min_t with P'_t = p_t * scale_t (bf16 hi + lo in the B
-// operand) and the exact codes in the A operand; the second sum is a
-// per-column numerator term kept beside o.
+// Scores of one INT4 tile in log2 units, from its raw products sc (before
+// the per-column min term corr). MASKED: some slots of the tile are outside
+// the attended range (partial block, window, causal columns); they get -inf
+// and valid false.
 template <bool MASKED>
-__device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const f32x4_t &sc, float corr,
-                                              int tok0, int tlo, int thi, bool partial, bool mask, const Column &col,
-                                              int G, MfmaState<128> &st) {
-    float sv[4];
-    bool valid[4];
-    float mx = -INFINITY;
+__device__ __forceinline__ void q4_scores(const AttnParams &p, const f32x4_t &sc, float corr, int tok0, int tlo,
+                                          int thi, bool partial, bool mask, const Column &col, int G, float (&sv)[4],
+                                          bool (&valid)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int tt = 4 * G + r, tp = tok0 + tt;
@@ -781,8 +772,20 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
         }
         valid[r] = ok;
         sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
     }
+}
+
+// Online softmax and value update of one INT4 tile, given its scores sv.
+// Slots that are not valid get weight 0 and their V parameters, which may be
+// anything, are not used. Full and masked tiles share this code (only their
+// scores differ), so the accumulators are updated in place.
+// Values: sum_t p_t (min_t + scale_t * code_tc) = sum_t P'_t * code_tc +
+// sum_t p_t * min_t with P'_t = p_t * scale_t (bf16 hi + lo in the B
+// operand) and the exact codes in the A operand; the second sum is a
+// per-column numerator term kept beside o.
+__device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const float (&sv)[4],
+                                              const bool (&valid)[4], int G, MfmaState<128> &st) {
+    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     const float cm = col_max(mx);
     if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
         const float mn = fmaxf(st.m, cm);
@@ -899,10 +902,13 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         }
     }
     const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
-    if (partial || mask)  // uniform: the rare masked form and the common one are separate code
-        q4_softmax_pv<true>(p, T, sc, corr, tok0, tlo, thi, partial, mask, col, G, st);
+    float sv[4];
+    bool valid[4];
+    if (partial || mask)  // uniform: only the rare masked tiles test positions
+        q4_scores<true>(p, sc, corr, tok0, tlo, thi, partial, mask, col, G, sv, valid);
     else
-        q4_softmax_pv<false>(p, T, sc, corr, tok0, tlo, thi, partial, mask, col, G, st);
+        q4_scores<false>(p, sc, corr, tok0, tlo, thi, partial, mask, col, G, sv, valid);
+    q4_softmax_pv(p, T, sv, valid, G, st);
 }
 
 // Fused append of a decode step with one new token per sequence, INT4 pool
