@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PARITY_TOL = 2e-3  # max |error| of the fp32 attention output vs the fp64 oracle
 MALL_BYTES = 256 << 20
 
 
@@ -337,17 +338,24 @@ def main():
             Kh, Vh = wl.to_host_bits(p0.K), wl.to_host_bits(p0.V)
         threads = oracle.max_threads()
         done_tokens, t_cpu, runs = 0, 0.0, 0
+        ref = None
         # whole-batch oracle passes until the time budget is spent (at least one)
         while t_cpu < args.cpu_seconds or runs == 0:
             t1 = time.perf_counter()
-            oracle.attention(Kh, Vh, qh, tab, ctx_np, c.scale)
+            ref = oracle.attention(Kh, Vh, qh, tab, ctx_np, c.scale)
             t_cpu += time.perf_counter() - t1
             done_tokens += tokens_per_step
             runs += 1
+        # the timed steps' output against the oracle on the same inputs
+        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))) if ref.size else 0.0
         cpu = {"value": done_tokens / t_cpu, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"{runs} full pass(es) of the {name} attention ({tokens_per_step} tokens x {n_h} heads, "
-                         f"fp64, OpenMP over (sequence, head)), {t_cpu:.1f} s"}
-        log(f"[bench] oracle: {cpu['value']/1e6:.3f} M KV-tokens/s on {threads} threads ({runs} runs, {t_cpu:.1f}s)")
+                         f"fp64, OpenMP over (sequence, head)), {t_cpu:.1f} s",
+               "gpu_max_abs_err": err, "tolerance": PARITY_TOL}
+        log(f"[bench] oracle: {cpu['value']/1e6:.3f} M KV-tokens/s on {threads} threads ({runs} runs, {t_cpu:.1f}s); "
+            f"GPU output vs oracle: max |err| {err:.2e}")
+        if not err <= PARITY_TOL:
+            raise SystemExit(f"bench: GPU output differs from the oracle by {err:.3e} (> {PARITY_TOL})")
 
     line = {
         "metric": "paged GQA decode attention: KV-tokens/s and achieved HBM GB/s (% of peak)",
