@@ -30,6 +30,8 @@
  *     access; attention then writes NaN to the affected sequence's output
  *     and append/quantize/rotate skip the affected rows.
  *     kv_validate_tables checks host copies of the same arrays.
+ *   - Table widths: max_blocks lies in [1, INT32_MAX / 16] (so max_blocks * 16
+ *     tokens fit in 32 bits); other values are KV_ERR_INVALID_ARG.
  */
 #ifndef KVCACHE_H
 #define KVCACHE_H

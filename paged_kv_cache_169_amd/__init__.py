@@ -514,4 +514,5 @@ raw = {
     "kv_topk_select": _kv_topk_select, "kv_decode_step": _kv_decode_step,
     "paged_decode_attention_shared": _paged_decode_attention_shared,
     "paged_decode_attention_shared_workspace_bytes": _paged_decode_attention_shared_workspace_bytes,
+    "kv_validate_tables": _kv_validate_tables,
 }

@@ -92,6 +92,10 @@ kv_status hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Table widths whose token count (max_blocks * 16) the kernels can hold in 32
+// bits.
+bool max_blocks_ok(int32_t max_blocks) { return max_blocks >= 1 && max_blocks <= INT32_MAX / KV_BLOCK_TOKENS; }
+
 // Attention launch geometry for a call.
 struct AttnGeom {
     int kernel;        // 1 VALU, 2 MFMA
@@ -325,7 +329,7 @@ kv_status kv_pool_get_desc(kv_pool_t pool, kv_pool_desc *desc) {
 kv_status kv_append_tokens(kv_pool_t pool, const void *k_new, const void *v_new, const int32_t *block_tables,
                            int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
                            int32_t n_new, void *stream) {
-    if (!pool || batch < 0 || max_blocks < 1 || n_new < 1) return KV_ERR_INVALID_ARG;
+    if (!pool || batch < 0 || !max_blocks_ok(max_blocks) || n_new < 1) return KV_ERR_INVALID_ARG;
     if (batch == 0) return KV_OK;
     if (!k_new || !v_new || !block_tables || !seq_lens) return KV_ERR_INVALID_ARG;
     if (!aligned16(k_new) || !aligned16(v_new)) return KV_ERR_INVALID_ARG;
@@ -377,7 +381,7 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
                          const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace, size_t ws_bytes,
                          const kv_attn_opts *opts, void *stream, int32_t ctx_add, const void *k_new,
                          const void *v_new) {
-    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0 || q_len < 1)
+    if (!pool || batch < 0 || num_q_heads < 1 || !max_blocks_ok(max_blocks) || max_ctx < 0 || q_len < 1)
         return KV_ERR_INVALID_ARG;
     if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
@@ -487,7 +491,8 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
                                         const int32_t *ctx_lens, int32_t batch, int32_t max_ctx,
                                         const kv_prefix_groups *groups, void *workspace, size_t ws_bytes,
                                         const kv_attn_opts *opts, void *stream) {
-    if (!pool || batch < 0 || num_q_heads < 1 || max_blocks < 1 || max_ctx < 0) return KV_ERR_INVALID_ARG;
+    if (!pool || batch < 0 || num_q_heads < 1 || !max_blocks_ok(max_blocks) || max_ctx < 0)
+        return KV_ERR_INVALID_ARG;
     if (max_ctx > max_blocks * KV_BLOCK_TOKENS) return KV_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return KV_ERR_INVALID_ARG;
     SharedGeom g;
@@ -537,7 +542,7 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
 
 kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables, int32_t max_blocks,
                            const int32_t *lens, const int32_t *seq_slots, int32_t batch, void *stream) {
-    if (!dst || !src || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (!dst || !src || batch < 0 || !max_blocks_ok(max_blocks)) return KV_ERR_INVALID_ARG;
     if (dst->desc.dtype != KV_INT4 || src->desc.dtype != KV_BF16) return KV_ERR_INVALID_ARG;
     if (dst->desc.num_blocks != src->desc.num_blocks || dst->desc.num_kv_heads != src->desc.num_kv_heads ||
         dst->desc.head_dim != src->desc.head_dim)
@@ -562,6 +567,7 @@ kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_ta
 kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t first_slot, int32_t num_tokens,
                         int32_t delta, float base, int32_t style, void *stream) {
     if (!pool || first_slot < 0 || num_tokens < 0 || (style != 0 && style != 1)) return KV_ERR_INVALID_ARG;
+    if ((int64_t)first_slot + num_tokens > INT32_MAX) return KV_ERR_INVALID_ARG;
     if (!(base > 0.0f) || !std::isfinite(base)) return KV_ERR_INVALID_ARG;
     if (pool->desc.dtype == KV_INT4) return KV_ERR_UNSUPPORTED;
     if (num_tokens == 0) return KV_OK;
@@ -659,7 +665,7 @@ kv_status kv_scatter_blocks(kv_pool_t pool, const int32_t *blocks, int32_t n, co
 kv_status kv_token_deviation(kv_pool_t pool, const int32_t *block_tables, int32_t max_blocks, int32_t batch,
                              const int32_t *row_seq, const int32_t *row_pos, int32_t n_rows, const void *k_re,
                              const void *v_re, double *deviation, void *stream) {
-    if (!pool || max_blocks < 1 || batch < 0 || n_rows < 0) return KV_ERR_INVALID_ARG;
+    if (!pool || !max_blocks_ok(max_blocks) || batch < 0 || n_rows < 0) return KV_ERR_INVALID_ARG;
     if (pool->desc.dtype == KV_INT4) return KV_ERR_UNSUPPORTED;
     if (n_rows == 0) return KV_OK;
     if (!block_tables || !row_seq || !row_pos || !k_re || !v_re || !deviation) return KV_ERR_INVALID_ARG;
@@ -718,7 +724,7 @@ int32_t kv_recompute_count(double ratio, int32_t num_tokens) {
 kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
                              const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row) {
     if (bad_row) *bad_row = -1;
-    if (!desc_ok(desc) || batch < 0 || max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || batch < 0 || !max_blocks_ok(max_blocks)) return KV_ERR_INVALID_ARG;
     if (batch > 0 && (!block_tables || !lens)) return KV_ERR_INVALID_ARG;
     std::set<std::pair<int, int>> slots;
     for (int b = 0; b < batch; ++b) {

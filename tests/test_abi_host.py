@@ -143,7 +143,14 @@ def test_argument_errors_before_launch(kv):
     assert P(h32, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o3), None) == kv.KV_ERR_UNSUPPORTED
     # balanced schedule without its workspace
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o3), None) == kv.KV_ERR_WORKSPACE
+    # a table too wide for max_blocks * 16 tokens in 32 bits
+    wide = 2**31 // 16
+    assert A(h, FAKE, FAKE, FAKE, wide, FAKE, None, 2, None) == kv.KV_ERR_INVALID_ARG
+    assert P(h, FAKE, FAKE, 4, 0.125, FAKE, wide, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) \
+        == kv.KV_ERR_INVALID_ARG
+    assert kv.raw["kv_validate_tables"](ctypes.byref(desc), FAKE, wide, FAKE, 2, 0, None) == kv.KV_ERR_INVALID_ARG
     R = kv.raw["rope_rerotate"]
+    assert R(h, FAKE, 2**31 - 8, 10, 5, 10000.0, 0, None) == kv.KV_ERR_INVALID_ARG   # last position past 2^31 - 1
     assert R(h, FAKE, 0, 10, 5, 10000.0, 2, None) == kv.KV_ERR_INVALID_ARG
     assert R(h, FAKE, 0, 10, 5, -1.0, 0, None) == kv.KV_ERR_INVALID_ARG
     assert R(h, None, 0, 10, 5, 10000.0, 0, None) == kv.KV_ERR_INVALID_ARG
