@@ -572,18 +572,55 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     }
 }
 
+// Block ids [j0, j1) of one sequence's table row (at most kSidsWindow of
+// them), staged in LDS before a piece's tile loop. A segment longer than that
+// runs as several pieces that carry the softmax state (run_pieces), so a
+// workgroup's dynamic LDS holds at most kSidsWindow ids however long its
+// segments are. Ids are not range-checked here.
+constexpr int kSidsWindow = 256;
+struct BlockIds {
+    int *sids;
+    const int32_t *row;  // the sequence's table row
+    int j0;
+    __device__ __forceinline__ int id(int j) const { return __builtin_amdgcn_readfirstlane(sids[j - j0]); }
+};
+__device__ __forceinline__ BlockIds stage_block_ids(const AttnParams &p, int b, int j0, int j1, int lane,
+                                                    int *sids) {
+    BlockIds ids;
+    ids.sids = sids;
+    ids.row = p.tables + (size_t)b * p.max_blocks;
+    ids.j0 = j0;
+    __syncthreads();  // earlier reads of sids are done
+    for (int i = lane; i < j1 - j0; i += 64) sids[i] = ids.row[j0 + i];
+    __syncthreads();
+    return ids;
+}
+
+// Runs seg(c0, c1, init) over [j0, j1) in pieces of at most kSidsWindow
+// blocks; init is true for the first piece only (it resets the softmax
+// state, the others continue it). An empty range still makes one call.
+template <class Seg>
+__device__ __forceinline__ void run_pieces(int j0, int j1, Seg seg) {
+    for (int c0 = j0;; c0 += kSidsWindow) {
+        const int c1 = min(j1, c0 + kSidsWindow);
+        seg(c0, c1, c0 == j0);
+        if (c1 >= j1) break;
+    }
+}
+
 // One lane's run of the online softmax over blocks [j0, j1) of sequence b,
-// kv head kvh. On return st.l is still the lane's partial sum (the caller
+// kv head kvh (at most kSidsWindow blocks; init: start a new state, else
+// continue st). On return st.l is still the lane's partial sum (the caller
 // adds the 4 token quads).
 //
 // Every tile iteration issues the same vector-memory loads and nothing else:
-// the segment's block ids are staged in LDS (sids, at least j1 - j0 entries)
-// before the loop and the fused append's rows are written before it, so the
-// waits inside the loop cover exactly the tile's own loads.
+// the piece's block ids are staged in LDS before the loop and the fused
+// append's rows are written before it, so the waits inside the loop cover
+// exactly the tile's own loads.
 template <int D>
 __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const Column &col,
                                              const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st,
-                                             bool &bad, bool write_new, int *sids) {
+                                             bool &bad, bool write_new, int *sids, bool init) {
     constexpr int KS = D / 32, MS = D / 16;
     const int n16 = lane & 15, G = lane >> 4;
     // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of its column.
@@ -595,18 +632,18 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
             v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + col.row * D + s * 32 + 8 * G);
         qB[s] = __builtin_bit_cast(bf16x8_t, v);
     }
+    if (init) {
 #pragma unroll
-    for (int m = 0; m < MS; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    st.m = -INFINITY;
-    st.l = 0.0f;
-    st.bv = 0.0f;
+        for (int m = 0; m < MS; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        st.m = -INFINITY;
+        st.l = 0.0f;
+        st.bv = 0.0f;
+    }
     if (j0 >= j1) return;
 
-    __syncthreads();  // the previous segment's reads of sids are done
-    for (int i = lane; i < j1 - j0; i += 64) sids[i] = p.tables[(size_t)b * p.max_blocks + j0 + i];
-    __syncthreads();
+    const BlockIds ids = stage_block_ids(p, b, j0, j1, lane, sids);
     auto pid_of = [&](int j) {
-        int pid = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+        int pid = ids.id(j);
         if (pid < 0 || pid >= p.num_blocks) {
             bad = true;
             pid = 0;
@@ -618,7 +655,7 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
     const int L0 = p.k_new ? r.n - p.ctx_add : INT_MAX;
     if (write_new && L0 != INT_MAX) {
         for (int j = max(j0, L0 / kBlock); j < j1; ++j) {
-            const int id = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+            const int id = ids.id(j);
             if (id >= 0 && id < p.num_blocks) store_new_rows<D>(p, b, kvh, id, L0 - j * kBlock, lane);
         }
     }
@@ -936,10 +973,12 @@ __device__ __forceinline__ void q4_append_token(const AttnParams &p, int b, int 
     }
 }
 
+// Blocks [j0, j1) (at most kSidsWindow) of sequence b, kv head kvh, column
+// tile ct; init: start a new state, else continue st.
 template <int D, int NP>
 __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
-                                           int *sids) {
+                                           int *sids, bool init) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
     int slot = uniform(p.seq_slots ? p.seq_slots[b] : b);
@@ -964,15 +1003,16 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
             Q.q[pi][2 * k + 1] = bf16_hi(w[k]);
         }
     }
+    if (init) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    st.m = -INFINITY;
-    st.l = 0.0f;
-    st.bv = 0.0f;
+        for (int m = 0; m < 8; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        st.m = -INFINITY;
+        st.l = 0.0f;
+        st.bv = 0.0f;
+    }
     if (j0 >= j1) return;
     __shared__ Q4Lds L;
-    __syncthreads();  // the previous segment's reads of sids and L are done
-    for (int i = lane; i < j1 - j0; i += 64) sids[i] = p.tables[(size_t)b * p.max_blocks + j0 + i];
+    __syncthreads();  // the previous segment's reads of L are done
     // columns past the passes are never written: zero B rows (padded columns)
     for (int i = lane; i < (16 - 4 * Q.npass) * 17; i += 64) {
         const int c = 4 * Q.npass + i / 17, k = i % 17;
@@ -980,9 +1020,9 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         L.b[1][c][k] = make_uint4(0, 0, 0, 0);
         if (k < 16) L.corr[c][k] = 0.0f;
     }
-    __syncthreads();
+    const BlockIds ids = stage_block_ids(p, b, j0, j1, lane, sids);  // its barriers also cover the zeroing
     auto pid_of = [&](int j) {
-        int pid = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+        int pid = ids.id(j);
         if (pid < 0 || pid >= p.num_blocks) {
             bad = true;
             pid = 0;
@@ -1011,7 +1051,8 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     Q4Tile A, B;
     if (!append || j0 < j1 - 1) fetch(j0, A);
     if (append) {
-        const int pid = pid_of(j1 - 1);
+        const int pid = ids.id(j1 - 1);
+        if (pid < 0 || pid >= p.num_blocks) bad = true;
         if (!bad) q4_append_token(p, b, kvh, slot, pid, (r.n - 1) % kBlock, lane);
         appended = true;
         if (j0 == j1 - 1) fetch(j0, A);
@@ -1033,9 +1074,13 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
                                             int *sids) {
     if constexpr (Q4 > 0)
-        q4_segment<D, Q4>(p, b, kvh, ct, col, r, j0, j1, lane, st, bad, sids);
+        run_pieces(j0, j1, [&](int c0, int c1, bool init) {
+            q4_segment<D, Q4>(p, b, kvh, ct, col, r, c0, c1, lane, st, bad, sids, init);
+        });
     else
-        bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, ct == 0, sids);
+        run_pieces(j0, j1, [&](int c0, int c1, bool init) {
+            bf16_segment<D>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct == 0, sids, init);
+        });
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
@@ -1045,7 +1090,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 
 template <int D, int Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
-    extern __shared__ int sids[];  // [split_blocks] block ids of the segment
+    extern __shared__ int sids[];  // [min(split_blocks, kSidsWindow)] staged block ids
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int split = blockIdx.x, unit = blockIdx.y, b = blockIdx.z;
     const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
@@ -1098,7 +1143,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
 
 template <int D, int Q4>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
-    extern __shared__ int pre[];  // [batch + 1] block prefix sums, then [split_blocks] block ids of a segment
+    extern __shared__ int pre[];  // [batch + 1] block prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
@@ -1226,7 +1271,7 @@ __device__ __forceinline__ void store_partial(const AttnParams &p, size_t row, i
 
 template <int D>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(AttnParams p, PrefixArgs g) {
-    extern __shared__ int sids[];  // [split_blocks] block ids of the work item
+    extern __shared__ int sids[];  // [min(split_blocks, kSidsWindow)] staged block ids
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int n_pref = g.n_groups * g.units_p * g.max_chunks;
     const int item = blockIdx.x;
@@ -1254,7 +1299,9 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(Attn
         r.nsplit = w.nchunk;
         r.bad = false;
         bool bad = false;  // a bad block id in the shared table
-        bf16_segment<D>(p, first, kvh, col, r, j0, j1, lane, st, bad, false, sids);
+        run_pieces(j0, j1, [&](int c0, int c1, bool init) {
+            bf16_segment<D>(p, first, kvh, col, r, c0, c1, lane, st, bad, false, sids, init);
+        });
         const float l = col_sum(st.l);
         if (col.valid) {
             float res[D / 4];
@@ -1293,7 +1340,9 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(Attn
     }
     const int j0 = P + split * p.split_blocks, j1 = min(w.blk_hi, j0 + p.split_blocks);
     bool bad = w.bad;
-    bf16_segment<D>(p, b, kvh, col, r, j0, j1, lane, st, bad, false, sids);
+    run_pieces(j0, j1, [&](int c0, int c1, bool init) {
+        bf16_segment<D>(p, b, kvh, col, r, c0, c1, lane, st, bad, false, sids, init);
+    });
     const float l = col_sum(st.l);
     if (col.valid) {
         float res[D / 4];
@@ -1483,7 +1532,7 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
     if (kernel == 2) {
         const bool q4 = dtype == KV_INT4;
         if (p.schedule == KV_SCHED_BALANCED) {
-            const uint32_t lds = (uint32_t)((p.batch + 1 + p.split_blocks) * sizeof(int));
+            const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
             if (q4 && p.ncols <= 4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
@@ -1494,7 +1543,7 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
             else
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0>), bg, dim3(64), lds, s, e0, e1, 0, p);
         } else {
-            const uint32_t lds = (uint32_t)(p.split_blocks * sizeof(int));
+            const uint32_t lds = (uint32_t)(min(p.split_blocks, kSidsWindow) * sizeof(int));
             if (q4 && p.ncols <= 4)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
@@ -1515,7 +1564,7 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     // compute units x resident workgroups per compute unit; 256 x 2 when the
     // runtime cannot tell (no device: only the size of a workspace is asked)
     int dev = 0, cus = 0, per_cu = 0;
-    const size_t lds = (size_t)(batch + 1 + max_blocks) * sizeof(int);
+    const size_t lds = (size_t)(batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 256 * 2;
@@ -1550,7 +1599,7 @@ hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hip
                                    hipEvent_t e1, hipEvent_t e_end) {
     if (p.batch == 0) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
     const long items = (long)g.n_groups * g.units_p * g.max_chunks + (long)p.batch * p.units * g.suffix_splits;
-    const uint32_t lds = (uint32_t)(p.split_blocks * sizeof(int));
+    const uint32_t lds = (uint32_t)(min(p.split_blocks, kSidsWindow) * sizeof(int));
     if (p.head_dim == 64)
         hipExtLaunchKernelGGL((attn_mfma_shared_kernel<64>), dim3((uint32_t)items), dim3(64), lds, s, e0, e1, 0, p, g);
     else

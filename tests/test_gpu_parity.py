@@ -201,6 +201,38 @@ def test_rising_scores(n_h, amp, dtype, split):
     assert max_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("schedule,split", [(0, 0), (1, 70000), (1, 300)])
+def test_million_token_context(schedule, split):
+    """A 1,000,000-token sequence beside a short one (bf16, MFMA): the
+    balanced schedule, one split over the whole sequence (62,500 blocks, far
+    more block ids than a workgroup stages at once) and 300-block splits."""
+    lens = [1_000_000, 5000]
+    c = wl.make_case(901, len(lens), lens, 8, 1, 64, "bf16", append=False, device=DEV)
+    pool = new_pool(c)
+    out = gpu_attention(pool, c, kernel=2, split_blocks=split, schedule=schedule)
+    ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref) <= TOL
+
+
+def test_int4_long_context():
+    """INT4 over 300,000 tokens in one split (18,750 blocks) and balanced."""
+    lens = [300_000, 33]
+    c = wl.make_case(902, len(lens), lens, 8, 1, 128, "bf16", append=False, device=DEV, outliers=4)
+    slots = torch.arange(len(lens), dtype=torch.int32, device=DEV)
+    src, dst, img = int4_pools(c, len(lens))
+    kv.kv_quantize_int4(dst, src, c.tables, c.ctx_lens, slots)
+    tab, ctx, sl = c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), slots.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, ctx, sl)
+    assert_img_equal(dst, img)
+    Kd, Vd = orc.q4_dequant(img, tab, ctx, sl)
+    ref = orc.attention(Kd, Vd, bits(c.q), tab, ctx, c.scale)
+    for schedule, split in [(0, 0), (1, 20000)]:
+        out = gpu_attention(dst, c, kernel=2, split_blocks=split, schedule=schedule, seq_slots=slots)
+        assert np.all(np.isfinite(out))
+        assert max_err(out, ref) <= TOL
+
+
 @pytest.mark.parametrize("kernel,split", [(1, 2), (2, 2), (2, 0)])
 def test_permutation_and_repeat_are_bit_identical(kernel, split):
     c = wl.make_case(300, 4, [70, 15, 128, 99], 16, 4, 128, "bf16", num_blocks=40, append=False, device=DEV)
@@ -376,6 +408,18 @@ def test_shared_prefix_parity(case, split):
     c = shared_case(60 + case, lens, n_h, n_kv, d, groups)
     pool = new_pool(c)
     out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=split)
+    ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
+    assert max_err(out, ref) <= TOL
+
+
+def test_shared_prefix_items_longer_than_the_id_window():
+    """Prefix chunks and suffix splits of 400-1000 blocks: the kernels stage
+    their block ids in windows of 256 and restage inside the item."""
+    lens = [20000, 16000, 9000]
+    groups = ([0, 3], [400])
+    c = shared_case(75, lens, 8, 2, 128, groups)
+    pool = new_pool(c)
+    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=1000)
     ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
     assert max_err(out, ref) <= TOL
 
