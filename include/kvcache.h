@@ -32,6 +32,10 @@
  *     kv_validate_tables checks host copies of the same arrays.
  *   - Table widths: max_blocks lies in [1, INT32_MAX / 16] (so max_blocks * 16
  *     tokens fit in 32 bits); other values are KV_ERR_INVALID_ARG.
+ *   - Launch-grid limits: batch, num_kv_heads and the attention's work units
+ *     per sequence (num_kv_heads * ceil(query columns / 16)) are at most
+ *     65535; a call above them returns KV_ERR_UNSUPPORTED (a descriptor with
+ *     more kv heads is KV_ERR_INVALID_ARG).
  */
 #ifndef KVCACHE_H
 #define KVCACHE_H

@@ -27,12 +27,16 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kNone = (size_t)-1;
+// Largest batch, kv-head count and work units per sequence: launch grids put
+// them in the y or z dimension (at most 65535 workgroups).
+constexpr int kMaxGridYZ = 65535;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool desc_ok(const kv_pool_desc *d) {
     if (!d) return false;
     if (d->num_blocks < 1 || d->block_size != KV_BLOCK_TOKENS || d->num_kv_heads < 1) return false;
+    if (d->num_kv_heads > kMaxGridYZ) return false;
     if (d->head_dim != 64 && d->head_dim != 128) return false;
     if (d->dtype != KV_F32 && d->dtype != KV_BF16 && d->dtype != KV_INT4) return false;
     if (d->dtype == KV_INT4 && d->max_seqs < 1) return false;
@@ -117,6 +121,7 @@ constexpr int kMaxBalancedBatch = 8192;
 kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
                     const kv_attn_opts *opts, AttnGeom *g) {
     if (batch < 0 || n_h < 1 || max_ctx < 0 || q_len < 1) return KV_ERR_INVALID_ARG;
+    if (batch > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
     const int n_kv = pool->desc.num_kv_heads;
     const int dtype = pool->desc.dtype;
     if (n_h % n_kv) return KV_ERR_INVALID_ARG;
@@ -132,8 +137,10 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
     // the VALU kernel serves one query token and groups of up to 16 heads; the
     // MFMA kernels tile any number of query columns (group * q_len) by 16
     if (kernel == 1 && (q_len > 1 || group > kMaxGroup)) return KV_ERR_UNSUPPORTED;
+    if ((int64_t)group * q_len > INT32_MAX - 15) return KV_ERR_UNSUPPORTED;
     g->ncols = group * q_len;
     g->ctiles = (g->ncols + 15) / 16;
+    if ((int64_t)n_kv * g->ctiles > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
     g->units = kernel == 2 ? n_kv * g->ctiles : n_kv;
     int sb = opts ? opts->split_blocks : 0;
     int sched = opts ? opts->schedule : 0;
@@ -201,6 +208,7 @@ struct SharedGeom {
 kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx,
                       const kv_prefix_groups *groups, const kv_attn_opts *opts, SharedGeom *g, PrefixArgs *pa) {
     if (batch < 0 || n_h < 1 || max_ctx < 0 || !groups) return KV_ERR_INVALID_ARG;
+    if (batch > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
     const int n_kv = pool->desc.num_kv_heads;
     if (n_h % n_kv) return KV_ERR_INVALID_ARG;
     if (opts && (opts->kernel < 0 || opts->kernel > 2 || opts->schedule < 0 || opts->schedule > 2 ||
@@ -251,6 +259,9 @@ kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t m
     pa->max_chunks = std::max(1, (max_prefix + sb - 1) / sb);
     pa->suffix_splits = (nblk + sb - 1) / sb;
     g->max_splits = pa->max_chunks + pa->suffix_splits;
+    // one flat grid over the prefix and suffix work items
+    const int64_t items = (int64_t)ng * pa->units_p * pa->max_chunks + (int64_t)batch * g->units * pa->suffix_splits;
+    if (items > INT32_MAX) return KV_ERR_UNSUPPORTED;
     const size_t D = pool->desc.head_dim;
     const size_t rows = (size_t)batch * n_h * g->max_splits;
     g->off_ml = align_up(rows * D * sizeof(float));
@@ -330,6 +341,7 @@ kv_status kv_append_tokens(kv_pool_t pool, const void *k_new, const void *v_new,
                            int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
                            int32_t n_new, void *stream) {
     if (!pool || batch < 0 || !max_blocks_ok(max_blocks) || n_new < 1) return KV_ERR_INVALID_ARG;
+    if (batch > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
     if (batch == 0) return KV_OK;
     if (!k_new || !v_new || !block_tables || !seq_lens) return KV_ERR_INVALID_ARG;
     if (!aligned16(k_new) || !aligned16(v_new)) return KV_ERR_INVALID_ARG;
@@ -543,6 +555,7 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
 kv_status kv_quantize_int4(kv_pool_t dst, kv_pool_t src, const int32_t *block_tables, int32_t max_blocks,
                            const int32_t *lens, const int32_t *seq_slots, int32_t batch, void *stream) {
     if (!dst || !src || batch < 0 || !max_blocks_ok(max_blocks)) return KV_ERR_INVALID_ARG;
+    if (batch > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
     if (dst->desc.dtype != KV_INT4 || src->desc.dtype != KV_BF16) return KV_ERR_INVALID_ARG;
     if (dst->desc.num_blocks != src->desc.num_blocks || dst->desc.num_kv_heads != src->desc.num_kv_heads ||
         dst->desc.head_dim != src->desc.head_dim)

@@ -149,6 +149,16 @@ def test_argument_errors_before_launch(kv):
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, wide, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) \
         == kv.KV_ERR_INVALID_ARG
     assert kv.raw["kv_validate_tables"](ctypes.byref(desc), FAKE, wide, FAKE, 2, 0, None) == kv.KV_ERR_INVALID_ARG
+    # launch-grid limits: batch and work units per sequence at most 65535
+    assert A(h, FAKE, FAKE, FAKE, 4, FAKE, None, 65536, None) == kv.KV_ERR_UNSUPPORTED
+    assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 65536, 50, None, 0, ctypes.byref(o), None) \
+        == kv.KV_ERR_UNSUPPORTED
+    # 2 kv heads x 16384 query tokens x group 4 = 2 x 4096 column tiles: fine; x 16 more is not
+    assert M(h, FAKE, FAKE, 4, 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
+        == kv.KV_ERR_WORKSPACE
+    assert M(h, FAKE, FAKE, 4, 16 * 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
+        == kv.KV_ERR_UNSUPPORTED
+    assert kv.kv_pool_required_bytes(kv.make_desc(16, 65536, 64, "bf16")) == 0
     R = kv.raw["rope_rerotate"]
     assert R(h, FAKE, 2**31 - 8, 10, 5, 10000.0, 0, None) == kv.KV_ERR_INVALID_ARG   # last position past 2^31 - 1
     assert R(h, FAKE, 0, 10, 5, 10000.0, 2, None) == kv.KV_ERR_INVALID_ARG
