@@ -198,11 +198,15 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
 }
 
 
-// Geometry of paged_decode_attention_shared: blocks per work item, the
-// prefix group record the kernels get by value, and the workspace.
+// Geometry of paged_decode_attention_shared: the schedule, blocks per work
+// item (split schedule), the prefix group record the kernels get by value,
+// and the workspace.
 struct SharedGeom {
     int split_blocks, max_splits, ncols, ctiles, units;
+    int schedule;      // KV_SCHED_SPLIT or KV_SCHED_BALANCED
+    int n_wg;          // balanced: persistent grid
     size_t ws_bytes, off_ml;
+    size_t off_plan;   // balanced: the plan's prefix sums (int32)
 };
 
 kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t max_ctx,
@@ -215,8 +219,7 @@ kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t m
                  opts->window < 0 || opts->split_blocks < 0))
         return KV_ERR_INVALID_ARG;
     if (pool->desc.dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
-    if (opts && (opts->kernel == 1 || opts->window > 0 || opts->schedule == KV_SCHED_BALANCED))
-        return KV_ERR_UNSUPPORTED;
+    if (opts && (opts->kernel == 1 || opts->window > 0)) return KV_ERR_UNSUPPORTED;
     const int ng = groups->n_groups;
     if (ng < 0 || ng > KV_MAX_PREFIX_GROUPS) return KV_ERR_INVALID_ARG;
     if (ng > 0 && (!groups->group_start || !groups->prefix_blocks)) return KV_ERR_INVALID_ARG;
@@ -226,6 +229,7 @@ kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t m
     pa->n_groups = ng;
     int max_members = 0, max_prefix = 0;
     long prefix_tiles = 0, member_prefix = 0;  // shared tile loads; prefix blocks summed over members
+    int64_t n_pseg = 0;                          // balanced: prefix segments (group, kv head, column tile)
     for (int i = 0; i < ng; ++i) {
         const int a = groups->group_start[i], b = groups->group_start[i + 1], P = groups->prefix_blocks[i];
         if (a < 0 || b < a || b > batch || (i > 0 && a < groups->group_start[i - 1]) || P < 0 || P > nblk)
@@ -235,12 +239,37 @@ kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t m
         max_members = std::max(max_members, b - a);
         max_prefix = std::max(max_prefix, P);
         member_prefix += (long)P * (b - a);
-        prefix_tiles += (long)P * (((long)(b - a) * group + 15) / 16);
+        const long ct = ((long)(b - a) * group + 15) / 16;
+        prefix_tiles += (long)P * ct;
+        if (P > 0) n_pseg += (int64_t)n_kv * ct;
     }
     if (ng > 0) pa->start[ng] = groups->group_start[ng];
     g->ncols = group;
     g->ctiles = (group + 15) / 16;
     g->units = n_kv * g->ctiles;
+    const size_t D = pool->desc.head_dim;
+    // Balanced schedule (the default): every tile numbered, equal contiguous
+    // shares of one persistent grid; its tile numbers are 32-bit
+    const int64_t bal_tiles = (int64_t)n_kv * prefix_tiles + (int64_t)g->units * batch * nblk;
+    const bool bal_ok = batch <= kMaxBalancedBatch && bal_tiles <= INT32_MAX;
+    int sched = opts ? opts->schedule : 0;
+    if (sched == KV_SCHED_AUTO)
+        sched = ((opts ? opts->split_blocks : 0) == 0 && bal_ok) ? KV_SCHED_BALANCED : KV_SCHED_SPLIT;
+    if (sched == KV_SCHED_BALANCED && !bal_ok) return KV_ERR_UNSUPPORTED;
+    g->schedule = sched;
+    g->n_wg = 0;
+    g->off_plan = 0;
+    if (sched == KV_SCHED_BALANCED) {
+        g->split_blocks = nblk;  // the longest segment: sizes the staged block ids
+        g->max_splits = 1;
+        g->n_wg = shared_balanced_grid((int)D, shared_balanced_lds(ng, batch, nblk));
+        // slots of 16 rows: two per workgroup, then one per segment
+        const size_t rows = ((size_t)2 * g->n_wg + (size_t)n_pseg + (size_t)batch * g->units) * 16;
+        g->off_ml = align_up(rows * D * sizeof(float));
+        g->off_plan = g->off_ml + align_up(rows * 2 * sizeof(float));
+        g->ws_bytes = g->off_plan + align_up(((size_t)2 * (ng + 1) + batch + 1) * sizeof(int32_t));
+        return KV_OK;
+    }
     pa->ctiles_p = std::max(1, (max_members * group + 15) / 16);
     pa->units_p = n_kv * pa->ctiles_p;
     int sb = opts ? opts->split_blocks : 0;
@@ -262,7 +291,6 @@ kv_status shared_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t m
     // one flat grid over the prefix and suffix work items
     const int64_t items = (int64_t)ng * pa->units_p * pa->max_chunks + (int64_t)batch * g->units * pa->suffix_splits;
     if (items > INT32_MAX) return KV_ERR_UNSUPPORTED;
-    const size_t D = pool->desc.head_dim;
     const size_t rows = (size_t)batch * n_h * g->max_splits;
     g->off_ml = align_up(rows * D * sizeof(float));
     g->ws_bytes = g->off_ml + align_up(rows * 2 * sizeof(float));
@@ -527,7 +555,7 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
     char *ws = static_cast<char *>(workspace);
     a.ws_o = reinterpret_cast<float *>(ws);
     a.ws_ml = reinterpret_cast<float *>(ws + g.off_ml);
-    a.ws_prefix = nullptr;
+    a.ws_prefix = g.off_plan ? reinterpret_cast<int32_t *>(ws + g.off_plan) : nullptr;
     a.max_blocks = max_blocks;
     a.batch = batch;
     a.n_h = num_q_heads;
@@ -544,8 +572,8 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
     a.ctiles = g.ctiles;
     a.units = g.units;
     a.slot_cols = g.ncols < 16 ? g.ncols : 16;
-    a.schedule = KV_SCHED_SPLIT;
-    a.n_wg = 0;
+    a.schedule = g.schedule;
+    a.n_wg = g.n_wg;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     void *const *ev = opts ? opts->events : nullptr;
     auto evt = [&](int i) { return ev ? static_cast<hipEvent_t>(ev[i]) : nullptr; };

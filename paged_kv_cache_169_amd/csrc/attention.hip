@@ -1360,6 +1360,241 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(Attn
 }
 
 // ---------------------------------------------------------------------------
+// shared-prefix decode attention, balanced schedule
+//
+// Every tile of the call is numbered: the prefix tiles first (group, its
+// units, block), then the suffix tiles (sequence, unit, block of its own
+// part). Workgroup w of the persistent grid takes [w * per, (w+1) * per) and
+// walks it one segment (a group's unit over its prefix, or a sequence's unit
+// over its own blocks) at a time, as the balanced schedule does. A piece (a
+// segment's part inside one workgroup) leaves its partials in the segment's
+// own slot when the piece is the whole segment, else in the workgroup's slot
+// 0 (the piece starts the workgroup's range) or slot 1 (it ends it); a
+// sequence without a prefix whose suffix is one whole piece writes its output
+// directly. Workspace rows (16 columns each): the workgroups' slots
+// [n_wg][2], then one slot per segment (prefix segments, then suffix
+// segments [batch][units]). Workgroup 0 stores the plan's prefix sums for the
+// merge.
+// ---------------------------------------------------------------------------
+
+// Prefix sums of the call's tiles, in LDS: prefix tiles and prefix segments
+// before group i, own blocks before sequence b (per unit).
+struct SharedPlan {
+    int *gtile, *gseg, *stile;
+    int ng;
+};
+
+// Column tiles of group i's prefix units (0: no prefix or no member).
+__device__ __forceinline__ int group_ctiles(const AttnParams &p, const PrefixArgs &g, int i) {
+    const int m = g.start[i + 1] - g.start[i], P = g.blocks[i];
+    return (m > 0 && P > 0) ? (m * p.group + 15) / 16 : 0;
+}
+
+// Own (suffix) blocks of sequence b and its prefix blocks; bad as in
+// shared_row.
+__device__ __forceinline__ int own_blocks(const AttnParams &p, const PrefixArgs &g, int b, int *P_out,
+                                          bool *bad_out) {
+    const int gi = prefix_group_of(g, b);
+    const int P = gi < 0 ? 0 : g.blocks[gi];
+    const SharedRow w = shared_row(p, ctx_of(p, b), P);
+    *P_out = P;
+    *bad_out = w.bad;
+    return w.bad ? 0 : w.blk_hi - P;
+}
+
+// Inclusive scan over the wave.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ void shared_plan(const AttnParams &p, const PrefixArgs &g, const SharedPlan &pl,
+                                            int lane) {
+    if (lane == 0) {
+        pl.gtile[0] = 0;
+        pl.gseg[0] = 0;
+        pl.stile[0] = 0;
+    }
+    int ct = 0, cs = 0;
+    for (int base = 0; base < pl.ng; base += 64) {
+        const int i = base + lane;
+        int segs = 0, tiles = 0;
+        if (i < pl.ng) {
+            segs = p.n_kv * group_ctiles(p, g, i);
+            tiles = segs * g.blocks[i];
+        }
+        segs = wave_scan(segs, lane);
+        tiles = wave_scan(tiles, lane);
+        if (i < pl.ng) {
+            pl.gseg[i + 1] = cs + segs;
+            pl.gtile[i + 1] = ct + tiles;
+        }
+        cs += __shfl(segs, 63);
+        ct += __shfl(tiles, 63);
+    }
+    int cb = 0;
+    for (int base = 0; base < p.batch; base += 64) {
+        const int b = base + lane;
+        int nb = 0;
+        if (b < p.batch) {
+            int P;
+            bool bad;
+            nb = own_blocks(p, g, b, &P, &bad);
+        }
+        nb = wave_scan(nb, lane);
+        if (b < p.batch) pl.stile[b + 1] = cb + nb;
+        cb += __shfl(nb, 63);
+    }
+    __syncthreads();
+}
+
+// Workspace row of a piece's partial: the segment's own slot, or slot 0 / 1
+// of workgroup w, for segment tiles [a, a + len) and a range share `per`.
+__device__ __forceinline__ size_t shared_piece_row(const AttnParams &p, long a, int len, long per, int w,
+                                                   int seg, int n16) {
+    const long lo = max(a, (long)w * per), hi = min(a + len, (long)(w + 1) * per);
+    size_t slot;
+    if (lo == a && hi == a + len)
+        slot = (size_t)2 * p.n_wg + seg;
+    else
+        slot = (size_t)w * 2 + (lo == (long)w * per ? 0 : 1);
+    return slot * 16 + n16;
+}
+
+template <int D>
+__device__ __forceinline__ void store_piece(const AttnParams &p, size_t row, int G, const float *res, float m,
+                                            float l, bool bad) {
+    const float nan = __uint_as_float(0x7fc00000u);
+    float *dst = p.ws_o + row * D + G * (D / 4);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c];
+    if (G == 0) {
+        p.ws_ml[row * 2] = m;
+        p.ws_ml[row * 2 + 1] = bad ? nan : l;
+    }
+}
+
+// Largest i in [0, n) with v[i] <= t (v ascending, v[0] <= t).
+__device__ __forceinline__ int last_le(const int *v, int n, long t) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long)v[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_kernel(AttnParams p, PrefixArgs g) {
+    extern __shared__ int lds[];  // plan [ng + 1][2] + [batch + 1], then the staged block ids
+    SharedPlan pl;
+    pl.ng = g.n_groups;
+    pl.gtile = lds;
+    pl.gseg = lds + pl.ng + 1;
+    pl.stile = lds + 2 * (pl.ng + 1);
+    int *sids = pl.stile + p.batch + 1;
+    const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
+    const int wg = blockIdx.x;
+    shared_plan(p, g, pl, lane);
+    if (wg == 0) {
+        for (int i = lane; i < 2 * (pl.ng + 1) + p.batch + 1; i += 64) p.ws_prefix[i] = lds[i];
+    }
+    const long tp = pl.gtile[pl.ng];  // prefix tiles
+    const long total = tp + (long)pl.stile[p.batch] * p.units;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long s = (long)wg * per;
+    const long e = min(total, s + per);
+    for (long t = s; t < e;) {
+        MfmaState<D> st;
+        long seg_end;
+        if (t < tp) {
+            // prefix segment: group gi, unit (kvh, ct) over its P shared blocks
+            const int gi = last_le(pl.gtile, pl.ng + 1, t);
+            const int P = g.blocks[gi], first = g.start[gi], members = g.start[gi + 1] - first;
+            const int cti = group_ctiles(p, g, gi);
+            const long a0 = pl.gtile[gi];
+            const int unit = (int)((t - a0) / P), jr = (int)(t - a0 - (long)unit * P);
+            const long a = a0 + (long)unit * P;
+            seg_end = min(e, a + P);
+            const int kvh = unit / cti, ct = unit % cti;
+            const int ci = ct * 16 + n16, k = ci / p.group, hq = ci % p.group;
+            Column col;
+            col.valid = k < members;
+            col.row = (size_t)(first + (col.valid ? k : 0)) * p.n_h + kvh * p.group + hq;
+            col.lo = 0;
+            col.hi = P * kBlock;
+            const SharedRow w = shared_row(p, col.valid ? ctx_of(p, first + k) : P * kBlock, P);
+            SeqRange r;  // the prefix: P full blocks, attended whole by every member
+            r.n = r.hi = r.all_hi = P * kBlock;
+            r.lo = r.all_lo = 0;
+            r.blk_lo = 0;
+            r.nblk = P;
+            r.nsplit = 1;
+            r.bad = false;
+            bool bad = false;  // a bad block id in the shared table
+            run_pieces(jr, jr + (int)(seg_end - t), [&](int c0, int c1, bool init) {
+                bf16_segment<D>(p, first, kvh, col, r, c0, c1, lane, st, bad, false, sids, init);
+            });
+            const float l = col_sum(st.l);
+            if (col.valid) {
+                float res[D / 4];
+                mfma_gather_run<D>(st, 0.0f, res);
+                const size_t row = shared_piece_row(p, a, P, per, wg, pl.gseg[gi] + unit, n16);
+                store_piece<D>(p, row, G, res, st.m, l, bad || w.bad);
+            }
+        } else {
+            // suffix segment: sequence b, unit (kvh, ct) over its own blocks
+            const long u = t - tp;
+            const int b = last_le(pl.stile, p.batch + 1, u / p.units);
+            const int nb = pl.stile[b + 1] - pl.stile[b];
+            const long a0 = (long)pl.stile[b] * p.units;
+            const int unit = (int)((u - a0) / nb), jr = (int)(u - a0 - (long)unit * nb);
+            const long a = tp + a0 + (long)unit * nb;
+            seg_end = min(e, a + nb);
+            const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
+            int P;
+            bool bad;
+            own_blocks(p, g, b, &P, &bad);
+            const int n = uniform(ctx_of(p, b));
+            SeqRange r;
+            r.n = r.hi = r.all_hi = n;
+            r.lo = r.all_lo = 0;
+            r.blk_lo = 0;
+            r.nblk = P + nb;
+            r.nsplit = 1;
+            r.bad = false;
+            const Column col = column_of(p, b, kvh, ct, n16, r);
+            run_pieces(P + jr, P + jr + (int)(seg_end - t), [&](int c0, int c1, bool init) {
+                bf16_segment<D>(p, b, kvh, col, r, c0, c1, lane, st, bad, false, sids, init);
+            });
+            const float l = col_sum(st.l);
+            if (col.valid) {
+                float res[D / 4];
+                mfma_gather_run<D>(st, 0.0f, res);
+                if (P == 0 && jr == 0 && seg_end - t == nb) {  // the row's only part: the output itself
+                    const float nan = __uint_as_float(0x7fc00000u);
+                    float *dst = p.out + col.row * D + G * (D / 4);
+                    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+                    for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
+                } else {
+                    const int seg = pl.gseg[pl.ng] + b * p.units + unit;
+                    store_piece<D>(p, shared_piece_row(p, a, nb, per, wg, seg, n16), G, res, st.m, l, bad);
+                }
+            }
+        }
+        t = seg_end;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // merge of split partials
 // ---------------------------------------------------------------------------
 
@@ -1498,6 +1733,56 @@ __global__ __launch_bounds__(64) void attn_merge_shared_kernel(AttnParams p, Pre
     merge_partials(p, total, [&](int s) { return base + s; }, lane, cv, dst);
 }
 
+// Merge of the balanced shared-prefix call: one wave per (sequence, head)
+// row. Finds the pieces of the row's prefix segment and of its own (suffix)
+// segment from the plan the attention kernel stored, and combines their
+// partials; a sequence that is bad or shorter than its prefix gets NaN, one
+// with no token 0.
+__global__ __launch_bounds__(64) void attn_merge_shared_balanced_kernel(AttnParams p, PrefixArgs g) {
+    const int b = blockIdx.y, lane = threadIdx.x, head = blockIdx.x;
+    const int ng = g.n_groups;
+    const int *gtile = p.ws_prefix, *gseg = gtile + ng + 1, *stile = gseg + ng + 1;
+    const size_t row = (size_t)b * p.n_h + head;
+    const int cv = p.head_dim / 64;
+    float *dst = p.out + row * p.head_dim + lane * cv;
+    const int kvh = head / p.group, hq = head % p.group;
+    int P;
+    bool bad;
+    const int nb = own_blocks(p, g, b, &P, &bad);
+    if (bad || (P == 0 && nb == 0)) {
+        const float v = bad ? __uint_as_float(0x7fc00000u) : 0.0f;
+        for (int c = 0; c < cv; ++c) dst[c] = v;
+        return;
+    }
+    const long tp = gtile[ng];
+    const long total = tp + (long)stile[p.batch] * p.units;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    // prefix segment of the row: group gi, column k * group + hq
+    long pa = 0;
+    int pseg = 0, pw0 = 0, npre = 0, pn16 = 0;
+    if (P > 0) {
+        const int gi = prefix_group_of(g, b);
+        const int ci = (b - g.start[gi]) * p.group + hq, cti = group_ctiles(p, g, gi);
+        const int unit = kvh * cti + ci / 16;
+        pn16 = ci % 16;
+        pa = gtile[gi] + (long)unit * P;
+        pseg = gseg[gi] + unit;
+        pw0 = (int)(pa / per);
+        npre = (int)((pa + P - 1) / per) - pw0 + 1;
+    }
+    // own segment of the row
+    const int unit = kvh * p.ctiles + hq / 16, sn16 = hq % 16;
+    const long sa = tp + (long)stile[b] * p.units + (long)unit * nb;
+    const int sseg = gseg[ng] + b * p.units + unit;
+    const int sw0 = nb > 0 ? (int)(sa / per) : 0;
+    const int nsuf = nb > 0 ? (int)((sa + nb - 1) / per) - sw0 + 1 : 0;
+    if (P == 0 && nsuf == 1) return;  // written by the attention kernel
+    merge_partials(p, npre + nsuf, [&](int i) {
+        return i < npre ? shared_piece_row(p, pa, P, per, pw0 + i, pseg, pn16)
+                        : shared_piece_row(p, sa, nb, per, sw0 + i - npre, sseg, sn16);
+    }, lane, cv, dst);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -1583,6 +1868,24 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     return cus * per_cu;
 }
 
+size_t shared_balanced_lds(int n_groups, int batch, int max_blocks) {
+    return (size_t)(2 * (n_groups + 1) + batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
+}
+
+int shared_balanced_grid(int head_dim, size_t lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256 * 2;
+    const hipError_t e =
+        head_dim == 64
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_shared_balanced_kernel<64>, 64, lds)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_shared_balanced_kernel<128>, 64, lds);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 2;
+    if (per_cu > 8) per_cu = 8;  // two waves per SIMD, as balanced_grid
+    return cus * per_cu;
+}
+
 hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
     const bool none = p.batch == 0 || (p.schedule != KV_SCHED_BALANCED && p.max_splits <= 1);
     if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
@@ -1598,6 +1901,20 @@ hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
 hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hipStream_t s, hipEvent_t e0,
                                    hipEvent_t e1, hipEvent_t e_end) {
     if (p.batch == 0) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
+    if (p.schedule == KV_SCHED_BALANCED) {
+        const uint32_t lds = (uint32_t)shared_balanced_lds(g.n_groups, p.batch, p.split_blocks);
+        if (p.head_dim == 64)
+            hipExtLaunchKernelGGL((attn_mfma_shared_balanced_kernel<64>), dim3(p.n_wg), dim3(64), lds, s, e0, e1, 0,
+                                  p, g);
+        else
+            hipExtLaunchKernelGGL((attn_mfma_shared_balanced_kernel<128>), dim3(p.n_wg), dim3(64), lds, s, e0, e1, 0,
+                                  p, g);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipExtLaunchKernelGGL(attn_merge_shared_balanced_kernel, dim3(p.n_h, p.batch), dim3(64), 0, s, nullptr, e_end,
+                              0, p, g);
+        return hipGetLastError();
+    }
     const long items = (long)g.n_groups * g.units_p * g.max_chunks + (long)p.batch * p.units * g.suffix_splits;
     const uint32_t lds = (uint32_t)(min(p.split_blocks, kSidsWindow) * sizeof(int));
     if (p.head_dim == 64)

@@ -110,10 +110,12 @@ struct TopkParams {
 // Groups of sequences whose tables share a prefix of physical blocks
 // (paged_decode_attention_shared). Passed by value beside AttnParams.
 // Group i is sequences start[i] .. start[i+1]-1; their first blocks[i]
-// logical blocks name the same physical blocks. Work items of the shared
-// kernel: first the prefix items (group, unit, chunk), then the suffix items
-// (sequence, unit, split); partial slots of a row: the group's prefix chunks
-// first, then the sequence's suffix splits.
+// logical blocks name the same physical blocks. Split schedule: work items
+// of the shared kernel are first the prefix items (group, unit, chunk), then
+// the suffix items (sequence, unit, split); partial slots of a row: the
+// group's prefix chunks first, then the sequence's suffix splits. Balanced
+// schedule: only n_groups, start and blocks are used (the kernel plans the
+// rest itself).
 struct PrefixArgs {
     int32_t n_groups;
     int32_t units_p;      // prefix units per group: n_kv * column tiles of the largest group
@@ -141,6 +143,10 @@ hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hip
                                    hipEvent_t e1, hipEvent_t e_end);
 // Persistent grid of the balanced schedule: resident workgroups per device.
 int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
+// The balanced shared-prefix kernel: its dynamic LDS (max_blocks: the longest
+// segment in blocks) and its persistent grid for that LDS.
+size_t shared_balanced_lds(int n_groups, int batch, int max_blocks);
+int shared_balanced_grid(int head_dim, size_t lds);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 

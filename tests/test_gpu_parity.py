@@ -379,9 +379,9 @@ def shared_case(seed, lens, n_h, n_kv, d, groups):
     return c
 
 
-def gpu_shared(pool, c, group_start, prefix_blocks, split_blocks=0):
+def gpu_shared(pool, c, group_start, prefix_blocks, split_blocks=0, schedule=0):
     g = kv.prefix_groups(group_start, prefix_blocks)
-    opts = kv.attn_opts(split_blocks=split_blocks)
+    opts = kv.attn_opts(split_blocks=split_blocks, schedule=schedule)
     max_ctx = int(c.ctx_lens.max().item())
     nbytes = kv.paged_decode_attention_shared_workspace_bytes(pool, c.batch, c.n_h, max_ctx, g, opts)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
@@ -402,32 +402,35 @@ SHARED_CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(SHARED_CASES)))
-@pytest.mark.parametrize("split", [0, 1, 5])
-def test_shared_prefix_parity(case, split):
+@pytest.mark.parametrize("schedule,split", [(0, 0), (2, 0), (1, 0), (1, 1), (1, 5)])
+def test_shared_prefix_parity(case, schedule, split):
+    """Balanced (auto and explicit) and item schedules of the shared-prefix call."""
     lens, n_h, n_kv, d, groups = SHARED_CASES[case]
     c = shared_case(60 + case, lens, n_h, n_kv, d, groups)
     pool = new_pool(c)
-    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=split)
+    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=split, schedule=schedule)
     ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
     assert max_err(out, ref) <= TOL
 
 
-def test_shared_prefix_items_longer_than_the_id_window():
-    """Prefix chunks and suffix splits of 400-1000 blocks: the kernels stage
-    their block ids in windows of 256 and restage inside the item."""
+@pytest.mark.parametrize("schedule,split", [(1, 1000), (0, 0)])
+def test_shared_prefix_items_longer_than_the_id_window(schedule, split):
+    """Prefix and suffix segments of 400-850 blocks (items of 1000 blocks, or
+    the balanced shares): the kernels run them in pieces of 256 blocks."""
     lens = [20000, 16000, 9000]
     groups = ([0, 3], [400])
     c = shared_case(75, lens, 8, 2, 128, groups)
     pool = new_pool(c)
-    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=1000)
+    out = gpu_shared(pool, c, groups[0], groups[1], split_blocks=split, schedule=schedule)
     ref = orc.attention(bits(c.K), bits(c.V), bits(c.q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(), c.scale)
     assert max_err(out, ref) <= TOL
 
 
-def test_shared_prefix_member_shorter_than_prefix_is_nan():
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_shared_prefix_member_shorter_than_prefix_is_nan(schedule):
     c = shared_case(71, [300, 100, 250], 4, 2, 128, ([0, 2], [10]))   # member 1 has 100 < 160 prefix tokens
     pool = new_pool(c)
-    out = gpu_shared(pool, c, [0, 2], [10])
+    out = gpu_shared(pool, c, [0, 2], [10], schedule=schedule)
     assert np.isnan(out[1]).all()
     keep = [0, 2]
     ref = orc.attention(bits(c.K), bits(c.V), bits(c.q)[keep], c.tables.cpu().numpy()[keep],

@@ -176,10 +176,12 @@ def draw_shared(i):
                 split=r.choice([0, 1, 4, 9]))
 
 
+@pytest.mark.parametrize("schedule", [0, 1])
 @pytest.mark.parametrize("i", range(16))
-def test_random_shared_prefix(i):
+def test_random_shared_prefix(i, schedule):
+    """schedule 0: balanced unless the case fixes blocks per item; 1: items."""
     cfg = draw_shared(i)
-    print(f"random shared case {i}: {cfg}", flush=True)
+    print(f"random shared case {i} schedule {schedule}: {cfg}", flush=True)
     lens = cfg["lens"]
     c = wl.make_case(8000 + i, len(lens), lens, cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", append=False,
                      device=DEV)
@@ -192,7 +194,7 @@ def test_random_shared_prefix(i):
     pool.K.copy_(c.K)
     pool.V.copy_(c.V)
     g = kv.prefix_groups(cfg["starts"], cfg["prefix"])
-    opts = kv.attn_opts(split_blocks=cfg["split"])
+    opts = kv.attn_opts(split_blocks=cfg["split"], schedule=schedule)
     max_ctx = max(int(c.ctx_lens.max().item()), 1)
     nbytes = kv.paged_decode_attention_shared_workspace_bytes(pool, c.batch, c.n_h, max_ctx, g, opts)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
