@@ -259,10 +259,14 @@ size_t paged_decode_attention_shared_workspace_bytes(kv_pool_t pool, int32_t bat
  * A member attends its whole shared prefix and then its own blocks; a member
  * whose ctx_lens is below its prefix (prefix_blocks * 16 tokens) gets NaN.
  * bf16 pools only (MFMA kernel; opts->kernel 0 or 2), no window
- * (opts->window 0), fixed splits (opts->schedule 0 or KV_SCHED_SPLIT;
- * opts->split_blocks 0 lets the library choose the blocks per work item).
- * Other arguments as for paged_decode_attention. Errors: KV_ERR_UNSUPPORTED
- * for other pools or options, KV_ERR_INVALID_ARG for malformed groups. */
+ * (opts->window 0). Schedules: KV_SCHED_BALANCED (the default: every prefix
+ * tile of every group and every own tile of every sequence is numbered, and
+ * each workgroup of a persistent grid takes an equal contiguous share; up to
+ * 8192 sequences) or KV_SCHED_SPLIT (work items of opts->split_blocks prefix
+ * or own blocks, 0 = chosen by the library; a nonzero split_blocks selects it
+ * under KV_SCHED_AUTO). Other arguments as for paged_decode_attention.
+ * Errors: KV_ERR_UNSUPPORTED for other pools or options, KV_ERR_INVALID_ARG
+ * for malformed groups. */
 kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads,
                                         float scale, const int32_t *block_tables, int32_t max_blocks,
                                         const int32_t *ctx_lens, int32_t batch, int32_t max_ctx,
