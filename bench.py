@@ -311,7 +311,7 @@ def main():
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic_bytes = None
     if args.kernel == 0 and args.split == 0 and args.schedule == 0 and k == 1:  # the counters' configuration
-        traffic_bytes = profiled_traffic(name, "attn_mfma_shared" if shared else "attn_mfma_balanced")
+        traffic_bytes = profiled_traffic(name, "attn_mfma_shared_balanced" if shared else "attn_mfma_balanced")
     traffic = traffic_bytes / (split_avg * 1e-3) / 1e9 if traffic_bytes else None
     log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
         f"{split_avg*1e3:.1f} us, merge {merge_avg*1e3:.1f} us, {achieved:.0f} GB/s "
