@@ -117,6 +117,9 @@ struct AttnGeom {
 
 // Largest batch of the balanced schedule (its block prefix sums live in LDS).
 constexpr int kMaxBalancedBatch = 8192;
+// Balanced schedule: tiles' worth of time a (sequence, unit) pair costs on
+// top of its tiles (its block ids, query and first tile).
+constexpr int kSegCost = 1;
 
 kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
                     const kv_attn_opts *opts, AttnGeom *g) {
@@ -476,6 +479,7 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     a.slot_cols = g.ncols < 16 ? g.ncols : 16;
     a.schedule = g.schedule;
     a.n_wg = g.n_wg;
+    a.seg_cost = g.schedule == KV_SCHED_BALANCED ? kSegCost : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
     void *const *ev = opts ? opts->events : nullptr;

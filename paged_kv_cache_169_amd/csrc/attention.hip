@@ -1108,17 +1108,22 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
     }
 }
 
-// Balanced schedule. The attended (sequence, kv head, block) tiles are
-// numbered in sequence-major, kv-head, block order; workgroup w of the
-// persistent grid takes tiles [w * per, (w+1) * per), per = ceil(total /
-// grid). A workgroup walks its range one (sequence, kv head) segment at a
-// time; a segment that covers its whole pair writes the output directly.
-// Only a workgroup's first and last segments can be partial, so partials go
-// to slot 0 (first) or 1 (last) of the workgroup's two workspace slots and
-// attn_merge_balanced_kernel combines them. Workgroup 0 also stores the block
+// Balanced schedule. The attended (sequence, unit, block) tiles are laid out
+// in sequence-major, unit, block order on a cost axis where every (sequence,
+// unit) pair also takes seg_cost positions after its tiles: the start of a
+// segment (its block ids, query and first tile) costs about that many tiles
+// of time. Workgroup w of the persistent grid takes positions [w * per,
+// (w+1) * per), per = ceil(total / grid), and works the tiles among them.
+// A workgroup walks its range one pair at a time; a pair whose tiles all
+// fall in its range writes the output directly. Otherwise the piece leaves a
+// partial in slot 0 of the workgroup's two workspace slots when the pair
+// started before the range (only a workgroup's first piece can), else in
+// slot 1 (the pair goes on past the range: only its last piece can);
+// attn_merge_balanced_kernel combines them. Workgroup 0 also stores the
 // prefix sums for the merge.
 __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, int lane) {
-    // pre[b] = attended blocks of sequences < b, in LDS; returns pre[batch]
+    // pre[b] = positions of sequences < b per unit (attended blocks plus
+    // seg_cost for a sequence with any), in LDS; returns pre[batch]
     int carry = 0;
     if (lane == 0) pre[0] = 0;
     for (int base = 0; base < p.batch; base += 64) {
@@ -1126,7 +1131,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
         int nb = 0;
         if (b < p.batch) {
             const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
-            nb = r.nblk;
+            nb = r.nblk > 0 ? r.nblk + p.seg_cost : 0;
         }
         // inclusive wave scan
 #pragma unroll
@@ -1151,15 +1156,15 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     // search and everything derived from it are moved to scalar registers.
     // The bf16 path keeps them in vector registers (measured faster: the
     // scalar form runs out of scalar registers there).
-    const int nblk_total = Q4 ? uniform(balanced_prefix(p, pre, lane)) : balanced_prefix(p, pre, lane);
+    const int npos = Q4 ? uniform(balanced_prefix(p, pre, lane)) : balanced_prefix(p, pre, lane);
     if (wg == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
-    const long total = (long)nblk_total * p.units;
+    const long total = (long)npos * p.units;
     const long per = (total + p.n_wg - 1) / p.n_wg;
     const long s = (long)wg * per;
     const long e = min(total, s + per);
     for (long t = s; t < e;) {
-        // sequence holding tile t: largest b with units * pre[b] <= t
+        // sequence holding position t: largest b with units * pre[b] <= t
         auto pre_s = [&](int i) { return Q4 ? uniform(pre[i]) : pre[i]; };
         int lo = 0, hi = p.batch - 1;
         while (lo < hi) {
@@ -1171,12 +1176,18 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         }
         const int b = lo;
         const int pb = pre_s(b);
-        const int nb = pre_s(b + 1) - pb;
+        const int span = pre_s(b + 1) - pb;  // nb + seg_cost positions per unit
+        const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
-        const int unit = (int)((t - pair0) / nb);
+        const int unit = (int)((t - pair0) / span);
+        const long pair_t = pair0 + (long)unit * span;  // position of the pair's first tile
+        const int jr = (int)(t - pair_t);
+        if (jr >= nb) {  // in the pair's start cost: go on at the next pair
+            t = pair_t + span;
+            continue;
+        }
         const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
-        const int jr = (int)(t - pair0 - (long)unit * nb);
-        const long seg_end = min(e, pair0 + (long)(unit + 1) * nb);
+        const long seg_end = min(e, pair_t + nb);
         const int cnt = (int)(seg_end - t);
         const int ctx = ctx_of(p, b);
         const SeqRange r = seq_range(Q4 ? uniform(ctx) : ctx, p.max_blocks, p.window, p.split_blocks, p.max_splits,
@@ -1196,7 +1207,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 #pragma unroll
                 for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
             } else {
-                const int slot = t == s ? 0 : 1;
+                const int slot = jr > 0 ? 0 : 1;
                 const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + n16;
                 float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
@@ -1690,7 +1701,8 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     const int D = p.head_dim, cv = D / 64;
     const int kvh = head / p.group, ci = qi * p.group + head % p.group;
     const int unit = kvh * p.ctiles + ci / 16, n16 = ci % 16;
-    const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
+    const int span = p.ws_prefix[b + 1] - p.ws_prefix[b];  // nb + seg_cost, or 0
+    const int nb = span > 0 ? span - p.seg_cost : 0;
     float *dst = p.out + ((size_t)b * p.q_len * p.n_h + blockIdx.x) * D + lane * cv;
     if (nb == 0) {
         const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
@@ -1700,13 +1712,15 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     }
     const long total = (long)p.ws_prefix[p.batch] * p.units;
     const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * nb;
+    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
     const long end = start + nb;
     const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
     if (w0 == w1) return;  // complete inside one workgroup: already written
-    // workspace row of the partial that workgroup w holds for this pair
+    // workspace row of the partial that workgroup w holds for this pair: the
+    // first piece goes on past its range (slot 1), the others started before
+    // theirs (slot 0)
     auto ws_row = [&](int w) {
-        const int slot = (w == w0 && start > (long)w * per) ? 1 : 0;
+        const int slot = w == w0 ? 1 : 0;
         return ((size_t)w * 2 + slot) * p.slot_cols + n16;
     };
     merge_partials(p, w1 - w0 + 1, [&](int i) { return ws_row(w0 + i); }, lane, cv, dst);
