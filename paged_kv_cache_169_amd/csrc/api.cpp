@@ -105,7 +105,9 @@ struct AttnGeom {
     int kernel;        // 1 VALU, 2 MFMA
     int ncols;         // query columns per kv head
     int ctiles;        // 16-column tiles per kv head
+    int ctw;           // column tiles per work unit
     int units;         // work units per sequence
+    int slot_cols;     // balanced: rows of one workspace slot
     int schedule;      // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int split_blocks;
     int max_splits;
@@ -143,8 +145,13 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
     if ((int64_t)group * q_len > INT32_MAX - 15) return KV_ERR_UNSUPPORTED;
     g->ncols = group * q_len;
     g->ctiles = (g->ncols + 15) / 16;
-    if ((int64_t)n_kv * g->ctiles > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
-    g->units = kernel == 2 ? n_kv * g->ctiles : n_kv;
+    // the bf16 MFMA kernels take two column tiles per unit when there are
+    // several: each K/V tile is then read once per two column tiles
+    g->ctw = (kernel == 2 && dtype == KV_BF16 && g->ctiles > 1) ? 2 : 1;
+    const int cgroups = (g->ctiles + g->ctw - 1) / g->ctw;
+    if ((int64_t)n_kv * cgroups > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
+    g->units = kernel == 2 ? n_kv * cgroups : n_kv;
+    g->slot_cols = std::min(16 * g->ctw, g->ncols);
     int sb = opts ? opts->split_blocks : 0;
     int sched = opts ? opts->schedule : 0;
     if (sched == KV_SCHED_AUTO)
@@ -169,7 +176,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         g->split_blocks = nblk;
         g->max_splits = 1;
         g->n_wg = balanced_grid(dtype, (int)D, batch, nblk);
-        const size_t rows = (size_t)g->n_wg * 2 * (g->ncols < 16 ? g->ncols : 16);
+        const size_t rows = (size_t)g->n_wg * 2 * g->slot_cols;
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));
         g->ws_bytes = g->off_prefix + align_up(((size_t)batch + 1) * sizeof(int32_t));
@@ -475,8 +482,9 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     a.q_len = q_len;
     a.ncols = g.ncols;
     a.ctiles = g.ctiles;
+    a.ctw = g.ctw;
     a.units = g.units;
-    a.slot_cols = g.ncols < 16 ? g.ncols : 16;
+    a.slot_cols = g.slot_cols;
     a.schedule = g.schedule;
     a.n_wg = g.n_wg;
     a.seg_cost = g.schedule == KV_SCHED_BALANCED ? kSegCost : 0;
@@ -574,6 +582,7 @@ kv_status paged_decode_attention_shared(kv_pool_t pool, const void *q, float *ou
     a.q_len = 1;
     a.ncols = g.ncols;
     a.ctiles = g.ctiles;
+    a.ctw = 1;
     a.units = g.units;
     a.slot_cols = g.ncols < 16 ? g.ncols : 16;
     a.schedule = g.schedule;

@@ -610,34 +610,42 @@ __device__ __forceinline__ void run_pieces(int j0, int j1, Seg seg) {
 
 // One lane's run of the online softmax over blocks [j0, j1) of sequence b,
 // kv head kvh (at most kSidsWindow blocks; init: start a new state, else
-// continue st). On return st.l is still the lane's partial sum (the caller
-// adds the 4 token quads).
+// continue st), for CT column tiles at once (col[c], st[c]): each K/V tile is
+// loaded once and multiplied with every column tile's queries. On return
+// st[c].l is still the lane's partial sum (the caller adds the 4 token
+// quads).
 //
 // Every tile iteration issues the same vector-memory loads and nothing else:
 // the piece's block ids are staged in LDS before the loop and the fused
 // append's rows are written before it, so the waits inside the loop cover
 // exactly the tile's own loads.
-template <int D>
-__device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const Column &col,
-                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st,
-                                             bool &bad, bool write_new, int *sids, bool init) {
+template <int D, int CT>
+__device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int kvh, const Column *col,
+                                                const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st,
+                                                bool &bad, bool write_new, int *sids, bool init) {
     constexpr int KS = D / 32, MS = D / 16;
     const int n16 = lane & 15, G = lane >> 4;
     // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of its column.
-    bf16x8_t qB[KS];
+    bf16x8_t qB[CT][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (col.valid)
-            v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + col.row * D + s * 32 + 8 * G);
-        qB[s] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col[c].valid)
+                v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + col[c].row * D + s * 32 +
+                                                     8 * G);
+            qB[c][s] = __builtin_bit_cast(bf16x8_t, v);
+        }
     if (init) {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) st.o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        st.m = -INFINITY;
-        st.l = 0.0f;
-        st.bv = 0.0f;
+        for (int c = 0; c < CT; ++c) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) st[c].o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            st[c].m = -INFINITY;
+            st[c].l = 0.0f;
+            st[c].bv = 0.0f;
+        }
     }
     if (j0 >= j1) return;
 
@@ -666,7 +674,8 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
     auto compute = [&](const MfmaTile<D> &T, int j) {
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
-        mfma_block<D>(p, T, qB, tok0, tlo, thi, needs_mask(tok0, r), col, G, st);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
     };
     // No software prefetch: each tile is loaded and then used. The waves that
     // share a SIMD cover each other's compute; a deeper prefetch puts more
@@ -677,6 +686,13 @@ __device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh
         fetch(j, T);
         compute(T, j);
     }
+}
+
+template <int D>
+__device__ __forceinline__ void bf16_segment(const AttnParams &p, int b, int kvh, const Column &col,
+                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st,
+                                             bool &bad, bool write_new, int *sids, bool init) {
+    bf16_segment_ct<D, 1>(p, b, kvh, &col, r, j0, j1, lane, &st, bad, write_new, sids, init);
 }
 
 // lane (G, n16) holds channel (4G + r) * (D/16) + m of head n16 in o[m][r]:
@@ -1067,20 +1083,23 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     }
 }
 
-// Column tile ct of kv head kvh. Only column tile 0 stores the fused
+// Column tiles ct0 .. ct0 + CT - 1 of kv head kvh (col[c], st[c]; CT > 1 on
+// the bf16 path only). Only the unit holding column tile 0 stores the fused
 // append's rows, so that each new row is written once.
-template <int D, int Q4>
-__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
-                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
+template <int D, int Q4, int CT>
+__device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct0, const Column *col,
+                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st, bool &bad,
                                             int *sids) {
-    if constexpr (Q4 > 0)
+    if constexpr (Q4 > 0) {
+        static_assert(CT == 1, "the INT4 path takes one column tile per unit");
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
-            q4_segment<D, Q4>(p, b, kvh, ct, col, r, c0, c1, lane, st, bad, sids, init);
+            q4_segment<D, Q4>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init);
         });
-    else
+    } else {
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
-            bf16_segment<D>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct == 0, sids, init);
+            bf16_segment_ct<D, CT>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct0 == 0, sids, init);
         });
+    }
 }
 
 // Fixed-split schedule: grid (max_splits, n_kv, batch).
@@ -1088,23 +1107,31 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 // (no spills; the INT4 path would otherwise take 1 wave per SIMD).
 #define KV_MFMA_WAVES __attribute__((amdgpu_waves_per_eu(2)))
 
-template <int D, int Q4>
+// Work unit u of a sequence: kv head u / groups, column tiles CT * (u % groups)
+// .. + CT - 1 (groups = units / n_kv).
+template <int D, int Q4, int CT>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     extern __shared__ int sids[];  // [min(split_blocks, kSidsWindow)] staged block ids
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int split = blockIdx.x, unit = blockIdx.y, b = blockIdx.z;
-    const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
+    const int cgroups = p.units / p.n_kv;
+    const int kvh = unit / cgroups, ct0 = (unit % cgroups) * CT;
     SplitWork w;
     if (!split_work(p, b, split, w)) return;
     bool bad = w.r.bad;
-    const Column col = column_of(p, b, kvh, ct, n16, w.r);
-    MfmaState<D> st;
-    run_segment<D, Q4>(p, b, kvh, ct, col, w.r, w.j0, w.j1, lane, st, bad, sids);
-    const float l = col_sum(st.l), bv = col_sum(st.bv);
-    if (col.valid) {
-        float res[D / 4];
-        mfma_gather_run<D>(st, bv, res);
-        store_result(p, col.row, split, w.r.nsplit, G * (D / 4), res, D / 4, st.m, l, bad, G == 0);
+    Column col[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, w.r);
+    MfmaState<D> st[CT];
+    run_segment<D, Q4, CT>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
+        if (col[c].valid) {
+            float res[D / 4];
+            mfma_gather_run<D>(st[c], bv, res);
+            store_result(p, col[c].row, split, w.r.nsplit, G * (D / 4), res, D / 4, st[c].m, l, bad, G == 0);
+        }
     }
 }
 
@@ -1146,7 +1173,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
     return carry;
 }
 
-template <int D, int Q4>
+template <int D, int Q4, int CT>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] block prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
@@ -1186,35 +1213,42 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
             t = pair_t + span;
             continue;
         }
-        const int kvh = unit / p.ctiles, ct = unit % p.ctiles;
+        const int cgroups = p.units / p.n_kv;
+        const int kvh = unit / cgroups, ct0 = (unit % cgroups) * CT;
         const long seg_end = min(e, pair_t + nb);
         const int cnt = (int)(seg_end - t);
         const int ctx = ctx_of(p, b);
         const SeqRange r = seq_range(Q4 ? uniform(ctx) : ctx, p.max_blocks, p.window, p.split_blocks, p.max_splits,
                                      p.q_len);
         bool bad = r.bad;
-        const Column col = column_of(p, b, kvh, ct, n16, r);
-        MfmaState<D> st;
-        run_segment<D, Q4>(p, b, kvh, ct, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
-        const float l = col_sum(st.l), bv = col_sum(st.bv);
-        if (col.valid) {
-            float res[D / 4];
-            mfma_gather_run<D>(st, bv, res);
-            const float nan = __uint_as_float(0x7fc00000u);
-            if (jr == 0 && cnt == nb) {
-                float *dst = p.out + col.row * D + G * (D / 4);
-                const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        Column col[CT];
 #pragma unroll
-                for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
-            } else {
-                const int slot = jr > 0 ? 0 : 1;
-                const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + n16;
-                float *dst = p.ws_o + row * D + G * (D / 4);
+        for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, r);
+        MfmaState<D> st[CT];
+        run_segment<D, Q4, CT>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
 #pragma unroll
-                for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c];
-                if (G == 0) {
-                    p.ws_ml[row * 2] = st.m;
-                    p.ws_ml[row * 2 + 1] = bad ? nan : l;
+        for (int c = 0; c < CT; ++c) {
+            const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
+            if (col[c].valid) {
+                float res[D / 4];
+                mfma_gather_run<D>(st[c], bv, res);
+                const float nan = __uint_as_float(0x7fc00000u);
+                if (jr == 0 && cnt == nb) {
+                    float *dst = p.out + col[c].row * D + G * (D / 4);
+                    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k] * inv;
+                } else {
+                    // slot row: column tile c of the unit at 16 c + n16
+                    const int slot = jr > 0 ? 0 : 1;
+                    const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + c * 16 + n16;
+                    float *dst = p.ws_o + row * D + G * (D / 4);
+#pragma unroll
+                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k];
+                    if (G == 0) {
+                        p.ws_ml[row * 2] = st[c].m;
+                        p.ws_ml[row * 2 + 1] = bad ? nan : l;
+                    }
                 }
             }
         }
@@ -1700,7 +1734,8 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     const int head = blockIdx.x % p.n_h, qi = blockIdx.x / p.n_h;
     const int D = p.head_dim, cv = D / 64;
     const int kvh = head / p.group, ci = qi * p.group + head % p.group;
-    const int unit = kvh * p.ctiles + ci / 16, n16 = ci % 16;
+    const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;  // column groups per kv head, columns per unit
+    const int unit = kvh * cgroups + ci / ucols, n16 = ci % ucols;  // n16: the row within the unit's slot
     const int span = p.ws_prefix[b + 1] - p.ws_prefix[b];  // nb + seg_cost, or 0
     const int nb = span > 0 ? span - p.seg_cost : 0;
     float *dst = p.out + ((size_t)b * p.q_len * p.n_h + blockIdx.x) * D + lane * cv;
@@ -1834,23 +1869,31 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
             const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
             if (q4 && p.ncols <= 4)
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.head_dim == 64 && p.ctw == 2)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0, 2>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.ctw == 2)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0, 2>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0>), bg, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
         } else {
             const uint32_t lds = (uint32_t)(min(p.split_blocks, kSidsWindow) * sizeof(int));
             if (q4 && p.ncols <= 4)
-                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
-                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.head_dim == 64 && p.ctw == 2)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0, 2>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
-                hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.ctw == 2)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0, 2>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else
-                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0>), grid, dim3(64), lds, s, e0, e1, 0, p);
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
         }
         return hipGetLastError();
     }
@@ -1869,11 +1912,11 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
         return 256 * 2;
     hipError_t e;
     if (dtype == KV_INT4)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 4>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 4, 1>, 64, lds);
     else if (head_dim == 64)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<64, 0>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<64, 0, 2>, 64, lds);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 0>, 64, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 0, 2>, 64, lds);
     if (e != hipSuccess || per_cu <= 0) per_cu = 2;
     // at most two waves per SIMD: with more, more tile bytes are in flight
     // and the 8B- and 70B-shaped decode layers measured slower (109 vs 104 us

@@ -36,8 +36,9 @@ struct AttnParams {
     int32_t q_len;     // query tokens per sequence (1: decode)
     int32_t ncols;     // query columns per kv head: group * q_len
     int32_t ctiles;    // 16-column tiles per kv head
-    int32_t units;     // work units per sequence: n_kv * ctiles
-    int32_t slot_cols; // balanced: columns of one workspace slot, min(16, ncols)
+    int32_t ctw;       // column tiles per work unit (MFMA kernels: 2 on the bf16 path when ctiles > 1, else 1)
+    int32_t units;     // work units per sequence: n_kv * ceil(ctiles / ctw)
+    int32_t slot_cols; // balanced: columns of one workspace slot, min(16 * ctw, ncols)
     int32_t schedule;  // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int32_t n_wg;      // balanced: persistent grid size
     int32_t seg_cost;  // balanced: schedule positions a (sequence, unit) pair takes beyond its tiles

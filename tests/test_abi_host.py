@@ -153,10 +153,11 @@ def test_argument_errors_before_launch(kv):
     assert A(h, FAKE, FAKE, FAKE, 4, FAKE, None, 65536, None) == kv.KV_ERR_UNSUPPORTED
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 65536, 50, None, 0, ctypes.byref(o), None) \
         == kv.KV_ERR_UNSUPPORTED
-    # 2 kv heads x 16384 query tokens x group 4 = 2 x 4096 column tiles: fine; x 16 more is not
+    # 2 kv heads x 16384 query tokens x group 2 = 2 x 2048 column tiles, two per unit: fine;
+    # x 32 more is 2 x 32768 units
     assert M(h, FAKE, FAKE, 4, 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
         == kv.KV_ERR_WORKSPACE
-    assert M(h, FAKE, FAKE, 4, 16 * 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
+    assert M(h, FAKE, FAKE, 4, 32 * 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
         == kv.KV_ERR_UNSUPPORTED
     assert kv.kv_pool_required_bytes(kv.make_desc(16, 65536, 64, "bf16")) == 0
     R = kv.raw["rope_rerotate"]
@@ -236,9 +237,10 @@ def test_multi_token_workspace_sizes(kv):
     # 4 query tokens, 4 heads: rows = batch * q_len * n_h * splits (50 tokens: 4 splits)
     rows = 2 * 4 * 4 * 4
     assert W(h, 2, 4, 4, 50, ctypes.byref(o1)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256
-    # balanced: slot rows = min(16, group * q_len) = 16 for group 2 and 9 query tokens
+    # balanced: group 2 and 9 query tokens = 18 columns, two column tiles in one
+    # unit: slot rows = min(16 * 2, 18)
     ob = kv.attn_opts(schedule=kv.KV_SCHED_BALANCED)
-    rows = 512 * 2 * 16
+    rows = 512 * 2 * 18
     assert W(h, 3, 4, 9, 50, ctypes.byref(ob)) == (rows * 64 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256 + 256
     assert W(h, 2, 4, 0, 50, None) == ctypes.c_size_t(-1).value
     kv.raw["kv_pool_destroy"](h)
