@@ -82,6 +82,48 @@ def test_random_decode_step(i):
     pool.close()
 
 
+def draw_multi(i):
+    r = random.Random(7000 + i)
+    batch = r.randint(1, 8)
+    k = r.randint(2, 12)
+    lens = [k + (r.choice([0, 1, 15, 16, 17]) if r.random() < 0.3 else r.randint(0, 500)) for _ in range(batch)]
+    n_kv = r.choice([1, 2, 4, 8])
+    g = r.choice([1, 2, 3, 4, 6, 8, 16])
+    d = r.choice([64, 128])
+    schedule = r.choice([0, 1, 2])
+    split = r.choice([0, 1, 3]) if schedule != 2 else 0
+    window = r.choice([0, 0, 1, 20, 150])
+    return dict(lens=lens, k=k, n_kv=n_kv, n_h=n_kv * g, d=d, schedule=schedule, split=split, window=window)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_multi_token(i):
+    """Several query tokens per sequence (g * k query columns per kv head, up
+    to 192: one or two 16-column tiles per work unit) on the MFMA kernels."""
+    cfg = draw_multi(i)
+    print(f"random multi-token case {i}: {cfg}", flush=True)
+    lens = cfg["lens"]
+    c = wl.make_case(9000 + i, len(lens), lens, cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", append=False, device=DEV)
+    pool = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    g = torch.Generator(device=DEV).manual_seed(i)
+    q = torch.randn((c.batch, cfg["k"], c.n_h, c.d), generator=g, device=DEV).to(torch.bfloat16)
+    opts = kv.attn_opts(split_blocks=cfg["split"], kernel=2, window=cfg["window"], schedule=cfg["schedule"])
+    max_ctx = int(c.ctx_lens.max().item())
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(pool, c.batch, c.n_h, cfg["k"], max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full((c.batch, cfg["k"], c.n_h, c.d), float("nan"), dtype=torch.float32, device=DEV)
+    kv.paged_multi_token_attention(pool, q, out, c.tables, c.ctx_lens, c.scale, max_ctx, ws, None, opts)
+    torch.cuda.synchronize()
+    ref = orc.attention_multi(wl.to_host_bits(c.K), wl.to_host_bits(c.V), wl.to_host_bits(q), c.tables.cpu().numpy(),
+                              c.ctx_lens.cpu().numpy(), c.scale, window=cfg["window"])
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= TOL
+    pool.close()
+
+
 def draw_int4(i):
     r = random.Random(5000 + i)
     batch = r.randint(1, 10)
