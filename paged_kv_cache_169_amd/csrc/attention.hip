@@ -1761,6 +1761,49 @@ __global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
     merge_partials(p, w1 - w0 + 1, [&](int i) { return ws_row(w0 + i); }, lane, cv, dst);
 }
 
+// The same merge with one workgroup of four waves per (sequence, unit) pair,
+// the waves taking the unit's output rows (query token, head) in turn: fewer,
+// larger workgroups.
+__global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParams p) {
+    const int unit = blockIdx.x, b = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = 4;
+    const int D = p.head_dim, cv = D / 64;
+    const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;  // column groups per kv head, columns per unit
+    const int kvh = unit / cgroups, ci0 = (unit % cgroups) * ucols;
+    const int rows = min(ucols, p.ncols - ci0);
+    auto dst_of = [&](int r) {  // output of the unit's row r (query column ci0 + r)
+        const int ci = ci0 + r, qi = ci / p.group, head = kvh * p.group + ci % p.group;
+        return p.out + ((size_t)b * p.q_len + qi) * p.n_h * D + (size_t)head * D + lane * cv;
+    };
+    const int span = p.ws_prefix[b + 1] - p.ws_prefix[b];  // nb + seg_cost, or 0
+    const int nb = span > 0 ? span - p.seg_cost : 0;
+    if (nb == 0) {
+        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
+        for (int row = wave; row < rows; row += nwaves) {
+            float *dst = dst_of(row);
+            for (int c = 0; c < cv; ++c) dst[c] = v;
+        }
+        return;
+    }
+    const long total = (long)p.ws_prefix[p.batch] * p.units;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
+    const long end = start + nb;
+    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
+    if (w0 == w1) return;  // complete inside one workgroup: already written
+    for (int row = wave; row < rows; row += nwaves) {
+        // workspace row of the partial that workgroup w holds for this pair:
+        // the first piece goes on past its range (slot 1), the others started
+        // before theirs (slot 0)
+        auto ws_row = [&](int w) {
+            const int slot = w == w0 ? 1 : 0;
+            return ((size_t)w * 2 + slot) * p.slot_cols + row;
+        };
+        merge_partials(p, w1 - w0 + 1, [&](int i) { return ws_row(w0 + i); }, lane, cv, dst_of(row));
+    }
+}
+
 
 // Merge of the shared-prefix call: one wave per (sequence, head) row with
 // more than one part (a prefix, or several suffix splits).
@@ -1943,14 +1986,24 @@ int shared_balanced_grid(int head_dim, size_t lds) {
     return cus * per_cu;
 }
 
+// One four-wave workgroup per unit rather than one wave per row: for units
+// of 5-16 rows when there are at least 2048 units (measured: the 70B-shaped
+// merge 8.7 -> 4.4 us; with 512 units, 8 or 16 rows each, it was slower).
+constexpr int kMergeUnitRows = 5, kMergeUnitMin = 2048;
+
 hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
     const bool none = p.batch == 0 || (p.schedule != KV_SCHED_BALANCED && p.max_splits <= 1);
     if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
-    const dim3 grid(p.n_h * p.q_len, p.batch);
-    if (p.schedule == KV_SCHED_BALANCED)
-        hipExtLaunchKernelGGL(attn_merge_balanced_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
+    if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
+        (long)p.batch * p.units >= kMergeUnitMin)
+        hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel, dim3(p.units, p.batch), dim3(256), 0, s, nullptr, e_end,
+                              0, p);
+    else if (p.schedule == KV_SCHED_BALANCED)
+        hipExtLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, nullptr,
+                              e_end, 0, p);
     else
-        hipExtLaunchKernelGGL(attn_merge_kernel, grid, dim3(64), 0, s, nullptr, e_end, 0, p);
+        hipExtLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, nullptr, e_end, 0,
+                              p);
     return hipGetLastError();
 }
 

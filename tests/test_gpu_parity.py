@@ -201,6 +201,25 @@ def test_rising_scores(n_h, amp, dtype, split):
     assert max_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("g,q_len", [(8, 1), (4, 2), (2, 8)])
+@pytest.mark.parametrize("window", [0, 30])
+def test_many_units_merge(g, q_len, window):
+    """300 sequences x 8 kv heads (2400 units of 8 or 16 query columns: the
+    merge with one workgroup per unit), lengths 0-400 with empty sequences."""
+    r = np.random.default_rng(70 + g + q_len)
+    lens = [int(x) for x in r.integers(q_len, 400, 300)]
+    lens[5] = lens[17] = 0
+    c = wl.make_case(980 + g, len(lens), lens, 8 * g, 8, 128, "bf16", append=False, device=DEV)
+    pool = new_pool(c)
+    gq = torch.Generator(device=DEV).manual_seed(g)
+    q = torch.randn((c.batch, q_len, 8 * g, 128), generator=gq, device=DEV).to(torch.bfloat16)
+    out = gpu_multi(pool, c, q, window=window, schedule=2)
+    ref = orc.attention_multi(bits(c.K), bits(c.V), bits(q), c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy(),
+                              c.scale, window=window)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref) <= TOL
+
+
 @pytest.mark.parametrize("schedule,split", [(0, 0), (1, 70000), (1, 300)])
 def test_million_token_context(schedule, split):
     """A 1,000,000-token sequence beside a short one (bf16, MFMA): the
