@@ -1,4 +1,5 @@
-// attention.hip -- split-context paged decode attention for gfx950.
+// attention.hip -- paged decode attention for gfx950 (one or several query
+// tokens per sequence).
 //
 // Computes, for every sequence b and query head h,
 //   out[b][h] = softmax(q[b][h] . K_b^T * scale) . V_b
@@ -10,29 +11,43 @@
 // vLLM", section "PagedAttention"] and query head h reads kv head
 // h / (n_h / n_kv) ["KV 캐시 시스템", section "MQA / GQA"].
 //
-// Decomposition: one wave64 workgroup per (context split, kv head, sequence).
-// It streams its split's (block, kv head) tiles once and serves all g = n_h /
-// n_kv query heads of the group from each tile, keeping an online softmax
-// (running max m and sum l, in log2 units: scores are pre-multiplied by
-// scale * log2 e so exp becomes the hardware exp2). A sequence with one split
-// writes its output directly; otherwise each split writes (o, m, l) to the
-// workspace and attn_merge_kernel combines them:
-//   M = max_s m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Work units. The query columns of a kv head are its g = n_h / n_kv query
+// heads times the q_len query tokens, in 16-column tiles; a work unit is a
+// kv head and one column tile (two on the bf16 MFMA path when there are
+// several). A workgroup is one wave64. It streams the unit's (block, kv head)
+// tiles once and serves all its columns from each tile, keeping an online
+// softmax (running max m and sum l, in log2 units: scores are pre-multiplied
+// by scale * log2 e so exp becomes the hardware exp2; the max moves lazily,
+// see kLazyLog2).
 //
-// Two inner kernels:
+// Schedules (which workgroup takes which tiles):
+//  * fixed splits (attn_mfma_kernel, attn_valu_kernel): grid (split, unit,
+//    sequence), split_blocks blocks per split; attn_merge_kernel combines the
+//    splits' (o, m, l): M = max_s m_s, out = sum_s 2^(m_s - M) o_s /
+//    sum_s 2^(m_s - M) l_s.
+//  * balanced (attn_mfma_balanced_kernel, the default): a persistent grid of
+//    two waves per SIMD; every workgroup takes an equal share of all tiles of
+//    the call; pairs cut between workgroups are merged by
+//    attn_merge_balanced_kernel / attn_merge_balanced_unit_kernel.
+//  * shared prefixes (attn_mfma_shared_balanced_kernel, attn_mfma_shared_kernel):
+//    a group's shared blocks are read once with the members' queries as the
+//    columns.
+//
+// Tile engines:
 //  * attn_valu_kernel (fp32, bf16, INT4): VALU dot products. Lane l takes
 //    token l/4 of a block and a quarter of its channels for q.K (two xor
 //    shuffles finish each dot product); for p.V lane l owns head_dim/64
 //    channels and walks the block's tokens, the weights broadcast through LDS.
-//  * attn_mfma_bf16_kernel (bf16): the block's scores for the whole query
-//    group are one 16x16 MFMA tile, S^T[token][head] = K_tile . Q^T (heads
-//    padded to 16), and the value update is O^T[channel][head] +=
-//    V_tile^T . P^T. P is split into bf16 hi + lo parts so the weights keep
-//    ~16 bits (a single bf16 would cost up to 2^-9 relative error per
-//    weight); both parts go into one 16x16x32 MFMA per channel tile, the
-//    tile's 4 tokens repeated along k against hi then lo. The QK output
-//    layout (lane = head + 16 * token-quad) is exactly the B-operand layout
-//    the PV product needs, so P never leaves registers.
+//  * mfma_block (bf16): the block's scores for a column tile are one 16x16
+//    MFMA tile, S^T[token][column] = K_tile . Q^T, and the value update is
+//    O^T[channel][column] += V_tile^T . P^T. P is split into bf16 hi + lo
+//    parts so the weights keep ~16 bits (a single bf16 would cost up to 2^-9
+//    relative error per weight); both parts go into one 16x16x32 MFMA per
+//    channel tile, the tile's 4 tokens repeated along k against hi then lo.
+//    The QK output layout (lane = column + 16 * token-quad) is exactly the
+//    B-operand layout the PV product needs, so P never leaves registers.
+//  * q4_block (INT4): the same products on the codes, with the scales and
+//    minimums folded into the query and weight operands (see q4_block).
 #include "device.h"
 #include <hip/hip_ext.h>
 
