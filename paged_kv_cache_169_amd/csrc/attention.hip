@@ -417,7 +417,10 @@ __device__ __forceinline__ int load_block_ids(const AttnParams &p, int b, int jb
 // Tile of block j. Rows of positions in [L0, L0 + n_new) come from the step's
 // k_new / v_new instead of the pool (fused append); newpos = L0 - 16 j is
 // uniform, and >= 16 when the block holds no new token.
-template <int D>
+// KEEP: ordinary (cached) loads instead of non-temporal ones. A template
+// argument, not a run-time flag: a select between the two loads of one
+// address is merged into one load without the non-temporal hint.
+template <int D, bool KEEP = false>
 __device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh, int n16, int G, MfmaTile<D> &T,
                                            int b = 0, int newpos = kBlock) {
     constexpr int KS = D / 32, VC = D / 16;
@@ -439,18 +442,21 @@ __device__ __forceinline__ void fetch_tile(const AttnParams &p, int pid, int kvh
         }
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) T.k[s] = __builtin_bit_cast(bf16x8_t, stream_load16(krow + s * 32 + 8 * G));
+    for (int s = 0; s < KS; ++s) {
+        gu16_t *src = krow + s * 32 + 8 * G;
+        T.k[s] = __builtin_bit_cast(bf16x8_t, KEEP ? *reinterpret_cast<gu32x4_t *>(src) : stream_load16(src));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         gu16_t *src = vrow[i] + n16 * VC;
         if constexpr (VC == 8) {
-            const u32x4_t v = stream_load16(src);
+            const u32x4_t v = KEEP ? *reinterpret_cast<gu32x4_t *>(src) : stream_load16(src);
             T.v[i][0] = v[0];
             T.v[i][1] = v[1];
             T.v[i][2] = v[2];
             T.v[i][3] = v[3];
         } else {
-            const u32x2_t v = stream_load8(src);
+            const u32x2_t v = KEEP ? *reinterpret_cast<gu32x2_t *>(src) : stream_load8(src);
             T.v[i][0] = v[0];
             T.v[i][1] = v[1];
         }
@@ -634,7 +640,7 @@ __device__ __forceinline__ void run_pieces(int j0, int j1, Seg seg) {
 // the piece's block ids are staged in LDS before the loop and the fused
 // append's rows are written before it, so the waits inside the loop cover
 // exactly the tile's own loads.
-template <int D, int CT>
+template <int D, int CT, bool KEEP = false>
 __device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int kvh, const Column *col,
                                                 const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st,
                                                 bool &bad, bool write_new, int *sids, bool init) {
@@ -684,7 +690,7 @@ __device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int 
     }
     auto fetch = [&](int j, MfmaTile<D> &T) {
         const int newpos = L0 == INT_MAX ? kBlock : min(L0 - j * kBlock, kBlock);  // may be negative
-        fetch_tile<D>(p, pid_of(j), kvh, n16, G, T, b, newpos);
+        fetch_tile<D, KEEP>(p, pid_of(j), kvh, n16, G, T, b, newpos);
     };
     auto compute = [&](const MfmaTile<D> &T, int j) {
         const int tok0 = j * kBlock;
@@ -1100,19 +1106,24 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
 
 // Column tiles ct0 .. ct0 + CT - 1 of kv head kvh (col[c], st[c]; CT > 1 on
 // the bf16 path only). Only the unit holding column tile 0 stores the fused
-// append's rows, so that each new row is written once.
-template <int D, int Q4, int CT>
+// append's rows, so that each new row is written once. KEEP: ordinary loads
+// (the launch sets it when a kv head's columns take several units, each
+// reading every K/V tile: the tiles then stay in the caches for the other
+// units, which read them about the same time; 8B shape, 16 query tokens:
+// 286 -> 256 us; with one unit per kv head they cost 4 %).
+template <int D, int Q4, int CT, bool KEEP>
 __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct0, const Column *col,
                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st, bool &bad,
                                             int *sids) {
     if constexpr (Q4 > 0) {
         static_assert(CT == 1, "the INT4 path takes one column tile per unit");
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
+            static_assert(!KEEP, "the INT4 path streams its tiles");
             q4_segment<D, Q4>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init);
         });
     } else {
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
-            bf16_segment_ct<D, CT>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct0 == 0, sids, init);
+            bf16_segment_ct<D, CT, KEEP>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct0 == 0, sids, init);
         });
     }
 }
@@ -1124,7 +1135,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 
 // Work unit u of a sequence: kv head u / groups, column tiles CT * (u % groups)
 // .. + CT - 1 (groups = units / n_kv).
-template <int D, int Q4, int CT>
+template <int D, int Q4, int CT, bool KEEP = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     extern __shared__ int sids[];  // [min(split_blocks, kSidsWindow)] staged block ids
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
@@ -1138,7 +1149,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
 #pragma unroll
     for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, w.r);
     MfmaState<D> st[CT];
-    run_segment<D, Q4, CT>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
+    run_segment<D, Q4, CT, KEEP>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
         const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
@@ -1188,7 +1199,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
     return carry;
 }
 
-template <int D, int Q4, int CT>
+template <int D, int Q4, int CT, bool KEEP = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] block prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
@@ -1240,7 +1251,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 #pragma unroll
         for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, r);
         MfmaState<D> st[CT];
-        run_segment<D, Q4, CT>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
+        run_segment<D, Q4, CT, KEEP>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
@@ -1923,6 +1934,7 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
     if (p.batch == 0) return hipSuccess;
     if (kernel == 2) {
         const bool q4 = dtype == KV_INT4;
+        const bool keep = p.units > p.n_kv;  // several units per kv head: cached loads
         if (p.schedule == KV_SCHED_BALANCED) {
             const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
@@ -1930,10 +1942,14 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.head_dim == 64 && p.ctw == 2 && keep)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0, 2, true>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64 && p.ctw == 2)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0, 2>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<64, 0, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.ctw == 2 && keep)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0, 2, true>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.ctw == 2)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0, 2>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else
@@ -1944,10 +1960,14 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.head_dim == 64 && p.ctw == 2 && keep)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0, 2, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64 && p.ctw == 2)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0, 2>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.head_dim == 64)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<64, 0, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (p.ctw == 2 && keep)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0, 2, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (p.ctw == 2)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 0, 2>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else
