@@ -146,17 +146,21 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
     g->ncols = group * q_len;
     g->ctiles = (g->ncols + 15) / 16;
     // the bf16 MFMA kernels take two column tiles per unit when there are
-    // several: each K/V tile is then read once per two column tiles
-    g->ctw = (kernel == 2 && dtype == KV_BF16 && g->ctiles > 1) ? 2 : 1;
-    const int cgroups = (g->ctiles + g->ctw - 1) / g->ctw;
-    if ((int64_t)n_kv * cgroups > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
-    g->units = kernel == 2 ? n_kv * cgroups : n_kv;
-    g->slot_cols = std::min(16 * g->ctw, g->ncols);
+    // several: each K/V tile is then read once per two column tiles. The
+    // balanced schedule takes up to 8 per unit (wide units: a workgroup of
+    // up to 4 waves sharing each K/V tile through LDS)
     int sb = opts ? opts->split_blocks : 0;
     int sched = opts ? opts->schedule : 0;
     if (sched == KV_SCHED_AUTO)
         sched = (kernel == 2 && sb == 0 && batch <= kMaxBalancedBatch) ? KV_SCHED_BALANCED : KV_SCHED_SPLIT;
     if (sched == KV_SCHED_BALANCED && (kernel != 2 || batch > kMaxBalancedBatch)) return KV_ERR_UNSUPPORTED;
+    const bool bf16_mfma = kernel == 2 && dtype == KV_BF16;
+    g->ctw = (bf16_mfma && g->ctiles > 1) ? 2 : 1;
+    if (bf16_mfma && sched == KV_SCHED_BALANCED && g->ctiles > 2) g->ctw = g->ctiles > 4 ? 8 : 4;
+    const int cgroups = (g->ctiles + g->ctw - 1) / g->ctw;
+    if ((int64_t)n_kv * cgroups > kMaxGridYZ) return KV_ERR_UNSUPPORTED;
+    g->units = kernel == 2 ? n_kv * cgroups : n_kv;
+    g->slot_cols = std::min(16 * g->ctw, g->ncols);
     const int window = opts ? opts->window : 0;
     int nblk = (max_ctx + KV_BLOCK_TOKENS - 1) / KV_BLOCK_TOKENS;
     if (window > 0) {
@@ -175,7 +179,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         // longer than max_ctx does not fit the promise and reads as bad
         g->split_blocks = nblk;
         g->max_splits = 1;
-        g->n_wg = balanced_grid(dtype, (int)D, batch, nblk);
+        g->n_wg = g->ctw > 2 ? wide_grid((int)D, g->ctw / 2, batch, nblk) : balanced_grid(dtype, (int)D, batch, nblk);
         const size_t rows = (size_t)g->n_wg * 2 * g->slot_cols;
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));

@@ -1283,6 +1283,234 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 }
 
 // ---------------------------------------------------------------------------
+// wide work units (bf16, many query columns per kv head)
+//
+// A unit of 2W column tiles is one workgroup of W waves (two column tiles per
+// wave, as in bf16_segment_ct): the waves load each (block, kv head) K/V tile
+// once, together, into LDS and each reads it back in the MFMA operand layout.
+// So a K/V tile leaves HBM once per 2W column tiles instead of once per two.
+// The LDS tiles are double-buffered: the next tile's global loads are in
+// flight while the current one is used, and one barrier per tile orders both.
+// ---------------------------------------------------------------------------
+
+// One K/V tile in LDS: 16 rows of D bf16 for K, then for V, in 16-byte
+// slots. Slot column c of row r sits at position c ^ (r % SPR) of the row, so
+// that the 16 lanes of one operand read (16 rows of one column, or 16
+// columns of one row) fall on distinct banks.
+template <int D>
+struct TileLds {
+    static constexpr int SPR = D * 2 / 16;          // slots per row
+    static constexpr int SLOTS = 2 * kBlock * SPR;  // K rows, then V rows
+    u32x4_t slot[SLOTS];
+    __device__ __forceinline__ static int at(int which, int row, int col) {
+        return (which * kBlock + row) * SPR + (col ^ (row % SPR));
+    }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Issues this wave's share of one tile's loads straight into LDS
+// (global_load_lds, 16 bytes per lane): instruction q of the tile fills slots
+// [64 q, 64 q + 64), wave w issues q = w, w + W, ... Rows of the step's new
+// tokens (slots from newpos on) come from k_new / v_new. Complete after the
+// wave's vector-memory counter reaches 0.
+template <int D, int W>
+__device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh, int b, int newpos, int wave,
+                                           int lane, TileLds<D> &t) {
+    constexpr int SPR = TileLds<D>::SPR, NI = TileLds<D>::SLOTS / 64;
+#pragma unroll
+    for (int q = wave; q < NI; q += W) {
+        const int sl = q * 64 + lane;
+        const int which = sl / (kBlock * SPR), rem = sl % (kBlock * SPR);
+        const int row = rem / SPR, col = (rem % SPR) ^ (row % SPR);
+        gu16_t *src;
+        if (row >= newpos && row < newpos + p.ctx_add)
+            src = global_u16(which ? p.v_new : p.k_new) + (((size_t)b * p.ctx_add + (row - newpos)) * p.n_kv + kvh) * D;
+        else
+            src = global_u16(which ? p.pool.v : p.pool.k) + (((size_t)pid * p.n_kv + kvh) * kBlock + row) * D;
+        __builtin_amdgcn_global_load_lds(src + col * 8, (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
+    }
+}
+
+// The MFMA operands of a tile in LDS (layout of MfmaTile).
+template <int D>
+__device__ __forceinline__ void wide_operands(const TileLds<D> &t, int n16, int G, MfmaTile<D> &T) {
+    constexpr int KS = D / 32, VC = D / 16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) T.k[s] = __builtin_bit_cast(bf16x8_t, t.slot[TileLds<D>::at(0, n16, 4 * s + G)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * G + i;
+        if constexpr (VC == 8) {
+            const u32x4_t v = t.slot[TileLds<D>::at(1, r, n16)];
+            T.v[i][0] = v[0];
+            T.v[i][1] = v[1];
+            T.v[i][2] = v[2];
+            T.v[i][3] = v[3];
+        } else {  // 8 bytes: half n16 & 1 of slot n16 / 2
+            const u32x2_t v = *reinterpret_cast<const u32x2_t *>(
+                reinterpret_cast<const uint8_t *>(&t.slot[TileLds<D>::at(1, r, n16 >> 1)]) + (n16 & 1) * 8);
+            T.v[i][0] = v[0];
+            T.v[i][1] = v[1];
+        }
+    }
+}
+
+// Blocks [j0, j1) (at most kSidsWindow) of sequence b, kv head kvh for this
+// wave's two column tiles (col, st; init: start a new state). Every wave of
+// the workgroup calls it with the same blocks.
+template <int D, int W>
+__device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh, const Column *col,
+                                             const SeqRange &r, int j0, int j1, int tid, MfmaState<D> *st, bool &bad,
+                                             bool write_new, int *sids, TileLds<D> (&tl)[2], bool init) {
+    constexpr int KS = D / 32, MS = D / 16;
+    const int lane = tid & 63, n16 = lane & 15, G = lane >> 4;
+    bf16x8_t qB[2][KS];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col[c].valid)
+                v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + col[c].row * D + s * 32 +
+                                                     8 * G);
+            qB[c][s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    if (init) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) st[c].o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            st[c].m = -INFINITY;
+            st[c].l = 0.0f;
+            st[c].bv = 0.0f;
+        }
+    }
+    if (j0 >= j1) return;
+    // block ids of the piece, staged by the whole workgroup
+    const int32_t *row_ids = p.tables + (size_t)b * p.max_blocks;
+    __syncthreads();  // earlier reads of sids and of the tile buffers are done
+    for (int i = tid; i < j1 - j0; i += 64 * W) sids[i] = row_ids[j0 + i];
+    __syncthreads();
+    auto pid_of = [&](int j) {
+        int pid = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+        if (pid < 0 || pid >= p.num_blocks) {
+            bad = true;
+            pid = 0;
+        }
+        return pid;
+    };
+    const int L0 = p.k_new ? r.n - p.ctx_add : INT_MAX;
+    if (write_new && tid < 64 && L0 != INT_MAX) {
+        for (int j = max(j0, L0 / kBlock); j < j1; ++j) {
+            const int id = __builtin_amdgcn_readfirstlane(sids[j - j0]);
+            if (id >= 0 && id < p.num_blocks) store_new_rows<D>(p, b, kvh, id, L0 - j * kBlock, lane);
+        }
+    }
+    auto newpos_of = [&](int j) { return L0 == INT_MAX ? kBlock : min(L0 - j * kBlock, kBlock); };
+    const int wave = tid >> 6;
+    wide_issue<D, W>(p, pid_of(j0), kvh, b, newpos_of(j0), wave, lane, tl[0]);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the tile is in LDS
+    __syncthreads();
+    for (int j = j0; j < j1; ++j) {
+        const int cur = (j - j0) & 1;
+        // the next tile's loads fill the other buffer while this one is used
+        // (all waves passed the last barrier, so nobody reads it any more)
+        if (j + 1 < j1) wide_issue<D, W>(p, pid_of(j + 1), kvh, b, newpos_of(j + 1), wave, lane, tl[cur ^ 1]);
+        MfmaTile<D> T;
+        wide_operands<D>(tl[cur], n16, G, T);
+        const int tok0 = j * kBlock;
+        const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads have landed
+        __syncthreads();
+    }
+}
+
+// Balanced schedule over wide units: as attn_mfma_balanced_kernel, with one
+// workgroup of W waves per share; wave w takes column tiles 2w, 2w + 1 of the
+// unit. Partial slots hold the unit's 32 W columns (row 16 c + n16 for the
+// unit's column tile c).
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(AttnParams p) {
+    extern __shared__ int pre[];  // [batch + 1] prefix sums, then the staged block ids
+    int *sids = pre + p.batch + 1;
+    __shared__ TileLds<D> tl[2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n16 = lane & 15, G = lane >> 4;
+    const int wg = blockIdx.x;
+    // every wave computes the same sums (identical LDS writes)
+    const int npos = balanced_prefix(p, pre, lane);
+    if (wg == 0 && wave == 0)
+        for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
+    const long total = (long)npos * p.units;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long s = (long)wg * per;
+    const long e = min(total, s + per);
+    for (long t = s; t < e;) {
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((long)pre[mid] * p.units <= t)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int b = lo;
+        const int pb = pre[b];
+        const int span = pre[b + 1] - pb;
+        const int nb = span - p.seg_cost;
+        const long pair0 = (long)pb * p.units;
+        const int unit = (int)((t - pair0) / span);
+        const long pair_t = pair0 + (long)unit * span;
+        const int jr = (int)(t - pair_t);
+        if (jr >= nb) {
+            t = pair_t + span;
+            continue;
+        }
+        const int cgroups = p.units / p.n_kv;
+        const int kvh = unit / cgroups, cu = (unit % cgroups) * p.ctw;  // first column tile of the unit
+        const long seg_end = min(e, pair_t + nb);
+        const int cnt = (int)(seg_end - t);
+        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        bool bad = r.bad;
+        Column col[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) col[c] = column_of(p, b, kvh, cu + 2 * wave + c, n16, r);
+        MfmaState<D> st[2];
+        run_pieces(r.blk_lo + jr, r.blk_lo + jr + cnt, [&](int c0, int c1, bool init) {
+            wide_segment<D, W>(p, b, kvh, col, r, c0, c1, tid, st, bad, cu == 0, sids, tl, init);
+        });
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
+            if (col[c].valid) {
+                float res[D / 4];
+                mfma_gather_run<D>(st[c], bv, res);
+                const float nan = __uint_as_float(0x7fc00000u);
+                if (jr == 0 && cnt == nb) {
+                    float *dst = p.out + col[c].row * D + G * (D / 4);
+                    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k] * inv;
+                } else {
+                    const int slot = jr > 0 ? 0 : 1;
+                    const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + (2 * wave + c) * 16 + n16;
+                    float *dst = p.ws_o + row * D + G * (D / 4);
+#pragma unroll
+                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k];
+                    if (G == 0) {
+                        p.ws_ml[row * 2] = st[c].m;
+                        p.ws_ml[row * 2 + 1] = bad ? nan : l;
+                    }
+                }
+            }
+        }
+        t = seg_end;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // shared-prefix decode attention (bf16 MFMA path)
 //
 // Sequences of a prefix group name the same physical blocks for their first
@@ -1938,7 +2166,16 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
         if (p.schedule == KV_SCHED_BALANCED) {
             const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
-            if (q4 && p.ncols <= 4)
+            if (!q4 && p.ctw > 2) {  // wide units: W = ctw / 2 waves per workgroup
+                if (p.head_dim == 64 && p.ctw == 4)
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, 2>), bg, dim3(128), lds, s, e0, e1, 0, p);
+                else if (p.head_dim == 64)
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, 4>), bg, dim3(256), lds, s, e0, e1, 0, p);
+                else if (p.ctw == 4)
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 2>), bg, dim3(128), lds, s, e0, e1, 0, p);
+                else
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 4>), bg, dim3(256), lds, s, e0, e1, 0, p);
+            } else if (q4 && p.ncols <= 4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
@@ -2000,6 +2237,24 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     // and the 8B- and 70B-shaped decode layers measured slower (109 vs 104 us
     // at three waves on the 8B shape)
     if (per_cu > 8) per_cu = 8;
+    return cus * per_cu;
+}
+
+int wide_grid(int head_dim, int waves, int batch, int max_blocks) {
+    int dev = 0, cus = 0, per_cu = 0;
+    const size_t lds = (size_t)(batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256 * 2 / waves;
+    hipError_t e;
+    if (head_dim == 64)
+        e = waves == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, 2>, 128, lds)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, 4>, 256, lds);
+    else
+        e = waves == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, 2>, 128, lds)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, 4>, 256, lds);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+    if (per_cu > 8 / waves) per_cu = 8 / waves;  // two waves per SIMD, as balanced_grid
     return cus * per_cu;
 }
 

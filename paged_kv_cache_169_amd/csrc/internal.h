@@ -36,7 +36,8 @@ struct AttnParams {
     int32_t q_len;     // query tokens per sequence (1: decode)
     int32_t ncols;     // query columns per kv head: group * q_len
     int32_t ctiles;    // 16-column tiles per kv head
-    int32_t ctw;       // column tiles per work unit (MFMA kernels: 2 on the bf16 path when ctiles > 1, else 1)
+    int32_t ctw;       // column tiles per work unit (MFMA kernels: 2 on the bf16 path when ctiles > 1, else 1;
+                       // balanced bf16 with more than 2 tiles: 4 or 8, one workgroup of ctw / 2 waves)
     int32_t units;     // work units per sequence: n_kv * ceil(ctiles / ctw)
     int32_t slot_cols; // balanced: columns of one workspace slot, min(16 * ctw, ncols)
     int32_t schedule;  // KV_SCHED_SPLIT or KV_SCHED_BALANCED
@@ -145,6 +146,8 @@ hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hip
                                    hipEvent_t e1, hipEvent_t e_end);
 // Persistent grid of the balanced schedule: resident workgroups per device.
 int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
+// The same for wide units (bf16; `waves` waves per workgroup, 2 or 4).
+int wide_grid(int head_dim, int waves, int batch, int max_blocks);
 // The balanced shared-prefix kernel: its dynamic LDS (max_blocks: the longest
 // segment in blocks) and its persistent grid for that LDS.
 size_t shared_balanced_lds(int n_groups, int batch, int max_blocks);

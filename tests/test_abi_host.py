@@ -153,11 +153,11 @@ def test_argument_errors_before_launch(kv):
     assert A(h, FAKE, FAKE, FAKE, 4, FAKE, None, 65536, None) == kv.KV_ERR_UNSUPPORTED
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 65536, 50, None, 0, ctypes.byref(o), None) \
         == kv.KV_ERR_UNSUPPORTED
-    # 2 kv heads x 16384 query tokens x group 2 = 2 x 2048 column tiles, two per unit: fine;
-    # x 32 more is 2 x 32768 units
-    assert M(h, FAKE, FAKE, 4, 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
+    # fixed splits: 2 kv heads x 16384 query tokens x group 2 = 2 x 2048 column tiles, two per
+    # unit: fine; x 32 more is 2 x 32768 units
+    assert M(h, FAKE, FAKE, 4, 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o1), None) \
         == kv.KV_ERR_WORKSPACE
-    assert M(h, FAKE, FAKE, 4, 32 * 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) \
+    assert M(h, FAKE, FAKE, 4, 32 * 16384, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o1), None) \
         == kv.KV_ERR_UNSUPPORTED
     assert kv.kv_pool_required_bytes(kv.make_desc(16, 65536, 64, "bf16")) == 0
     R = kv.raw["rope_rerotate"]
