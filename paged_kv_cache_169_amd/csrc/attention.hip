@@ -115,11 +115,26 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // butterfly steps inside the VALU (no LDS round trip); every lane of the
 // four ends with the same bits (each step adds the same two operands in the
 // same order on both lanes of a pair).
+// Larger of two floats by the hardware maximum alone. fmaxf also quiets
+// signalling NaNs first (an extra instruction per operand that the compiler
+// cannot prove canonical, e.g. a lane-swap result); no arithmetic produces
+// one, and a quiet NaN operand gives the other operand either way.
+__device__ __forceinline__ float max_raw(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float col_max(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float col_sum(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -830,36 +845,45 @@ struct Q4Query {
 
 // Scores of one INT4 tile in log2 units, from its raw products sc (before
 // the per-column min term corr). MASKED: some slots of the tile are outside
-// the attended range (partial block, window, causal columns); they get -inf
-// and valid false.
+// the attended range (partial block, window, causal columns); they get -inf,
+// and their V scale and min, which may be anything there, are set to 0 so
+// that their zero weights contribute exactly 0.
 template <bool MASKED>
 __device__ __forceinline__ void q4_scores(const AttnParams &p, const f32x4_t &sc, float corr, int tok0, int tlo,
-                                          int thi, bool partial, bool mask, const Column &col, int G, float (&sv)[4],
-                                          bool (&valid)[4]) {
+                                          int thi, const Column &col, int G, float (&sv)[4], uint2 &vs, uint2 &vm) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int tt = 4 * G + r, tp = tok0 + tt;
-        bool ok = true;
+        const float s = (sc[r] + corr) * p.scale_log2;
         if (MASKED) {
-            if (partial) ok = (tt >= tlo) & (tt < thi);
-            if (mask) ok = ok & (tp >= col.lo) & (tp < col.hi);
+            const int tt = 4 * G + r, tp = tok0 + tt;
+            const bool ok = (tt >= tlo) & (tt < thi) & (tp >= col.lo) & (tp < col.hi);
+            sv[r] = ok ? s : -INFINITY;
+            const uint32_t keep = ok ? 0xffffffffu : 0u, half = (r & 1) ? 0xffff0000u : 0x0000ffffu;
+            const uint32_t clear = ~half | keep;  // all ones, or the slot's half cleared
+            if (r < 2) {
+                vs.x &= clear;
+                vm.x &= clear;
+            } else {
+                vs.y &= clear;
+                vm.y &= clear;
+            }
+        } else {
+            sv[r] = s;
         }
-        valid[r] = ok;
-        sv[r] = ok ? (sc[r] + corr) * p.scale_log2 : -INFINITY;
     }
 }
 
-// Online softmax and value update of one INT4 tile, given its scores sv.
-// Slots that are not valid get weight 0 and their V parameters, which may be
-// anything, are not used. Full and masked tiles share this code (only their
-// scores differ), so the accumulators are updated in place.
+// Online softmax and value update of one INT4 tile, given its scores sv and
+// V scales / mins vs, vm (fp16 pairs; masked slots have score -inf and zero
+// parameters). Full and masked tiles share this code (only their inputs
+// differ), so the accumulators are updated in place.
 // Values: sum_t p_t (min_t + scale_t * code_tc) = sum_t P'_t * code_tc +
 // sum_t p_t * min_t with P'_t = p_t * scale_t (bf16 hi + lo in the B
 // operand) and the exact codes in the A operand; the second sum is a
 // per-column numerator term kept beside o.
-__device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const float (&sv)[4],
-                                              const bool (&valid)[4], int G, MfmaState<128> &st) {
-    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+__device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const float (&sv)[4], uint2 vs,
+                                              uint2 vm, MfmaState<128> &st) {
+    const float mx = max_raw(max3_raw(sv[0], sv[1], sv[2]), sv[3]);
     const float cm = col_max(mx);
     if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
         const float mn = fmaxf(st.m, cm);
@@ -870,7 +894,7 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
         for (int m = 0; m < 8; ++m) st.o[m] *= alpha;
         st.m = mn;
     }
-    const uint32_t vsw[2] = {T.vs.x, T.vs.y}, vmw[2] = {T.vm.x, T.vm.y};
+    const uint32_t vsw[2] = {vs.x, vs.y}, vmw[2] = {vm.x, vm.y};
     const float mref = st.m == -INFINITY ? 0.0f : st.m;  // no token seen yet: weights 0
     float pv[4];
     float bv = 0.0f;
@@ -880,8 +904,8 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
         st.l += pr;
         const float vsc = (r & 1) ? f16_hi(vsw[r >> 1]) : f16_lo(vsw[r >> 1]);
         const float vmn = (r & 1) ? f16_hi(vmw[r >> 1]) : f16_lo(vmw[r >> 1]);
-        pv[r] = valid[r] ? pr * vsc : 0.0f;
-        bv = valid[r] ? fmaf(pr, vmn, bv) : bv;
+        pv[r] = pr * vsc;
+        bv = fmaf(pr, vmn, bv);
     }
     st.bv += bv;
     const uint32_t h01 = cvt_pk_bf16(pv[0], pv[1]), h23 = cvt_pk_bf16(pv[2], pv[3]);
@@ -923,9 +947,11 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
 // 8 n16 ..) and exchanged through LDS into the MFMA B layout; the min term is
 // summed per column the same way. A partial last block takes bf16 K from the
 // tail row (global, 16 x 128 per sequence and kv head) with plain q.
+// masked (uniform): some slot of the tile lies outside a column's range
+// (partial block, window, causal columns); every other tile is a full block.
 template <int NP>
-__device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const Q4Query<NP> &Q, bool full,
-                                         gu16_t *tail_row, int tok0, int tlo, int thi, bool mask,
+__device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const Q4Query<NP> &Q, bool masked,
+                                         bool full, gu16_t *tail_row, int tok0, int tlo, int thi,
                                          const Column &col, int n16, int G, Q4Lds &L, MfmaState<128> &st) {
     __syncthreads();  // the previous tile's reads of L are done
     const uint32_t sw[4] = {T.ks.x, T.ks.y, T.ks.z, T.ks.w}, mw[4] = {T.km.x, T.km.y, T.km.z, T.km.w};
@@ -939,7 +965,9 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float q0 = Q.q[pi][2 * k], q1 = Q.q[pi][2 * k + 1];
-                const float p0 = q0 * f16_lo(sw[k]), p1 = q1 * f16_hi(sw[k]);  // exact products
+                // exact products (an fma with -0 added: one mixed-precision
+                // instruction per product, fp16 operand widened inside it)
+                const float p0 = fmaf(q0, f16_lo(sw[k]), -0.0f), p1 = fmaf(q1, f16_hi(sw[k]), -0.0f);
                 cp = fmaf(q0, f16_lo(mw[k]), cp);
                 cp = fmaf(q1, f16_hi(mw[k]), cp);
                 hi[k] = cvt_pk_bf16(p0, p1);
@@ -975,14 +1003,13 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
         }
     }
-    const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
     float sv[4];
-    bool valid[4];
-    if (partial || mask)  // uniform: only the rare masked tiles test positions
-        q4_scores<true>(p, sc, corr, tok0, tlo, thi, partial, mask, col, G, sv, valid);
+    uint2 vs = T.vs, vm = T.vm;
+    if (masked)  // only the rare masked tiles test positions
+        q4_scores<true>(p, sc, corr, tok0, tlo, thi, col, G, sv, vs, vm);
     else
-        q4_scores<false>(p, sc, corr, tok0, tlo, thi, partial, mask, col, G, sv, valid);
-    q4_softmax_pv(p, T, sv, valid, G, st);
+        q4_scores<false>(p, sc, corr, tok0, tlo, thi, col, G, sv, vs, vm);
+    q4_softmax_pv(p, T, sv, vs, vm, st);
 }
 
 // Fused append of a decode step with one new token per sequence, INT4 pool
@@ -1068,10 +1095,14 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     };
     auto is_full = [&](int j) { return (j + 1) * kBlock <= r.n; };
     gu16_t *tail_row = global_u16(p.pool.ktail) + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
+    // blocks [jA, jB) lie inside every column's range (needs_mask is false
+    // there); a partial or last block never does
+    const int jA = (r.all_lo + kBlock - 1) / kBlock, jB = r.all_hi > 0 ? r.all_hi / kBlock : 0;
     auto step = [&](const Q4Tile &T, int j) {
         const int tok0 = j * kBlock;
+        const bool masked = j < jA || j >= jB;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
-        q4_block<NP>(p, T, Q, is_full(j), tail_row, tok0, tlo, thi, needs_mask(tok0, r), col, n16, G, L, st);
+        q4_block<NP>(p, T, Q, masked, !masked || is_full(j), tail_row, tok0, tlo, thi, col, n16, G, L, st);
     };
     // Fused append (decode step, one new token at position r.n - 1): the
     // segment that ends with the sequence's last block codes the token into
