@@ -89,6 +89,11 @@ PoolPtrs pool_ptrs(const kv_pool *p) {
     q.vs = reinterpret_cast<uint16_t *>(at(KV_REGION_VS));
     q.vm = reinterpret_cast<uint16_t *>(at(KV_REGION_VM));
     q.ktail = reinterpret_cast<uint16_t *>(at(KV_REGION_KTAIL));
+    q.q4_span = 0;
+    if (p->desc.dtype == KV_INT4) {
+        const size_t span = p->off[KV_REGION_VM] + p->len[KV_REGION_VM] - p->off[KV_REGION_KQ];
+        if (span <= UINT32_MAX) q.q4_span = (uint32_t)span;
+    }
     return q;
 }
 

@@ -803,6 +803,42 @@ __device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, 
     T.vm = make_uint2(m[0], m[1]);
 }
 
+// The same loads when the pool's INT4 arrays, from the K codes to the end
+// of the V minimums, span less than 4 GiB: one buffer descriptor over that
+// span for the whole segment, and each tile reached through 32-bit scalar
+// offsets (a handful of scalar instructions per tile instead of six
+// descriptors built from 64-bit addresses).
+struct Q4Flat {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t vq, ks, km, vs, vm;  // byte offsets of the other arrays from the K codes
+};
+__device__ __forceinline__ Q4Flat q4_flat(const AttnParams &p) {
+    const char *kq = reinterpret_cast<const char *>(p.pool.kq);
+    auto off = [&](const void *a) { return (uint32_t)(reinterpret_cast<const char *>(a) - kq); };
+    Q4Flat f;
+    f.rsrc = tile_rsrc(p.pool.kq, (int)p.pool.q4_span);
+    f.vq = off(p.pool.vq);
+    f.ks = off(p.pool.ks);
+    f.km = off(p.pool.km);
+    f.vs = off(p.pool.vs);
+    f.vm = off(p.pool.vm);
+    return f;
+}
+__device__ __forceinline__ void q4_fetch_flat(const Q4Flat &f, uint32_t tile, int n16, int G, Q4Tile &T) {
+    const uint32_t codes = tile * (kBlock * 64), kpar = tile * 256, vpar = tile * (kBlock * 2);
+    T.kc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, n16 * 64 + 16 * G, codes,
+                                                                           kLoadStream));
+    T.ks = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, 16 * n16, f.ks + kpar, kLoadStream));
+    T.km = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, 16 * n16, f.km + kpar, kLoadStream));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        T.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(f.rsrc, (4 * G + i) * 64 + 4 * n16, f.vq + codes, kLoadStream);
+    const u32x2_t s = __builtin_amdgcn_raw_buffer_load_b64(f.rsrc, 8 * G, f.vs + vpar, kLoadStream);
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(f.rsrc, 8 * G, f.vm + vpar, kLoadStream);
+    T.vs = make_uint2(s[0], s[1]);
+    T.vm = make_uint2(m[0], m[1]);
+}
+
 
 // 8 codes of one dword (channel 2k in the low nibble of byte k) as exact bf16.
 // Each code goes to a byte of its own, in channel order; a byte c < 16 read
@@ -1038,8 +1074,9 @@ __device__ __forceinline__ void q4_append_token(const AttnParams &p, int b, int 
 }
 
 // Blocks [j0, j1) (at most kSidsWindow) of sequence b, kv head kvh, column
-// tile ct; init: start a new state, else continue st.
-template <int D, int NP>
+// tile ct; init: start a new state, else continue st. FLAT: tiles addressed
+// as in q4_fetch_flat (the launch checks the pool's span).
+template <int D, int NP, bool FLAT>
 __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
                                            int *sids, bool init) {
@@ -1111,10 +1148,14 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     // tile waits for the coded token's stores.
     const bool append = p.k_new && ct == 0 && j1 == r.blk_lo + r.nblk && !bad;
     bool appended = false;
+    const Q4Flat flat = FLAT ? q4_flat(p) : Q4Flat{};
     auto fetch = [&](int j, Q4Tile &T) {
         const int jc = j < j1 ? j : j1 - 1;  // past the end: re-read the last tile (cached)
         if (appended && jc == j1 - 1) __builtin_amdgcn_s_waitcnt(0);
-        q4_fetch(p, pid_of(jc), kvh, n16, G, T);
+        if constexpr (FLAT)
+            q4_fetch_flat(flat, (uint32_t)(pid_of(jc) * p.n_kv + kvh), n16, G, T);
+        else
+            q4_fetch(p, pid_of(jc), kvh, n16, G, T);
     };
     Q4Tile A, B;
     if (!append || j0 < j1 - 1) fetch(j0, A);
@@ -1141,8 +1182,9 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
 // (the launch sets it when a kv head's columns take several units, each
 // reading every K/V tile: the tiles then stay in the caches for the other
 // units, which read them about the same time; 8B shape, 16 query tokens:
-// 286 -> 256 us; with one unit per kv head they cost 4 %).
-template <int D, int Q4, int CT, bool KEEP>
+// 286 -> 256 us; with one unit per kv head they cost 4 %). FLAT: INT4 tiles
+// addressed through one descriptor (q4_fetch_flat).
+template <int D, int Q4, int CT, bool KEEP, bool FLAT>
 __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct0, const Column *col,
                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st, bool &bad,
                                             int *sids) {
@@ -1150,7 +1192,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
         static_assert(CT == 1, "the INT4 path takes one column tile per unit");
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
             static_assert(!KEEP, "the INT4 path streams its tiles");
-            q4_segment<D, Q4>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init);
+            q4_segment<D, Q4, FLAT>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init);
         });
     } else {
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
@@ -1166,7 +1208,7 @@ __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh,
 
 // Work unit u of a sequence: kv head u / groups, column tiles CT * (u % groups)
 // .. + CT - 1 (groups = units / n_kv).
-template <int D, int Q4, int CT, bool KEEP = false>
+template <int D, int Q4, int CT, bool KEEP = false, bool FLAT = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams p) {
     extern __shared__ int sids[];  // [min(split_blocks, kSidsWindow)] staged block ids
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
@@ -1180,7 +1222,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
 #pragma unroll
     for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, w.r);
     MfmaState<D> st[CT];
-    run_segment<D, Q4, CT, KEEP>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
+    run_segment<D, Q4, CT, KEEP, FLAT>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
         const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
@@ -1230,7 +1272,7 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
     return carry;
 }
 
-template <int D, int Q4, int CT, bool KEEP = false>
+template <int D, int Q4, int CT, bool KEEP = false, bool FLAT = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] block prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
@@ -1282,7 +1324,8 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 #pragma unroll
         for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, r);
         MfmaState<D> st[CT];
-        run_segment<D, Q4, CT, KEEP>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad, sids);
+        run_segment<D, Q4, CT, KEEP, FLAT>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad,
+                                           sids);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
@@ -2194,6 +2237,7 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
     if (kernel == 2) {
         const bool q4 = dtype == KV_INT4;
         const bool keep = p.units > p.n_kv;  // several units per kv head: cached loads
+        const bool flat = p.pool.q4_span > 0;  // INT4 arrays within 4 GiB: one descriptor
         if (p.schedule == KV_SCHED_BALANCED) {
             const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
@@ -2206,7 +2250,13 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
                     hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 2>), bg, dim3(128), lds, s, e0, e1, 0, p);
                 else
                     hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 4>), bg, dim3(256), lds, s, e0, e1, 0, p);
-            } else if (q4 && p.ncols <= 4)
+            } else if (q4 && p.ncols <= 4 && flat)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1, false, true>), bg, dim3(64), lds, s, e0, e1,
+                                      0, p);
+            else if (q4 && flat)
+                hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4, 1, false, true>), bg, dim3(64), lds, s, e0, e1,
+                                      0, p);
+            else if (q4 && p.ncols <= 4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 4, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
@@ -2224,7 +2274,11 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 0, 1>), bg, dim3(64), lds, s, e0, e1, 0, p);
         } else {
             const uint32_t lds = (uint32_t)(min(p.split_blocks, kSidsWindow) * sizeof(int));
-            if (q4 && p.ncols <= 4)
+            if (q4 && p.ncols <= 4 && flat)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1, 1, false, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (q4 && flat)
+                hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4, 1, false, true>), grid, dim3(64), lds, s, e0, e1, 0, p);
+            else if (q4 && p.ncols <= 4)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 1, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);
             else if (q4)
                 hipExtLaunchKernelGGL((attn_mfma_kernel<128, 4, 1>), grid, dim3(64), lds, s, e0, e1, 0, p);

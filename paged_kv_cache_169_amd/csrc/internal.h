@@ -19,6 +19,7 @@ struct PoolPtrs {
     uint8_t *kq, *vq;            // int4 codes
     uint16_t *ks, *km, *vs, *vm; // fp16 scale / min
     uint16_t *ktail;             // bf16 K tail
+    uint32_t q4_span;            // INT4: bytes from kq to the end of vm when below 4 GiB, else 0
 };
 
 // Everything a kernel needs about one attention call. Passed by value.

@@ -6,6 +6,8 @@ bit-exact for append, INT4 coding and RoPE; max |error| <= 2e-3 for attention
 (fp32 outputs vs fp64 oracle). Unused pool slots hold NaN so that a stray
 read shows up as NaN in the output.
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -779,6 +781,43 @@ def test_multi_token_int4(split):
     Kd, Vd = orc.q4_dequant(img, tab, lens_np)
     ref = orc.attention_multi(Kd, Vd, bits(q), tab, lens_np, c.scale)
     assert max_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_int4_pool_over_4gib(k):
+    """The same INT4 tiles in a small pool (its INT4 arrays span less than
+    4 GiB: one buffer descriptor, 32-bit tile offsets) and at the far end of a
+    4.4 GB pool (per-tile descriptors from 64-bit addresses): bitwise equal
+    outputs on both schedules, for one query token (at most four query
+    columns per kv head) and for three."""
+    lens = [700, 37, 1500]
+    c = int4_case(995 + k, lens, n_h=16, n_kv=8, d=128)
+    c.append = False
+    c.ctx_lens = c.seq_lens.clone()
+    src, dst, img = int4_pools(c, len(lens))
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
+    nb_big = 210_000
+    big = kv.KVPool(nb_big, c.n_kv, c.d, "int4", max_seqs=len(lens), device=DEV)
+    assert big.nbytes > (1 << 32) + (1 << 26)  # the INT4 arrays alone span more than 4 GiB
+    ids = torch.arange(c.num_blocks, device=DEV)
+    moved = nb_big - 1 - ids  # block i of the small pool -> block nb_big - 1 - i
+    for name in ["KQ", "KS", "KM", "VQ", "VS", "VM"]:
+        getattr(big, name)[moved] = getattr(dst, name)[ids]
+    big.KTAIL.copy_(dst.KTAIL)
+    far = copy.copy(c)
+    far.tables = torch.where(c.tables >= 0, nb_big - 1 - c.tables, c.tables)
+    g = torch.Generator(device=DEV).manual_seed(40 + k)
+    q = torch.randn((c.batch, k, c.n_h, 128), generator=g, device=DEV).to(torch.bfloat16)
+    tab, lens_np = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens_np)
+    Kd, Vd = orc.q4_dequant(img, tab, lens_np)
+    ref = orc.attention_multi(Kd, Vd, bits(q), tab, lens_np, c.scale)
+    for schedule, split in [(0, 0), (1, 40)]:
+        a = gpu_multi(dst, c, q, split_blocks=split, schedule=schedule)
+        b = gpu_multi(big, far, q, split_blocks=split, schedule=schedule)
+        assert np.array_equal(a, b)
+        assert max_err(a, ref) <= TOL
+    del big
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "int4"])
