@@ -110,6 +110,15 @@ constexpr float kLazyLog2 = 8.0f;
 // registers and cost vector instructions on every tile.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Orders one wave's LDS accesses for its other lanes, for workgroups of a
+// single wave: the LDS executes a wave's instructions in issue order, so no
+// barrier or wait is needed, only that the compiler keeps the order.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Max / sum over lanes l, l^16, l^32, l^48: the four lanes that hold one
 // column in the 16x16 MFMA layouts. gfx950's lane-swap instructions do both
 // butterfly steps inside the VALU (no LDS round trip); every lane of the
@@ -879,32 +888,25 @@ struct Q4Query {
     int npass;
 };
 
-// Scores of one INT4 tile in log2 units, from its raw products sc (before
-// the per-column min term corr). MASKED: some slots of the tile are outside
-// the attended range (partial block, window, causal columns); they get -inf,
-// and their V scale and min, which may be anything there, are set to 0 so
-// that their zero weights contribute exactly 0.
-template <bool MASKED>
-__device__ __forceinline__ void q4_scores(const AttnParams &p, const f32x4_t &sc, float corr, int tok0, int tlo,
-                                          int thi, const Column &col, int G, float (&sv)[4], uint2 &vs, uint2 &vm) {
+// Masking of an INT4 tile some of whose slots are outside the attended
+// range (partial block, window, causal columns), in place: their scores sv
+// become -inf, and their V scale and min (vs, vm), which may be anything
+// there, 0, so that their zero weights contribute exactly 0.
+__device__ __forceinline__ void q4_mask(int tok0, int tlo, int thi, const Column &col, int G, float (&sv)[4],
+                                        uint2 &vs, uint2 &vm) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float s = (sc[r] + corr) * p.scale_log2;
-        if (MASKED) {
-            const int tt = 4 * G + r, tp = tok0 + tt;
-            const bool ok = (tt >= tlo) & (tt < thi) & (tp >= col.lo) & (tp < col.hi);
-            sv[r] = ok ? s : -INFINITY;
-            const uint32_t keep = ok ? 0xffffffffu : 0u, half = (r & 1) ? 0xffff0000u : 0x0000ffffu;
-            const uint32_t clear = ~half | keep;  // all ones, or the slot's half cleared
-            if (r < 2) {
-                vs.x &= clear;
-                vm.x &= clear;
-            } else {
-                vs.y &= clear;
-                vm.y &= clear;
-            }
+        const int tt = 4 * G + r, tp = tok0 + tt;
+        const bool ok = (tt >= tlo) & (tt < thi) & (tp >= col.lo) & (tp < col.hi);
+        sv[r] = ok ? sv[r] : -INFINITY;
+        const uint32_t keep = ok ? 0xffffffffu : 0u, half = (r & 1) ? 0xffff0000u : 0x0000ffffu;
+        const uint32_t clear = ~half | keep;  // all ones, or the slot's half cleared
+        if (r < 2) {
+            vs.x &= clear;
+            vm.x &= clear;
         } else {
-            sv[r] = s;
+            vs.y &= clear;
+            vm.y &= clear;
         }
     }
 }
@@ -989,7 +991,7 @@ template <int NP>
 __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const Q4Query<NP> &Q, bool masked,
                                          bool full, gu16_t *tail_row, int tok0, int tlo, int thi,
                                          const Column &col, int n16, int G, Q4Lds &L, MfmaState<128> &st) {
-    __syncthreads();  // the previous tile's reads of L are done
+    wave_lds_sync();  // the previous tile's reads of L come first (one-wave workgroup)
     const uint32_t sw[4] = {T.ks.x, T.ks.y, T.ks.z, T.ks.w}, mw[4] = {T.km.x, T.km.y, T.km.z, T.km.w};
 #pragma unroll
     for (int pi = 0; pi < NP; ++pi) {
@@ -1017,7 +1019,7 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         }
         L.b[0][c][n16] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     }
-    __syncthreads();
+    wave_lds_sync();
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
@@ -1039,12 +1041,11 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
         }
     }
-    float sv[4];
+    float sv[4];  // scores in log2 units
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (sc[r] + corr) * p.scale_log2;
     uint2 vs = T.vs, vm = T.vm;
-    if (masked)  // only the rare masked tiles test positions
-        q4_scores<true>(p, sc, corr, tok0, tlo, thi, col, G, sv, vs, vm);
-    else
-        q4_scores<false>(p, sc, corr, tok0, tlo, thi, col, G, sv, vs, vm);
+    if (masked) q4_mask(tok0, tlo, thi, col, G, sv, vs, vm);  // only the rare masked tiles test positions
     q4_softmax_pv(p, T, sv, vs, vm, st);
 }
 
