@@ -1360,10 +1360,10 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 // ---------------------------------------------------------------------------
 // wide work units (bf16, many query columns per kv head)
 //
-// A unit of 2W column tiles is one workgroup of W waves (two column tiles per
-// wave, as in bf16_segment_ct): the waves load each (block, kv head) K/V tile
-// once, together, into LDS and each reads it back in the MFMA operand layout.
-// So a K/V tile leaves HBM once per 2W column tiles instead of once per two.
+// A unit of CT W column tiles is one workgroup of W waves (CT column tiles
+// per wave, as in bf16_segment_ct): the waves load each (block, kv head) K/V
+// tile once, together, into LDS and each reads it back in the MFMA operand
+// layout. So a K/V tile leaves HBM once per CT W column tiles.
 // The LDS tiles are double-buffered: the next tile's global loads are in
 // flight while the current one is used, and one barrier per tile orders both.
 // ---------------------------------------------------------------------------
@@ -1383,6 +1383,12 @@ struct TileLds {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Column tiles per wave of the wide kernels (units of 4 or 8 column tiles).
+// One per wave (4 or 8 waves, no spilled registers) measured slower than two
+// (the K/V operands read from LDS serve both): 8B shape, 16 query tokens 218
+// vs 203 us, 32 tokens 384 vs 326 us.
+constexpr int kWideCT = 2;
 
 // Issues this wave's share of one tile's loads straight into LDS
 // (global_load_lds, 16 bytes per lane): instruction q of the tile fills slots
@@ -1432,17 +1438,17 @@ __device__ __forceinline__ void wide_operands(const TileLds<D> &t, int n16, int 
 }
 
 // Blocks [j0, j1) (at most kSidsWindow) of sequence b, kv head kvh for this
-// wave's two column tiles (col, st; init: start a new state). Every wave of
+// wave's CT column tiles (col, st; init: start a new state). Every wave of
 // the workgroup calls it with the same blocks.
-template <int D, int W>
+template <int D, int W, int CT>
 __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh, const Column *col,
                                              const SeqRange &r, int j0, int j1, int tid, MfmaState<D> *st, bool &bad,
                                              bool write_new, int *sids, TileLds<D> (&tl)[2], bool init) {
     constexpr int KS = D / 32, MS = D / 16;
     const int lane = tid & 63, n16 = lane & 15, G = lane >> 4;
-    bf16x8_t qB[2][KS];
+    bf16x8_t qB[CT][KS];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -1453,7 +1459,7 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
         }
     if (init) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < CT; ++c) {
 #pragma unroll
             for (int m = 0; m < MS; ++m) st[c].o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             st[c].m = -INFINITY;
@@ -1497,17 +1503,17 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
+        for (int c = 0; c < CT; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
         __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads have landed
         __syncthreads();
     }
 }
 
 // Balanced schedule over wide units: as attn_mfma_balanced_kernel, with one
-// workgroup of W waves per share; wave w takes column tiles 2w, 2w + 1 of the
-// unit. Partial slots hold the unit's 32 W columns (row 16 c + n16 for the
-// unit's column tile c).
-template <int D, int W>
+// workgroup of W waves per share; wave w takes column tiles CT w .. CT w +
+// CT - 1 of the unit. Partial slots hold the unit's 16 CT W columns (row
+// 16 c + n16 for the unit's column tile c).
+template <int D, int W, int CT>
 __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
@@ -1549,15 +1555,15 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
         const int cnt = (int)(seg_end - t);
         const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         bool bad = r.bad;
-        Column col[2];
+        Column col[CT];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) col[c] = column_of(p, b, kvh, cu + 2 * wave + c, n16, r);
-        MfmaState<D> st[2];
+        for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, cu + CT * wave + c, n16, r);
+        MfmaState<D> st[CT];
         run_pieces(r.blk_lo + jr, r.blk_lo + jr + cnt, [&](int c0, int c1, bool init) {
-            wide_segment<D, W>(p, b, kvh, col, r, c0, c1, tid, st, bad, cu == 0, sids, tl, init);
+            wide_segment<D, W, CT>(p, b, kvh, col, r, c0, c1, tid, st, bad, cu == 0, sids, tl, init);
         });
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < CT; ++c) {
             const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
             if (col[c].valid) {
                 float res[D / 4];
@@ -1570,7 +1576,7 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
                     for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k] * inv;
                 } else {
                     const int slot = jr > 0 ? 0 : 1;
-                    const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + (2 * wave + c) * 16 + n16;
+                    const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + (CT * wave + c) * 16 + n16;
                     float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
                     for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k];
@@ -2242,15 +2248,16 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
         if (p.schedule == KV_SCHED_BALANCED) {
             const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
             const dim3 bg(p.n_wg);
-            if (!q4 && p.ctw > 2) {  // wide units: W = ctw / 2 waves per workgroup
+            if (!q4 && p.ctw > 2) {  // wide units: ctw / kWideCT waves per workgroup
+                constexpr int C = kWideCT, W4 = 4 / C, W8 = 8 / C;
                 if (p.head_dim == 64 && p.ctw == 4)
-                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, 2>), bg, dim3(128), lds, s, e0, e1, 0, p);
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, W4, C>), bg, dim3(64 * W4), lds, s, e0, e1, 0, p);
                 else if (p.head_dim == 64)
-                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, 4>), bg, dim3(256), lds, s, e0, e1, 0, p);
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<64, W8, C>), bg, dim3(64 * W8), lds, s, e0, e1, 0, p);
                 else if (p.ctw == 4)
-                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 2>), bg, dim3(128), lds, s, e0, e1, 0, p);
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, W4, C>), bg, dim3(64 * W4), lds, s, e0, e1, 0, p);
                 else
-                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 4>), bg, dim3(256), lds, s, e0, e1, 0, p);
+                    hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, W8, C>), bg, dim3(64 * W8), lds, s, e0, e1, 0, p);
             } else if (q4 && p.ncols <= 4 && flat)
                 hipExtLaunchKernelGGL((attn_mfma_balanced_kernel<128, 1, 1, false, true>), bg, dim3(64), lds, s, e0, e1,
                                       0, p);
@@ -2326,21 +2333,24 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     return cus * per_cu;
 }
 
-int wide_grid(int head_dim, int waves, int batch, int max_blocks) {
+int wide_grid(int head_dim, int ctw, int batch, int max_blocks) {
+    constexpr int C = kWideCT, W4 = 4 / C, W8 = 8 / C;
+    const int waves = ctw / C;
     int dev = 0, cus = 0, per_cu = 0;
     const size_t lds = (size_t)(batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256 * 2 / waves;
+        return 1024 / ctw;
     hipError_t e;
     if (head_dim == 64)
-        e = waves == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, 2>, 128, lds)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, 4>, 256, lds);
+        e = ctw == 4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, W4, C>, 64 * W4, lds)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<64, W8, C>, 64 * W8, lds);
     else
-        e = waves == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, 2>, 128, lds)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, 4>, 256, lds);
+        e = ctw == 4
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, W4, C>, 64 * W4, lds)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_wide_kernel<128, W8, C>, 64 * W8, lds);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    if (per_cu > 8 / waves) per_cu = 8 / waves;  // two waves per SIMD, as balanced_grid
+    if (per_cu > std::max(8 / waves, 1)) per_cu = std::max(8 / waves, 1);  // two waves per SIMD, as balanced_grid
     return cus * per_cu;
 }
 
