@@ -2140,6 +2140,81 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParam
 }
 
 
+// The same merge for units of many rows (several query tokens): one
+// workgroup per group of rows of a (sequence, unit) pair, each thread one
+// 8-channel chunk of one row, so the pair's pieces are found once per group
+// and every thread's loads (the pieces' m, l and o) go out together.
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M the largest m_i,
+// as in merge_partials: a NaN l or o makes the row NaN, and a row no piece
+// saw a token for gets 0. Grid (units * groups, batch), 256 threads; a group
+// is 256 / (D / 8) rows, and a unit's slot_cols rows take groups of them.
+__global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParams p) {
+    const int D = p.head_dim, chunks = D / 8, rpg = 256 / chunks;  // chunks per row, rows per group
+    const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;      // column groups per kv head, columns per unit
+    const int groups = (p.slot_cols + rpg - 1) / rpg;              // as the launch: slot_cols = min(ucols, ncols)
+    const int unit = blockIdx.x / groups, b = blockIdx.y;
+    const int row = (blockIdx.x % groups) * rpg + (int)threadIdx.x / chunks, ch = (int)threadIdx.x % chunks;
+    const int kvh = unit / cgroups, ci0 = (unit % cgroups) * ucols;
+    const int rows = min(ucols, p.ncols - ci0);
+    if (row >= rows) return;
+    const int ci = ci0 + row, qi = ci / p.group, head = kvh * p.group + ci % p.group;
+    float4 *dst = reinterpret_cast<float4 *>(p.out + (((size_t)b * p.q_len + qi) * p.n_h + head) * D + ch * 8);
+    const int span = p.ws_prefix[b + 1] - p.ws_prefix[b];  // nb + seg_cost, or 0
+    const int nb = span > 0 ? span - p.seg_cost : 0;
+    if (nb == 0) {
+        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
+        dst[0] = make_float4(v, v, v, v);
+        dst[1] = make_float4(v, v, v, v);
+        return;
+    }
+    const long total = (long)p.ws_prefix[p.batch] * p.units;
+    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
+    const long end = start + nb;
+    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
+    if (w0 == w1) return;  // complete inside one workgroup: already written
+    const int n = w1 - w0 + 1;
+    // workspace row of piece i: the first piece goes on past its range (slot
+    // 1 of its workgroup), the others started before theirs (slot 0)
+    auto ws_row = [&](int i) { return ((size_t)(w0 + i) * 2 + (i == 0 ? 1 : 0)) * p.slot_cols + row; };
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[ws_row(i) * 2]);
+    float L = 0.0f;
+    float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
+    if (M != -INFINITY) {
+        constexpr int NB = 4;  // pieces whose loads go out together
+        for (int i0 = 0; i0 < n; i0 += NB) {
+            float m[NB], l[NB];
+            float4 o[NB][2];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const size_t r = ws_row(min(i0 + k, n - 1));  // past the end: re-read, weight 0
+                m[k] = p.ws_ml[r * 2];
+                l[k] = p.ws_ml[r * 2 + 1];
+                const float4 *src = reinterpret_cast<const float4 *>(p.ws_o + r * D + ch * 8);
+                o[k][0] = src[0];
+                o[k][1] = src[1];
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const float w = i0 + k < n ? fast_exp2(m[k] - M) : 0.0f;
+                L = fmaf(w, l[k], L);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    acc[h].x = fmaf(w, o[k][h].x, acc[h].x);
+                    acc[h].y = fmaf(w, o[k][h].y, acc[h].y);
+                    acc[h].z = fmaf(w, o[k][h].z, acc[h].z);
+                    acc[h].w = fmaf(w, o[k][h].w, acc[h].w);
+                }
+            }
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dst[h] = make_float4(acc[h].x * inv, acc[h].y * inv, acc[h].z * inv, acc[h].w * inv);
+}
+
 // Merge of the shared-prefix call: one wave per (sequence, head) row with
 // more than one part (a prefix, or several suffix splits).
 __global__ __launch_bounds__(64) void attn_merge_shared_kernel(AttnParams p, PrefixArgs g) {
@@ -2376,11 +2451,17 @@ int shared_balanced_grid(int head_dim, size_t lds) {
 // of 5-16 rows when there are at least 2048 units (measured: the 70B-shaped
 // merge 8.7 -> 4.4 us; with 512 units, 8 or 16 rows each, it was slower).
 constexpr int kMergeUnitRows = 5, kMergeUnitMin = 2048;
+// Units of more rows than this take attn_merge_balanced_rows_kernel.
+constexpr int kMergeRowsMin = 17;
 
 hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
     const bool none = p.batch == 0 || (p.schedule != KV_SCHED_BALANCED && p.max_splits <= 1);
     if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
-    if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
+    if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeRowsMin) {
+        const int groups = (p.slot_cols + 256 / (p.head_dim / 8) - 1) / (256 / (p.head_dim / 8));
+        hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel, dim3(p.units * groups, p.batch), dim3(256), 0, s,
+                              nullptr, e_end, 0, p);
+    } else if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
         (long)p.batch * p.units >= kMergeUnitMin)
         hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel, dim3(p.units, p.batch), dim3(256), 0, s, nullptr, e_end,
                               0, p);
