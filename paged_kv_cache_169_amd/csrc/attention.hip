@@ -2178,12 +2178,18 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParam
     // workspace row of piece i: the first piece goes on past its range (slot
     // 1 of its workgroup), the others started before theirs (slot 0)
     auto ws_row = [&](int i) { return ((size_t)(w0 + i) * 2 + (i == 0 ? 1 : 0)) * p.slot_cols + row; };
+    constexpr int NB = 4;  // pieces whose loads go out together
     float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[ws_row(i) * 2]);
+    for (int i0 = 0; i0 < n; i0 += NB) {
+        float m[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) m[k] = p.ws_ml[ws_row(min(i0 + k, n - 1)) * 2];  // past the end: a repeat
+#pragma unroll
+        for (int k = 0; k < NB; ++k) M = fmaxf(M, m[k]);
+    }
     float L = 0.0f;
     float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
     if (M != -INFINITY) {
-        constexpr int NB = 4;  // pieces whose loads go out together
         for (int i0 = 0; i0 < n; i0 += NB) {
             float m[NB], l[NB];
             float4 o[NB][2];
