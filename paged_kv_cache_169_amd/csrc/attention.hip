@@ -28,7 +28,7 @@
 //  * balanced (attn_mfma_balanced_kernel, the default): a persistent grid of
 //    two waves per SIMD; every workgroup takes an equal share of all tiles of
 //    the call; pairs cut between workgroups are merged by
-//    attn_merge_balanced_kernel / attn_merge_balanced_unit_kernel.
+//    attn_merge_balanced_rows_kernel / attn_merge_balanced_unit_kernel.
 //  * shared prefixes (attn_mfma_shared_balanced_kernel, attn_mfma_shared_kernel):
 //    a group's shared blocks are read once with the members' queries as the
 //    columns.
@@ -1246,8 +1246,8 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
 // partial in slot 0 of the workgroup's two workspace slots when the pair
 // started before the range (only a workgroup's first piece can), else in
 // slot 1 (the pair goes on past the range: only its last piece can);
-// attn_merge_balanced_kernel combines them. Workgroup 0 also stores the
-// prefix sums for the merge.
+// attn_merge_balanced_rows_kernel (or _unit_kernel) combines them.
+// Workgroup 0 also stores the prefix sums for the merge.
 __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, int lane) {
     // pre[b] = positions of sequences < b per unit (attended blocks plus
     // seg_cost for a sequence with any), in LDS; returns pre[batch]
@@ -2060,45 +2060,11 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
     merge_partials(p, r.nsplit, [&](int s) { return base + s; }, lane, cv, p.out + row * p.head_dim + lane * cv);
 }
 
-// Merge for the balanced schedule: one wave per output row (query token,
-// head) of each sequence. Finds the workgroups whose tile ranges cut the
-// row's (sequence, unit) pair and combines their partials; writes 0 (or NaN
-// for a bad sequence) when the sequence has no attended block.
-__global__ __launch_bounds__(64) void attn_merge_balanced_kernel(AttnParams p) {
-    const int b = blockIdx.y, lane = threadIdx.x;
-    const int head = blockIdx.x % p.n_h, qi = blockIdx.x / p.n_h;
-    const int D = p.head_dim, cv = D / 64;
-    const int kvh = head / p.group, ci = qi * p.group + head % p.group;
-    const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;  // column groups per kv head, columns per unit
-    const int unit = kvh * cgroups + ci / ucols, n16 = ci % ucols;  // n16: the row within the unit's slot
-    const int span = p.ws_prefix[b + 1] - p.ws_prefix[b];  // nb + seg_cost, or 0
-    const int nb = span > 0 ? span - p.seg_cost : 0;
-    float *dst = p.out + ((size_t)b * p.q_len * p.n_h + blockIdx.x) * D + lane * cv;
-    if (nb == 0) {
-        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
-        const float v = r.bad ? __uint_as_float(0x7fc00000u) : 0.0f;
-        for (int c = 0; c < cv; ++c) dst[c] = v;
-        return;
-    }
-    const long total = (long)p.ws_prefix[p.batch] * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
-    const long end = start + nb;
-    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
-    if (w0 == w1) return;  // complete inside one workgroup: already written
-    // workspace row of the partial that workgroup w holds for this pair: the
-    // first piece goes on past its range (slot 1), the others started before
-    // theirs (slot 0)
-    auto ws_row = [&](int w) {
-        const int slot = w == w0 ? 1 : 0;
-        return ((size_t)w * 2 + slot) * p.slot_cols + n16;
-    };
-    merge_partials(p, w1 - w0 + 1, [&](int i) { return ws_row(w0 + i); }, lane, cv, dst);
-}
-
-// The same merge with one workgroup of four waves per (sequence, unit) pair,
-// the waves taking the unit's output rows (query token, head) in turn: fewer,
-// larger workgroups.
+// Merge for the balanced schedule with one workgroup of four waves per
+// (sequence, unit) pair, the waves taking the unit's output rows (query
+// token, head) in turn; each row combines the partials of the workgroups
+// whose tile ranges cut the pair, and gets 0 (NaN for a bad sequence) when
+// the sequence has no attended block.
 __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParams p) {
     const int unit = blockIdx.x, b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = 4;
@@ -2140,16 +2106,16 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParam
 }
 
 
-// The same merge for units of many rows (several query tokens): one
-// workgroup per group of rows of a (sequence, unit) pair, each thread one
-// 8-channel chunk of one row, so the pair's pieces are found once per group
-// and every thread's loads (the pieces' m, l and o) go out together.
-// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M the largest m_i,
-// as in merge_partials: a NaN l or o makes the row NaN, and a row no piece
-// saw a token for gets 0. Grid (units * groups, batch), 256 threads; a group
-// is 256 / (D / 8) rows, and a unit's slot_cols rows take groups of them.
+// The same merge with one workgroup per group of rows of a (sequence, unit)
+// pair, each thread one 8-channel chunk of one row, so the pair's pieces are
+// found once per group and every thread's loads (the pieces' m, l and o) go
+// out together. out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M
+// the largest m_i, as in merge_partials: a NaN l or o makes the row NaN, and
+// a row no piece saw a token for gets 0. Grid (units * groups, batch); a
+// group is blockDim / (D / 8) rows, and a unit's slot_cols rows take groups
+// of them.
 __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParams p) {
-    const int D = p.head_dim, chunks = D / 8, rpg = 256 / chunks;  // chunks per row, rows per group
+    const int D = p.head_dim, chunks = D / 8, rpg = (int)blockDim.x / chunks;  // chunks per row, rows per group
     const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;      // column groups per kv head, columns per unit
     const int groups = (p.slot_cols + rpg - 1) / rpg;              // as the launch: slot_cols = min(ucols, ncols)
     const int unit = blockIdx.x / groups, b = blockIdx.y;
@@ -2453,28 +2419,27 @@ int shared_balanced_grid(int head_dim, size_t lds) {
     return cus * per_cu;
 }
 
-// One four-wave workgroup per unit rather than one wave per row: for units
-// of 5-16 rows when there are at least 2048 units (measured: the 70B-shaped
-// merge 8.7 -> 4.4 us; with 512 units, 8 or 16 rows each, it was slower).
+// One four-wave workgroup per unit for units of 5-16 rows when there are at
+// least 2048 units (the 70B-shaped merge 4.2 us, 4.6 with row groups);
+// otherwise row groups (one wave per row before them: 8B shape 5.4 -> 5.1
+// us, 4 query tokens 10.9 -> 7.3, 16 query tokens 25 -> 14).
 constexpr int kMergeUnitRows = 5, kMergeUnitMin = 2048;
-// Units of more rows than this take attn_merge_balanced_rows_kernel.
-constexpr int kMergeRowsMin = 17;
 
 hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
     const bool none = p.batch == 0 || (p.schedule != KV_SCHED_BALANCED && p.max_splits <= 1);
     if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
-    if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeRowsMin) {
-        const int groups = (p.slot_cols + 256 / (p.head_dim / 8) - 1) / (256 / (p.head_dim / 8));
-        hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel, dim3(p.units * groups, p.batch), dim3(256), 0, s,
-                              nullptr, e_end, 0, p);
-    } else if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
-        (long)p.batch * p.units >= kMergeUnitMin)
+    if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
+        (long)p.batch * p.units >= kMergeUnitMin) {
         hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel, dim3(p.units, p.batch), dim3(256), 0, s, nullptr, e_end,
                               0, p);
-    else if (p.schedule == KV_SCHED_BALANCED)
-        hipExtLaunchKernelGGL(attn_merge_balanced_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, nullptr,
-                              e_end, 0, p);
-    else
+    } else if (p.schedule == KV_SCHED_BALANCED) {
+        // whole waves, up to 256 threads: 16 rows of 128 channels, 32 of 64
+        const int chunks = p.head_dim / 8;
+        const int threads = std::min(256, (p.slot_cols * chunks + 63) / 64 * 64), rpg = threads / chunks;
+        const int groups = (p.slot_cols + rpg - 1) / rpg;
+        hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel, dim3(p.units * groups, p.batch), dim3(threads), 0, s,
+                              nullptr, e_end, 0, p);
+    } else
         hipExtLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, nullptr, e_end, 0,
                               p);
     return hipGetLastError();
