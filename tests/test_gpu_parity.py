@@ -783,6 +783,28 @@ def test_multi_token_int4(split):
     assert max_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("n_h,k", [(32, 16), (64, 3), (32, 4)])
+def test_multi_token_merge_many_pieces(n_h, k):
+    """Long contexts beside empty, short and invalid (negative length)
+    sequences, several query tokens: a (sequence, unit) pair is cut into many
+    pieces that the row-group merge combines (64, 24 and 16 rows per unit);
+    the invalid sequence's rows are NaN."""
+    lens = [9000, 4000, 0, 40, 20]
+    c = wl.make_case(1010 + k, len(lens), lens, n_h, 8, 128, "bf16", append=False, device=DEV)
+    pool = new_pool(c)
+    g = torch.Generator(device=DEV).manual_seed(k)
+    q = torch.randn((c.batch, k, n_h, 128), generator=g, device=DEV).to(torch.bfloat16)
+    bad = 4
+    c.ctx_lens[bad] = -5
+    out = gpu_multi(pool, c, q)
+    good = [0, 1, 2, 3]
+    tab, ctx = c.tables.cpu().numpy(), c.ctx_lens.cpu().numpy()
+    ref = orc.attention_multi(bits(c.K), bits(c.V), bits(q)[good], tab[good], ctx[good], c.scale)
+    assert np.all(np.isfinite(out[good]))
+    assert max_err(out[good], ref) <= TOL
+    assert np.all(np.isnan(out[bad]))
+
+
 @pytest.mark.parametrize("k", [1, 3])
 def test_int4_pool_over_4gib(k):
     """The same INT4 tiles in a small pool (its INT4 arrays span less than
