@@ -641,6 +641,27 @@ __device__ __forceinline__ BlockIds stage_block_ids(const AttnParams &p, int b, 
     return ids;
 }
 
+// The same, checking the ids once here rather than per tile (one-wave
+// workgroups): an id outside [0, num_blocks) is staged as 0 and sets bad.
+__device__ __forceinline__ BlockIds stage_checked_block_ids(const AttnParams &p, int b, int j0, int j1, int lane,
+                                                            int *sids, bool &bad) {
+    BlockIds ids;
+    ids.sids = sids;
+    ids.row = p.tables + (size_t)b * p.max_blocks;
+    ids.j0 = j0;
+    __syncthreads();  // earlier reads of sids are done
+    bool wrong = false;
+    for (int i = lane; i < j1 - j0; i += 64) {
+        const int id = ids.row[j0 + i];
+        const bool ok = id >= 0 && id < p.num_blocks;
+        wrong |= !ok;
+        sids[i] = ok ? id : 0;
+    }
+    if (__any(wrong)) bad = true;
+    __syncthreads();
+    return ids;
+}
+
 // Runs seg(c0, c1, init) over [j0, j1) in pieces of at most kSidsWindow
 // blocks; init is true for the first piece only (it resets the softmax
 // state, the others continue it). An empty range still makes one call.
@@ -1084,7 +1105,8 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
     int slot = uniform(p.seq_slots ? p.seq_slots[b] : b);
-    if (slot < 0 || slot >= p.max_seqs) {
+    const bool slot_bad = slot < 0 || slot >= p.max_seqs;
+    if (slot_bad) {
         bad = true;
         slot = 0;
     }
@@ -1122,15 +1144,8 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         L.b[1][c][k] = make_uint4(0, 0, 0, 0);
         if (k < 16) L.corr[c][k] = 0.0f;
     }
-    const BlockIds ids = stage_block_ids(p, b, j0, j1, lane, sids);  // its barriers also cover the zeroing
-    auto pid_of = [&](int j) {
-        int pid = ids.id(j);
-        if (pid < 0 || pid >= p.num_blocks) {
-            bad = true;
-            pid = 0;
-        }
-        return pid;
-    };
+    // every staged id is a valid block (bad ones were replaced by 0)
+    const BlockIds ids = stage_checked_block_ids(p, b, j0, j1, lane, sids, bad);  // its barriers cover the zeroing
     auto is_full = [&](int j) { return (j + 1) * kBlock <= r.n; };
     gu16_t *tail_row = global_u16(p.pool.ktail) + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
     // blocks [jA, jB) lie inside every column's range (needs_mask is false
@@ -1144,26 +1159,27 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     };
     // Fused append (decode step, one new token at position r.n - 1): the
     // segment that ends with the sequence's last block codes the token into
-    // the pool. The first tile's loads are issued before that work (unless
-    // the first tile is the last block), and every load of the last block's
-    // tile waits for the coded token's stores.
-    const bool append = p.k_new && ct == 0 && j1 == r.blk_lo + r.nblk && !bad;
+    // the pool, as the append kernel would: unless the sequence's length or
+    // tail slot is invalid, or its block id for the token. The first tile's
+    // loads are issued before that work (unless the first tile is the last
+    // block), and every load of the last block's tile waits for the coded
+    // token's stores.
+    const bool append = p.k_new && ct == 0 && j1 == r.blk_lo + r.nblk && !r.bad && !slot_bad;
     bool appended = false;
     const Q4Flat flat = FLAT ? q4_flat(p) : Q4Flat{};
     auto fetch = [&](int j, Q4Tile &T) {
         const int jc = j < j1 ? j : j1 - 1;  // past the end: re-read the last tile (cached)
         if (appended && jc == j1 - 1) __builtin_amdgcn_s_waitcnt(0);
         if constexpr (FLAT)
-            q4_fetch_flat(flat, (uint32_t)(pid_of(jc) * p.n_kv + kvh), n16, G, T);
+            q4_fetch_flat(flat, (uint32_t)(ids.id(jc) * p.n_kv + kvh), n16, G, T);
         else
-            q4_fetch(p, pid_of(jc), kvh, n16, G, T);
+            q4_fetch(p, ids.id(jc), kvh, n16, G, T);
     };
     Q4Tile A, B;
     if (!append || j0 < j1 - 1) fetch(j0, A);
     if (append) {
-        const int pid = ids.id(j1 - 1);
-        if (pid < 0 || pid >= p.num_blocks) bad = true;
-        if (!bad) q4_append_token(p, b, kvh, slot, pid, (r.n - 1) % kBlock, lane);
+        const int pid = uniform(ids.row[j1 - 1]);  // the table's entry (a bad one is staged as 0)
+        if (pid >= 0 && pid < p.num_blocks) q4_append_token(p, b, kvh, slot, pid, (r.n - 1) % kBlock, lane);
         appended = true;
         if (j0 == j1 - 1) fetch(j0, A);
     }

@@ -148,6 +148,26 @@ def test_step_int4_bad_rows():
     assert np.array_equal(a[keep].view(np.uint32), o[keep].view(np.uint32))
 
 
+@pytest.mark.parametrize("split", [0, 2])
+def test_step_int4_bad_block_before_the_last(split):
+    """INT4 fused step with an out-of-range block id before a sequence's last
+    block: that sequence's rows are NaN, its new token is still coded into
+    its (valid) last block as the append kernel codes it, and the pools
+    match the separate calls byte for byte."""
+    lens = [100, 60, 200, 31]
+    c = wl.make_case(55 + split, 4, lens, 32, 8, 128, "bf16", pool_slack=1.2, device=DEV, append=True)
+    tables = c.tables.clone()
+    tables[0, 5] = -7            # block 5 of 7; the token goes to block 6
+    tables[2, 0] = 1 << 30       # the first block; the token goes to block 12
+    pa, pb, out_a, out_b = run_both(c, "int4", 1, split, tables=tables)
+    assert np.array_equal(region_bytes(pa), region_bytes(pb)), "pool contents differ"
+    o = out_b.cpu().numpy()
+    assert np.all(np.isnan(o[0])) and np.all(np.isnan(o[2]))
+    a = out_a.cpu().numpy()
+    keep = [1, 3]
+    assert np.array_equal(a[keep].view(np.uint32), o[keep].view(np.uint32))
+
+
 @pytest.mark.parametrize("split", [0, 1])
 def test_step_f32_composed_matches_separate_calls(split):
     c = wl.make_case(51, 4, [37, 50, 16, 0], 4, 2, 64, "f32", pool_slack=1.3, device=DEV, append=True)
