@@ -152,6 +152,24 @@ __device__ __forceinline__ float col_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Cross-lane moves inside each row of 16 lanes (DPP). A row's four banks are
+// lanes 0-3, 4-7, 8-11, 12-15 of it.
+enum { kDppRowShl = 0x100, kDppRowShr = 0x110, kDppRowRor = 0x120 };
+// src moved by CTRL into the lanes of the banks in BANK; other lanes keep old.
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xf, BANK, false));
+}
+// Max / sum over lanes l, l^4, l^8, l^12 (the four banks of a row).
+__device__ __forceinline__ float bank_max(float x) {
+    x = max_raw(x, dpp_f<kDppRowRor + 4, 0xf>(x, x));
+    return max_raw(x, dpp_f<kDppRowRor + 8, 0xf>(x, x));
+}
+__device__ __forceinline__ float bank_sum(float x) {
+    x += dpp_f<kDppRowRor + 4, 0xf>(x, x);
+    return x + dpp_f<kDppRowRor + 8, 0xf>(x, x);
+}
+
 struct SplitWork {
     SeqRange r;
     int j0, j1;  // blocks [j0, j1) of this split
@@ -1000,6 +1018,84 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
     }
 }
 
+// The INT4 tile's softmax and value update for at most four query columns,
+// one score per lane. Only columns 0-3 of the 16-column score product are
+// real, so lane (G, n16) of the product holds four real scores when n16 < 4
+// and none otherwise. Moving them inside each 16-lane row gives lane
+// (G, n16) the score of token 4G + n16/4 and column n16 % 4 (from register
+// n16/4 of lane n16 % 4), so each exponential and weight is formed once. The
+// state (m, l, bv) is per lane for that column; l and bv are summed over the
+// banks and G at the end (q4_state_sum). The weights P' go back to the value
+// product's B layout (lane (G, c < 4) takes those of lane (G, 4i + c)), as
+// bf16 hi + lo parts. sc: raw products before corr (this lane's column's
+// min term); ok: the slot is attended (the caller's mask); vs, vm: the
+// lane's token's V scale and min words and their half (vsh = 0 or 16).
+__device__ __forceinline__ void q4_softmax_pv_one(const AttnParams &p, const Q4Tile &T, float s, bool ok,
+                                                  uint32_t vsw, uint32_t vmw, int vsh, MfmaState<128> &st) {
+    const float cm = col_max(bank_max(s));
+    if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
+        const float mn = fmaxf(st.m, cm);
+        const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
+        st.l *= alpha;
+        st.bv *= alpha;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) st.o[m] *= alpha;
+        st.m = mn;
+    }
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;  // no token seen yet: weight 0
+    const float pr = fast_exp2(s - mref);                 // 0 for a masked slot
+    st.l += pr;
+    // a masked slot's V parameters may be anything: 0 there
+    const float vsc = ok ? f16_bits_to_f((uint16_t)(vsw >> vsh)) : 0.0f;
+    const float vmn = ok ? f16_bits_to_f((uint16_t)(vmw >> vsh)) : 0.0f;
+    const float pv = pr * vsc;
+    st.bv = fmaf(pr, vmn, st.bv);
+    // bf16 hi (low half) and lo (high half) of this lane's weight
+    const uint32_t h = cvt_pk_bf16(pv, 0.0f);
+    const uint32_t hl = cvt_pk_bf16(pv, pv - __uint_as_float(h << 16));
+    // lane (G, c) of each row gathers tokens 4G + i from lanes (G, 4i + c)
+    const float hf = __uint_as_float(hl);
+    const uint32_t t0 = hl;
+    const uint32_t t1 = __float_as_uint(__int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(hf), kDppRowShl + 4, 0xf, 0xf, true)));
+    const uint32_t t2 = __float_as_uint(__int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(hf), kDppRowShl + 8, 0xf, 0xf, true)));
+    const uint32_t t3 = __float_as_uint(__int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(hf), kDppRowShl + 12, 0xf, 0xf, true)));
+    const bf16x4_t pHi = __builtin_bit_cast(
+        bf16x4_t, make_uint2(__builtin_amdgcn_perm(t1, t0, 0x05040100u), __builtin_amdgcn_perm(t3, t2, 0x05040100u)));
+    const bf16x4_t pLo = __builtin_bit_cast(
+        bf16x4_t, make_uint2(__builtin_amdgcn_perm(t1, t0, 0x07060302u), __builtin_amdgcn_perm(t3, t2, 0x07060302u)));
+    // the value product, as in q4_softmax_pv
+    uint32_t a01[8], a23[8];
+    auto spread = [](uint32_t x, uint32_t(&dst)[8], int c0) {
+        const uint32_t e = x & 0x0f0f0f0fu, o = (x >> 4) & 0x0f0f0f0fu;
+        dst[c0 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(e, 512.0f, false));
+        dst[c0 + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(e, 512.0f, true));
+        dst[c0 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(o, 512.0f, false));
+        dst[c0 + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(o, 512.0f, true));
+    };
+    spread(__builtin_amdgcn_perm(T.vc[1], T.vc[0], 0x05010400u), a01, 0);
+    spread(__builtin_amdgcn_perm(T.vc[1], T.vc[0], 0x07030602u), a01, 4);
+    spread(__builtin_amdgcn_perm(T.vc[3], T.vc[2], 0x05010400u), a23, 0);
+    spread(__builtin_amdgcn_perm(T.vc[3], T.vc[2], 0x07030602u), a23, 4);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const bf16x4_t a = __builtin_bit_cast(bf16x4_t, make_uint2(a01[m], a23[m]));
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pHi, st.o[m], 0, 0, 0);
+        st.o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pLo, st.o[m], 0, 0, 0);
+    }
+}
+
+// Row sums of an MFMA state at the end of a unit: over the four lanes that
+// hold a column (G), and for the INT4 path with at most four columns (one
+// score per lane, Q4 == 1) also over a row's four banks.
+template <int Q4>
+__device__ __forceinline__ float q4_state_sum(float x) {
+    if constexpr (Q4 == 1) x = bank_sum(x);
+    return col_sum(x);
+}
+
 // One (block, kv head) tile. Scores of a full block: s_t = sum_c code_tc *
 // (q_c * kscale_c) + sum_c q_c * kmin_c. The products are formed once per
 // (column, channel) by the lane that owns them (column 4 pi + G, channels
@@ -1012,6 +1108,8 @@ template <int NP>
 __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, const Q4Query<NP> &Q, bool masked,
                                          bool full, gu16_t *tail_row, int tok0, int tlo, int thi,
                                          const Column &col, int n16, int G, Q4Lds &L, MfmaState<128> &st) {
+    // NP == 1: col is the Column of query column n16 % 4 (one score per lane)
+    const int ccol = NP == 1 ? (n16 & 3) : n16;  // the column whose min term this lane adds
     wave_lds_sync();  // the previous tile's reads of L come first (one-wave workgroup)
     const uint32_t sw[4] = {T.ks.x, T.ks.y, T.ks.z, T.ks.w}, mw[4] = {T.km.x, T.km.y, T.km.z, T.km.w};
 #pragma unroll
@@ -1044,7 +1142,7 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
-        const float4 cq = *reinterpret_cast<const float4 *>(&L.corr[n16][4 * G]);
+        const float4 cq = *reinterpret_cast<const float4 *>(&L.corr[ccol][4 * G]);
         corr = col_sum((cq.x + cq.y) + (cq.z + cq.w));
         const uint32_t kcw[4] = {T.kc.x, T.kc.y, T.kc.z, T.kc.w};
         f32x4_t sl = {0.0f, 0.0f, 0.0f, 0.0f};  // hi and lo parts in two chains: half the dependent latency
@@ -1062,12 +1160,28 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, __builtin_bit_cast(bf16x8_t, L.b[0][n16][4 * G + s]), sc, 0, 0, 0);
         }
     }
-    float sv[4];  // scores in log2 units
+    if constexpr (NP == 1) {
+        // lane (G, n16): token 4G + n16 / 4, column n16 % 4
+        float raw = dpp_f<kDppRowShr + 4, 0x2>(sc[0], sc[1]);  // bank 1 takes register 1 of bank 0, ...
+        raw = dpp_f<kDppRowShr + 8, 0x4>(raw, sc[2]);
+        raw = dpp_f<kDppRowShr + 12, 0x8>(raw, sc[3]);
+        float s = (raw + corr) * p.scale_log2;  // log2 units
+        bool ok = true;
+        if (masked) {  // only the rare masked tiles test positions
+            const int tt = 4 * G + (n16 >> 2), tp = tok0 + tt;
+            ok = (tt >= tlo) & (tt < thi) & (tp >= col.lo) & (tp < col.hi);
+            s = ok ? s : -INFINITY;
+        }
+        const bool hiword = n16 & 8;
+        q4_softmax_pv_one(p, T, s, ok, hiword ? T.vs.y : T.vs.x, hiword ? T.vm.y : T.vm.x, (n16 & 4) * 4, st);
+    } else {
+        float sv[4];  // scores in log2 units
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (sc[r] + corr) * p.scale_log2;
-    uint2 vs = T.vs, vm = T.vm;
-    if (masked) q4_mask(tok0, tlo, thi, col, G, sv, vs, vm);  // only the rare masked tiles test positions
-    q4_softmax_pv(p, T, sv, vs, vm, st);
+        for (int r = 0; r < 4; ++r) sv[r] = (sc[r] + corr) * p.scale_log2;
+        uint2 vs = T.vs, vm = T.vm;
+        if (masked) q4_mask(tok0, tlo, thi, col, G, sv, vs, vm);  // only the rare masked tiles test positions
+        q4_softmax_pv(p, T, sv, vs, vm, st);
+    }
 }
 
 // Fused append of a decode step with one new token per sequence, INT4 pool
@@ -1151,11 +1265,13 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     // blocks [jA, jB) lie inside every column's range (needs_mask is false
     // there); a partial or last block never does
     const int jA = (r.all_lo + kBlock - 1) / kBlock, jB = r.all_hi > 0 ? r.all_hi / kBlock : 0;
+    // the column whose scores this lane masks: n16 % 4 with one score per lane
+    const Column colq = NP == 1 ? column_of(p, b, kvh, ct, n16 & 3, r) : col;
     auto step = [&](const Q4Tile &T, int j) {
         const int tok0 = j * kBlock;
         const bool masked = j < jA || j >= jB;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
-        q4_block<NP>(p, T, Q, masked, !masked || is_full(j), tail_row, tok0, tlo, thi, col, n16, G, L, st);
+        q4_block<NP>(p, T, Q, masked, !masked || is_full(j), tail_row, tok0, tlo, thi, colq, n16, G, L, st);
     };
     // Fused append (decode step, one new token at position r.n - 1): the
     // segment that ends with the sequence's last block codes the token into
@@ -1242,7 +1358,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
     run_segment<D, Q4, CT, KEEP, FLAT>(p, b, kvh, ct0, col, w.r, w.j0, w.j1, lane, st, bad, sids);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-        const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
+        const float l = q4_state_sum<Q4>(st[c].l), bv = q4_state_sum<Q4>(st[c].bv);
         if (col[c].valid) {
             float res[D / 4];
             mfma_gather_run<D>(st[c], bv, res);
@@ -1345,7 +1461,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
                                            sids);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
+            const float l = q4_state_sum<Q4>(st[c].l), bv = q4_state_sum<Q4>(st[c].bv);
             if (col[c].valid) {
                 float res[D / 4];
                 mfma_gather_run<D>(st[c], bv, res);

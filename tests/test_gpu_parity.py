@@ -783,6 +783,29 @@ def test_multi_token_int4(split):
     assert max_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("n_h,k", [(16, 2), (8, 3), (8, 4), (16, 1)])
+@pytest.mark.parametrize("split,window", [(0, 0), (0, 37), (2, 0), (3, 37)])
+def test_multi_token_int4_few_columns(n_h, k, split, window):
+    """INT4 with at most four query columns per kv head (1-2 query heads per
+    kv head times 1-4 query tokens: the one-score-per-lane softmax), causal
+    among the new tokens and with a window, both schedules, lengths with
+    partial blocks and shorter than the query count."""
+    lens = [3, 16, 21, 47, 200, 333, 2]
+    c = int4_case(975 + n_h + k, lens, n_h=n_h, n_kv=8, d=128)
+    c.append = False
+    c.ctx_lens = c.seq_lens.clone()
+    src, dst, img = int4_pools(c, len(lens))
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
+    tab, lens_np = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens_np)
+    g = torch.Generator(device=DEV).manual_seed(5 + k)
+    q = torch.randn((c.batch, k, c.n_h, 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = gpu_multi(dst, c, q, split_blocks=split, window=window)
+    Kd, Vd = orc.q4_dequant(img, tab, lens_np)
+    ref = orc.attention_multi(Kd, Vd, bits(q), tab, lens_np, c.scale, window=window)
+    assert max_err(out, ref) <= TOL
+
+
 @pytest.mark.parametrize("n_h,k", [(32, 16), (64, 3), (32, 4)])
 def test_multi_token_merge_many_pieces(n_h, k):
     """Long contexts beside empty, short and invalid (negative length)
