@@ -831,14 +831,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, in
 }
 enum { kLoadStream = 2 };  // cache policy of a raw buffer load: non-temporal
 
-__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int n16, int G, Q4Tile &T) {
+// none: issue the same loads with empty descriptors (they read nothing from
+// memory and return 0), for the prefetch slot past a segment's last tile.
+__device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, int n16, int G, Q4Tile &T,
+                                         bool none) {
     const size_t tile = (size_t)pid * p.n_kv + kvh;
-    const auto kq = tile_rsrc(p.pool.kq + tile * (kBlock * 64), kBlock * 64);
-    const auto vq = tile_rsrc(p.pool.vq + tile * (kBlock * 64), kBlock * 64);
-    const auto ks = tile_rsrc(p.pool.ks + tile * 128, 256);
-    const auto km = tile_rsrc(p.pool.km + tile * 128, 256);
-    const auto vs = tile_rsrc(p.pool.vs + tile * kBlock, kBlock * 2);
-    const auto vm = tile_rsrc(p.pool.vm + tile * kBlock, kBlock * 2);
+    const int on = none ? 0 : 1;
+    const auto kq = tile_rsrc(p.pool.kq + tile * (kBlock * 64), on * kBlock * 64);
+    const auto vq = tile_rsrc(p.pool.vq + tile * (kBlock * 64), on * kBlock * 64);
+    const auto ks = tile_rsrc(p.pool.ks + tile * 128, on * 256);
+    const auto km = tile_rsrc(p.pool.km + tile * 128, on * 256);
+    const auto vs = tile_rsrc(p.pool.vs + tile * kBlock, on * kBlock * 2);
+    const auto vm = tile_rsrc(p.pool.vm + tile * kBlock, on * kBlock * 2);
     T.kc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, n16 * 64 + 16 * G, 0, kLoadStream));
     T.ks = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ks, 16 * n16, 0, kLoadStream));
     T.km = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(km, 16 * n16, 0, kLoadStream));
@@ -857,14 +861,15 @@ __device__ __forceinline__ void q4_fetch(const AttnParams &p, int pid, int kvh, 
 // offsets (a handful of scalar instructions per tile instead of six
 // descriptors built from 64-bit addresses).
 struct Q4Flat {
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t vq, ks, km, vs, vm;  // byte offsets of the other arrays from the K codes
+    __amdgpu_buffer_rsrc_t rsrc, none;  // the span, and an empty descriptor (reads return 0)
+    uint32_t vq, ks, km, vs, vm;        // byte offsets of the other arrays from the K codes
 };
 __device__ __forceinline__ Q4Flat q4_flat(const AttnParams &p) {
     const char *kq = reinterpret_cast<const char *>(p.pool.kq);
     auto off = [&](const void *a) { return (uint32_t)(reinterpret_cast<const char *>(a) - kq); };
     Q4Flat f;
     f.rsrc = tile_rsrc(p.pool.kq, (int)p.pool.q4_span);
+    f.none = tile_rsrc(p.pool.kq, 0);
     f.vq = off(p.pool.vq);
     f.ks = off(p.pool.ks);
     f.km = off(p.pool.km);
@@ -872,17 +877,18 @@ __device__ __forceinline__ Q4Flat q4_flat(const AttnParams &p) {
     f.vm = off(p.pool.vm);
     return f;
 }
-__device__ __forceinline__ void q4_fetch_flat(const Q4Flat &f, uint32_t tile, int n16, int G, Q4Tile &T) {
+__device__ __forceinline__ void q4_fetch_flat(const Q4Flat &f, uint32_t tile, int n16, int G, Q4Tile &T,
+                                              bool none) {
     const uint32_t codes = tile * (kBlock * 64), kpar = tile * 256, vpar = tile * (kBlock * 2);
-    T.kc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, n16 * 64 + 16 * G, codes,
-                                                                           kLoadStream));
-    T.ks = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, 16 * n16, f.ks + kpar, kLoadStream));
-    T.km = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(f.rsrc, 16 * n16, f.km + kpar, kLoadStream));
+    const auto rs = none ? f.none : f.rsrc;
+    T.kc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, n16 * 64 + 16 * G, codes, kLoadStream));
+    T.ks = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * n16, f.ks + kpar, kLoadStream));
+    T.km = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * n16, f.km + kpar, kLoadStream));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        T.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(f.rsrc, (4 * G + i) * 64 + 4 * n16, f.vq + codes, kLoadStream);
-    const u32x2_t s = __builtin_amdgcn_raw_buffer_load_b64(f.rsrc, 8 * G, f.vs + vpar, kLoadStream);
-    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(f.rsrc, 8 * G, f.vm + vpar, kLoadStream);
+        T.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * G + i) * 64 + 4 * n16, f.vq + codes, kLoadStream);
+    const u32x2_t s = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * G, f.vs + vpar, kLoadStream);
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * G, f.vm + vpar, kLoadStream);
     T.vs = make_uint2(s[0], s[1]);
     T.vm = make_uint2(m[0], m[1]);
 }
@@ -1283,13 +1289,17 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     const bool append = p.k_new && ct == 0 && j1 == r.blk_lo + r.nblk && !r.bad && !slot_bad;
     bool appended = false;
     const Q4Flat flat = FLAT ? q4_flat(p) : Q4Flat{};
+    // The loop issues the same loads every iteration (so the compiler's waits
+    // cover exactly the tile in use); past the end they go through empty
+    // descriptors, which read nothing.
     auto fetch = [&](int j, Q4Tile &T) {
-        const int jc = j < j1 ? j : j1 - 1;  // past the end: re-read the last tile (cached)
+        const bool past = j >= j1;
+        const int jc = past ? j1 - 1 : j;
         if (appended && jc == j1 - 1) __builtin_amdgcn_s_waitcnt(0);
         if constexpr (FLAT)
-            q4_fetch_flat(flat, (uint32_t)(ids.id(jc) * p.n_kv + kvh), n16, G, T);
+            q4_fetch_flat(flat, (uint32_t)(ids.id(jc) * p.n_kv + kvh), n16, G, T, past);
         else
-            q4_fetch(p, ids.id(jc), kvh, n16, G, T);
+            q4_fetch(p, ids.id(jc), kvh, n16, G, T, past);
     };
     Q4Tile A, B;
     if (!append || j0 < j1 - 1) fetch(j0, A);
