@@ -14,8 +14,10 @@
 // Work units. The query columns of a kv head are its g = n_h / n_kv query
 // heads times the q_len query tokens, in 16-column tiles; a work unit is a
 // kv head and one column tile (two on the bf16 MFMA path when there are
-// several). A workgroup is one wave64. It streams the unit's (block, kv head)
-// tiles once and serves all its columns from each tile, keeping an online
+// several, four or eight in the wide units of attn_mfma_wide_kernel). A
+// workgroup is one wave64 (two or four for wide units, which share each tile
+// through LDS). It streams the unit's (block, kv head) tiles once and serves
+// all its columns from each tile, keeping an online
 // softmax (running max m and sum l, in log2 units: scores are pre-multiplied
 // by scale * log2 e so exp becomes the hardware exp2; the max moves lazily,
 // see kLazyLog2).
@@ -47,7 +49,9 @@
 //    The QK output layout (lane = column + 16 * token-quad) is exactly the
 //    B-operand layout the PV product needs, so P never leaves registers.
 //  * q4_block (INT4): the same products on the codes, with the scales and
-//    minimums folded into the query and weight operands (see q4_block).
+//    minimums folded into the query and weight operands (see q4_block); with
+//    at most four query columns the softmax runs on one score per lane
+//    (q4_softmax_pv_one).
 #include "device.h"
 #include <hip/hip_ext.h>
 
