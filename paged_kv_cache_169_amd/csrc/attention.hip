@@ -454,12 +454,6 @@ struct MfmaTile {
     uint32_t v[4][D / 32];       // rows 4G + i, channels n16 * (D/16) .. + D/16 (bf16 pairs)
 };
 
-// Block ids of a split, 64 at a time: lane i holds the id of block jbase + i.
-__device__ __forceinline__ int load_block_ids(const AttnParams &p, int b, int jbase, int j1, int lane) {
-    const int j = jbase + lane;
-    return j < j1 ? p.tables[(size_t)b * p.max_blocks + j] : 0;
-}
-
 // Tile of block j. Rows of positions in [L0, L0 + n_new) come from the step's
 // k_new / v_new instead of the pool (fused append); newpos = L0 - 16 j is
 // uniform, and >= 16 when the block holds no new token.
