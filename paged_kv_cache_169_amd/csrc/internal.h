@@ -147,7 +147,8 @@ hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hip
                                    hipEvent_t e1, hipEvent_t e_end);
 // Persistent grid of the balanced schedule: resident workgroups per device.
 int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
-// The same for wide units (bf16; units of ctw = 4 or 8 column tiles).
+// The same for wide units (bf16; units of ctw = 4 or 8 column tiles, or 2 at
+// head_dim 128).
 int wide_grid(int head_dim, int ctw, int batch, int max_blocks);
 // The balanced shared-prefix kernel: its dynamic LDS (max_blocks: the longest
 // segment in blocks) and its persistent grid for that LDS.
