@@ -96,7 +96,7 @@ def draw_multi(i):
     return dict(lens=lens, k=k, n_kv=n_kv, n_h=n_kv * g, d=d, schedule=schedule, split=split, window=window)
 
 
-@pytest.mark.parametrize("i", range(20))
+@pytest.mark.parametrize("i", range(60))
 def test_random_multi_token(i):
     """Several query tokens per sequence (g * k query columns per kv head, up
     to 192: one or two 16-column tiles per work unit) on the MFMA kernels."""
