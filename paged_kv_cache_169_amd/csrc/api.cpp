@@ -457,8 +457,13 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     const int dtype = pool->desc.dtype;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the append runs inside the attention kernel on the MFMA path: bf16
-    // pools for any q_len, INT4 pools for one new token per sequence
-    const bool fused = k_new && g.kernel == 2 && (dtype == KV_BF16 || (dtype == KV_INT4 && q_len == 1));
+    // pools for any q_len (every unit takes the new rows from k_new / v_new),
+    // INT4 pools for one new token per sequence when a kv head is one work
+    // unit. With several units per kv head (more than 16 query heads per kv
+    // head) only the first codes the token while the others read the same
+    // last block, so the append kernel runs first instead.
+    const bool fused = k_new && g.kernel == 2 &&
+                       (dtype == KV_BF16 || (dtype == KV_INT4 && q_len == 1 && g.ctiles == 1));
     if (k_new && !fused) {
         const kv_status st = kv_append_tokens(pool, k_new, v_new, block_tables, max_blocks, ctx_lens, seq_slots,
                                               batch, ctx_add, stream);

@@ -140,17 +140,15 @@ def draw_int4(i):
                 window=window)
 
 
-@pytest.mark.parametrize("i", range(24))
-def test_random_int4_decode_step(i):
+def int4_step_case(cfg, seed):
     """INT4 pool coded from bf16, then one decode step (the append fused into
-    the MFMA kernel): the pool image bit-exact against the oracle's coding and
-    append, the output against the oracle on the same dequantized values."""
-    cfg = draw_int4(i)
-    print(f"random int4 case {i}: {cfg}", flush=True)
+    the MFMA kernel where the library fuses it): the pool image bit-exact
+    against the oracle's coding and append, the output against the oracle on
+    the same dequantized values."""
     B = len(cfg["lens"])
-    c = wl.make_case(6000 + i, B, cfg["lens"], cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", pool_slack=1.3,
+    c = wl.make_case(6000 + seed, B, cfg["lens"], cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", pool_slack=1.3,
                      device=DEV, append=True, outliers=min(4, cfg["d"] // 32))
-    slots = torch.tensor(random.Random(i).sample(range(B + 2), B), dtype=torch.int32, device=DEV)
+    slots = torch.tensor(random.Random(seed).sample(range(B + 2), B), dtype=torch.int32, device=DEV)
     src = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
     src.K.copy_(c.K)
     src.V.copy_(c.V)
@@ -185,6 +183,34 @@ def test_random_int4_decode_step(i):
     assert float(np.max(np.abs(got - ref))) <= TOL
     src.close()
     dst.close()
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_int4_decode_step(i):
+    cfg = draw_int4(i)
+    print(f"random int4 case {i}: {cfg}", flush=True)
+    int4_step_case(cfg, i)
+
+
+# More than 16 query heads per kv head: a kv head's columns take several work
+# units. Lengths put the appended token at every place in a block, including
+# the 16th (the block's K is coded then).
+LARGE_GROUPS = [
+    dict(n_kv=1, n_h=32, lens=[15, 16, 47, 300, 0, 31]),     # MQA, two column tiles
+    dict(n_kv=1, n_h=64, lens=[15, 255, 100, 17]),           # MQA, four column tiles
+    dict(n_kv=2, n_h=64, lens=[31, 1, 200, 15, 64]),         # g = 32
+    dict(n_kv=4, n_h=128, lens=[15, 79, 143]),               # g = 32
+    dict(n_kv=1, n_h=20, lens=[15, 30, 63, 500]),            # g = 20: a partial second tile
+]
+
+
+@pytest.mark.parametrize("schedule", [0, 1, 2])
+@pytest.mark.parametrize("i", range(len(LARGE_GROUPS)))
+def test_int4_decode_step_large_groups(i, schedule):
+    cfg = dict(LARGE_GROUPS[i], d=128, kernel=0, schedule=schedule, split=3 if schedule == 1 else 0,
+               window=0)
+    print(f"int4 large-group case {i} schedule {schedule}: {cfg}", flush=True)
+    int4_step_case(cfg, 900 + 10 * i + schedule)
 
 
 def draw_shared(i):
