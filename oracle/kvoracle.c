@@ -30,7 +30,11 @@
  *   R4 INT4 is asymmetric: code = clamp(round((x - min) / s), 0, 15) with
  *      s = (max - min) / 15, rounding half away from zero, computed in fp32
  *      from the STORED fp16 s and min; a group whose fp16 s is 0 has all
- *      codes 0. A zero min or max of either sign is taken as +0.
+ *      codes 0. A zero min or max of either sign is taken as +0. The clamp
+ *      binds when fp16 rounding moves s or min: a subnormal fp16 s rounded
+ *      down, a min rounded up, or an fp16 min of -inf (quotient +inf: 15).
+ *      A quotient that is not a number (fp16 s and min both infinite) codes
+ *      as 0.
  *   R5 K groups are (block, kv head, channel) over the block's 16 tokens;
  *      V groups are (token, kv head) over the d_h channels. The K of a block
  *      that is not yet full stays in bf16 in a per-sequence tail.
@@ -284,7 +288,10 @@ static void q4_group(const float *x, int n, size_t xs, uint8_t *codes, size_t cs
         int c = 0;
         if (sf != 0.0f) {
             float v = (x[i * xs] - mf) / sf;
-            if (v <= 0.0f)
+            /* a quotient that is not a number (an infinite fp16 scale over an
+             * infinite difference, when the min and the range both overflow
+             * fp16) codes as 0, like a group whose scale is 0 */
+            if (isnan(v) || v <= 0.0f)
                 c = 0;
             else if (v >= 15.0f)
                 c = 15;
