@@ -27,6 +27,18 @@ MUTANTS = {
     "window": ("? n - window : 0;", "? n - window + 1 : 0;"),
     # INT4 rounding ties to even instead of half away from zero
     "round_even": ("c = (int)roundf(v);", "c = (int)rintf(v);"),
+    # INT4 codes not clamped above 15 (fp16 rounding of s can push the quotient past 15.5)
+    "no_clamp_high": ("            else if (v >= 15.0f)\n                c = 15;\n", ""),
+    # INT4 codes not clamped below 0 (an fp16 min rounded up can push the quotient below -0.5)
+    "no_clamp_low": ("if (isnan(v) || v <= 0.0f)", "if (isnan(v))"),
+    # no clamp at all
+    "no_clamp": ("            if (isnan(v) || v <= 0.0f)\n                c = 0;\n            else if (v >= 15.0f)\n"
+                 "                c = 15;\n            else\n                c = (int)roundf(v); /* half away from zero */",
+                 "            c = isnan(v) ? 0 : (int)roundf(v);"),
+    # a negative-zero min kept as -0 (stored min bits 0x8000)
+    "signed_zero_min": ("if (mn == 0.0f) mn = 0.0f;", ""),
+    # a negative-zero max kept as -0 (an all -0 group gets s = -0, bits 0x8000)
+    "signed_zero_max": ("if (mx == 0.0f) mx = 0.0f;", ""),
     # INT4 symmetric (min dropped)
     "no_min": ("float v = (x[i * xs] - mf) / sf;", "float v = x[i * xs] / sf;"),
     # INT4 codes from the unrounded min instead of the stored fp16 min

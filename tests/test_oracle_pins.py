@@ -330,9 +330,9 @@ def test_append_then_attend_matches_torch(orc):
 
 def test_int4_golden_groups(orc):
     rows = read_golden("int4_groups.txt")
-    assert len(rows) == 5
+    assert len(rows) == 13
     for label, xs, codes, s16, m16, _why in rows:
-        x = np.array([float(v) for v in xs.split(",")], dtype=np.float32)
+        x = np.array([float.fromhex(v) if "0x" in v else float(v) for v in xs.split(",")], dtype=np.float32)
         got_c, got_s, got_m = orc.q4_group(x)
         assert list(got_c) == [int(v) for v in codes.split(",")], label
         assert got_s == int(s16, 16), label
@@ -340,21 +340,32 @@ def test_int4_golden_groups(orc):
 
 
 def test_int4_error_bound_and_range(orc):
+    """Codes lie in [0, 15] at every magnitude, and where the stored s and min
+    are finite the reconstruction error obeys the closed-form bound. Scales
+    from 10^-7.5 (fp16 subnormal s and min: the clamp binds in many groups)
+    to 10^6 (fp16 overflow)."""
     rng = np.random.default_rng(5)
-    for trial in range(300):
+    clamped = 0
+    for trial in range(600):
         n = 16 if trial % 2 else 128
-        x32 = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        x32 = (rng.standard_normal(n) * 10.0 ** rng.uniform(-7.5, 6)).astype(np.float32)
         xb = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         x = as_f64(xb)
         codes, s16, m16 = orc.q4_group(xb)
-        assert codes.max() <= 15
+        assert codes.max() <= 15 and codes.min() >= 0, trial
         s = float(orc.f16_bits_to_f32(np.array([s16]))[0])
         m = float(orc.f16_bits_to_f32(np.array([m16]))[0])
+        if not (np.isfinite(s) and np.isfinite(m)) or s == 0.0:
+            continue
         mn, mx = x.min(), x.max()
         s32 = float(np.float32(np.float32(mx) - np.float32(mn)) / np.float32(15.0))
         xhat = m + codes.astype(np.float64) * s
         bound = max(s / 2, abs(mn - m) + 15 * abs(s32 - s)) + 1e-6 * max(abs(mn), abs(mx))
         assert np.max(np.abs(x - xhat)) <= bound, trial
+        # the exact quotient past 15.5 or below -0.5: a clamped code
+        v = (x - m) / s
+        clamped += int(np.any(v >= 15.5) or np.any(v < -0.5))
+    assert clamped >= 10  # the draw reaches the clamp regime (17 groups with this seed)
 
 
 def test_int4_requantizing_grid_values_is_stable(orc):
