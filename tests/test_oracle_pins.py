@@ -362,9 +362,9 @@ def test_int4_error_bound_and_range(orc):
         xhat = m + codes.astype(np.float64) * s
         bound = max(s / 2, abs(mn - m) + 15 * abs(s32 - s)) + 1e-6 * max(abs(mn), abs(mx))
         assert np.max(np.abs(x - xhat)) <= bound, trial
-        # the exact quotient past 15.5 or below -0.5: a clamped code
+        # an exact quotient of 15.5 or more, or -0.5 or less: a clamped code
         v = (x - m) / s
-        clamped += int(np.any(v >= 15.5) or np.any(v < -0.5))
+        clamped += int(np.any(v >= 15.5) or np.any(v <= -0.5))
     assert clamped >= 10  # the draw reaches the clamp regime (17 groups with this seed)
 
 
