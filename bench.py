@@ -19,6 +19,10 @@ synthetic inputs already resident in HBM.
 
 Consecutive steps rotate over pool replicas whose total size exceeds twice the
 256 MB last-level (Infinity) cache, so a step never finds its KV there.
+
+The default workload is the 70B-shaped decode layer (256 sequences of 2048
+tokens, 64 query and 8 kv heads), the largest configuration that fits one GPU;
+--workload selects the others (llama3_8b, kvquant_int4, long_shared, tiny).
 """
 from __future__ import annotations
 
@@ -148,15 +152,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b",
+    ap.add_argument("--workload", default="llama2_70b",
                     choices=["tiny", "llama3_8b", "llama2_70b", "kvquant_int4", "long_shared"])
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--split", type=int, default=0, help="blocks per split, 0 = library's choice")
     ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=0,
                     help="record the kernel-boundary events on every E-th timed step (each record costs the "
-                         "stream a few microseconds); 1 = every step")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
+                         "stream about a microsecond); 1 = every step; 0 (default): every step on the workloads "
+                         "whose step is several hundred microseconds, every 4th on the others")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget on all host threads, and again on one thread; 0 skips it")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence: 1 is decode; k > 1 appends k tokens and runs the "
                          "multi-token (verification) attention over them")
@@ -257,7 +263,7 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronized on both sides
-    every = max(1, args.event_every)
+    every = args.event_every if args.event_every > 0 else (1 if name in ("llama2_70b", "long_shared") else 4)
     ev = [[hip.create() for _ in range(3)] if i % every == 0 else None for i in range(args.steps)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -281,6 +287,7 @@ def main():
     split_sorted = sorted(split_ms)
     pct = lambda f: split_sorted[min(len(split_sorted) - 1, int(f * len(split_sorted)))] * 1e3
     copy_rate = streaming_copy_rate(torch, stream)
+    read_rate, read_wg = read_ceiling(torch, kv, stream)
 
     # algorithmic bytes of one split-kernel launch: K and V of every attended
     # (token, kv head) once, q, the output, the block-table entries and lengths.
@@ -316,8 +323,8 @@ def main():
     log(f"[bench] step {ms_per_step*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), split kernel "
         f"{split_avg*1e3:.1f} us, merge {merge_avg*1e3:.1f} us, {achieved:.0f} GB/s "
         f"({100*achieved/PEAK_HBM_GBS:.1f}% of 8 TB/s), {value/1e9:.3f} G KV-tokens/s")
-    log(f"[bench] achievable on this device: streaming copy {copy_rate:.0f} GB/s "
-        f"(kernel at {100*achieved/copy_rate:.1f}% of it); kernel p10/p50/p90 "
+    log(f"[bench] achievable on this device: streaming read {read_rate:.0f} GB/s (kernel at "
+        f"{100*achieved/read_rate:.1f}% of it), streaming copy {copy_rate:.0f} GB/s; kernel p10/p50/p90 "
         f"{pct(0.1):.1f}/{pct(0.5):.1f}/{pct(0.9):.1f} us")
 
     cpu = None
@@ -346,14 +353,37 @@ def main():
             t_cpu += time.perf_counter() - t1
             done_tokens += tokens_per_step
             runs += 1
-        # the timed steps' output against the oracle on the same inputs
+        # the timed steps' output against the oracle on the same inputs, every row
         err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))) if ref.size else 0.0
+        # one thread: passes over the first sequences (a bounded sample of the
+        # same workload, about a tenth of the budget per pass) until the budget
+        # is spent
+        per_seq = t_cpu / runs * threads / max(1, B)  # estimated one-thread seconds per sequence
+        n1 = int(max(1, min(B, args.cpu_seconds / 10 / max(per_seq, 1e-9))))
+        sub = slice(0, n1)
+        tok1 = int(ctx_np[sub].sum())
+        oracle.set_threads(1)
+        done1, t1_cpu, runs1 = 0, 0.0, 0
+        try:
+            while t1_cpu < args.cpu_seconds or runs1 == 0:
+                t1 = time.perf_counter()
+                oracle.attention(Kh, Vh, qh[sub], tab[sub], ctx_np[sub], c.scale)
+                t1_cpu += time.perf_counter() - t1
+                done1 += tok1
+                runs1 += 1
+        finally:
+            oracle.set_threads(threads)
         cpu = {"value": done_tokens / t_cpu, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"{runs} full pass(es) of the {name} attention ({tokens_per_step} tokens x {n_h} heads, "
                          f"fp64, OpenMP over (sequence, head)), {t_cpu:.1f} s",
-               "gpu_max_abs_err": err, "tolerance": PARITY_TOL}
-        log(f"[bench] oracle: {cpu['value']/1e6:.3f} M KV-tokens/s on {threads} threads ({runs} runs, {t_cpu:.1f}s); "
-            f"GPU output vs oracle: max |err| {err:.2e}")
+               "single_thread_value": done1 / t1_cpu,
+               "single_thread_sample": f"{runs1} pass(es) over the first {n1} of {B} sequences ({tok1} tokens x "
+                                       f"{n_h} heads), one thread, {t1_cpu:.1f} s",
+               "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+               "gpu_max_abs_err": err, "gpu_rows_checked": int(B * k * n_h), "tolerance": PARITY_TOL}
+        log(f"[bench] oracle: {cpu['value']/1e6:.3f} M KV-tokens/s on {threads} threads ({runs} runs, {t_cpu:.1f}s), "
+            f"{cpu['single_thread_value']/1e6:.4f} M on one thread ({runs1} runs over {n1} sequences); "
+            f"GPU output vs oracle: max |err| {err:.2e} over all {B * n_h} rows")
         if not err <= PARITY_TOL:
             raise SystemExit(f"bench: GPU output differs from the oracle by {err:.3e} (> {PARITY_TOL})")
 
@@ -386,9 +416,13 @@ def main():
                      "timed_launches": len(split_ms),
                      "merge_avg_us": merge_avg * 1e3, "alg_bytes_per_launch": alg_bytes,
                      "logical_bytes_per_launch": logical_bytes,
-                     "achievable": {"copy_GBps": copy_rate, "frac_of_copy": achieved / copy_rate,
-                                    "how": "torch copy_ of a 1 GiB buffer on the same device, "
-                                           "bytes read + written per second"}},
+                     "achievable": {"read_GBps": read_rate, "frac_of_read": achieved / read_rate,
+                                    "read_how": f"kv_read_probe over a 2 GiB buffer (the attention kernels' tile "
+                                                f"loads, nothing written), best grid {read_wg} workgroups, "
+                                                "bytes read per second",
+                                    "copy_GBps": copy_rate, "frac_of_copy": achieved / copy_rate,
+                                    "copy_how": "torch copy_ of a 1 GiB buffer on the same device, "
+                                                "bytes read + written per second"}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -411,6 +445,41 @@ def streaming_copy_rate(torch, stream, nbytes: int = 1 << 30, iters: int = 10) -
     del a, b
     torch.cuda.empty_cache()
     return rate
+
+
+def read_ceiling(torch, kv, stream, nbytes: int = 2 << 30, iters: int = 10):
+    """Achievable read rate on this device for the attention kernels' access
+    pattern: kv_read_probe over a buffer far larger than the caches, the best
+    of a few grid sizes. Returns (GB/s, workgroups)."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best, best_wg = 0.0, 0
+    for wg in (1024, 2048, 4096, 8192):
+        kv.kv_read_probe(buf, sink, wg, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            kv.kv_read_probe(buf, sink, wg, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rate = nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if rate > best:
+            best, best_wg = rate, wg
+    del buf
+    torch.cuda.empty_cache()
+    return best, best_wg
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def hold_queue(torch, launches: int) -> None:

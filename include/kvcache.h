@@ -439,6 +439,16 @@ int32_t kv_recompute_count(double ratio, int32_t num_tokens);
 kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,
                              const int32_t *lens, int32_t batch, int32_t appending, int32_t *bad_row);
 
+/* Measurement: the device's read ceiling for the kernels above. Reads the
+ * `bytes` bytes at `buf` (device memory, 16-byte aligned, `bytes` a multiple
+ * of 4096) once, in the pattern the attention kernels read a (block, kv head)
+ * tile of a bf16 pool at head_dim 128: one wave per 4 KiB piece, four 16-byte
+ * non-temporal loads per lane, two pieces in flight, over `workgroups`
+ * workgroups of four waves (1 .. 65535; 0 = 2048). Nothing is written except
+ * that the XOR of all words read is stored to *sink (device uint32) when it
+ * equals 0x9e3779b9. Bytes read / the call's duration is the ceiling. */
+kv_status kv_read_probe(const void *buf, size_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

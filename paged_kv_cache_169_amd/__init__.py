@@ -119,6 +119,7 @@ _kv_token_deviation = _decl("kv_token_deviation", _I32, [_P, _P, _I32, _I32, _P,
 _kv_topk_select = _decl("kv_topk_select", _I32, [_P, _P, _P, _I32, _P, _P])
 _kv_recompute_ratio = _decl("kv_recompute_ratio", _D, [_D, _D, _I32, _D])
 _kv_recompute_count = _decl("kv_recompute_count", _I32, [_D, _I32])
+_kv_read_probe = _decl("kv_read_probe", _I32, [_P, _SZ, _I32, _P, _P])
 _kv_validate_tables = _decl("kv_validate_tables", _I32,
                             [ctypes.POINTER(kv_pool_desc), _P, _I32, _P, _I32, _I32, ctypes.POINTER(_I32)])
 
@@ -501,6 +502,15 @@ def kv_validate_tables(desc: kv_pool_desc, block_tables, lens, appending: bool =
     return int(st), int(bad.value)
 
 
+def kv_read_probe(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None) -> None:
+    """Read `buf` (a contiguous device tensor, a multiple of 4096 bytes) once:
+    the read-ceiling measurement of kvcache.h."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(_kv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(workgroups),
+                          _dev_ptr(sink, "sink", torch.int32, 1), _stream(stream)), "kv_read_probe")
+
+
 # raw entry points, for tests of the C ABI itself
 raw = {
     "kv_pool_create": _kv_pool_create, "kv_pool_destroy": _kv_pool_destroy, "kv_pool_region": _kv_pool_region,
@@ -514,5 +524,5 @@ raw = {
     "kv_topk_select": _kv_topk_select, "kv_decode_step": _kv_decode_step,
     "paged_decode_attention_shared": _paged_decode_attention_shared,
     "paged_decode_attention_shared_workspace_bytes": _paged_decode_attention_shared_workspace_bytes,
-    "kv_validate_tables": _kv_validate_tables,
+    "kv_validate_tables": _kv_validate_tables, "kv_read_probe": _kv_read_probe,
 }

@@ -32,6 +32,7 @@ SOURCES = {
     "copy.hip": [],
     "attention.hip": [],
     "blend.hip": [],
+    "measure.hip": [],
 }
 
 

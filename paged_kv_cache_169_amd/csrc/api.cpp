@@ -30,6 +30,8 @@ constexpr size_t kNone = (size_t)-1;
 // Largest batch, kv-head count and work units per sequence: launch grids put
 // them in the y or z dimension (at most 65535 workgroups).
 constexpr int kMaxGridYZ = 65535;
+// Largest grid of the read probe (its workgroups are a measurement knob).
+constexpr int kMaxGridX = 65535;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -788,6 +790,14 @@ int32_t kv_recompute_count(double ratio, int32_t num_tokens) {
     if (num_tokens <= 0 || !(ratio > 0.0)) return 0;
     const double c = std::ceil(ratio * (double)num_tokens);
     return c >= (double)num_tokens ? num_tokens : (int32_t)c;
+}
+
+kv_status kv_read_probe(const void *buf, size_t bytes, int32_t workgroups, uint32_t *sink, void *stream) {
+    if (!buf || !sink || !aligned16(buf) || bytes % 4096 != 0 || workgroups < 0 || workgroups > kMaxGridX)
+        return KV_ERR_INVALID_ARG;
+    if (bytes / 4096 > INT32_MAX) return KV_ERR_UNSUPPORTED;  // piece indices stay far from 2^32
+    return hip_status(launch_read_probe(buf, bytes, workgroups ? workgroups : 2048, sink,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 kv_status kv_validate_tables(const kv_pool_desc *desc, const int32_t *block_tables, int32_t max_blocks,

@@ -156,6 +156,7 @@ size_t shared_balanced_lds(int n_groups, int batch, int max_blocks);
 int shared_balanced_grid(int head_dim, size_t lds);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
+hipError_t launch_read_probe(const void *buf, size_t bytes, int workgroups, uint32_t *sink, hipStream_t s);
 
 // The attended block range of one sequence, shared by the split kernels and
 // the merge kernels so that both agree on the number of splits. With q_len

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -317,3 +317,16 @@ def test_shared_prefix_host_checks(kv):
         == kv.KV_ERR_INVALID_ARG                                                  # a group beyond the empty batch
     for x in (h, h32):
         kv.raw["kv_pool_destroy"](x)
+
+
+def test_read_probe_rejects_bad_arguments(kv):
+    """kv_read_probe checks its arguments before any launch (no GPU here)."""
+    f = kv.raw["kv_read_probe"]
+    ok_buf, sink = FAKE, FAKE + 4096
+    assert f(None, 4096, 0, sink, None) == kv.KV_ERR_INVALID_ARG
+    assert f(ok_buf, 4096, 0, None, None) == kv.KV_ERR_INVALID_ARG
+    assert f(ok_buf + 8, 4096, 0, sink, None) == kv.KV_ERR_INVALID_ARG      # not 16-byte aligned
+    assert f(ok_buf, 4096 + 16, 0, sink, None) == kv.KV_ERR_INVALID_ARG     # not whole 4 KiB pieces
+    assert f(ok_buf, 4096, -1, sink, None) == kv.KV_ERR_INVALID_ARG
+    assert f(ok_buf, 4096, 65536, sink, None) == kv.KV_ERR_INVALID_ARG
+    assert f(ok_buf, 4096 * (2 ** 31), 0, sink, None) == kv.KV_ERR_UNSUPPORTED

@@ -346,42 +346,8 @@ def test_balanced_merge_many_partials(lens, n_h, n_kv, window):
     assert max_err(out, ref) <= TOL
 
 
-# ---------------------------------------------------------------------------
-# full-size workloads (launch configuration of bench.py), sampled outputs
-# ---------------------------------------------------------------------------
-
-@pytest.mark.parametrize("name", ["llama3_8b", "llama2_70b"])
-def test_full_size_workload(name):
-    c = wl.workload(name, device=DEV)
-    pool = new_pool(c)
-    kv.kv_append(pool, c.k_new, c.v_new, c.tables, c.seq_lens)
-    out = gpu_attention(pool, c)            # auto kernel / split: what bench.py times
-    assert np.all(np.isfinite(out))
-    # append: the whole pool image, bit for bit
-    K, V = oracle_step(c)
-    assert np.array_equal(bits(pool.K), K) and np.array_equal(bits(pool.V), V)
-    # attention: a sample of sequences, every head
-    rows = sorted(set([0, c.batch - 1] + torch.randperm(c.batch, generator=torch.Generator().manual_seed(1))[:6].tolist()))
-    tab = c.tables.cpu().numpy()[rows]
-    ref = orc.attention(K, V, bits(c.q)[rows], tab, c.ctx_lens.cpu().numpy()[rows], c.scale)
-    assert max_err(out[rows], ref) <= TOL
-
-
-def test_long_shared_prefix_with_rerotation():
-    c = wl.workload("long_shared", device=DEV)
-    pool = new_pool(c)
-    kv.rope_rerotate(pool, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
-    out = gpu_attention(pool, c)
-    torch.cuda.synchronize()
-    K, V = bits(c.K), bits(c.V)
-    orc.rope_rerotate(K, c.chunk_blocks.cpu().numpy(), 0, c.chunk_tokens, c.delta, c.rope_base, 0)
-    assert np.array_equal(bits(pool.K), K)
-    rows = [0, 5]
-    ref = orc.attention(K, V, bits(c.q)[rows], c.tables.cpu().numpy()[rows], c.ctx_lens.cpu().numpy()[rows], c.scale)
-    assert max_err(out[rows], ref) <= TOL
-    # the shared prefix really is shared: same physical ids in every table
-    t = c.tables.cpu()
-    assert bool((t[:, :1024] == t[0, :1024]).all())
+# The full-size workloads, every row on the path bench.py times, are in
+# test_gpu_full_size.py.
 
 
 # ---------------------------------------------------------------------------
@@ -461,8 +427,9 @@ def test_shared_prefix_member_shorter_than_prefix_is_nan(schedule):
 
 def test_shared_prefix_long_workload_matches_plain_call():
     """The long shared-prefix workload (8 x 32768 tokens, 16384 shared, chunk
-    re-rotated) through the shared entry point: sampled rows against the oracle
-    and every row against the plain call."""
+    re-rotated) through the shared entry point and through the plain call:
+    every row of the two agrees (each is checked against the oracle on every
+    row in test_gpu_full_size.py and here at small sizes)."""
     c = wl.workload("long_shared", device=DEV)
     pool = new_pool(c)
     kv.rope_rerotate(pool, c.chunk_blocks, 0, c.chunk_tokens, c.delta, c.rope_base, 0)
@@ -470,10 +437,6 @@ def test_shared_prefix_long_workload_matches_plain_call():
     plain = gpu_attention(pool, c)
     assert np.all(np.isfinite(out))
     assert max_err(out, plain) <= TOL
-    K, V = bits(pool.K), bits(pool.V)
-    rows = [0, 3, 7]
-    ref = orc.attention(K, V, bits(c.q)[rows], c.tables.cpu().numpy()[rows], c.ctx_lens.cpu().numpy()[rows], c.scale)
-    assert max_err(out[rows], ref) <= TOL
 
 
 # ---------------------------------------------------------------------------
@@ -628,23 +591,6 @@ def test_int4_append_many_steps():
         lens += 1
     torch.cuda.synchronize()
     assert_img_equal(dst, img)
-
-
-def test_int4_full_size_workload():
-    c = wl.workload("kvquant_int4", device=DEV)
-    src, dst, img = int4_pools(c, c.batch)
-    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
-    kv.kv_append(dst, c.k_new, c.v_new, c.tables, c.seq_lens)
-    out = gpu_attention(dst, c)
-    tab, lens = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
-    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens)
-    orc.q4_append(img, bits(c.k_new), bits(c.v_new), tab, lens)
-    assert_img_equal(dst, img)
-    rows = [0, 17, 63]
-    Kd, Vd = orc.q4_dequant(img, tab[rows], c.ctx_lens.cpu().numpy()[rows], np.array(rows, dtype=np.int32))
-    ref = orc.attention(Kd, Vd, bits(c.q)[rows], tab[rows], c.ctx_lens.cpu().numpy()[rows], c.scale)
-    assert np.all(np.isfinite(out))
-    assert max_err(out[rows], ref) <= TOL
 
 
 @pytest.mark.parametrize("kernel,split", [(1, 0), (2, 0), (2, 1), (2, 3)])
@@ -905,3 +851,24 @@ def test_append_tokens_equals_sequential_appends(dtype, n_new):
         for t in range(n_new):
             orc.append(K, V, bits(kn[:, t]), bits(vn[:, t]), tab.numpy(), lens_np + t)
         assert np.array_equal(ibits(bits(pool.K)), ibits(K)) and np.array_equal(ibits(bits(pool.V)), ibits(V))
+
+
+# ---------------------------------------------------------------------------
+# read-ceiling probe (measurement)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pieces,at,workgroups", [(7, 6, 1), (7, 0, 0), (1001, 1000, 3), (4096, 2049, 2)])
+def test_read_probe_reads_every_piece(pieces, at, workgroups):
+    """A buffer of zeros with one word equal to the sink value, in piece `at`:
+    the probe's XOR fold equals it only if that piece was read, and then the
+    sink is written; with no such word the sink stays untouched."""
+    buf = torch.zeros(pieces * 1024, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kv_read_probe(buf, sink, workgroups)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    magic = np.array([0x9E3779B9], dtype=np.uint32).view(np.int32)[0]
+    buf[at * 1024 + 517] = int(magic)
+    kv.kv_read_probe(buf, sink, workgroups)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == int(magic)
