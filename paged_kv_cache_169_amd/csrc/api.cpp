@@ -183,7 +183,9 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
     g->off_prefix = 0;
     if (sched == KV_SCHED_BALANCED) {
         // every attended block of every sequence is one tile; a sequence
-        // longer than max_ctx does not fit the promise and reads as bad
+        // longer than max_ctx does not fit the promise and reads as bad. The
+        // kernels keep the schedule's per-unit prefix sums in 32 bits.
+        if ((int64_t)batch * (nblk + kSegCost) > INT32_MAX) return KV_ERR_UNSUPPORTED;
         g->split_blocks = nblk;
         g->max_splits = 1;
         const bool wide = g->ctw > 2 || (g->ctw == 2 && dtype == KV_BF16 && D == 128);  // as launch_attention

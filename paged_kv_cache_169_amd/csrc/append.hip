@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int t_new = (int)(r % p.n_new);
     const int b = (int)(r / p.n_new);
     const int L0 = p.seq_lens[b];
-    if (L0 < 0 || L0 + p.n_new > p.max_blocks * kBlock) return;  // the chunk must fit the table
+    if (!append_fits(L0, p.n_new, p.max_blocks)) return;  // the chunk must fit the table
     const int L = L0 + t_new;
     const int pid = p.tables[(size_t)b * p.max_blocks + L / kBlock];
     if (pid < 0 || pid >= p.num_blocks) return;

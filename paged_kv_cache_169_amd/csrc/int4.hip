@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64) void append_int4_kernel(AppendParams p) {
     const bool act = lane < hd;
     __shared__ uint32_t rows[kBlock][64];  // K rows of the open block, one word per lane
     const int L0 = p.seq_lens[b];
-    if (L0 < 0 || L0 + p.n_new > p.max_blocks * kBlock) return;
+    if (!append_fits(L0, p.n_new, p.max_blocks)) return;
     const int slot = p.seq_slots ? p.seq_slots[b] : b;
     if (slot < 0 || slot >= p.max_seqs) return;
     uint32_t *tail = reinterpret_cast<uint32_t *>(p.pool.ktail) + ((size_t)slot * p.n_kv + h) * kBlock * hd;

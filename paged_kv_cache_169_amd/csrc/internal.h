@@ -57,10 +57,25 @@ struct AttnParams {
     const void *k_new, *v_new;
 };
 
+// Length after adding `add` tokens to a length L read from device metadata,
+// summed in 64 bits (a corrupt L near INT32_MAX must not wrap); -1 when L is
+// negative or the sum leaves int32.
+__host__ __device__ inline int length_after(int L, int add) {
+    if (L < 0) return -1;
+    const long long n = (long long)L + add;
+    return n > 2147483647LL ? -1 : (int)n;
+}
+
+// Whether n_new tokens appended at positions L0 .. L0 + n_new - 1 fit a table
+// of max_blocks blocks (64-bit sum).
+__host__ __device__ inline bool append_fits(int L0, int n_new, int max_blocks) {
+    return L0 >= 0 && (long long)L0 + n_new <= (long long)max_blocks * kBlock;
+}
+
 // Attended length of sequence b (negative: invalid).
 __host__ __device__ inline int ctx_of(const AttnParams &p, int b) {
     const int L = p.ctx_lens[b];
-    return p.ctx_add == 0 ? L : (L < 0 ? -1 : L + p.ctx_add);
+    return p.ctx_add == 0 ? L : length_after(L, p.ctx_add);
 }
 
 struct AppendParams {
@@ -177,7 +192,7 @@ struct SeqRange {
 __host__ __device__ inline SeqRange seq_range(int n, int max_blocks, int window, int split_blocks,
                                               int max_splits, int q_len) {
     SeqRange r;
-    r.bad = n < 0 || n > max_blocks * kBlock;
+    r.bad = n < 0 || (long long)n > (long long)max_blocks * kBlock;
     auto lo_of = [&](int m) {
         const int first_hi = m - q_len + 1;  // range end of query token 0
         return window > 0 ? (first_hi - window > 0 ? first_hi - window : 0) : 0;

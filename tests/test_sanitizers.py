@@ -1,0 +1,86 @@
+"""The host code under the address and undefined-behaviour sanitizers (CPU).
+
+- The oracle (oracle/kvoracle.c) built with -fsanitize=address,undefined,
+  float-cast-overflow runs every oracle pin: an out-of-bounds access, a signed
+  overflow or an out-of-range float-to-int conversion (the INT4 coder's
+  rounding) aborts the run.
+- The library's host side (api.cpp: descriptors, argument checks, geometry,
+  workspace sizing) built the same way with g++, its kernel launchers replaced
+  by stand-ins that abort (tests/native/hostcheck_stubs.cpp), runs the C-ABI
+  host tests: none of them may reach a launch or trip a sanitizer.
+- The length predicates the kernels apply to device metadata run on the host
+  at the int32 limits (tests/native/host_predicates.cpp).
+
+Each sanitized build is loaded into a child Python process with the
+sanitizer runtime preloaded."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+NATIVE = os.path.join(ROOT, "tests", "native")
+CSRC = os.path.join(ROOT, "paged_kv_cache_169_amd", "csrc")
+HIP_INCLUDE = "/opt/rocm/include"
+SAN = ["-fsanitize=address,undefined,float-cast-overflow", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+       "-g", "-O1"]
+
+
+def _runtime():
+    path = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not path or not os.path.isabs(path) or not os.path.exists(path):
+        pytest.skip("no libasan for gcc")
+    return path
+
+
+def _env(extra):
+    env = dict(os.environ)
+    env.update(extra)
+    env["LD_PRELOAD"] = _runtime()
+    # Python itself keeps memory at exit; a leak report is not what is checked
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return env
+
+
+def _pytest(test_file, env, tmp_path):
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-s", "-p", "no:cacheprovider", "-m", "not gpu",
+                        os.path.join(ROOT, "tests", test_file)],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0, out[-4000:]
+    assert "runtime error" not in out and "AddressSanitizer" not in out, out[-4000:]
+    return out
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_oracle_pins_under_sanitizers(tmp_path):
+    lib = tmp_path / "libkvoracle_san.so"
+    subprocess.run(["gcc", "-std=c99", "-D_DEFAULT_SOURCE", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
+                   + SAN + [os.path.join(ROOT, "oracle", "kvoracle.c"), "-o", str(lib), "-lm"], check=True)
+    out = _pytest("test_oracle_pins.py", _env({"KVORACLE_LIB": str(lib), "OMP_NUM_THREADS": "2"}), tmp_path)
+    assert " passed" in out
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir(HIP_INCLUDE), reason="needs g++ and HIP headers")
+def test_host_abi_under_sanitizers(tmp_path):
+    lib = tmp_path / "libkvcache_hostcheck.so"
+    subprocess.run(["g++", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__", "-I", HIP_INCLUDE,
+                    "-I", os.path.join(ROOT, "include"), "-I", CSRC] + SAN +
+                   [os.path.join(CSRC, "api.cpp"), os.path.join(NATIVE, "hostcheck_stubs.cpp"), "-o", str(lib)],
+                   check=True)
+    out = _pytest("test_abi_host.py", _env({"KVCACHE_LIB": str(lib)}), tmp_path)
+    assert " passed" in out
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir(HIP_INCLUDE), reason="needs g++ and HIP headers")
+def test_length_predicates_at_int32_limits(tmp_path):
+    exe = tmp_path / "host_predicates"
+    subprocess.run(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", HIP_INCLUDE, "-I",
+                    os.path.join(ROOT, "include"), "-I", CSRC] + SAN +
+                   [os.path.join(NATIVE, "host_predicates.cpp"), "-o", str(exe)], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=60)
+    assert r.returncode == 0 and "host predicates ok" in r.stdout, r.stdout + r.stderr
