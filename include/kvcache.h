@@ -314,7 +314,9 @@ kv_status paged_multi_token_attention(kv_pool_t pool, const void *q, float *out,
  * fewer per step): on bf16 pools tiles take the new rows from k_new / v_new
  * and write them into the pool; on INT4 pools with q_len 1 the workgroup
  * that reads a sequence's last block codes the new token into the pool
- * first. Other pools and INT4 with q_len > 1 launch the append kernel first.
+ * first when each kv head has at most 16 query columns. Other pools, INT4
+ * with q_len > 1 and INT4 with more than 16 query heads per kv head launch
+ * the append kernel first.
  * seq_lens must not change between the two (same stream order). A sequence
  * whose length is out of range or above max_ctx gets NaN and may be left
  * unappended. */
