@@ -325,6 +325,31 @@ kv_status kv_decode_step(kv_pool_t pool, const void *k_new, const void *v_new, c
                          int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
                          int32_t max_ctx, void *workspace, size_t ws_bytes, const kv_attn_opts *opts, void *stream);
 
+/* Bytes of the device array kv_decode_step_noalloc uses as its workspace
+ * (64 MiB; every device the library runs on holds one until the process
+ * ends). It covers the one-token decode step on bf16 and INT4 pools at any
+ * batch the balanced schedule takes (its workspace depends on the device's
+ * persistent grid, 16 rows per slot and the batch's prefix sums). */
+#define KV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kv_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same call without workspace arguments. Its workspace is a file-scope
+ * device array of KV_NOALLOC_SCRATCH_BYTES bytes, looked up on the calling
+ * thread's current device on the first call there (the stream's device must
+ * be current). Calls no hipMalloc, hipFree or other allocating routine.
+ * Returns KV_ERR_WORKSPACE when the call's workspace
+ * (paged_multi_token_attention_workspace_bytes) exceeds the array, and
+ * KV_ERR_HIP if the array's address cannot be found. Every call on one device
+ * shares that device's array and nothing in it has to start at zero (each
+ * call writes what it reads), but calls that overlap on one device (two
+ * streams, or two threads) race on it: order them. Outputs and pool contents
+ * are those of kv_decode_step, bit for bit. */
+kv_status kv_decode_step_noalloc(kv_pool_t pool, const void *k_new, const void *v_new, const void *q, float *out,
+                                 int32_t num_q_heads, int32_t q_len, float scale, const int32_t *block_tables,
+                                 int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                                 int32_t max_ctx, const kv_attn_opts *opts, void *stream);
+
 /* Bulk KVQuant INT4 coding of bf16 pool contents [CORE, "KVQuant: 마지막 4배"]:
  * code = clamp(round((x - min) / s), 0, 15) with s = (max - min) / 15, s and min
  * stored in fp16 and the codes computed from the stored values (fp32

@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("KVCACHE_LIB", os.path.join(_PKG, "libkvcache.so"))
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP, KV_ERR_TABLE = 0, -1, -2, -3, -4, -5
 KV_F32, KV_BF16, KV_INT4 = 0, 1, 2
 BLOCK = 16
+KV_NOALLOC_SCRATCH_BYTES = 64 << 20  # the device array of kv_decode_step_noalloc
 (KV_REGION_K, KV_REGION_V, KV_REGION_KQ, KV_REGION_KS, KV_REGION_KM, KV_REGION_VQ, KV_REGION_VS,
  KV_REGION_VM, KV_REGION_KTAIL) = range(9)
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
@@ -109,6 +110,9 @@ _paged_multi_token_attention = _decl(
 _kv_decode_step = _decl(
     "kv_decode_step", _I32,
     [_P, _P, _P, _P, _P, _I32, _I32, _F, _P, _I32, _P, _P, _I32, _I32, _P, _SZ, ctypes.POINTER(kv_attn_opts), _P])
+_kv_decode_step_noalloc = _decl(
+    "kv_decode_step_noalloc", _I32,
+    [_P, _P, _P, _P, _P, _I32, _I32, _F, _P, _I32, _P, _P, _I32, _I32, ctypes.POINTER(kv_attn_opts), _P])
 _kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P])
 _rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
 _kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
@@ -400,6 +404,30 @@ def kv_decode_step(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, q: to
     _check(st, "kv_decode_step")
 
 
+def kv_decode_step_noalloc(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                           out: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                           max_ctx: int, seq_slots: torch.Tensor | None = None, opts: kv_attn_opts | None = None,
+                           stream=None) -> None:
+    """kv_decode_step with the library's own device workspace (see
+    kv_decode_step_noalloc in kvcache.h); shapes as kv_decode_step."""
+    d = pool.desc
+    if q.dim() == 3:
+        B, n_h, hd = q.shape
+        q_len = 1
+    else:
+        B, q_len, n_h, hd = q.shape
+    if hd != d.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out shape does not match the pool")
+    kdt = torch.float32 if d.dtype == KV_F32 else torch.bfloat16
+    n = B * q_len * d.num_kv_heads * d.head_dim
+    st = _kv_decode_step_noalloc(pool.handle, _dev_ptr(k_new, "k_new", kdt, n), _dev_ptr(v_new, "v_new", kdt, n),
+                                 _dev_ptr(q, "q", kdt), _dev_ptr(out, "out", torch.float32), n_h, q_len,
+                                 float(scale), _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                 _i32(seq_lens, "seq_lens"), _i32(seq_slots, "seq_slots"), B, int(max_ctx),
+                                 ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    _check(st, "kv_decode_step_noalloc")
+
+
 def kv_quantize_int4(dst: KVPool, src: KVPool, block_tables: torch.Tensor, lens: torch.Tensor,
                      seq_slots: torch.Tensor | None = None, stream=None) -> None:
     st = _kv_quantize_int4(dst.handle, src.handle, _i32(block_tables, "block_tables"), int(block_tables.shape[1]),
@@ -525,4 +553,5 @@ raw = {
     "paged_decode_attention_shared": _paged_decode_attention_shared,
     "paged_decode_attention_shared_workspace_bytes": _paged_decode_attention_shared_workspace_bytes,
     "kv_validate_tables": _kv_validate_tables, "kv_read_probe": _kv_read_probe,
+    "kv_decode_step_noalloc": _kv_decode_step_noalloc,
 }

@@ -33,6 +33,7 @@ SOURCES = {
     "attention.hip": [],
     "blend.hip": [],
     "measure.hip": [],
+    "noalloc.hip": [],
 }
 
 

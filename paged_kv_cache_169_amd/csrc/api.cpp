@@ -540,6 +540,26 @@ kv_status kv_decode_step(kv_pool_t pool, const void *k_new, const void *v_new, c
                           batch, max_ctx, workspace, ws_bytes, opts, stream, q_len, k_new, v_new);
 }
 
+
+kv_status kv_decode_step_noalloc(kv_pool_t pool, const void *k_new, const void *v_new, const void *q, float *out,
+                                 int32_t num_q_heads, int32_t q_len, float scale, const int32_t *block_tables,
+                                 int32_t max_blocks, const int32_t *seq_lens, const int32_t *seq_slots, int32_t batch,
+                                 int32_t max_ctx, const kv_attn_opts *opts, void *stream) {
+    if (!pool) return KV_ERR_INVALID_ARG;
+    const size_t need = paged_multi_token_attention_workspace_bytes(pool, batch, num_q_heads, q_len, max_ctx, opts);
+    if (need == (size_t)-1)  // a geometry the library refuses: the full call reports why, before any launch
+        return kv_decode_step(pool, k_new, v_new, q, out, num_q_heads, q_len, scale, block_tables, max_blocks,
+                              seq_lens, seq_slots, batch, max_ctx, nullptr, 0, opts, stream);
+    if (need > kNoallocScratchBytes) return KV_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0 && batch > 0) {
+        ws = noalloc_scratch();
+        if (!ws) return KV_ERR_HIP;
+    }
+    return kv_decode_step(pool, k_new, v_new, q, out, num_q_heads, q_len, scale, block_tables, max_blocks, seq_lens,
+                          seq_slots, batch, max_ctx, ws, ws ? kNoallocScratchBytes : 0, opts, stream);
+}
+
 kv_status paged_decode_attention(kv_pool_t pool, const void *q, float *out, int32_t num_q_heads, float scale,
                                  const int32_t *block_tables, int32_t max_blocks, const int32_t *ctx_lens,
                                  const int32_t *seq_slots, int32_t batch, int32_t max_ctx, void *workspace,

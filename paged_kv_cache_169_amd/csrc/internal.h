@@ -172,6 +172,11 @@ int shared_balanced_grid(int head_dim, size_t lds);
 hipError_t launch_quantize_int4(const QuantParams &p, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeParams &p, hipStream_t s);
 hipError_t launch_read_probe(const void *buf, size_t bytes, int workgroups, uint32_t *sink, hipStream_t s);
+// kv_decode_step_noalloc's workspace: a device array of kNoallocScratchBytes
+// (noalloc.hip). Its address on the current device, looked up there on the
+// first call (null if the lookup fails); allocates nothing.
+constexpr size_t kNoallocScratchBytes = (size_t)KV_NOALLOC_SCRATCH_BYTES;
+void *noalloc_scratch();
 
 // The attended block range of one sequence, shared by the split kernels and
 // the merge kernels so that both agree on the number of splits. With q_len

@@ -32,6 +32,8 @@ hipError_t launch_quantize_int4(const QuantParams &, hipStream_t) { reached("lau
 hipError_t launch_rope(int, const RopeParams &, hipStream_t) { reached("launch_rope"); }
 hipError_t launch_read_probe(const void *, size_t, int, uint32_t *, hipStream_t) { reached("launch_read_probe"); }
 
+void *noalloc_scratch() { reached("noalloc_scratch"); }
+
 int balanced_grid(int, int, int, int) { return 256 * 2; }
 int wide_grid(int, int ctw, int, int) { return 1024 / ctw; }
 size_t shared_balanced_lds(int n_groups, int batch, int max_blocks) {

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -330,3 +330,25 @@ def test_read_probe_rejects_bad_arguments(kv):
     assert f(ok_buf, 4096, -1, sink, None) == kv.KV_ERR_INVALID_ARG
     assert f(ok_buf, 4096, 65536, sink, None) == kv.KV_ERR_INVALID_ARG
     assert f(ok_buf, 4096 * (2 ** 31), 0, sink, None) == kv.KV_ERR_UNSUPPORTED
+
+
+def test_noalloc_step_refuses_before_any_launch(kv):
+    """kv_decode_step_noalloc: a NULL pool, and a call whose workspace exceeds
+    the library's device array (fixed splits of one block over 1M tokens),
+    are refused before the array is looked up or anything is launched. The
+    array's size in the header and in the binding agree."""
+    src = open(HEADER, encoding="utf-8").read()
+    m = re.search(r"#define KV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kv.KV_NOALLOC_SCRATCH_BYTES
+    f = kv.raw["kv_decode_step_noalloc"]
+    desc = kv.make_desc(64, 8, 128, "bf16")
+    st, h = make_handle(kv, desc)
+    assert st == 0
+    p = FAKE + (1 << 20)
+    assert f(None, p, p, p, p, 32, 1, 0.1, p, 65536, p, None, 4, 1 << 20, None, None) == kv.KV_ERR_INVALID_ARG
+    opts = kv.attn_opts(split_blocks=1, schedule=1)
+    st = f(h, p, p, p, p, 32, 1, 0.1, p, 65536, p, None, 4, 1 << 20, ctypes.byref(opts), None)
+    assert st == kv.KV_ERR_WORKSPACE
+    # a geometry the library refuses reports its own error
+    assert f(h, p, p, p, p, 33, 1, 0.1, p, 65536, p, None, 4, 1 << 20, None, None) == kv.KV_ERR_INVALID_ARG
+    assert kv.raw["kv_pool_destroy"](h) == 0
