@@ -127,8 +127,15 @@ struct AttnGeom {
 // Largest batch of the balanced schedule (its block prefix sums live in LDS).
 constexpr int kMaxBalancedBatch = 8192;
 // Balanced schedule: tiles' worth of time a (sequence, unit) pair costs on
-// top of its tiles (its block ids, query and first tile).
+// top of its tiles: its start (block ids, query, the first tile's latency,
+// the partial or output it writes). Fitted on MI355X to per-workgroup times
+// of the 8B-shaped layers: a bf16 pair start costs about 1.1 tiles, an INT4
+// one about 3.6. (A fused INT4 append costs about 2 more tiles, but it is not
+// charged: the schedule of the decode step must equal that of the separate
+// attention call, so that both give the same bits.)
 constexpr int kSegCost = 1;
+constexpr int kSegCostQ4 = 4;
+constexpr int kMaxPairCost = kSegCostQ4;
 
 kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
                     const kv_attn_opts *opts, AttnGeom *g) {
@@ -185,7 +192,7 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         // every attended block of every sequence is one tile; a sequence
         // longer than max_ctx does not fit the promise and reads as bad. The
         // kernels keep the schedule's per-unit prefix sums in 32 bits.
-        if ((int64_t)batch * (nblk + kSegCost) > INT32_MAX) return KV_ERR_UNSUPPORTED;
+        if ((int64_t)batch * (nblk + kMaxPairCost) > INT32_MAX) return KV_ERR_UNSUPPORTED;
         g->split_blocks = nblk;
         g->max_splits = 1;
         const bool wide = g->ctw > 2 || (g->ctw == 2 && dtype == KV_BF16 && D == 128);  // as launch_attention
@@ -506,7 +513,9 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     a.slot_cols = g.slot_cols;
     a.schedule = g.schedule;
     a.n_wg = g.n_wg;
-    a.seg_cost = g.schedule == KV_SCHED_BALANCED ? kSegCost : 0;
+    const bool balanced = g.schedule == KV_SCHED_BALANCED;
+    a.seg_cost = balanced ? (dtype == KV_INT4 ? kSegCostQ4 : kSegCost) : 0;
+    a.pace = balanced ? 1 : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
     void *const *ev = opts ? opts->events : nullptr;

@@ -681,6 +681,52 @@ __device__ __forceinline__ BlockIds stage_checked_block_ids(const AttnParams &p,
 // Runs seg(c0, c1, init) over [j0, j1) in pieces of at most kSidsWindow
 // blocks; init is true for the first piece only (it resets the softmax
 // state, the others continue it). An empty range still makes one call.
+// Pacing of the persistent balanced kernels. The two waves that share a SIMD
+// get equal shares, but issue goes to the older wave first, so one of them
+// used to finish long before the other (INT4, 8B shape: 40 vs 51 us on
+// average), which then ran alone and slower. Each wave instead sets its own
+// priority from its progress through its share (s_setprio: priority is
+// compared before age): 3 in the first half, 2 up to 80 %, 1 up to 95 %, 0
+// after. A wave that falls behind its partner is issued first until it
+// catches up, so the pair ends within a few percent of a share of each
+// other. The state is only values: block j of a piece sits at share
+// position base + j, and the band ends th1..th3 are fixed per workgroup
+// (share 0: no pacing). Kept in registers: a pacing state in memory made
+// every tile wait for the next tile's loads.
+struct Pace {
+    int base, th1, th2, th3;
+};
+
+__device__ __forceinline__ Pace pace_for(long share) {
+    Pace pc;
+    const int sh = (int)share;
+    pc.base = 0;
+    pc.th1 = sh > 0 ? sh / 2 : INT_MAX;
+    pc.th2 = sh > 0 ? (int)((long)sh * 4 / 5) : INT_MAX;
+    pc.th3 = sh > 0 ? (int)((long)sh * 19 / 20) : INT_MAX;
+    return pc;
+}
+
+// Priority of the band holding share position pos (uniform).
+__device__ __forceinline__ void pace_set(const Pace &pc, int pos) {
+    if (pc.th1 == INT_MAX) return;
+    if (pos >= pc.th3)
+        __builtin_amdgcn_s_setprio(0);
+    else if (pos >= pc.th2)
+        __builtin_amdgcn_s_setprio(1);
+    else if (pos >= pc.th1)
+        __builtin_amdgcn_s_setprio(2);
+    else
+        __builtin_amdgcn_s_setprio(3);
+}
+
+// After block j of a piece: the band changes when the next position reaches
+// one of its ends.
+__device__ __forceinline__ void pace_tick(const Pace &pc, int j) {
+    const int pos = pc.base + j + 1;
+    if (pos == pc.th1 || pos == pc.th2 || pos == pc.th3) pace_set(pc, pos);
+}
+
 template <class Seg>
 __device__ __forceinline__ void run_pieces(int j0, int j1, Seg seg) {
     for (int c0 = j0;; c0 += kSidsWindow) {
@@ -704,7 +750,8 @@ __device__ __forceinline__ void run_pieces(int j0, int j1, Seg seg) {
 template <int D, int CT, bool KEEP = false>
 __device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int kvh, const Column *col,
                                                 const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st,
-                                                bool &bad, bool write_new, int *sids, bool init) {
+                                                bool &bad, bool write_new, int *sids, bool init,
+                                                Pace pace = Pace{0, INT_MAX, INT_MAX, INT_MAX}) {
     constexpr int KS = D / 32, MS = D / 16;
     const int n16 = lane & 15, G = lane >> 4;
     // Q^T as B operand: lane (G, n16) holds channels s*32 + 8G .. +8 of its column.
@@ -767,6 +814,7 @@ __device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int 
         MfmaTile<D> T;
         fetch(j, T);
         compute(T, j);
+        pace_tick(pace, j);
     }
 }
 
@@ -1219,7 +1267,7 @@ __device__ __forceinline__ void q4_append_token(const AttnParams &p, int b, int 
 template <int D, int NP, bool FLAT>
 __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, int ct, const Column &col,
                                            const SeqRange &r, int j0, int j1, int lane, MfmaState<D> &st, bool &bad,
-                                           int *sids, bool init) {
+                                           int *sids, bool init, Pace pace = Pace{0, INT_MAX, INT_MAX, INT_MAX}) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
     int slot = uniform(p.seq_slots ? p.seq_slots[b] : b);
@@ -1276,6 +1324,7 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         const bool masked = j < jA || j >= jB;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
         q4_block<NP>(p, T, Q, masked, !masked || is_full(j), tail_row, tok0, tlo, thi, colq, n16, G, L, st);
+        pace_tick(pace, j);
     };
     // Fused append (decode step, one new token at position r.n - 1): the
     // segment that ends with the sequence's last block codes the token into
@@ -1328,16 +1377,16 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
 template <int D, int Q4, int CT, bool KEEP, bool FLAT>
 __device__ __forceinline__ void run_segment(const AttnParams &p, int b, int kvh, int ct0, const Column *col,
                                             const SeqRange &r, int j0, int j1, int lane, MfmaState<D> *st, bool &bad,
-                                            int *sids) {
+                                            int *sids, Pace pace = Pace{0, INT_MAX, INT_MAX, INT_MAX}) {
     if constexpr (Q4 > 0) {
         static_assert(CT == 1, "the INT4 path takes one column tile per unit");
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
             static_assert(!KEEP, "the INT4 path streams its tiles");
-            q4_segment<D, Q4, FLAT>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init);
+            q4_segment<D, Q4, FLAT>(p, b, kvh, ct0, col[0], r, c0, c1, lane, st[0], bad, sids, init, pace);
         });
     } else {
         run_pieces(j0, j1, [&](int c0, int c1, bool init) {
-            bf16_segment_ct<D, CT, KEEP>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct0 == 0, sids, init);
+            bf16_segment_ct<D, CT, KEEP>(p, b, kvh, col, r, c0, c1, lane, st, bad, ct0 == 0, sids, init, pace);
         });
     }
 }
@@ -1430,6 +1479,11 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     const long per = (total + p.n_wg - 1) / p.n_wg;
     const long s = (long)wg * per;
     const long e = min(total, s + per);
+    // paced on INT4 pools only (measured: INT4 60 vs 62-63.5 us on the 8B
+    // shape; the bf16 kernels unchanged, and without it they keep fewer
+    // registers)
+    Pace pace = pace_for(Q4 && p.pace ? e - s : 0);
+    pace_set(pace, 0);
     for (long t = s; t < e;) {
         // sequence holding position t: largest b with units * pre[b] <= t
         auto pre_s = [&](int i) { return Q4 ? uniform(pre[i]) : pre[i]; };
@@ -1443,6 +1497,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         }
         const int b = lo;
         const int pb = pre_s(b);
+        const int ctx = ctx_of(p, b);
         const int span = pre_s(b + 1) - pb;  // nb + seg_cost positions per unit
         const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
@@ -1457,7 +1512,6 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         const int kvh = unit / cgroups, ct0 = (unit % cgroups) * CT;
         const long seg_end = min(e, pair_t + nb);
         const int cnt = (int)(seg_end - t);
-        const int ctx = ctx_of(p, b);
         const SeqRange r = seq_range(Q4 ? uniform(ctx) : ctx, p.max_blocks, p.window, p.split_blocks, p.max_splits,
                                      p.q_len);
         bool bad = r.bad;
@@ -1465,8 +1519,11 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 #pragma unroll
         for (int c = 0; c < CT; ++c) col[c] = column_of(p, b, kvh, ct0 + c, n16, r);
         MfmaState<D> st[CT];
+        // block j of this piece sits at share position (t - s) + j - (blk_lo + jr)
+        pace.base = (int)(t - s) - (r.blk_lo + jr);
+        pace_set(pace, (int)(t - s));
         run_segment<D, Q4, CT, KEEP, FLAT>(p, b, kvh, ct0, col, r, r.blk_lo + jr, r.blk_lo + jr + cnt, lane, st, bad,
-                                           sids);
+                                           sids, pace);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const float l = q4_state_sum<Q4>(st[c].l), bv = q4_state_sum<Q4>(st[c].bv);

@@ -44,6 +44,7 @@ struct AttnParams {
     int32_t schedule;  // KV_SCHED_SPLIT or KV_SCHED_BALANCED
     int32_t n_wg;      // balanced: persistent grid size
     int32_t seg_cost;  // balanced: schedule positions a (sequence, unit) pair takes beyond its tiles
+    int32_t pace;      // balanced INT4: waves set their issue priority from their progress (1) or not (0)
     int32_t *ws_prefix;  // balanced: [batch + 1] schedule positions per unit before each sequence
     float scale_log2;  // scale * log2(e): scores are kept in log2 units
     // Decode step: the attended length of sequence b is ctx_lens[b] + ctx_add
