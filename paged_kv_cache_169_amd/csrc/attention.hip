@@ -1592,21 +1592,61 @@ constexpr int kWideCT = 2;
 // [64 q, 64 q + 64), wave w issues q = w, w + W, ... Rows of the step's new
 // tokens (slots from newpos on) come from k_new / v_new. Complete after the
 // wave's vector-memory counter reaches 0.
+// Slots of a K/V tile in LDS that wave `wave` of a wide unit loads: slot
+// q * 64 + lane for q = wave, wave + W, ...; the first TS slots are K, the
+// rest V. Byte offset of each of this lane's slots within its (block, kv
+// head) K or V tile; they do not change from tile to tile.
 template <int D, int W>
-__device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh, int b, int newpos, int wave,
-                                           int lane, TileLds<D> &t) {
-    constexpr int SPR = TileLds<D>::SPR, NI = TileLds<D>::SLOTS / 64;
+struct WideSlots {
+    static constexpr int SPR = TileLds<D>::SPR, NI = TileLds<D>::SLOTS / 64, TS = kBlock * SPR, NQ = NI / W;
+    static_assert(TS % 64 == 0 && NI % W == 0, "a wave's slots lie in one tile, every wave has as many");
+    uint32_t off[NQ];  // row * D * 2 + 16-byte column * 16
+    int wave;          // uniform
+};
+
+template <int D, int W>
+__device__ __forceinline__ WideSlots<D, W> wide_slots(int wave, int lane) {
+    using S = WideSlots<D, W>;
+    S w;
+    w.wave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int q = wave; q < NI; q += W) {
-        const int sl = q * 64 + lane;
-        const int which = sl / (kBlock * SPR), rem = sl % (kBlock * SPR);
-        const int row = rem / SPR, col = (rem % SPR) ^ (row % SPR);
-        gu16_t *src;
-        if (row >= newpos && row < newpos + p.ctx_add)
-            src = global_u16(which ? p.v_new : p.k_new) + (((size_t)b * p.ctx_add + (row - newpos)) * p.n_kv + kvh) * D;
-        else
-            src = global_u16(which ? p.pool.v : p.pool.k) + (((size_t)pid * p.n_kv + kvh) * kBlock + row) * D;
-        __builtin_amdgcn_global_load_lds(src + col * 8, (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
+    for (int k = 0; k < S::NQ; ++k) {
+        const uint32_t rem = (uint32_t)((w.wave + k * W) * 64 % S::TS) + (uint32_t)lane;
+        const uint32_t row = rem / S::SPR, col = (rem % S::SPR) ^ (row % S::SPR);
+        w.off[k] = (row * D + col * 8) * 2;
+    }
+    return w;
+}
+
+// Issue the global-to-LDS loads of this wave's slots of one (block pid, kv
+// head) K/V tile into t. The XOR swizzle of TileLds is applied on the global
+// side. Decode step with the append fused: rows of the step's new tokens
+// (slots from newpos on) come from k_new / v_new. Complete after the wave's
+// vector-memory counter reaches 0.
+template <int D, int W>
+__device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh, int b, int newpos,
+                                           const WideSlots<D, W> &S, TileLds<D> &t) {
+    using WS = WideSlots<D, W>;
+    typedef const __attribute__((address_space(1))) char gchar_t;
+    // the tile's base (uniform), and each lane's fixed offset within it
+    const size_t tile = ((size_t)pid * p.n_kv + kvh) * kBlock * D * 2;
+    gchar_t *kt = (gchar_t *)(p.pool.k) + tile, *vt = (gchar_t *)(p.pool.v) + tile;
+    // only a tile that holds new tokens tests rows (newpos is uniform: in a
+    // scalar register the test is a branch, not an exec mask)
+    newpos = __builtin_amdgcn_readfirstlane(newpos);
+    const bool fresh = newpos < kBlock && newpos + p.ctx_add > 0;
+#pragma unroll
+    for (int k = 0; k < WS::NQ; ++k) {
+        const int q = S.wave + k * W;
+        const bool v = q * 64 >= WS::TS;  // uniform: K or V
+        gchar_t *src = (v ? vt : kt) + S.off[k];
+        if (fresh) {
+            const int row = (int)(S.off[k] / (D * 2));
+            if (row >= newpos && row < newpos + p.ctx_add)
+                src = (gchar_t *)(v ? p.v_new : p.k_new) +
+                      (((size_t)b * p.ctx_add + (row - newpos)) * p.n_kv + kvh) * D * 2 + S.off[k] % (D * 2);
+        }
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
     }
 }
 
@@ -1686,15 +1726,15 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
         }
     }
     auto newpos_of = [&](int j) { return L0 == INT_MAX ? kBlock : min(L0 - j * kBlock, kBlock); };
-    const int wave = tid >> 6;
-    wide_issue<D, W>(p, pid_of(j0), kvh, b, newpos_of(j0), wave, lane, tl[0]);
+    const WideSlots<D, W> slots = wide_slots<D, W>(tid >> 6, lane);
+    wide_issue<D, W>(p, pid_of(j0), kvh, b, newpos_of(j0), slots, tl[0]);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the tile is in LDS
     __syncthreads();
     for (int j = j0; j < j1; ++j) {
         const int cur = (j - j0) & 1;
         // the next tile's loads fill the other buffer while this one is used
         // (all waves passed the last barrier, so nobody reads it any more)
-        if (j + 1 < j1) wide_issue<D, W>(p, pid_of(j + 1), kvh, b, newpos_of(j + 1), wave, lane, tl[cur ^ 1]);
+        if (j + 1 < j1) wide_issue<D, W>(p, pid_of(j + 1), kvh, b, newpos_of(j + 1), slots, tl[cur ^ 1]);
         MfmaTile<D> T;
         wide_operands<D>(tl[cur], n16, G, T);
         const int tok0 = j * kBlock;
