@@ -559,7 +559,7 @@ __device__ __forceinline__ bool needs_mask(int tok0, const SeqRange &r) {
 template <int D>
 __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D> &T, const bf16x8_t (&qB)[D / 32],
                                            int tok0, int tlo, int thi, bool mask, const Column &col, int G,
-                                           MfmaState<D> &st) {
+                                           MfmaState<D> &st, bool sbranch = false) {
     constexpr int KS = D / 32, MS = D / 16, VC = D / 16;
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -567,13 +567,35 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
     float sv[4];
     float mx = -INFINITY;
+    if (sbranch) {
+        // mask is uniform; read into a scalar register the test is one
+        // branch per tile instead of lane masking around every score (the
+        // wide kernels: 16 query tokens 183.6 -> 174.6 us, 32: 299 -> 280
+        // us; the single-wave decode kernel measured 1 % slower with it)
+        if (__builtin_amdgcn_readfirstlane((int)mask)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int tp = tok0 + 4 * G + r;
-        bool ok = true;
-        if (mask) ok = (tp >= col.lo) & (tp < col.hi);  // mask is uniform
-        sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int tp = tok0 + 4 * G + r;
+                const bool ok = (tp >= col.lo) & (tp < col.hi);
+                sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sv[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sv[r] = sc[r] * p.scale_log2;
+                mx = fmaxf(mx, sv[r]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tp = tok0 + 4 * G + r;
+            bool ok = true;
+            if (mask) ok = (tp >= col.lo) & (tp < col.hi);  // mask is uniform
+            sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
+        }
     }
     const float cm = col_max(mx);
     if (__any(cm > st.m + kLazyLog2)) {
@@ -1740,7 +1762,8 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
 #pragma unroll
-        for (int c = 0; c < CT; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
+        for (int c = 0; c < CT; ++c)
+            mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c], true);
         __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads have landed
         __syncthreads();
     }
