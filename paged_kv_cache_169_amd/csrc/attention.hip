@@ -1620,8 +1620,9 @@ constexpr int kWideCT = 2;
 // head) K or V tile; they do not change from tile to tile.
 template <int D, int W>
 struct WideSlots {
-    static constexpr int SPR = TileLds<D>::SPR, NI = TileLds<D>::SLOTS / 64, TS = kBlock * SPR, NQ = NI / W;
-    static_assert(TS % 64 == 0 && NI % W == 0, "a wave's slots lie in one tile, every wave has as many");
+    static constexpr int SPR = TileLds<D>::SPR, NI = TileLds<D>::SLOTS / 64, TS = kBlock * SPR,
+                         NQ = (NI + W - 1) / W;  // a wave's slot groups (waves past NI - 1 have none)
+    static_assert(TS % 64 == 0, "a wave's 64 slots lie in the K or in the V tile");
     uint32_t off[NQ];  // row * D * 2 + 16-byte column * 16
     int wave;          // uniform
 };
@@ -1660,6 +1661,7 @@ __device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh
 #pragma unroll
     for (int k = 0; k < WS::NQ; ++k) {
         const int q = S.wave + k * W;
+        if (WS::NI % W != 0 && q >= WS::NI) break;  // uniform
         const bool v = q * 64 >= WS::TS;  // uniform: K or V
         gchar_t *src = (v ? vt : kt) + S.off[k];
         if (fresh) {
