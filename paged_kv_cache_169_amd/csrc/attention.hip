@@ -559,7 +559,7 @@ __device__ __forceinline__ bool needs_mask(int tok0, const SeqRange &r) {
 template <int D>
 __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D> &T, const bf16x8_t (&qB)[D / 32],
                                            int tok0, int tlo, int thi, bool mask, const Column &col, int G,
-                                           MfmaState<D> &st, bool sbranch = false) {
+                                           MfmaState<D> &st) {
     constexpr int KS = D / 32, MS = D / 16, VC = D / 16;
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -567,35 +567,13 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
     const bool partial = tlo > 0 || thi < kBlock;  // uniform: slots outside [tlo, thi) hold no token
     float sv[4];
     float mx = -INFINITY;
-    if (sbranch) {
-        // mask is uniform; read into a scalar register the test is one
-        // branch per tile instead of lane masking around every score (the
-        // wide kernels: 16 query tokens 183.6 -> 174.6 us, 32: 299 -> 280
-        // us; the single-wave decode kernel measured 1 % slower with it)
-        if (__builtin_amdgcn_readfirstlane((int)mask)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tp = tok0 + 4 * G + r;
-                const bool ok = (tp >= col.lo) & (tp < col.hi);
-                sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sv[r]);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sv[r] = sc[r] * p.scale_log2;
-                mx = fmaxf(mx, sv[r]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tp = tok0 + 4 * G + r;
-            bool ok = true;
-            if (mask) ok = (tp >= col.lo) & (tp < col.hi);  // mask is uniform
-            sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[r]);
-        }
+    for (int r = 0; r < 4; ++r) {
+        const int tp = tok0 + 4 * G + r;
+        bool ok = true;
+        if (mask) ok = (tp >= col.lo) & (tp < col.hi);  // mask is uniform
+        sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
     }
     const float cm = col_max(mx);
     if (__any(cm > st.m + kLazyLog2)) {
@@ -652,6 +630,117 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         const uint32_t a23 = __builtin_amdgcn_perm(vr[3][wi], vr[2][wi], sel);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
         st.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB, st.o[m], 0, 0, 0);
+    }
+}
+
+// The same for the CT column tiles one wave holds, on one tile, side by side
+// (CT > 1): the score products of every column tile first (each in two
+// MFMA chains), one lazy-rescale test for all of them, and each V operand
+// formed once for the CT value products. Independent work between the
+// dependent steps of each column tile, and fewer instructions: 8B shape, 16
+// query tokens 178 -> 166 us, 32 tokens 287 -> 256 us (wide units, which
+// also keep the sequence search in scalar registers).
+// The mask test is read into a scalar register: one branch per tile rather
+// than lane masking around every score.
+template <int D, int CT>
+__device__ __forceinline__ void mfma_block_ct(const AttnParams &p, const MfmaTile<D> &T,
+                                              const bf16x8_t (&qB)[CT][D / 32], int tok0, int tlo, int thi, bool mask,
+                                              const Column *col, int G, MfmaState<D> *st) {
+    constexpr int KS = D / 32, MS = D / 16, VC = D / 16;
+    static_assert(KS % 2 == 0, "two score chains of KS / 2 products");
+    f32x4_t sc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s], qB[c][s], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s + 1], qB[c][s + 1], s1, 0, 0, 0);
+        }
+        sc[c] = s0 + s1;
+    }
+    const bool partial = tlo > 0 || thi < kBlock;  // uniform
+    float sv[CT][4], mx[CT];
+    if (__builtin_amdgcn_readfirstlane((int)mask)) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            mx[c] = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tp = tok0 + 4 * G + r;
+                const bool ok = (tp >= col[c].lo) & (tp < col[c].hi);
+                sv[c][r] = ok ? sc[c][r] * p.scale_log2 : -INFINITY;
+                mx[c] = fmaxf(mx[c], sv[c][r]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            mx[c] = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sv[c][r] = sc[c][r] * p.scale_log2;
+                mx[c] = fmaxf(mx[c], sv[c][r]);
+            }
+        }
+    }
+    float cm[CT];
+    bool grow = false;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        cm[c] = col_max(mx[c]);
+        grow |= cm[c] > st[c].m + kLazyLog2;
+    }
+    if (__any(grow)) {  // as in mfma_block, for every column tile at once
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const float mn = fmaxf(st[c].m, cm[c]);
+            const float alpha = mn == st[c].m ? 1.0f : fast_exp2(st[c].m - mn);
+            st[c].l *= alpha;
+#pragma unroll
+            for (int m = 0; m < MS; ++m) st[c].o[m] *= alpha;
+            st[c].m = mn;
+        }
+    }
+    bf16x8_t pB[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const float mref = st[c].m == -INFINITY ? 0.0f : st[c].m;
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(sv[c][r] - mref);
+            st[c].l += pr[r];
+        }
+        const uint32_t h01 = cvt_pk_bf16(pr[0], pr[1]), h23 = cvt_pk_bf16(pr[2], pr[3]);
+        const uint32_t l01 = cvt_pk_bf16(pr[0] - __uint_as_float(h01 << 16), pr[1] - __uint_as_float(h01 & 0xffff0000u));
+        const uint32_t l23 = cvt_pk_bf16(pr[2] - __uint_as_float(h23 << 16), pr[3] - __uint_as_float(h23 & 0xffff0000u));
+        pB[c] = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));
+    }
+    uint32_t vr[4][VC / 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < VC / 2; ++k) vr[i][k] = T.v[i][k];
+    if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tt = 4 * G + i;
+            if (tt < tlo || tt >= thi) {
+#pragma unroll
+                for (int k = 0; k < VC / 2; ++k) vr[i][k] = 0u;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int wi = m >> 1;
+        const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t a01 = __builtin_amdgcn_perm(vr[1][wi], vr[0][wi], sel);
+        const uint32_t a23 = __builtin_amdgcn_perm(vr[3][wi], vr[2][wi], sel);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
+#pragma unroll
+        for (int c = 0; c < CT; ++c) st[c].o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[c], st[c].o[m], 0, 0, 0);
     }
 }
 
@@ -825,6 +914,9 @@ __device__ __forceinline__ void bf16_segment_ct(const AttnParams &p, int b, int 
     auto compute = [&](const MfmaTile<D> &T, int j) {
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
+        // one column tile after the other: the side-by-side form of the wide
+        // units (mfma_block_ct) measured no faster on this single-wave path
+        // (5 query tokens 121 vs 123 us)
 #pragma unroll
         for (int c = 0; c < CT; ++c) mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c]);
     };
@@ -1763,9 +1855,7 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
         wide_operands<D>(tl[cur], n16, G, T);
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-            mfma_block<D>(p, T, qB[c], tok0, tlo, thi, needs_mask(tok0, r), col[c], G, st[c], true);
+        mfma_block_ct<D, CT>(p, T, qB, tok0, tlo, thi, needs_mask(tok0, r), col, G, st);
         __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads have landed
         __syncthreads();
     }
@@ -1782,8 +1872,10 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
     __shared__ TileLds<D> tl[2];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
-    // every wave computes the same sums (identical LDS writes)
-    const int npos = balanced_prefix(p, pre, lane);
+    // every wave computes the same sums (identical LDS writes); the sequence
+    // search and what derives from it are kept in scalar registers, so the
+    // tile loop's bounds and masks are uniform branches
+    const int npos = uniform(balanced_prefix(p, pre, lane));
     if (wg == 0 && wave == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
@@ -1794,14 +1886,14 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
         int lo = 0, hi = p.batch - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((long)pre[mid] * p.units <= t)
+            if ((long)uniform(pre[mid]) * p.units <= t)
                 lo = mid;
             else
                 hi = mid - 1;
         }
         const int b = lo;
-        const int pb = pre[b];
-        const int span = pre[b + 1] - pb;
+        const int pb = uniform(pre[b]);
+        const int span = uniform(pre[b + 1]) - pb;
         const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
         const int unit = (int)((t - pair0) / span);
@@ -1815,7 +1907,7 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
         const int kvh = unit / cgroups, cu = (unit % cgroups) * p.ctw;  // first column tile of the unit
         const long seg_end = min(e, pair_t + nb);
         const int cnt = (int)(seg_end - t);
-        const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const SeqRange r = seq_range(uniform(ctx_of(p, b)), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         bool bad = r.bad;
         Column col[CT];
 #pragma unroll
