@@ -1700,6 +1700,30 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // (the K/V operands read from LDS serve both): 8B shape, 16 query tokens 218
 // vs 203 us, 32 tokens 384 vs 326 us.
 constexpr int kWideCT = 2;
+// K/V tile buffers in LDS per wide unit (two tiles in flight).
+constexpr int kWideBufs = 3;
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (N < 16; the LDS and export counters are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt field of s_waitcnt");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier of the wide tile loop. Each wave has already waited for
+// its own tile loads (wait_vm); here it waits for its LDS reads (so no wave
+// refills a buffer another is still reading) and meets the others. Unlike
+// __syncthreads() it carries no memory fence: a workgroup fence waits for
+// every outstanding global-to-LDS load, which would drain the second tile in
+// flight. The scheduling barriers keep the compiler from moving instructions
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // Issues this wave's share of one tile's loads straight into LDS
 // (global_load_lds, 16 bytes per lane): instruction q of the tile fills slots
@@ -1750,18 +1774,28 @@ __device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh
     // scalar register the test is a branch, not an exec mask)
     newpos = __builtin_amdgcn_readfirstlane(newpos);
     const bool fresh = newpos < kBlock && newpos + p.ctx_add > 0;
+    if (!fresh) {
+        // the common case: uniform base plus a 32-bit lane offset, the form
+        // with the base in scalar registers (no per-lane address arithmetic)
+#pragma unroll
+        for (int k = 0; k < WS::NQ; ++k) {
+            const int q = S.wave + k * W;
+            if (WS::NI % W != 0 && q >= WS::NI) break;  // uniform
+            gchar_t *base = q * 64 >= WS::TS ? vt : kt;  // uniform: K or V
+            __builtin_amdgcn_global_load_lds(base + S.off[k], (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
+        }
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < WS::NQ; ++k) {
         const int q = S.wave + k * W;
         if (WS::NI % W != 0 && q >= WS::NI) break;  // uniform
         const bool v = q * 64 >= WS::TS;  // uniform: K or V
         gchar_t *src = (v ? vt : kt) + S.off[k];
-        if (fresh) {
-            const int row = (int)(S.off[k] / (D * 2));
-            if (row >= newpos && row < newpos + p.ctx_add)
-                src = (gchar_t *)(v ? p.v_new : p.k_new) +
-                      (((size_t)b * p.ctx_add + (row - newpos)) * p.n_kv + kvh) * D * 2 + S.off[k] % (D * 2);
-        }
+        const int row = (int)(S.off[k] / (D * 2));
+        if (row >= newpos && row < newpos + p.ctx_add)
+            src = (gchar_t *)(v ? p.v_new : p.k_new) +
+                  (((size_t)b * p.ctx_add + (row - newpos)) * p.n_kv + kvh) * D * 2 + S.off[k] % (D * 2);
         __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
     }
 }
@@ -1796,7 +1830,7 @@ __device__ __forceinline__ void wide_operands(const TileLds<D> &t, int n16, int 
 template <int D, int W, int CT>
 __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh, const Column *col,
                                              const SeqRange &r, int j0, int j1, int tid, MfmaState<D> *st, bool &bad,
-                                             bool write_new, int *sids, TileLds<D> (&tl)[2], bool init) {
+                                             bool write_new, int *sids, TileLds<D> (&tl)[kWideBufs], bool init) {
     constexpr int KS = D / 32, MS = D / 16;
     const int lane = tid & 63, n16 = lane & 15, G = lane >> 4;
     bf16x8_t qB[CT][KS];
@@ -1843,21 +1877,45 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
     }
     auto newpos_of = [&](int j) { return L0 == INT_MAX ? kBlock : min(L0 - j * kBlock, kBlock); };
     const WideSlots<D, W> slots = wide_slots<D, W>(tid >> 6, lane);
+    // Three tile buffers, two tiles in flight: tile j is used while tiles j + 1
+    // and j + 2 load. Each wave issues kAhead loads per tile (when the waves
+    // share the slot groups evenly), so waiting until at most kAhead of its
+    // loads are outstanding means all but the newest tile have landed; with
+    // an uneven share every wait is a full one.
+    using WS = WideSlots<D, W>;
+    constexpr int kAhead = WS::NI % W == 0 ? WS::NQ : 0;
     wide_issue<D, W>(p, pid_of(j0), kvh, b, newpos_of(j0), slots, tl[0]);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the tile is in LDS
-    __syncthreads();
-    for (int j = j0; j < j1; ++j) {
-        const int cur = (j - j0) & 1;
-        // the next tile's loads fill the other buffer while this one is used
-        // (all waves passed the last barrier, so nobody reads it any more)
-        if (j + 1 < j1) wide_issue<D, W>(p, pid_of(j + 1), kvh, b, newpos_of(j + 1), slots, tl[cur ^ 1]);
+    if (j0 + 1 < j1) {
+        wide_issue<D, W>(p, pid_of(j0 + 1), kvh, b, newpos_of(j0 + 1), slots, tl[1]);
+        wait_vm<kAhead>();  // tile j0 is in LDS
+    } else {
+        wait_vm<0>();
+    }
+    lds_barrier();
+    // one step per buffer, unrolled, so that every LDS address is a
+    // constant offset from a per-lane base
+    auto step = [&](int j, const TileLds<D> &use, TileLds<D> &fill) {
+        // tile j + 2 goes into the buffer tile j - 1 used (every wave passed
+        // the barrier after using it)
+        if (j + 2 < j1) wide_issue<D, W>(p, pid_of(j + 2), kvh, b, newpos_of(j + 2), slots, fill);
         MfmaTile<D> T;
-        wide_operands<D>(tl[cur], n16, G, T);
+        wide_operands<D>(use, n16, G, T);
         const int tok0 = j * kBlock;
         const int tlo = max(r.lo - tok0, 0), thi = min(r.hi - tok0, kBlock);
         mfma_block_ct<D, CT>(p, T, qB, tok0, tlo, thi, needs_mask(tok0, r), col, G, st);
-        __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads have landed
-        __syncthreads();
+        if (j + 2 < j1)
+            wait_vm<kAhead>();  // tile j + 1 has landed
+        else
+            wait_vm<0>();
+        lds_barrier();
+    };
+    static_assert(kWideBufs == 3, "the loop below cycles through three buffers");
+    for (int j = j0; j < j1; j += 3) {
+        step(j, tl[0], tl[2]);
+        if (j + 1 >= j1) break;
+        step(j + 1, tl[1], tl[0]);
+        if (j + 2 >= j1) break;
+        step(j + 2, tl[2], tl[1]);
     }
 }
 
@@ -1869,7 +1927,7 @@ template <int D, int W, int CT>
 __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(AttnParams p) {
     extern __shared__ int pre[];  // [batch + 1] prefix sums, then the staged block ids
     int *sids = pre + p.batch + 1;
-    __shared__ TileLds<D> tl[2];
+    __shared__ TileLds<D> tl[kWideBufs];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
     // every wave computes the same sums (identical LDS writes); the sequence
