@@ -1781,8 +1781,8 @@ __device__ __forceinline__ void wide_issue(const AttnParams &p, int pid, int kvh
         for (int k = 0; k < WS::NQ; ++k) {
             const int q = S.wave + k * W;
             if (WS::NI % W != 0 && q >= WS::NI) break;  // uniform
-            gchar_t *base = q * 64 >= WS::TS ? vt : kt;  // uniform: K or V
-            __builtin_amdgcn_global_load_lds(base + S.off[k], (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
+            gchar_t *src = (q * 64 >= WS::TS ? vt : kt) + S.off[k];  // uniform base: K or V
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&t.slot[q * 64], 16, 0, kLoadStream);
         }
         return;
     }
