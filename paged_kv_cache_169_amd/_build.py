@@ -37,6 +37,23 @@ SOURCES = {
 }
 
 
+def sources_digest() -> str:
+    """sha256 over every source and header the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    names = sorted(SOURCES) + sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "include", "kvcache.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+DIGEST_FILE = LIB + ".sources"  # sources_digest() of the sources LIB was last built from
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC] + COMMON + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
@@ -56,6 +73,8 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(DIGEST_FILE, "w") as f:
+        f.write(sources_digest() + "\n")
     if verbose:
         print("built", LIB)
     return LIB

@@ -352,3 +352,17 @@ def test_noalloc_step_refuses_before_any_launch(kv):
     # a geometry the library refuses reports its own error
     assert f(h, p, p, p, p, 33, 1, 0.1, p, 65536, p, None, 4, 1 << 20, None, None) == kv.KV_ERR_INVALID_ARG
     assert kv.raw["kv_pool_destroy"](h) == 0
+
+
+def test_library_is_built_from_the_current_sources():
+    """The in-tree library was linked from the sources as they are now (a
+    build that failed leaves the previous library in place)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_kv_build", os.path.join(ROOT, "paged_kv_cache_169_amd", "_build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    if not os.path.exists(b.LIB):
+        pytest.skip("library not built")
+    assert os.path.exists(b.DIGEST_FILE), "library built without its source digest: rebuild"
+    with open(b.DIGEST_FILE) as f:
+        assert f.read().strip() == b.sources_digest(), "libkvcache.so is older than its sources: the last build failed or was not run"
