@@ -124,6 +124,58 @@ def test_random_multi_token(i):
     pool.close()
 
 
+def draw_multi_step(i):
+    r = random.Random(8000 + i)
+    batch = r.randint(1, 8)
+    k = r.randint(2, 12)
+    lens = [r.choice([0, 1, 14, 15, 16, 17, 31]) if r.random() < 0.3 else r.randint(0, 600) for _ in range(batch)]
+    n_kv = r.choice([1, 2, 4, 8])
+    g = r.choice([2, 3, 4, 8, 16])
+    if r.random() < 0.25:  # units of eight column tiles: 80 to 192 query columns per kv head
+        g, k = 16, r.randint(5, 12)
+    d = r.choice([64, 128])
+    schedule = r.choice([0, 0, 1])
+    split = r.choice([0, 1, 3]) if schedule == 1 else 0
+    window = r.choice([0, 0, 0, 7, 40])
+    return dict(lens=lens, k=k, n_kv=n_kv, n_h=n_kv * g, d=d, schedule=schedule, split=split, window=window)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_multi_token_decode_step(i):
+    """The decode step with k new tokens per sequence (append fused: the new
+    rows come from k_new / v_new inside the attention kernels, wide units
+    included) against the oracle's k appends and causal attention; the pool
+    image bit for bit."""
+    cfg = draw_multi_step(i)
+    print(f"random multi-token decode step {i}: {cfg}", flush=True)
+    lens, k = cfg["lens"], cfg["k"]
+    c = wl.make_case(11000 + i, len(lens), lens, cfg["n_h"], cfg["n_kv"], cfg["d"], "bf16", pool_slack=1.2,
+                     append=k, device=DEV)
+    pool = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    opts = kv.attn_opts(split_blocks=cfg["split"], window=cfg["window"], schedule=cfg["schedule"])
+    max_ctx = int(c.ctx_lens.max().item())
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(pool, c.batch, c.n_h, k, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kv_decode_step(pool, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=opts)
+    torch.cuda.synchronize()
+    K, V = wl.to_host_bits(c.K), wl.to_host_bits(c.V)
+    tab, sl = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
+    kn, vn = wl.to_host_bits(c.k_new), wl.to_host_bits(c.v_new)
+    for t in range(k):
+        orc.append(K, V, np.ascontiguousarray(kn[:, t]), np.ascontiguousarray(vn[:, t]), tab, sl + t)
+    assert np.array_equal(wl.to_host_bits(pool.K), K) and np.array_equal(wl.to_host_bits(pool.V), V), \
+        "pool after the step"
+    ref = orc.attention_multi(K, V, wl.to_host_bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale,
+                              window=cfg["window"])
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= TOL
+    pool.close()
+
+
 def draw_int4(i):
     r = random.Random(5000 + i)
     batch = r.randint(1, 10)
