@@ -70,24 +70,69 @@ __device__ __forceinline__ Q4Params q4_params(float mn, float mx) {
 // code = clamp(round((x - m) / s), 0, 15), rounding half away from zero, from
 // the stored (fp16) m and s; every code is 0 when s is 0.
 // The quotient is first taken through the hardware reciprocal: with a 1-ulp
-// reciprocal and a rounded product it lies within 2^-18 of the exact
-// (x - m) / s for quotients below 16, and f1 = quotient + 0.5 (rounded)
-// within 2^-17 of the exact value plus one half. When f1's fraction is more
+// reciprocal, d * r lies within 2^-19 of the exact (x - m) / s for quotients
+// below 16, and f1 = d * r + 0.5 (one fused multiply-add, one rounding at
+// most 2^-20) within 2^-17 of the exact value plus one half. When f1's fraction is more
 // than 2^-16 from an integer, floor(f1) is therefore the code itself; the
 // few quotients that close to a half-integer take the correctly rounded
 // division and the exact half-away rounding.
-__device__ __forceinline__ uint32_t q4_code(float x, const Q4Params &p) {
-    // s = 0: r = 0 makes every quotient 0 (NaN for a non-finite x), code 0
+//
+// q4_code_fast: floor(f1) before the clamp. worst keeps the largest
+// |fraction(f1) - 1/2| seen; a value is near (one of those few) when that
+// distance reaches 1/2 - 2^-16 (q4_near). (s = 0: r = 0 makes every
+// quotient 0, f1 = 0.5, distance 0; a non-finite x gives NaN, which fmaxf
+// ignores, and the clamp turns its code into 0.)
+constexpr float kQ4NearTie = 0.5f - 0x1p-16f;
+__device__ __forceinline__ float q4_code_fast(float x, const Q4Params &p, float &worst) {
     const float d = __fsub_rn(x, p.m);
-    const float f1 = __fadd_rn(__fmul_rn(d, p.r), 0.5f);
-    float c = floorf(f1);
-    const float fr = __fsub_rn(f1, c);
-    if (fr <= 0x1p-16f || fr >= 1.0f - 0x1p-16f) {  // near a tie (rare)
-        const float v = __fdiv_rn(d, p.s);
-        const float t = truncf(v);  // v - t is exact
-        c = t + (__fsub_rn(v, t) >= 0.5f ? 1.0f : 0.0f);
+    const float f1 = __fmaf_rn(d, p.r, 0.5f);
+    const float c = floorf(f1);
+    const float e = __fsub_rn(__fsub_rn(f1, c), 0.5f);  // both exact
+    worst = fmaxf(worst, fabsf(e));
+    return c;
+}
+__device__ __forceinline__ bool q4_near(float worst) { return worst >= kQ4NearTie; }
+// The exact rounding, for the values q4_code_fast marks near.
+__device__ __forceinline__ float q4_code_exact(float x, const Q4Params &p) {
+    const float v = __fdiv_rn(__fsub_rn(x, p.m), p.s);
+    const float t = truncf(v);  // v - t is exact
+    return t + (__fsub_rn(v, t) >= 0.5f ? 1.0f : 0.0f);
+}
+__device__ __forceinline__ uint32_t q4_clamp(float c) {
+    return (uint32_t)fminf(fmaxf(c, 0.0f), 15.0f);  // a NaN quotient gives 0
+}
+__device__ __forceinline__ uint32_t q4_code(float x, const Q4Params &p) {
+    float worst = 0.0f;
+    float c = q4_code_fast(x, p, worst);
+    if (q4_near(worst)) c = q4_code_exact(x, p);
+    return q4_clamp(c);
+}
+
+// The codes of N bf16 pairs w[i] (the low value coded with pa, the high one
+// with pb) as bytes code[i] = low code | high code << 4. The same codes as
+// q4_code, with the near-tie test of all 2N values behind one branch
+// instead of one branch per value.
+template <int N>
+__device__ __forceinline__ void q4_code_pairs(const uint32_t (&w)[N], const Q4Params &pa, const Q4Params &pb,
+                                              uint32_t (&code)[N]) {
+    // codes are packed as soon as they are formed (few live registers)
+    float worst = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float lo = q4_code_fast(bf16_lo(w[i]), pa, worst);
+        const float hi = q4_code_fast(bf16_hi(w[i]), pb, worst);
+        code[i] = q4_clamp(lo) | (q4_clamp(hi) << 4);
     }
-    return (uint32_t)fminf(fmaxf(c, 0.0f), 15.0f);  // clamp; a NaN quotient gives 0
+    if (q4_near(worst)) {  // rare: only the values near a tie take the exact division
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float w0 = 0.0f, w1 = 0.0f;
+            q4_code_fast(bf16_lo(w[i]), pa, w0);
+            q4_code_fast(bf16_hi(w[i]), pb, w1);
+            if (q4_near(w0)) code[i] = (code[i] & 0xf0u) | q4_clamp(q4_code_exact(bf16_lo(w[i]), pa));
+            if (q4_near(w1)) code[i] = (code[i] & 0x0fu) | (q4_clamp(q4_code_exact(bf16_hi(w[i]), pb)) << 4);
+        }
+    }
 }
 
 // Lane mapping of the two coders below (one wave64 per row or block): lane l

@@ -117,10 +117,9 @@ __global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
         }
         if (t >= r) continue;
         const Q4Params q = q4_params(mn, mx);
-        uint32_t packed = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            packed |= (q4_code(bf16_lo(x[k]), q) | (q4_code(bf16_hi(x[k]), q) << 4)) << (8 * k);
+        uint32_t code[4];
+        q4_code_pairs<4>(x, q, q, code);
+        const uint32_t packed = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
         const size_t row = tile * kBlock + t;
         reinterpret_cast<uint32_t *>(p.dst.vq + row * hd)[cc] = packed;
         if (cc == 0) {
@@ -142,9 +141,16 @@ __global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
         }
         const Q4Params q0 = q4_params(mn0, mx0), q1 = q4_params(mn1, mx1);
         if (act) {
+            // four rows at a time: one near-tie branch per 8 values, and few
+            // values live at once
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t)
-                kc[t * hd + lane] = (uint8_t)(q4_code(bf16_lo(w[t]), q0) | (q4_code(bf16_hi(w[t]), q1) << 4));
+            for (int t0 = 0; t0 < kBlock; t0 += 4) {
+                const uint32_t wg[4] = {w[t0], w[t0 + 1], w[t0 + 2], w[t0 + 3]};
+                uint32_t code[4];
+                q4_code_pairs<4>(wg, q0, q1, code);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) kc[(t0 + t) * hd + lane] = (uint8_t)code[t];
+            }
             reinterpret_cast<uint32_t *>(p.dst.ks + tile * D)[lane] = (uint32_t)q0.s16 | ((uint32_t)q1.s16 << 16);
             reinterpret_cast<uint32_t *>(p.dst.km + tile * D)[lane] = (uint32_t)q0.m16 | ((uint32_t)q1.m16 << 16);
         }
