@@ -72,6 +72,30 @@ __global__ __launch_bounds__(64) void append_int4_kernel(AppendParams p) {
 }
 
 // Bulk coding. Grid (max_blocks, n_kv, batch), one wave per (block, head, seq).
+// DPP move inside each 16-lane row (every source lane is in the row).
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+enum { kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140 };
+
+// Min and max over each aligned group of `lanes` lanes (8 or 16) of a row,
+// in registers: pairs, quads, then the half-row mirror (lane i with 7 - i)
+// joins the two quads of a half row and the row mirror (i with 15 - i) its
+// two halves. (fminf / fmaxf ignore NaN; the order does not matter.)
+__device__ __forceinline__ void row_group_min_max(float &mn, float &mx, int lanes) {
+    mn = fminf(mn, row_dpp<kQuadXor1>(mn));
+    mx = fmaxf(mx, row_dpp<kQuadXor1>(mx));
+    mn = fminf(mn, row_dpp<kQuadXor2>(mn));
+    mx = fmaxf(mx, row_dpp<kQuadXor2>(mx));
+    mn = fminf(mn, row_dpp<kRowHalfMirror>(mn));
+    mx = fmaxf(mx, row_dpp<kRowHalfMirror>(mx));
+    if (lanes == 16) {
+        mn = fminf(mn, row_dpp<kRowMirror>(mn));
+        mx = fmaxf(mx, row_dpp<kRowMirror>(mx));
+    }
+}
+
 __global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
     const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int D = p.head_dim, hd = D / 2;
@@ -111,10 +135,7 @@ __global__ __launch_bounds__(64) void quantize_int4_kernel(QuantParams p) {
             mn = fminf(mn, fminf(bf16_lo(x[k]), bf16_hi(x[k])));
             mx = fmaxf(mx, fmaxf(bf16_lo(x[k]), bf16_hi(x[k])));
         }
-        for (int o = lpt / 2; o >= 1; o >>= 1) {
-            mn = fminf(mn, __shfl_xor(mn, o));
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-        }
+        row_group_min_max(mn, mx, lpt);
         if (t >= r) continue;
         const Q4Params q = q4_params(mn, mx);
         uint32_t code[4];
