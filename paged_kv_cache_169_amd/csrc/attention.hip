@@ -1675,8 +1675,8 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
 // per wave, as in bf16_segment_ct): the waves load each (block, kv head) K/V
 // tile once, together, into LDS and each reads it back in the MFMA operand
 // layout. So a K/V tile leaves HBM once per CT W column tiles.
-// The LDS tiles are double-buffered: the next tile's global loads are in
-// flight while the current one is used, and one barrier per tile orders both.
+// Three LDS tile buffers: the next two tiles' global loads are in flight
+// while the current one is used, and one barrier per tile orders them.
 // ---------------------------------------------------------------------------
 
 // One K/V tile in LDS: 16 rows of D bf16 for K, then for V, in 16-byte
@@ -2709,10 +2709,10 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
             const dim3 bg(p.n_wg);
             if (!q4 && p.ctw == 2 && p.head_dim == 128) {
                 // two column tiles: two waves share each tile through LDS,
-                // one column tile each (double-buffered: the next tile's
-                // loads fly while this one is used; one wave with both
-                // column tiles has no room for that). 8B shape, 5 query
-                // tokens: 135.6 -> 124.6 us; 8: 146 -> 139 us.
+                // one column tile each (the next tiles' loads fly while this
+                // one is used; one wave with both column tiles has no
+                // register room for that). 8B shape, 5 query tokens: 135.6
+                // -> 124.6 us; 8: 146 -> 139 us.
                 hipExtLaunchKernelGGL((attn_mfma_wide_kernel<128, 2, 1>), bg, dim3(128), lds, s, e0, e1, 0, p);
             } else if (!q4 && p.ctw > 2) {  // wide units: ctw / kWideCT waves per workgroup
                 constexpr int C = kWideCT, W4 = 4 / C, W8 = 8 / C;
