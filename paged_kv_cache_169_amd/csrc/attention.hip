@@ -1054,19 +1054,19 @@ __device__ __forceinline__ void q4_fetch_flat(const Q4Flat &f, uint32_t tile, in
 }
 
 
-// 8 codes of one dword (channel 2k in the low nibble of byte k) as exact bf16.
-// Each code goes to a byte of its own, in channel order; a byte c < 16 read
-// as an OCP E4M3 value is exactly c * 2^-9 (a subnormal for c < 8, exponent
-// field 1 for 8 <= c < 16), so the hardware fp8 -> bf16 conversion with scale
-// 2^9 gives c itself, two codes per instruction.
+// 8 codes of one dword (channel 2k in the low nibble of byte k) as exact bf16,
+// in the order channels 0, 2, 4, 6, 1, 3, 5, 7 (even channels from the low
+// nibbles, odd ones from the high nibbles: no byte permutes). The score
+// product's B operand (q4_block) takes its channels in the same order.
+// A byte c < 16 read as an OCP E4M3 value is exactly c * 2^-9 (a subnormal
+// for c < 8, exponent field 1 for 8 <= c < 16), so the hardware fp8 -> bf16
+// conversion with scale 2^9 gives c itself, two codes per instruction.
 __device__ __forceinline__ bf16x8_t q4_codes_bf16(uint32_t w) {
     const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes of channels 0,2,4,6 / 1,3,5,7
-    const uint32_t c03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // bytes: c0 c1 c2 c3
-    const uint32_t c47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // bytes: c4 c5 c6 c7
-    const bf16x2_t d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c03, 512.0f, false);
-    const bf16x2_t d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c03, 512.0f, true);
-    const bf16x2_t d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c47, 512.0f, false);
-    const bf16x2_t d3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c47, 512.0f, true);
+    const bf16x2_t d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 512.0f, false);  // channels 0, 2
+    const bf16x2_t d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 512.0f, true);   // 4, 6
+    const bf16x2_t d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 512.0f, false);  // 1, 3
+    const bf16x2_t d3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 512.0f, true);   // 5, 7
     return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
                                                    __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)));
 }
@@ -1284,21 +1284,28 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
         const int c = 4 * pi + G;
         uint32_t hi[4], lo[4];
         if (full) {
-            float cp = 0.0f;
+            float cp = 0.0f, pr[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float q0 = Q.q[pi][2 * k], q1 = Q.q[pi][2 * k + 1];
                 // exact products (an fma with -0 added: one mixed-precision
                 // instruction per product, fp16 operand widened inside it)
-                const float p0 = fmaf(q0, f16_lo(sw[k]), -0.0f), p1 = fmaf(q1, f16_hi(sw[k]), -0.0f);
+                pr[2 * k] = fmaf(q0, f16_lo(sw[k]), -0.0f);
+                pr[2 * k + 1] = fmaf(q1, f16_hi(sw[k]), -0.0f);
                 cp = fmaf(q0, f16_lo(mw[k]), cp);
                 cp = fmaf(q1, f16_hi(mw[k]), cp);
+            }
+            // channel order of q4_codes_bf16: pairs (0, 2), (4, 6), (1, 3), (5, 7)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c0 = (k & 1) * 4 + (k >> 1);  // 0, 4, 1, 5
+                const float p0 = pr[c0], p1 = pr[c0 + 2];
                 hi[k] = cvt_pk_bf16(p0, p1);
                 lo[k] = cvt_pk_bf16(p0 - __uint_as_float(hi[k] << 16), p1 - __uint_as_float(hi[k] & 0xffff0000u));
             }
             L.b[1][c][n16] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             L.corr[c][n16] = cp;
-        } else {
+        } else {  // the tail row's bf16 K in natural channel order
 #pragma unroll
             for (int k = 0; k < 4; ++k) hi[k] = cvt_pk_bf16(Q.q[pi][2 * k], Q.q[pi][2 * k + 1]);  // exact
         }
