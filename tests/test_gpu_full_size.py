@@ -81,6 +81,36 @@ def test_decode_step_full_size_every_row(name):
     pool.close()
 
 
+@pytest.mark.parametrize("k", [8, 16])
+def test_multi_token_decode_step_full_size_every_row(k):
+    """The 8B-shaped layer with k new tokens per sequence as bench.py --q-len k
+    runs it: one kv_decode_step, the k appends fused into the attention kernels
+    (units of two column tiles at 8 tokens, wide units of four at 16). Every
+    output row against the oracle's k appends and causal attention; the pool
+    image bit for bit."""
+    c = wl.workload("llama3_8b", device=DEV, n_new=k)
+    print(f"full-size multi-token decode step: llama3_8b, batch {c.batch}, {k} new tokens", flush=True)
+    pool = kv.KVPool(c.num_blocks, c.n_kv, c.d, c.dtype, device=DEV)
+    pool.K.copy_(c.K)
+    pool.V.copy_(c.V)
+    max_ctx = int(c.ctx_lens.max().item())
+    opts = kv.attn_opts()
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(pool, c.batch, c.n_h, k, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kv_decode_step(pool, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=opts)
+    torch.cuda.synchronize()
+    K, V = bits(c.K), bits(c.V)
+    tab, sl = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy()
+    kn, vn = bits(c.k_new), bits(c.v_new)
+    for t in range(k):
+        orc.append(K, V, np.ascontiguousarray(kn[:, t]), np.ascontiguousarray(vn[:, t]), tab, sl + t)
+    assert np.array_equal(bits(pool.K), K) and np.array_equal(bits(pool.V), V), "pool image after the step"
+    ref = orc.attention_multi(K, V, bits(c.q), tab, c.ctx_lens.cpu().numpy(), c.scale)
+    check_rows(out.cpu().numpy().astype(np.float64), ref, f"llama3_8b, {k} new tokens")
+    pool.close()
+
+
 def test_int4_decode_step_full_size_every_row():
     """The INT4 workload: bf16 cache coded in bulk, then the decode step with
     the append fused (V coded per token, K into the tail or coded per channel
