@@ -145,6 +145,49 @@ def test_int4_decode_step_full_size_every_row():
     dst.close()
 
 
+def test_int4_multi_token_decode_step_full_size_every_row():
+    """The INT4 workload with 4 new tokens per sequence as bench.py
+    --workload kvquant_int4 --q-len 4 runs it (the appends coded by the append
+    kernel, then the 16-column INT4 attention): the INT4 image bit-exact
+    against the oracle's coding and four appends, every row against the
+    oracle's causal attention on the same dequantized values."""
+    k = 4
+    c = wl.workload("kvquant_int4", device=DEV, n_new=k)
+    print(f"full-size INT4 multi-token decode step: batch {c.batch}, {k} new tokens", flush=True)
+    src = kv.KVPool(c.num_blocks, c.n_kv, c.d, "bf16", device=DEV)
+    src.K.copy_(c.K)
+    src.V.copy_(c.V)
+    dst = kv.KVPool(c.num_blocks, c.n_kv, c.d, "int4", max_seqs=c.batch, device=DEV)
+    dst.blob.fill_(0x5A)
+    kv.kv_quantize_int4(dst, src, c.tables, c.seq_lens)
+    max_ctx = int(c.ctx_lens.max().item())
+    opts = kv.attn_opts()
+    nbytes = kv.paged_multi_token_attention_workspace_bytes(dst, c.batch, c.n_h, k, max_ctx, opts)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kv_decode_step(dst, c.k_new, c.v_new, c.q, out, c.tables, c.seq_lens, c.scale, max_ctx, ws, opts=opts)
+    torch.cuda.synchronize()
+    tab, lens, ctx = c.tables.cpu().numpy(), c.seq_lens.cpu().numpy(), c.ctx_lens.cpu().numpy()
+    img = orc.Q4Image(c.num_blocks, c.n_kv, c.d, c.batch)
+    for a in img.arrays():
+        a.view(np.uint8)[...] = 0x5A
+    orc.q4_quantize_pool(img, bits(c.K), bits(c.V), tab, lens)
+    kn, vn = bits(c.k_new), bits(c.v_new)
+    for t in range(k):
+        orc.q4_append(img, np.ascontiguousarray(kn[:, t]), np.ascontiguousarray(vn[:, t]), tab, lens + t)
+    for name, t, a in [("K codes", dst.KQ, img.kq), ("K scale", dst.KS, img.ks), ("K min", dst.KM, img.km),
+                       ("V codes", dst.VQ, img.vq), ("V scale", dst.VS, img.vs), ("V min", dst.VM, img.vm),
+                       ("K tail", dst.KTAIL, img.kt)]:
+        h = t.detach().cpu().contiguous()
+        h = h.view(torch.int16).numpy().view(np.uint16) if h.element_size() == 2 else h.numpy()
+        assert np.array_equal(h, a), f"{name} after the step"
+    Kd, Vd = orc.q4_dequant(img, tab, ctx)
+    ref = orc.attention_multi(Kd, Vd, bits(c.q), tab, ctx, c.scale)
+    check_rows(out.cpu().numpy().astype(np.float64), ref, "kvquant_int4, 4 new tokens")
+    src.close()
+    dst.close()
+
+
 def test_long_shared_full_size_every_row():
     """The long shared-prefix workload as bench.py runs it: the reused chunk's
     keys re-rotated in place, then the shared-prefix call with all 8 sequences
