@@ -127,8 +127,10 @@ def test_argument_errors_before_launch(kv):
     assert M(h, FAKE, FAKE, 4, 0, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, None, None) == kv.KV_ERR_INVALID_ARG
     # max_ctx beyond the table
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 65, None, 0, ctypes.byref(o), None) == kv.KV_ERR_INVALID_ARG
-    # non-finite scale
-    assert P(h, FAKE, FAKE, 4, float("nan"), FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) == kv.KV_ERR_INVALID_ARG
+    # non-finite scale (any finite one, negative and zero included, is valid)
+    for bad_scale in (float("nan"), float("inf"), float("-inf")):
+        assert P(h, FAKE, FAKE, 4, bad_scale, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o), None) \
+            == kv.KV_ERR_INVALID_ARG
     # workspace missing when splits are needed
     o1 = kv.attn_opts(split_blocks=1)
     assert P(h, FAKE, FAKE, 4, 0.125, FAKE, 4, FAKE, None, 2, 50, None, 0, ctypes.byref(o1), None) == kv.KV_ERR_WORKSPACE
