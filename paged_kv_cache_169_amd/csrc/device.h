@@ -121,7 +121,11 @@ __device__ __forceinline__ void q4_code_pairs(const uint32_t (&w)[N], const Q4Pa
     for (int i = 0; i < N; ++i) {
         const float lo = q4_code_fast(bf16_lo(w[i]), pa, worst);
         const float hi = q4_code_fast(bf16_hi(w[i]), pb, worst);
-        code[i] = q4_clamp(lo) | (q4_clamp(hi) << 4);
+        // the clamp as one median-of-three (a NaN operand gives the minimum
+        // of the other two, 0, like q4_clamp), then both nibbles at once:
+        // lo + 16 hi is an exact integer in [0, 255]
+        const float cl = __builtin_amdgcn_fmed3f(lo, 0.0f, 15.0f), ch = __builtin_amdgcn_fmed3f(hi, 0.0f, 15.0f);
+        code[i] = (uint32_t)__fmaf_rn(ch, 16.0f, cl);
     }
     if (q4_near(worst)) {  // rare: only the values near a tie take the exact division
 #pragma unroll
