@@ -164,15 +164,28 @@ template <int CTRL, int BANK>
 __device__ __forceinline__ float dpp_f(float old, float src) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xf, BANK, false));
 }
+// x combined with x as moved by a DPP control that every lane of every row
+// takes part in, in one instruction (the DPP move as a source modifier: no
+// copy of x, no separate move). The s_nop gives the two wait states a DPP
+// read needs after a vector write of its source.
+#define KVC_DPP_OP(name, op, ctrl)                                                              \
+    __device__ __forceinline__ float name(float x) {                                           \
+        float r;                                                                               \
+        asm("s_nop 1\n\t" op "_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x)); \
+        return r;                                                                              \
+    }
+KVC_DPP_OP(dpp_max_ror4, "v_max_f32", "row_ror:4")
+KVC_DPP_OP(dpp_max_ror8, "v_max_f32", "row_ror:8")
+KVC_DPP_OP(dpp_add_ror4, "v_add_f32", "row_ror:4")
+KVC_DPP_OP(dpp_add_ror8, "v_add_f32", "row_ror:8")
+KVC_DPP_OP(dpp_add_xor1, "v_add_f32", "quad_perm:[1,0,3,2]")
+KVC_DPP_OP(dpp_add_xor2, "v_add_f32", "quad_perm:[2,3,0,1]")
+#undef KVC_DPP_OP
 // Max / sum over lanes l, l^4, l^8, l^12 (the four banks of a row).
-__device__ __forceinline__ float bank_max(float x) {
-    x = max_raw(x, dpp_f<kDppRowRor + 4, 0xf>(x, x));
-    return max_raw(x, dpp_f<kDppRowRor + 8, 0xf>(x, x));
-}
-__device__ __forceinline__ float bank_sum(float x) {
-    x += dpp_f<kDppRowRor + 4, 0xf>(x, x);
-    return x + dpp_f<kDppRowRor + 8, 0xf>(x, x);
-}
+__device__ __forceinline__ float bank_max(float x) { return dpp_max_ror8(dpp_max_ror4(x)); }
+__device__ __forceinline__ float bank_sum(float x) { return dpp_add_ror8(dpp_add_ror4(x)); }
+// Sum over the 16 lanes of a row, in every lane of it.
+__device__ __forceinline__ float row_sum(float x) { return bank_sum(dpp_add_xor2(dpp_add_xor1(x))); }
 
 struct SplitWork {
     SeqRange r;
@@ -748,45 +761,70 @@ __device__ __forceinline__ void mfma_block_ct(const AttnParams &p, const MfmaTil
 // them), staged in LDS before a piece's tile loop. A segment longer than that
 // runs as several pieces that carry the softmax state (run_pieces), so a
 // workgroup's dynamic LDS holds at most kSidsWindow ids however long its
-// segments are. Ids are not range-checked here.
+// segments are.
 constexpr int kSidsWindow = 256;
+constexpr int kSidsPerLane = kSidsWindow / 64;
 struct BlockIds {
     int *sids;
     const int32_t *row;  // the sequence's table row
     int j0;
+    int last;  // the table's entry for block j1 - 1, as read (unchecked; uniform)
     __device__ __forceinline__ int id(int j) const { return __builtin_amdgcn_readfirstlane(sids[j - j0]); }
 };
-__device__ __forceinline__ BlockIds stage_block_ids(const AttnParams &p, int b, int j0, int j1, int lane,
-                                                    int *sids) {
+
+// For the one-wave workgroups of the decode kernels: the LDS executes a
+// wave's accesses in issue order, so the staging needs no barrier (a
+// workgroup barrier's fence would also wait for the wave's earlier global
+// stores and loads, e.g. the previous segment's results). All of the piece's
+// table loads go out before any is used: one memory round trip, however
+// many ids. CHECK: an id outside [0, num_blocks) is staged as 0 and sets bad
+// (the ids are then checked once here rather than per tile); otherwise ids
+// are staged as read.
+template <bool CHECK>
+__device__ __forceinline__ BlockIds stage_ids(const AttnParams &p, int b, int j0, int j1, int lane, int *sids,
+                                              bool &bad) {
     BlockIds ids;
     ids.sids = sids;
     ids.row = p.tables + (size_t)b * p.max_blocks;
     ids.j0 = j0;
-    __syncthreads();  // earlier reads of sids are done
-    for (int i = lane; i < j1 - j0; i += 64) sids[i] = ids.row[j0 + i];
-    __syncthreads();
+    const int n = j1 - j0;  // 1 .. kSidsWindow
+    int v[kSidsPerLane];
+#pragma unroll
+    for (int k = 0; k < kSidsPerLane; ++k) {
+        const int i = lane + 64 * k;
+        v[k] = i < n ? ids.row[j0 + i] : 0;
+    }
+    ids.last = 0;
+#pragma unroll
+    for (int k = 0; k < kSidsPerLane; ++k)
+        if (k == (n - 1) >> 6) ids.last = __builtin_amdgcn_readlane(v[k], (n - 1) & 63);
+    wave_lds_sync();  // this wave's earlier reads of sids come first
+    bool wrong = false;
+#pragma unroll
+    for (int k = 0; k < kSidsPerLane; ++k) {
+        const int i = lane + 64 * k;
+        if (i < n) {
+            int id = v[k];
+            if constexpr (CHECK) {
+                const bool ok = id >= 0 && id < p.num_blocks;
+                wrong |= !ok;
+                id = ok ? id : 0;
+            }
+            sids[i] = id;
+        }
+    }
+    if (CHECK && __any(wrong)) bad = true;
+    wave_lds_sync();
     return ids;
 }
-
-// The same, checking the ids once here rather than per tile (one-wave
-// workgroups): an id outside [0, num_blocks) is staged as 0 and sets bad.
+__device__ __forceinline__ BlockIds stage_block_ids(const AttnParams &p, int b, int j0, int j1, int lane,
+                                                    int *sids) {
+    bool unused = false;
+    return stage_ids<false>(p, b, j0, j1, lane, sids, unused);
+}
 __device__ __forceinline__ BlockIds stage_checked_block_ids(const AttnParams &p, int b, int j0, int j1, int lane,
                                                             int *sids, bool &bad) {
-    BlockIds ids;
-    ids.sids = sids;
-    ids.row = p.tables + (size_t)b * p.max_blocks;
-    ids.j0 = j0;
-    __syncthreads();  // earlier reads of sids are done
-    bool wrong = false;
-    for (int i = lane; i < j1 - j0; i += 64) {
-        const int id = ids.row[j0 + i];
-        const bool ok = id >= 0 && id < p.num_blocks;
-        wrong |= !ok;
-        sids[i] = ok ? id : 0;
-    }
-    if (__any(wrong)) bad = true;
-    __syncthreads();
-    return ids;
+    return stage_ids<true>(p, b, j0, j1, lane, sids, bad);
 }
 
 // Runs seg(c0, c1, init) over [j0, j1) in pieces of at most kSidsWindow
@@ -1081,7 +1119,7 @@ __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f((uint
 // each, fall in distinct banks.
 struct Q4Lds {
     uint4 b[2][16][17];   // [hi / lo][column][channel chunk]
-    float corr[16][20];   // [column][channel chunk], padded
+    float corr[16];       // [column]: the column's sum over channels of q times K min
 };
 
 // Query of the columns this lane computes products for: column 4 pi + G,
@@ -1091,6 +1129,7 @@ template <int NP>
 struct Q4Query {
     float q[NP][8];
     int npass;
+    float nz;  // -0.0, hidden from the compiler: fma(q, s, nz) would otherwise become a plain multiply
 };
 
 // Masking of an INT4 tile some of whose slots are outside the attended
@@ -1290,8 +1329,8 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
                 const float q0 = Q.q[pi][2 * k], q1 = Q.q[pi][2 * k + 1];
                 // exact products (an fma with -0 added: one mixed-precision
                 // instruction per product, fp16 operand widened inside it)
-                pr[2 * k] = fmaf(q0, f16_lo(sw[k]), -0.0f);
-                pr[2 * k + 1] = fmaf(q1, f16_hi(sw[k]), -0.0f);
+                pr[2 * k] = fmaf(q0, f16_lo(sw[k]), Q.nz);
+                pr[2 * k + 1] = fmaf(q1, f16_hi(sw[k]), Q.nz);
                 cp = fmaf(q0, f16_lo(mw[k]), cp);
                 cp = fmaf(q1, f16_hi(mw[k]), cp);
             }
@@ -1304,7 +1343,8 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
                 lo[k] = cvt_pk_bf16(p0 - __uint_as_float(hi[k] << 16), p1 - __uint_as_float(hi[k] & 0xffff0000u));
             }
             L.b[1][c][n16] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            L.corr[c][n16] = cp;
+            cp = row_sum(cp);  // row G of the wave holds column c's 16 channel chunks
+            if (n16 == 0) L.corr[c] = cp;
         } else {  // the tail row's bf16 K in natural channel order
 #pragma unroll
             for (int k = 0; k < 4; ++k) hi[k] = cvt_pk_bf16(Q.q[pi][2 * k], Q.q[pi][2 * k + 1]);  // exact
@@ -1315,8 +1355,7 @@ __device__ __forceinline__ void q4_block(const AttnParams &p, const Q4Tile &T, c
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     float corr = 0.0f;
     if (full) {
-        const float4 cq = *reinterpret_cast<const float4 *>(&L.corr[ccol][4 * G]);
-        corr = col_sum((cq.x + cq.y) + (cq.z + cq.w));
+        corr = L.corr[ccol];
         const uint32_t kcw[4] = {T.kc.x, T.kc.y, T.kc.z, T.kc.w};
         f32x4_t sl = {0.0f, 0.0f, 0.0f, 0.0f};  // hi and lo parts in two chains: half the dependent latency
 #pragma unroll
@@ -1391,28 +1430,31 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
                                            int *sids, bool init, Pace pace = Pace{0, INT_MAX, INT_MAX, INT_MAX}) {
     static_assert(D == 128, "INT4 MFMA path is built for head_dim 128");
     const int n16 = lane & 15, G = lane >> 4;
-    int slot = uniform(p.seq_slots ? p.seq_slots[b] : b);
-    const bool slot_bad = slot < 0 || slot >= p.max_seqs;
-    if (slot_bad) {
-        bad = true;
-        slot = 0;
-    }
+    // The segment's first global loads (the sequence's tail slot, the query,
+    // the block ids) go out together and are waited on once, in the id
+    // staging: values loaded here are used only after it.
+    const int slot_v = p.seq_slots ? p.seq_slots[b] : b;  // the same value in every lane
+    auto take_slot = [&]() {
+        int s = uniform(slot_v);
+        if (s < 0 || s >= p.max_seqs) {
+            bad = true;
+            s = -1;
+        }
+        return s;
+    };
     // query of the product layout: column 4 pi + G of this column tile,
     // channels 8 n16 .. 8 n16 + 7
     Q4Query<NP> Q;
     Q.npass = min((min(p.ncols - ct * 16, 16) + 3) / 4, NP);
+    Q.nz = -0.0f;
+    asm("" : "+v"(Q.nz));
+    uint4 qraw[NP];
 #pragma unroll
     for (int pi = 0; pi < NP; ++pi) {
         const Column cq = column_of(p, b, kvh, ct, 4 * pi + G, r);
-        uint4 v = make_uint4(0, 0, 0, 0);
+        qraw[pi] = make_uint4(0, 0, 0, 0);
         if (pi < Q.npass && cq.valid)
-            v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + cq.row * 128 + 8 * n16);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            Q.q[pi][2 * k] = bf16_lo(w[k]);
-            Q.q[pi][2 * k + 1] = bf16_hi(w[k]);
-        }
+            qraw[pi] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + cq.row * 128 + 8 * n16);
     }
     if (init) {
 #pragma unroll
@@ -1421,18 +1463,33 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
         st.l = 0.0f;
         st.bv = 0.0f;
     }
-    if (j0 >= j1) return;
+    if (j0 >= j1) {
+        take_slot();
+        return;
+    }
     __shared__ Q4Lds L;
-    __syncthreads();  // the previous segment's reads of L are done
+    wave_lds_sync();  // this wave's reads of L in the previous segment come first (one-wave workgroup)
     // columns past the passes are never written: zero B rows (padded columns)
     for (int i = lane; i < (16 - 4 * Q.npass) * 17; i += 64) {
         const int c = 4 * Q.npass + i / 17, k = i % 17;
         L.b[0][c][k] = make_uint4(0, 0, 0, 0);
         L.b[1][c][k] = make_uint4(0, 0, 0, 0);
-        if (k < 16) L.corr[c][k] = 0.0f;
+        if (k == 0) L.corr[c] = 0.0f;
     }
     // every staged id is a valid block (bad ones were replaced by 0)
-    const BlockIds ids = stage_checked_block_ids(p, b, j0, j1, lane, sids, bad);  // its barriers cover the zeroing
+    const BlockIds ids = stage_checked_block_ids(p, b, j0, j1, lane, sids, bad);
+    int slot = take_slot();
+    const bool slot_bad = slot < 0;
+    slot = slot_bad ? 0 : slot;
+#pragma unroll
+    for (int pi = 0; pi < NP; ++pi) {
+        const uint32_t w[4] = {qraw[pi].x, qraw[pi].y, qraw[pi].z, qraw[pi].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            Q.q[pi][2 * k] = bf16_lo(w[k]);
+            Q.q[pi][2 * k + 1] = bf16_hi(w[k]);
+        }
+    }
     auto is_full = [&](int j) { return (j + 1) * kBlock <= r.n; };
     gu16_t *tail_row = global_u16(p.pool.ktail) + (((size_t)slot * p.n_kv + kvh) * kBlock + n16) * 128 + 32 * G;
     // blocks [jA, jB) lie inside every column's range (needs_mask is false
@@ -1472,7 +1529,7 @@ __device__ __forceinline__ void q4_segment(const AttnParams &p, int b, int kvh, 
     Q4Tile A, B;
     if (!append || j0 < j1 - 1) fetch(j0, A);
     if (append) {
-        const int pid = uniform(ids.row[j1 - 1]);  // the table's entry (a bad one is staged as 0)
+        const int pid = ids.last;  // the table's entry as read (a bad one is staged as 0)
         if (pid >= 0 && pid < p.num_blocks) q4_append_token(p, b, kvh, slot, pid, (r.n - 1) % kBlock, lane);
         appended = true;
         if (j0 == j1 - 1) fetch(j0, A);
@@ -1558,16 +1615,43 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
 // slot 1 (the pair goes on past the range: only its last piece can);
 // attn_merge_balanced_rows_kernel (or _unit_kernel) combines them.
 // Workgroup 0 also stores the prefix sums for the merge.
-__device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, int lane) {
+// Dynamic LDS of the balanced kernels: the prefix sums [batch + 1]; for
+// batches of at most kCtxInLds sequences their attended lengths [batch]
+// (read once by the prefix pass: a segment then takes its sequence's length
+// from LDS, not from a global load that would wait behind the previous
+// segment's result stores); then the staged block ids.
+constexpr int kCtxInLds = 512;
+__host__ __device__ inline int balanced_lds_ints(int batch, int max_ids) {
+    return batch + 1 + (batch <= kCtxInLds ? batch : 0) + (max_ids < kSidsWindow ? max_ids : kSidsWindow);
+}
+struct BalancedLds {
+    int *pre, *ctx, *sids;  // ctx: null for larger batches
+};
+__device__ __forceinline__ BalancedLds balanced_lds(const AttnParams &p, int *base) {
+    BalancedLds l;
+    l.pre = base;
+    l.ctx = p.batch <= kCtxInLds ? base + p.batch + 1 : nullptr;
+    l.sids = base + p.batch + 1 + (p.batch <= kCtxInLds ? p.batch : 0);
+    return l;
+}
+// Attended length of sequence b in a balanced kernel.
+__device__ __forceinline__ int balanced_ctx(const AttnParams &p, const BalancedLds &l, int b) {
+    return l.ctx ? l.ctx[b] : ctx_of(p, b);
+}
+
+__device__ __forceinline__ int balanced_prefix(const AttnParams &p, const BalancedLds &l, int lane) {
     // pre[b] = positions of sequences < b per unit (attended blocks plus
     // seg_cost for a sequence with any), in LDS; returns pre[batch]
+    int *pre = l.pre;
     int carry = 0;
     if (lane == 0) pre[0] = 0;
     for (int base = 0; base < p.batch; base += 64) {
         const int b = base + lane;
         int nb = 0;
         if (b < p.batch) {
-            const SeqRange r = seq_range(ctx_of(p, b), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+            const int ctx = ctx_of(p, b);
+            if (l.ctx) l.ctx[b] = ctx;
+            const SeqRange r = seq_range(ctx, p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
             nb = r.nblk > 0 ? r.nblk + p.seg_cost : 0;
         }
         // inclusive wave scan
@@ -1585,15 +1669,16 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, int *pre, in
 
 template <int D, int Q4, int CT, bool KEEP = false, bool FLAT = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
-    extern __shared__ int pre[];  // [batch + 1] block prefix sums, then the staged block ids
-    int *sids = pre + p.batch + 1;
+    extern __shared__ int lds_ints[];  // BalancedLds
+    const BalancedLds bl = balanced_lds(p, lds_ints);
+    int *pre = bl.pre, *sids = bl.sids;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
     // The INT4 path is bound by vector instructions: there the sequence
     // search and everything derived from it are moved to scalar registers.
     // The bf16 path keeps them in vector registers (measured faster: the
     // scalar form runs out of scalar registers there).
-    const int npos = Q4 ? uniform(balanced_prefix(p, pre, lane)) : balanced_prefix(p, pre, lane);
+    const int npos = Q4 ? uniform(balanced_prefix(p, bl, lane)) : balanced_prefix(p, bl, lane);
     if (wg == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
@@ -1618,7 +1703,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
         }
         const int b = lo;
         const int pb = pre_s(b);
-        const int ctx = ctx_of(p, b);
+        const int ctx = balanced_ctx(p, bl, b);
         const int span = pre_s(b + 1) - pb;  // nb + seg_cost positions per unit
         const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
@@ -1932,15 +2017,16 @@ __device__ __forceinline__ void wide_segment(const AttnParams &p, int b, int kvh
 // 16 c + n16 for the unit's column tile c).
 template <int D, int W, int CT>
 __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(AttnParams p) {
-    extern __shared__ int pre[];  // [batch + 1] prefix sums, then the staged block ids
-    int *sids = pre + p.batch + 1;
+    extern __shared__ int lds_ints[];  // BalancedLds
+    const BalancedLds bl = balanced_lds(p, lds_ints);
+    int *pre = bl.pre, *sids = bl.sids;
     __shared__ TileLds<D> tl[kWideBufs];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n16 = lane & 15, G = lane >> 4;
     const int wg = blockIdx.x;
     // every wave computes the same sums (identical LDS writes); the sequence
     // search and what derives from it are kept in scalar registers, so the
     // tile loop's bounds and masks are uniform branches
-    const int npos = uniform(balanced_prefix(p, pre, lane));
+    const int npos = uniform(balanced_prefix(p, bl, lane));
     if (wg == 0 && wave == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
@@ -1972,7 +2058,8 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
         const int kvh = unit / cgroups, cu = (unit % cgroups) * p.ctw;  // first column tile of the unit
         const long seg_end = min(e, pair_t + nb);
         const int cnt = (int)(seg_end - t);
-        const SeqRange r = seq_range(uniform(ctx_of(p, b)), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
+        const SeqRange r =
+            seq_range(uniform(balanced_ctx(p, bl, b)), p.max_blocks, p.window, p.split_blocks, p.max_splits, p.q_len);
         bool bad = r.bad;
         Column col[CT];
 #pragma unroll
@@ -2712,7 +2799,7 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
         const bool keep = p.units > p.n_kv;  // several units per kv head: cached loads
         const bool flat = p.pool.q4_span > 0;  // INT4 arrays within 4 GiB: one descriptor
         if (p.schedule == KV_SCHED_BALANCED) {
-            const uint32_t lds = (uint32_t)((p.batch + 1 + min(p.split_blocks, kSidsWindow)) * sizeof(int));
+            const uint32_t lds = (uint32_t)(balanced_lds_ints(p.batch, p.split_blocks) * sizeof(int));
             const dim3 bg(p.n_wg);
             if (!q4 && p.ctw == 2 && p.head_dim == 128) {
                 // two column tiles: two waves share each tile through LDS,
@@ -2787,7 +2874,7 @@ int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
     // compute units x resident workgroups per compute unit; 256 x 2 when the
     // runtime cannot tell (no device: only the size of a workspace is asked)
     int dev = 0, cus = 0, per_cu = 0;
-    const size_t lds = (size_t)(batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
+    const size_t lds = (size_t)balanced_lds_ints(batch, max_blocks) * sizeof(int);
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 256 * 2;
@@ -2810,7 +2897,7 @@ int wide_grid(int head_dim, int ctw, int batch, int max_blocks) {
     constexpr int C = kWideCT, W4 = 4 / C, W8 = 8 / C;
     const int waves = ctw == 2 ? 2 : ctw / C;  // two column tiles: two waves of one
     int dev = 0, cus = 0, per_cu = 0;
-    const size_t lds = (size_t)(batch + 1 + std::min(max_blocks, kSidsWindow)) * sizeof(int);
+    const size_t lds = (size_t)balanced_lds_ints(batch, max_blocks) * sizeof(int);
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 1024 / ctw;
