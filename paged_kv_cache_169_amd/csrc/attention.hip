@@ -1667,6 +1667,37 @@ __device__ __forceinline__ int balanced_prefix(const AttnParams &p, const Balanc
     return carry;
 }
 
+// Largest i < n with mult * v[i] <= t, for v in LDS, non-decreasing, with
+// mult * v[0] <= t. The whole wave searches: each round tests 64 evenly
+// spaced candidates at once (one LDS read per lane and a ballot) and narrows
+// the range 64-fold, so up to 64 entries take one round and up to 4096 two,
+// instead of a chain of log2(n) dependent LDS reads (about 1.3 us at the start
+// of the INT4 8B-shaped kernel). The result is uniform.
+__device__ __forceinline__ int last_le(const int *v, int n, long mult, long t, int lane) {
+    int lo = 0;
+    for (;;) {
+        const int step = n <= 64 ? 1 : (n + 63) >> 6;
+        const bool in = lane * step < n;
+        const int x = in ? v[lo + lane * step] : 0;
+        const unsigned long long le = __ballot(in && (long)x * mult <= t);
+        const int k = __popcll(le) - 1;  // candidates 0 .. k pass (lane 0 always)
+        lo += k * step;
+        if (step == 1) return uniform(lo);
+        n = min(step, n - k * step);
+    }
+}
+// The sequence holding share position t of a balanced kernel.
+__device__ __forceinline__ int sequence_at(const int *pre, int batch, int units, long t, int lane) {
+    return last_le(pre, batch, units, t, lane);
+}
+
+// Work unit of share position t inside the pair run starting at pair0 (span
+// positions per unit): in 32 bits when the sequence's positions fit them.
+__device__ __forceinline__ int unit_at(long t, long pair0, int span, int units) {
+    if ((long)units * span <= INT_MAX) return (int)(t - pair0) / span;
+    return (int)((t - pair0) / span);
+}
+
 template <int D, int Q4, int CT, bool KEEP = false, bool FLAT = false>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int lds_ints[];  // BalancedLds
@@ -1691,23 +1722,14 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(At
     Pace pace = pace_for(Q4 && p.pace ? e - s : 0);
     pace_set(pace, 0);
     for (long t = s; t < e;) {
-        // sequence holding position t: largest b with units * pre[b] <= t
         auto pre_s = [&](int i) { return Q4 ? uniform(pre[i]) : pre[i]; };
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((long)pre_s(mid) * p.units <= t)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int b = lo;
+        const int b = sequence_at(pre, p.batch, p.units, t, lane);
         const int pb = pre_s(b);
         const int ctx = balanced_ctx(p, bl, b);
         const int span = pre_s(b + 1) - pb;  // nb + seg_cost positions per unit
         const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
-        const int unit = (int)((t - pair0) / span);
+        const int unit = unit_at(t, pair0, span, p.units);
         const long pair_t = pair0 + (long)unit * span;  // position of the pair's first tile
         const int jr = (int)(t - pair_t);
         if (jr >= nb) {  // in the pair's start cost: go on at the next pair
@@ -2034,20 +2056,12 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
     const long s = (long)wg * per;
     const long e = min(total, s + per);
     for (long t = s; t < e;) {
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((long)uniform(pre[mid]) * p.units <= t)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int b = lo;
+        const int b = sequence_at(pre, p.batch, p.units, t, lane);
         const int pb = uniform(pre[b]);
         const int span = uniform(pre[b + 1]) - pb;
         const int nb = span - p.seg_cost;
         const long pair0 = (long)pb * p.units;
-        const int unit = (int)((t - pair0) / span);
+        const int unit = unit_at(t, pair0, span, p.units);
         const long pair_t = pair0 + (long)unit * span;
         const int jr = (int)(t - pair_t);
         if (jr >= nb) {
@@ -2364,19 +2378,6 @@ __device__ __forceinline__ void store_piece(const AttnParams &p, size_t row, int
     }
 }
 
-// Largest i in [0, n) with v[i] <= t (v ascending, v[0] <= t).
-__device__ __forceinline__ int last_le(const int *v, int n, long t) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((long)v[mid] <= t)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
 template <int D>
 __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_kernel(AttnParams p, PrefixArgs g) {
     extern __shared__ int lds[];  // plan [ng + 1][2] + [batch + 1], then the staged block ids
@@ -2402,7 +2403,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
         long seg_end;
         if (t < tp) {
             // prefix segment: group gi, unit (kvh, ct) over its P shared blocks
-            const int gi = last_le(pl.gtile, pl.ng + 1, t);
+            const int gi = last_le(pl.gtile, pl.ng + 1, 1, t, lane);
             const int P = g.blocks[gi], first = g.start[gi], members = g.start[gi + 1] - first;
             const int cti = group_ctiles(p, g, gi);
             const long a0 = pl.gtile[gi];
@@ -2438,7 +2439,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
         } else {
             // suffix segment: sequence b, unit (kvh, ct) over its own blocks
             const long u = t - tp;
-            const int b = last_le(pl.stile, p.batch + 1, u / p.units);
+            const int b = last_le(pl.stile, p.batch + 1, p.units, u, lane);
             const int nb = pl.stile[b + 1] - pl.stile[b];
             const long a0 = (long)pl.stile[b] * p.units;
             const int unit = (int)((u - a0) / nb), jr = (int)(u - a0 - (long)unit * nb);
