@@ -196,7 +196,8 @@ kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_l
         g->split_blocks = nblk;
         g->max_splits = 1;
         const bool wide = g->ctw > 2 || (g->ctw == 2 && dtype == KV_BF16 && D == 128);  // as launch_attention
-        g->n_wg = wide ? wide_grid((int)D, g->ctw, batch, nblk) : balanced_grid(dtype, (int)D, batch, nblk);
+        const bool q4_one_score = dtype == KV_INT4 && g->ncols <= 4;  // as launch_attention
+        g->n_wg = wide ? wide_grid((int)D, g->ctw, batch, nblk) : balanced_grid(dtype, (int)D, batch, nblk, q4_one_score);
         const size_t rows = (size_t)g->n_wg * 2 * g->slot_cols;
         g->off_ml = align_up(rows * D * sizeof(float));
         g->off_prefix = g->off_ml + align_up(rows * 2 * sizeof(float));

@@ -1698,8 +1698,16 @@ __device__ __forceinline__ int unit_at(long t, long pair0, int span, int units) 
     return (int)((t - pair0) / span);
 }
 
+// The INT4 kernel with one score per lane (at most four query columns) runs
+// three waves per SIMD (168 registers; the few spilled ones are stored and
+// reloaded once per segment, outside the tile loop): its waves are bound by
+// the dependency chains inside a tile, which the third wave covers (8B shape
+// 55 -> 52 us, the merge of the larger grid 4.9 -> 5.8 us). The others stay at two.
+#define KV_BALANCED_WAVES(Q4) __attribute__((amdgpu_waves_per_eu((Q4) == 1 ? 3 : 2)))
+constexpr int kBalancedWavesQ4One = 3;
+
 template <int D, int Q4, int CT, bool KEEP = false, bool FLAT = false>
-__global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_balanced_kernel(AttnParams p) {
+__global__ __launch_bounds__(64) KV_BALANCED_WAVES(Q4) void attn_mfma_balanced_kernel(AttnParams p) {
     extern __shared__ int lds_ints[];  // BalancedLds
     const BalancedLds bl = balanced_lds(p, lds_ints);
     int *pre = bl.pre, *sids = bl.sids;
@@ -2871,26 +2879,30 @@ hipError_t launch_attention(int dtype, int kernel, const AttnParams &p, hipStrea
     return launch_valu<KIND_BF16>(p, grid, s, e0, e1);
 }
 
-int balanced_grid(int dtype, int head_dim, int batch, int max_blocks) {
+int balanced_grid(int dtype, int head_dim, int batch, int max_blocks, bool q4_one_score) {
     // compute units x resident workgroups per compute unit; 256 x 2 when the
     // runtime cannot tell (no device: only the size of a workspace is asked)
     int dev = 0, cus = 0, per_cu = 0;
     const size_t lds = (size_t)balanced_lds_ints(batch, max_blocks) * sizeof(int);
+    const int waves = dtype == KV_INT4 && q4_one_score ? kBalancedWavesQ4One : 2;  // per SIMD
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256 * 2;
+        return 256 * waves;
     hipError_t e;
-    if (dtype == KV_INT4)
+    if (dtype == KV_INT4 && q4_one_score)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 1, 1, false, true>, 64,
+                                                         lds);
+    else if (dtype == KV_INT4)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 4, 1>, 64, lds);
     else if (head_dim == 64)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<64, 0, 2>, 64, lds);
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_balanced_kernel<128, 0, 2>, 64, lds);
     if (e != hipSuccess || per_cu <= 0) per_cu = 2;
-    // at most two waves per SIMD: with more, more tile bytes are in flight
-    // and the 8B- and 70B-shaped decode layers measured slower (109 vs 104 us
-    // at three waves on the 8B shape)
-    if (per_cu > 8) per_cu = 8;
+    // bf16: at most two waves per SIMD: with more, more tile bytes are in
+    // flight and the 8B- and 70B-shaped decode layers measured slower (109
+    // vs 104 us at three waves on the 8B shape)
+    if (per_cu > 4 * waves) per_cu = 4 * waves;
     return cus * per_cu;
 }
 

@@ -161,8 +161,10 @@ hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end = n
 // then the merge of every row's partials (events as for launch_attention).
 hipError_t launch_attention_shared(const AttnParams &p, const PrefixArgs &g, hipStream_t s, hipEvent_t e0,
                                    hipEvent_t e1, hipEvent_t e_end);
-// Persistent grid of the balanced schedule: resident workgroups per device.
-int balanced_grid(int dtype, int head_dim, int batch, int max_blocks);
+// Persistent grid of the balanced schedule: resident workgroups per device
+// (q4_one_score: the INT4 kernel with at most four query columns, which runs
+// three waves per SIMD; the others run two).
+int balanced_grid(int dtype, int head_dim, int batch, int max_blocks, bool q4_one_score = false);
 // The same for wide units (bf16; units of ctw = 4 or 8 column tiles, or 2 at
 // head_dim 128).
 int wide_grid(int head_dim, int ctw, int batch, int max_blocks);

@@ -34,7 +34,7 @@ hipError_t launch_read_probe(const void *, size_t, int, uint32_t *, hipStream_t)
 
 void *noalloc_scratch() { reached("noalloc_scratch"); }
 
-int balanced_grid(int, int, int, int) { return 256 * 2; }
+int balanced_grid(int dtype, int, int, int, bool q4_one_score) { return 256 * (dtype == KV_INT4 && q4_one_score ? 3 : 2); }
 int wide_grid(int, int ctw, int, int) { return 1024 / ctw; }
 size_t shared_balanced_lds(int n_groups, int batch, int max_blocks) {
     return (size_t)(2 * (n_groups + 1) + batch + 1 + (max_blocks < 256 ? max_blocks : 256)) * sizeof(int);
