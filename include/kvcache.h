@@ -327,10 +327,10 @@ kv_status kv_decode_step(kv_pool_t pool, const void *k_new, const void *v_new, c
 
 /* Bytes of the device array kv_decode_step_noalloc uses as its workspace
  * (64 MiB; every device the library runs on holds one until the process
- * ends). It covers the one-token decode step of the balanced schedule on
- * bf16 and INT4 pools for batches of up to 3.9 million sequences on a 256-CU
- * device (the workspace is about 51 MB for that device's persistent grid,
- * 16 rows per slot, plus 4 bytes per sequence). */
+ * ends). It covers the one-token decode step on bf16 and INT4 pools at any
+ * batch the balanced schedule takes (its workspace depends on the device's
+ * persistent grid, 16 rows per slot and the batch's prefix sums: at most
+ * about 51 MB on a 256-CU device). */
 #define KV_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* kv_decode_step for callers that cannot allocate device memory (code under

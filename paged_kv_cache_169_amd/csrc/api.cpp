@@ -129,12 +129,13 @@ constexpr int kMaxBalancedBatch = 8192;
 // Balanced schedule: tiles' worth of time a (sequence, unit) pair costs on
 // top of its tiles: its start (block ids, query, the first tile's latency,
 // the partial or output it writes). Fitted on MI355X to per-workgroup times
-// of the 8B-shaped layers: a bf16 pair start costs about 1.1 tiles, an INT4
-// one about 3.6. (A fused INT4 append costs about 2 more tiles, but it is not
-// charged: the schedule of the decode step must equal that of the separate
-// attention call, so that both give the same bits.)
+// of the 8B-shaped layers: a bf16 pair start costs about 1.1 tiles; on INT4
+// pools 5 measured best (8B shape, three waves per SIMD: 51.2 against 52.4 us
+// at 4 and 52.5 at 3). (A fused INT4 append costs about 2 more tiles, but it
+// is not charged: the schedule of the decode step must equal that of the
+// separate attention call, so that both give the same bits.)
 constexpr int kSegCost = 1;
-constexpr int kSegCostQ4 = 4;
+constexpr int kSegCostQ4 = 5;
 constexpr int kMaxPairCost = kSegCostQ4;
 
 kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
