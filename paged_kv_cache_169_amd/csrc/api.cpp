@@ -128,14 +128,19 @@ struct AttnGeom {
 constexpr int kMaxBalancedBatch = 8192;
 // Balanced schedule: tiles' worth of time a (sequence, unit) pair costs on
 // top of its tiles: its start (block ids, query, the first tile's latency,
-// the partial or output it writes). Fitted on MI355X to per-workgroup times
-// of the 8B-shaped layers: a bf16 pair start costs about 1.1 tiles; on INT4
-// pools 5 measured best (8B shape, three waves per SIMD: 51.2 against 52.4 us
-// at 4 and 52.5 at 3). (A fused INT4 append costs about 2 more tiles, but it
-// is not charged: the schedule of the decode step must equal that of the
-// separate attention call, so that both give the same bits.)
-constexpr int kSegCost = 1;
-constexpr int kSegCostQ4 = 5;
+// the partial or output it writes). Fitted on MI355X to the 8B-shaped
+// layers: per-workgroup times showed workgroups that start a second pair
+// ending 2-3 us after those with one at the earlier weights (1 for bf16, 5
+// for INT4); the kernels measured best at 2 (bf16, 16 query tokens 159 ->
+// 156 us, one token level) and 7 (INT4, three waves per SIMD: 51.4 -> 50.5
+// us; 52.4 at 4). (A fused INT4 append costs about 2 more tiles, but it is
+// not charged: the schedule of the decode step must equal that of the
+// separate attention call, so that both give the same bits.) The INT4 kernel
+// with more than four query columns (two waves per SIMD) keeps 5: 7 made it
+// 1 % slower at 4 query tokens.
+constexpr int kSegCost = 2;
+constexpr int kSegCostQ4 = 7;
+constexpr int kSegCostQ4Cols = 5;
 constexpr int kMaxPairCost = kSegCostQ4;
 
 kv_status attn_geom(const kv_pool *pool, int32_t batch, int32_t n_h, int32_t q_len, int32_t max_ctx,
@@ -516,7 +521,7 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     a.schedule = g.schedule;
     a.n_wg = g.n_wg;
     const bool balanced = g.schedule == KV_SCHED_BALANCED;
-    a.seg_cost = balanced ? (dtype == KV_INT4 ? kSegCostQ4 : kSegCost) : 0;
+    a.seg_cost = !balanced ? 0 : dtype != KV_INT4 ? kSegCost : g.ncols <= 4 ? kSegCostQ4 : kSegCostQ4Cols;
     a.pace = balanced ? 1 : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
