@@ -159,8 +159,8 @@ def main():
     ap.add_argument("--schedule", type=int, default=0, help="0 auto, 1 fixed splits, 2 balanced")
     ap.add_argument("--event-every", type=int, default=0,
                     help="record the kernel-boundary events on every E-th timed step (each record costs the "
-                         "stream about a microsecond); 1 = every step; 0 (default): every step on the workloads "
-                         "whose step is several hundred microseconds, every 4th on the others")
+                         "stream about a microsecond: 3-4 us per step, 1 %% of the 70B-shaped step); 1 = every "
+                         "step; 0 (default): every 4th step, every 2nd when fewer than 40 steps are timed")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget on all host threads, and again on one thread; 0 skips it")
     ap.add_argument("--q-len", type=int, default=1,
@@ -263,7 +263,7 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronized on both sides
-    every = args.event_every if args.event_every > 0 else (1 if name in ("llama2_70b", "long_shared") else 4)
+    every = args.event_every if args.event_every > 0 else (4 if args.steps >= 40 else 2)
     ev = [[hip.create() for _ in range(3)] if i % every == 0 else None for i in range(args.steps)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
