@@ -114,6 +114,30 @@ constexpr float kLazyLog2 = 8.0f;
 // registers and cost vector instructions on every tile.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Positions [0, total) of a balanced schedule over n workgroups, as evenly
+// as whole positions allow: q = total / n each, and the first total % n one
+// more. No share is left empty while others hold one position above the
+// average (a share of ceil(total / n) each left up to n - 1 positions' worth
+// of workgroups idle at the end: 40 of 2048 on the 8B shape), and the longer
+// shares go to the workgroups dispatched first: the grid fills the SIMDs in
+// index order, and a SIMD issues to its oldest wave first.
+struct Shares {
+    long q;
+    int r;
+    __device__ __forceinline__ long start(int w) const { return (long)w * q + min(w, r); }
+    // the workgroup whose share holds position x (0 <= x < total)
+    __device__ __forceinline__ int wg_of(long x) const {
+        const long big = (long)r * (q + 1);
+        return x < big ? (int)(x / (q + 1)) : r + (int)((x - big) / q);
+    }
+};
+__device__ __forceinline__ Shares shares_of(long total, int n) {
+    Shares sh;
+    sh.q = total / n;
+    sh.r = (int)(total - sh.q * n);
+    return sh;
+}
+
 // Orders one wave's LDS accesses for its other lanes, for workgroups of a
 // single wave: the LDS executes a wave's instructions in issue order, so no
 // barrier or wait is needed, only that the compiler keeps the order.
@@ -1606,8 +1630,9 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_kernel(AttnParams 
 // in sequence-major, unit, block order on a cost axis where every (sequence,
 // unit) pair also takes seg_cost positions after its tiles: the start of a
 // segment (its block ids, query and first tile) costs about that many tiles
-// of time. Workgroup w of the persistent grid takes positions [w * per,
-// (w+1) * per), per = ceil(total / grid), and works the tiles among them.
+// of time. Workgroup w of the persistent grid takes the positions of its
+// share (Shares: total / grid each, one more for the first total % grid) and
+// works the tiles among them.
 // A workgroup walks its range one pair at a time; a pair whose tiles all
 // fall in its range writes the output directly. Otherwise the piece leaves a
 // partial in slot 0 of the workgroup's two workspace slots when the pair
@@ -1721,9 +1746,9 @@ __global__ __launch_bounds__(64) KV_BALANCED_WAVES(Q4) void attn_mfma_balanced_k
     if (wg == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long s = (long)wg * per;
-    const long e = min(total, s + per);
+    const Shares sh = shares_of(total, p.n_wg);
+    const long s = sh.start(wg);
+    const long e = sh.start(wg + 1);
     // paced on INT4 pools only (measured: INT4 60 vs 62-63.5 us on the 8B
     // shape; the bf16 kernels unchanged, and without it they keep fewer
     // registers)
@@ -2060,9 +2085,9 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
     if (wg == 0 && wave == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long s = (long)wg * per;
-    const long e = min(total, s + per);
+    const Shares sh = shares_of(total, p.n_wg);
+    const long s = sh.start(wg);
+    const long e = sh.start(wg + 1);
     for (long t = s; t < e;) {
         const int b = sequence_at(pre, p.batch, p.units, t, lane);
         const int pb = uniform(pre[b]);
@@ -2272,7 +2297,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_kernel(Attn
 //
 // Every tile of the call is numbered: the prefix tiles first (group, its
 // units, block), then the suffix tiles (sequence, unit, block of its own
-// part). Workgroup w of the persistent grid takes [w * per, (w+1) * per) and
+// part). Workgroup w of the persistent grid takes its share (Shares) and
 // walks it one segment (a group's unit over its prefix, or a sequence's unit
 // over its own blocks) at a time, as the balanced schedule does. A piece (a
 // segment's part inside one workgroup) leaves its partials in the segment's
@@ -2362,14 +2387,14 @@ __device__ __forceinline__ void shared_plan(const AttnParams &p, const PrefixArg
 
 // Workspace row of a piece's partial: the segment's own slot, or slot 0 / 1
 // of workgroup w, for segment tiles [a, a + len) and a range share `per`.
-__device__ __forceinline__ size_t shared_piece_row(const AttnParams &p, long a, int len, long per, int w,
+__device__ __forceinline__ size_t shared_piece_row(const AttnParams &p, long a, int len, const Shares &sh, int w,
                                                    int seg, int n16) {
-    const long lo = max(a, (long)w * per), hi = min(a + len, (long)(w + 1) * per);
+    const long lo = max(a, sh.start(w)), hi = min(a + len, sh.start(w + 1));
     size_t slot;
     if (lo == a && hi == a + len)
         slot = (size_t)2 * p.n_wg + seg;
     else
-        slot = (size_t)w * 2 + (lo == (long)w * per ? 0 : 1);
+        slot = (size_t)w * 2 + (lo == sh.start(w) ? 0 : 1);
     return slot * 16 + n16;
 }
 
@@ -2403,9 +2428,9 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
     }
     const long tp = pl.gtile[pl.ng];  // prefix tiles
     const long total = tp + (long)pl.stile[p.batch] * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
-    const long s = (long)wg * per;
-    const long e = min(total, s + per);
+    const Shares sh = shares_of(total, p.n_wg);
+    const long s = sh.start(wg);
+    const long e = sh.start(wg + 1);
     for (long t = s; t < e;) {
         MfmaState<D> st;
         long seg_end;
@@ -2441,7 +2466,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
             if (col.valid) {
                 float res[D / 4];
                 mfma_gather_run<D>(st, 0.0f, res);
-                const size_t row = shared_piece_row(p, a, P, per, wg, pl.gseg[gi] + unit, n16);
+                const size_t row = shared_piece_row(p, a, P, sh, wg, pl.gseg[gi] + unit, n16);
                 store_piece<D>(p, row, G, res, st.m, l, bad || w.bad);
             }
         } else {
@@ -2481,7 +2506,7 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
                     for (int c = 0; c < D / 4; ++c) dst[c] = bad ? nan : res[c] * inv;
                 } else {
                     const int seg = pl.gseg[pl.ng] + b * p.units + unit;
-                    store_piece<D>(p, shared_piece_row(p, a, nb, per, wg, seg, n16), G, res, st.m, l, bad);
+                    store_piece<D>(p, shared_piece_row(p, a, nb, sh, wg, seg, n16), G, res, st.m, l, bad);
                 }
             }
         }
@@ -2603,10 +2628,10 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParam
         return;
     }
     const long total = (long)p.ws_prefix[p.batch] * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const Shares sh = shares_of(total, p.n_wg);
     const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
     const long end = start + nb;
-    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
+    const int w0 = sh.wg_of(start), w1 = sh.wg_of(end - 1);
     if (w0 == w1) return;  // complete inside one workgroup: already written
     for (int row = wave; row < rows; row += nwaves) {
         // workspace row of the partial that workgroup w holds for this pair:
@@ -2650,10 +2675,10 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParam
         return;
     }
     const long total = (long)p.ws_prefix[p.batch] * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const Shares sh = shares_of(total, p.n_wg);
     const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
     const long end = start + nb;
-    const int w0 = (int)(start / per), w1 = (int)((end - 1) / per);
+    const int w0 = sh.wg_of(start), w1 = sh.wg_of(end - 1);
     if (w0 == w1) return;  // complete inside one workgroup: already written
     const int n = w1 - w0 + 1;
     // workspace row of piece i: the first piece goes on past its range (slot
@@ -2745,7 +2770,7 @@ __global__ __launch_bounds__(64) void attn_merge_shared_balanced_kernel(AttnPara
     }
     const long tp = gtile[ng];
     const long total = tp + (long)stile[p.batch] * p.units;
-    const long per = (total + p.n_wg - 1) / p.n_wg;
+    const Shares sh = shares_of(total, p.n_wg);
     // prefix segment of the row: group gi, column k * group + hq
     long pa = 0;
     int pseg = 0, pw0 = 0, npre = 0, pn16 = 0;
@@ -2756,19 +2781,19 @@ __global__ __launch_bounds__(64) void attn_merge_shared_balanced_kernel(AttnPara
         pn16 = ci % 16;
         pa = gtile[gi] + (long)unit * P;
         pseg = gseg[gi] + unit;
-        pw0 = (int)(pa / per);
-        npre = (int)((pa + P - 1) / per) - pw0 + 1;
+        pw0 = sh.wg_of(pa);
+        npre = sh.wg_of(pa + P - 1) - pw0 + 1;
     }
     // own segment of the row
     const int unit = kvh * p.ctiles + hq / 16, sn16 = hq % 16;
     const long sa = tp + (long)stile[b] * p.units + (long)unit * nb;
     const int sseg = gseg[ng] + b * p.units + unit;
-    const int sw0 = nb > 0 ? (int)(sa / per) : 0;
-    const int nsuf = nb > 0 ? (int)((sa + nb - 1) / per) - sw0 + 1 : 0;
+    const int sw0 = nb > 0 ? sh.wg_of(sa) : 0;
+    const int nsuf = nb > 0 ? sh.wg_of(sa + nb - 1) - sw0 + 1 : 0;
     if (P == 0 && nsuf == 1) return;  // written by the attention kernel
     merge_partials(p, npre + nsuf, [&](int i) {
-        return i < npre ? shared_piece_row(p, pa, P, per, pw0 + i, pseg, pn16)
-                        : shared_piece_row(p, sa, nb, per, sw0 + i - npre, sseg, sn16);
+        return i < npre ? shared_piece_row(p, pa, P, sh, pw0 + i, pseg, pn16)
+                        : shared_piece_row(p, sa, nb, sh, sw0 + i - npre, sseg, sn16);
     }, lane, cv, dst);
 }
 
