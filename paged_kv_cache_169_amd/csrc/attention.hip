@@ -612,10 +612,13 @@ __device__ __forceinline__ void mfma_block(const AttnParams &p, const MfmaTile<D
         sv[r] = ok ? sc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
     }
-    const float cm = col_max(mx);
-    if (__any(cm > st.m + kLazyLog2)) {
+    // A column's maximum exceeds its reference by more than the slack
+    // exactly when one of its lanes' maxima does: the test needs no
+    // reduction, and the column maxima are formed only when it passes.
+    if (__any(mx > st.m + kLazyLog2)) {
         // some column's maximum moved past its reference by more than the
         // slack: move every column's reference to its maximum and rescale
+        const float cm = col_max(mx);
         const float mn = fmaxf(st.m, cm);
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
@@ -721,17 +724,13 @@ __device__ __forceinline__ void mfma_block_ct(const AttnParams &p, const MfmaTil
             }
         }
     }
-    float cm[CT];
     bool grow = false;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        cm[c] = col_max(mx[c]);
-        grow |= cm[c] > st[c].m + kLazyLog2;
-    }
+    for (int c = 0; c < CT; ++c) grow |= mx[c] > st[c].m + kLazyLog2;
     if (__any(grow)) {  // as in mfma_block, for every column tile at once
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            const float mn = fmaxf(st[c].m, cm[c]);
+            const float mn = fmaxf(st[c].m, col_max(mx[c]));
             const float alpha = mn == st[c].m ? 1.0f : fast_exp2(st[c].m - mn);
             st[c].l *= alpha;
 #pragma unroll
@@ -1190,9 +1189,8 @@ __device__ __forceinline__ void q4_mask(int tok0, int tlo, int thi, const Column
 __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile &T, const float (&sv)[4], uint2 vs,
                                               uint2 vm, MfmaState<128> &st) {
     const float mx = max_raw(max3_raw(sv[0], sv[1], sv[2]), sv[3]);
-    const float cm = col_max(mx);
-    if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
-        const float mn = fmaxf(st.m, cm);
+    if (__any(mx > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
+        const float mn = fmaxf(st.m, col_max(mx));
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
         st.bv *= alpha;
@@ -1261,9 +1259,8 @@ __device__ __forceinline__ void q4_softmax_pv(const AttnParams &p, const Q4Tile 
 // lane's token's V scale and min words and their half (vsh = 0 or 16).
 __device__ __forceinline__ void q4_softmax_pv_one(const AttnParams &p, const Q4Tile &T, float s, bool ok,
                                                   uint32_t vsw, uint32_t vmw, int vsh, MfmaState<128> &st) {
-    const float cm = col_max(bank_max(s));
-    if (__any(cm > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
-        const float mn = fmaxf(st.m, cm);
+    if (__any(s > st.m + kLazyLog2)) {  // lazy rescale, as in mfma_block
+        const float mn = fmaxf(st.m, col_max(bank_max(s)));
         const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);  // unchanged (even -inf): 1
         st.l *= alpha;
         st.bv *= alpha;
