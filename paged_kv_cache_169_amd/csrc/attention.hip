@@ -1786,21 +1786,23 @@ __global__ __launch_bounds__(64) KV_BALANCED_WAVES(Q4) void attn_mfma_balanced_k
         for (int c = 0; c < CT; ++c) {
             const float l = q4_state_sum<Q4>(st[c].l), bv = q4_state_sum<Q4>(st[c].bv);
             if (col[c].valid) {
-                float res[D / 4];
-                mfma_gather_run<D>(st[c], bv, res);
                 const float nan = __uint_as_float(0x7fc00000u);
+                // a bad sequence's row is NaN: the NaN enters through the
+                // term every output value adds (no select per value)
+                float res[D / 4];
+                mfma_gather_run<D>(st[c], bad ? nan : bv, res);
                 if (jr == 0 && cnt == nb) {
                     float *dst = p.out + col[c].row * D + G * (D / 4);
                     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k] * inv;
+                    for (int k = 0; k < D / 4; ++k) dst[k] = res[k] * inv;
                 } else {
                     // slot row: column tile c of the unit at 16 c + n16
                     const int slot = jr > 0 ? 0 : 1;
                     const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + c * 16 + n16;
                     float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
-                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k];
+                    for (int k = 0; k < D / 4; ++k) dst[k] = res[k];
                     if (G == 0) {
                         p.ws_ml[row * 2] = st[c].m;
                         p.ws_ml[row * 2 + 1] = bad ? nan : l;
@@ -2116,20 +2118,20 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
         for (int c = 0; c < CT; ++c) {
             const float l = col_sum(st[c].l), bv = col_sum(st[c].bv);
             if (col[c].valid) {
-                float res[D / 4];
-                mfma_gather_run<D>(st[c], bv, res);
                 const float nan = __uint_as_float(0x7fc00000u);
+                float res[D / 4];
+                mfma_gather_run<D>(st[c], bad ? nan : bv, res);  // NaN row for a bad sequence, as above
                 if (jr == 0 && cnt == nb) {
                     float *dst = p.out + col[c].row * D + G * (D / 4);
                     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k] * inv;
+                    for (int k = 0; k < D / 4; ++k) dst[k] = res[k] * inv;
                 } else {
                     const int slot = jr > 0 ? 0 : 1;
                     const size_t row = ((size_t)wg * 2 + slot) * p.slot_cols + (CT * wave + c) * 16 + n16;
                     float *dst = p.ws_o + row * D + G * (D / 4);
 #pragma unroll
-                    for (int k = 0; k < D / 4; ++k) dst[k] = bad ? nan : res[k];
+                    for (int k = 0; k < D / 4; ++k) dst[k] = res[k];
                     if (G == 0) {
                         p.ws_ml[row * 2] = st[c].m;
                         p.ws_ml[row * 2 + 1] = bad ? nan : l;
