@@ -523,6 +523,7 @@ kv_status attention_impl(kv_pool_t pool, const void *q, float *out, int32_t num_
     const bool balanced = g.schedule == KV_SCHED_BALANCED;
     a.seg_cost = !balanced ? 0 : dtype != KV_INT4 ? kSegCost : g.ncols <= 4 ? kSegCostQ4 : kSegCostQ4Cols;
     a.pace = balanced ? 1 : 0;
+    a.xcd_shares = balanced && dtype == KV_INT4 ? 1 : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
     void *const *ev = opts ? opts->events : nullptr;

@@ -114,28 +114,14 @@ constexpr float kLazyLog2 = 8.0f;
 // registers and cost vector instructions on every tile.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Positions [0, total) of a balanced schedule over n workgroups, as evenly
-// as whole positions allow: q = total / n each, and the first total % n one
-// more. No share is left empty while others hold one position above the
-// average (a share of ceil(total / n) each left up to n - 1 positions' worth
-// of workgroups idle at the end: 40 of 2048 on the 8B shape), and the longer
-// shares go to the workgroups dispatched first: the grid fills the SIMDs in
-// index order, and a SIMD issues to its oldest wave first.
-struct Shares {
-    long q;
-    int r;
-    __device__ __forceinline__ long start(int w) const { return (long)w * q + min(w, r); }
-    // the workgroup whose share holds position x (0 <= x < total)
-    __device__ __forceinline__ int wg_of(long x) const {
-        const long big = (long)r * (q + 1);
-        return x < big ? (int)(x / (q + 1)) : r + (int)((x - big) / q);
-    }
-};
-__device__ __forceinline__ Shares shares_of(long total, int n) {
-    Shares sh;
-    sh.q = total / n;
-    sh.r = (int)(total - sh.q * n);
-    return sh;
+// The balanced schedule's split: shares numbered XCD by XCD on INT4 pools
+// (XcdShares), in workgroup order otherwise (Shares).
+template <bool XCD>
+__device__ __forceinline__ auto split_of(long total, int n) {
+    if constexpr (XCD)
+        return xcd_shares_of(total, n);
+    else
+        return shares_of(total, n);
 }
 
 // Orders one wave's LDS accesses for its other lanes, for workgroups of a
@@ -1734,16 +1720,16 @@ __global__ __launch_bounds__(64) KV_BALANCED_WAVES(Q4) void attn_mfma_balanced_k
     const BalancedLds bl = balanced_lds(p, lds_ints);
     int *pre = bl.pre, *sids = bl.sids;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
-    const int wg = blockIdx.x;
     // The INT4 path is bound by vector instructions: there the sequence
     // search and everything derived from it are moved to scalar registers.
     // The bf16 path keeps them in vector registers (measured faster: the
     // scalar form runs out of scalar registers there).
     const int npos = Q4 ? uniform(balanced_prefix(p, bl, lane)) : balanced_prefix(p, bl, lane);
-    if (wg == 0)
+    if (blockIdx.x == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
-    const Shares sh = shares_of(total, p.n_wg);
+    const auto sh = split_of<Q4 != 0>(total, p.n_wg);
+    const int wg = sh.share_of(blockIdx.x);
     const long s = sh.start(wg);
     const long e = sh.start(wg + 1);
     // paced on INT4 pools only (measured: INT4 60 vs 62-63.5 us on the 8B
@@ -2076,15 +2062,15 @@ __global__ __launch_bounds__(64 * W) KV_MFMA_WAVES void attn_mfma_wide_kernel(At
     int *pre = bl.pre, *sids = bl.sids;
     __shared__ TileLds<D> tl[kWideBufs];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n16 = lane & 15, G = lane >> 4;
-    const int wg = blockIdx.x;
     // every wave computes the same sums (identical LDS writes); the sequence
     // search and what derives from it are kept in scalar registers, so the
     // tile loop's bounds and masks are uniform branches
     const int npos = uniform(balanced_prefix(p, bl, lane));
-    if (wg == 0 && wave == 0)
+    if (blockIdx.x == 0 && wave == 0)
         for (int i = lane; i <= p.batch; i += 64) p.ws_prefix[i] = pre[i];
     const long total = (long)npos * p.units;
     const Shares sh = shares_of(total, p.n_wg);
+    const int wg = sh.share_of(blockIdx.x);
     const long s = sh.start(wg);
     const long e = sh.start(wg + 1);
     for (long t = s; t < e;) {
@@ -2420,14 +2406,14 @@ __global__ __launch_bounds__(64) KV_MFMA_WAVES void attn_mfma_shared_balanced_ke
     pl.stile = lds + 2 * (pl.ng + 1);
     int *sids = pl.stile + p.batch + 1;
     const int lane = threadIdx.x, n16 = lane & 15, G = lane >> 4;
-    const int wg = blockIdx.x;
     shared_plan(p, g, pl, lane);
-    if (wg == 0) {
+    if (blockIdx.x == 0) {
         for (int i = lane; i < 2 * (pl.ng + 1) + p.batch + 1; i += 64) p.ws_prefix[i] = lds[i];
     }
     const long tp = pl.gtile[pl.ng];  // prefix tiles
     const long total = tp + (long)pl.stile[p.batch] * p.units;
     const Shares sh = shares_of(total, p.n_wg);
+    const int wg = sh.share_of(blockIdx.x);
     const long s = sh.start(wg);
     const long e = sh.start(wg + 1);
     for (long t = s; t < e;) {
@@ -2604,6 +2590,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p) {
 // token, head) in turn; each row combines the partials of the workgroups
 // whose tile ranges cut the pair, and gets 0 (NaN for a bad sequence) when
 // the sequence has no attended block.
+template <bool XCD>
 __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParams p) {
     const int unit = blockIdx.x, b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = 4;
@@ -2627,7 +2614,7 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParam
         return;
     }
     const long total = (long)p.ws_prefix[p.batch] * p.units;
-    const Shares sh = shares_of(total, p.n_wg);
+    const auto sh = split_of<XCD>(total, p.n_wg);
     const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
     const long end = start + nb;
     const int w0 = sh.wg_of(start), w1 = sh.wg_of(end - 1);
@@ -2653,6 +2640,7 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_unit_kernel(AttnParam
 // a row no piece saw a token for gets 0. Grid (units * groups, batch); a
 // group is blockDim / (D / 8) rows, and a unit's slot_cols rows take groups
 // of them.
+template <bool XCD>
 __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParams p) {
     const int D = p.head_dim, chunks = D / 8, rpg = (int)blockDim.x / chunks;  // chunks per row, rows per group
     const int cgroups = p.units / p.n_kv, ucols = 16 * p.ctw;      // column groups per kv head, columns per unit
@@ -2674,7 +2662,7 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParam
         return;
     }
     const long total = (long)p.ws_prefix[p.batch] * p.units;
-    const Shares sh = shares_of(total, p.n_wg);
+    const auto sh = split_of<XCD>(total, p.n_wg);
     const long start = (long)p.ws_prefix[b] * p.units + (long)unit * span;
     const long end = start + nb;
     const int w0 = sh.wg_of(start), w1 = sh.wg_of(end - 1);
@@ -2684,6 +2672,51 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParam
     // 1 of its workgroup), the others started before theirs (slot 0)
     auto ws_row = [&](int i) { return ((size_t)(w0 + i) * 2 + (i == 0 ? 1 : 0)) * p.slot_cols + row; };
     constexpr int NB = 4;  // pieces whose loads go out together
+    float L = 0.0f;
+    float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
+    if (n <= 2 * NB) {
+        // up to 8 pieces (the usual count): every load of every piece goes
+        // out at once, one memory round trip instead of one per 4 pieces in
+        // each of the two passes below. The same operations in the same
+        // order as those passes, so the same bits.
+        constexpr int NB2 = 2 * NB;
+        const int used = (n + NB - 1) / NB * NB;  // the passes below touch whole groups of 4
+        float m[NB2], l[NB2];
+        float4 o[NB2][2];
+#pragma unroll
+        for (int k = 0; k < NB2; ++k) {
+            const size_t r = ws_row(min(k, n - 1));  // past the end: a repeat, weight 0
+            m[k] = p.ws_ml[r * 2];
+            l[k] = p.ws_ml[r * 2 + 1];
+            const float4 *src = reinterpret_cast<const float4 *>(p.ws_o + r * D + ch * 8);
+            o[k][0] = src[0];
+            o[k][1] = src[1];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NB2; ++k)
+            if (k < used) M = fmaxf(M, m[k]);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < NB2; ++k) {
+                if (k >= used) break;
+                const float w = k < n ? fast_exp2(m[k] - M) : 0.0f;
+                L = fmaf(w, l[k], L);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    acc[h].x = fmaf(w, o[k][h].x, acc[h].x);
+                    acc[h].y = fmaf(w, o[k][h].y, acc[h].y);
+                    acc[h].z = fmaf(w, o[k][h].z, acc[h].z);
+                    acc[h].w = fmaf(w, o[k][h].w, acc[h].w);
+                }
+            }
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            dst[h] = make_float4(acc[h].x * inv, acc[h].y * inv, acc[h].z * inv, acc[h].w * inv);
+        return;
+    }
     float M = -INFINITY;
     for (int i0 = 0; i0 < n; i0 += NB) {
         float m[NB];
@@ -2692,8 +2725,6 @@ __global__ __launch_bounds__(256) void attn_merge_balanced_rows_kernel(AttnParam
 #pragma unroll
         for (int k = 0; k < NB; ++k) M = fmaxf(M, m[k]);
     }
-    float L = 0.0f;
-    float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
     if (M != -INFINITY) {
         for (int i0 = 0; i0 < n; i0 += NB) {
             float m[NB], l[NB];
@@ -2982,15 +3013,23 @@ hipError_t launch_merge(const AttnParams &p, hipStream_t s, hipEvent_t e_end) {
     if (none) return e_end ? hipEventRecord(e_end, s) : hipSuccess;
     if (p.schedule == KV_SCHED_BALANCED && p.slot_cols >= kMergeUnitRows && p.slot_cols <= 16 &&
         (long)p.batch * p.units >= kMergeUnitMin) {
-        hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel, dim3(p.units, p.batch), dim3(256), 0, s, nullptr, e_end,
-                              0, p);
+        if (p.xcd_shares)
+            hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel<true>, dim3(p.units, p.batch), dim3(256), 0, s,
+                                  nullptr, e_end, 0, p);
+        else
+            hipExtLaunchKernelGGL(attn_merge_balanced_unit_kernel<false>, dim3(p.units, p.batch), dim3(256), 0, s,
+                                  nullptr, e_end, 0, p);
     } else if (p.schedule == KV_SCHED_BALANCED) {
         // whole waves, up to 256 threads: 16 rows of 128 channels, 32 of 64
         const int chunks = p.head_dim / 8;
         const int threads = std::min(256, (p.slot_cols * chunks + 63) / 64 * 64), rpg = threads / chunks;
         const int groups = (p.slot_cols + rpg - 1) / rpg;
-        hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel, dim3(p.units * groups, p.batch), dim3(threads), 0, s,
-                              nullptr, e_end, 0, p);
+        if (p.xcd_shares)
+            hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel<true>, dim3(p.units * groups, p.batch),
+                                  dim3(threads), 0, s, nullptr, e_end, 0, p);
+        else
+            hipExtLaunchKernelGGL(attn_merge_balanced_rows_kernel<false>, dim3(p.units * groups, p.batch),
+                                  dim3(threads), 0, s, nullptr, e_end, 0, p);
     } else
         hipExtLaunchKernelGGL(attn_merge_kernel, dim3(p.n_h * p.q_len, p.batch), dim3(64), 0, s, nullptr, e_end, 0,
                               p);

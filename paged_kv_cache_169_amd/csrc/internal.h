@@ -45,6 +45,7 @@ struct AttnParams {
     int32_t n_wg;      // balanced: persistent grid size
     int32_t seg_cost;  // balanced: schedule positions a (sequence, unit) pair takes beyond its tiles
     int32_t pace;      // balanced INT4: waves set their issue priority from their progress (1) or not (0)
+    int32_t xcd_shares;  // balanced: shares numbered XCD by XCD (XcdShares: INT4 pools) (1) or not (Shares) (0)
     int32_t *ws_prefix;  // balanced: [batch + 1] schedule positions per unit before each sequence
     float scale_log2;  // scale * log2(e): scores are kept in log2 units
     // Decode step: the attended length of sequence b is ctx_lens[b] + ctx_add
@@ -71,6 +72,94 @@ __host__ __device__ inline int length_after(int L, int add) {
 // of max_blocks blocks (64-bit sum).
 __host__ __device__ inline bool append_fits(int L0, int n_new, int max_blocks) {
     return L0 >= 0 && (long long)L0 + n_new <= (long long)max_blocks * kBlock;
+}
+
+// Positions [0, total) of a balanced schedule over n workgroups, as evenly
+// as whole positions allow: q = total / n each, and one more for the
+// total % n workgroups dispatched first (no share is left empty while others
+// hold one position above the average; a SIMD issues to its oldest wave
+// first). Share i is workgroup i.
+struct Shares {
+    long q;
+    int r;
+    __host__ __device__ inline long start(int w) const { return (long)w * q + (w < r ? w : r); }
+    // the share that holds position p (0 <= p < total)
+    __host__ __device__ inline int wg_of(long p) const {
+        const long big = (long)r * (q + 1);
+        return p < big ? (int)(p / (q + 1)) : r + (int)((p - big) / q);
+    }
+    __host__ __device__ inline int share_of(int i) const { return i; }
+};
+__host__ __device__ inline Shares shares_of(long total, int n) {
+    Shares sh;
+    sh.q = total / n;
+    sh.r = (int)(total - sh.q * n);
+    return sh;
+}
+
+// The same split with the shares numbered XCD by XCD, for the INT4 decode
+// kernels. Workgroup i of a launch runs on XCD i mod 8, and each of the 8
+// XCDs has an L2 of its own. When every share holds a position (q > 0), XCD x
+// holds the consecutive shares first(x) ... first(x + 1) - 1, share
+// first(x) + k being workgroup 8 k + x, and the total % n longer shares are
+// still the workgroups dispatched first. Pairs next to each other in the
+// schedule (the kv heads of one sequence, whose INT4 V scale and min rows
+// share cache lines) thus run on one XCD at the same time, and each XCD's run
+// of positions differs from the others' by at most one position beyond q
+// times its workgroup count. With fewer positions than workgroups (q = 0) it
+// is Shares' numbering, so the shares that hold a position are always the
+// first ones: a pair's pieces sit in consecutive shares, which the merges
+// rely on. (The bf16 kernels read no cache line twice; there this numbering
+// measured no faster.)
+struct XcdShares {
+    long q;
+    bool xcd;       // q > 0
+    int n, q8, r8;  // XCD x holds q8 + (x < r8) workgroups
+    int a, b;       // total % n = 8 a + b: XCD x has a + (x < b) longer shares
+    __host__ __device__ inline int first(int x) const { return x * q8 + (x < r8 ? x : r8); }
+    __host__ __device__ inline int longer(int x) const { return a + (x < b ? 1 : 0); }
+    // first position of XCD x's run
+    __host__ __device__ inline long xcd_start(int x) const { return (long)first(x) * q + (long)a * x + (x < b ? x : b); }
+    // the share workgroup i works on
+    __host__ __device__ inline int share_of(int i) const { return xcd ? first(i & 7) + (i >> 3) : i; }
+    __host__ __device__ inline long start(int w) const {
+        if (!xcd) {
+            const int r = 8 * a + b;
+            return w < r ? w : r;  // q = 0
+        }
+        if (w >= n) return xcd_start(8);
+        const int big = r8 * (q8 + 1);
+        const int x = w < big ? w / (q8 + 1) : r8 + (w - big) / q8;
+        const int k = w - first(x);
+        return xcd_start(x) + (long)k * q + (k < longer(x) ? k : longer(x));
+    }
+    // the share that holds position p (0 <= p < total)
+    __host__ __device__ inline int wg_of(long p) const {
+        if (!xcd) return (int)p;  // q = 0: share p holds position p
+        int x = 0;
+        long s0 = 0, s1 = (long)(q8 + (r8 > 0 ? 1 : 0)) * q + longer(0);  // XCD x's run is [s0, s1)
+        while (x < 7 && s1 <= p) {
+            ++x;
+            s0 = s1;
+            s1 += (long)(q8 + (x < r8 ? 1 : 0)) * q + longer(x);
+        }
+        const long off = p - s0;
+        const int e = longer(x);
+        const long big = (long)e * (q + 1);
+        return first(x) + (off < big ? (int)(off / (q + 1)) : e + (int)((off - big) / q));
+    }
+};
+__host__ __device__ inline XcdShares xcd_shares_of(long total, int n) {
+    XcdShares sh;
+    sh.q = total / n;
+    const int r = (int)(total - sh.q * n);
+    sh.xcd = sh.q > 0;
+    sh.n = n;
+    sh.q8 = n >> 3;
+    sh.r8 = n & 7;
+    sh.a = r >> 3;
+    sh.b = r & 7;
+    return sh;
 }
 
 // Attended length of sequence b (negative: invalid).

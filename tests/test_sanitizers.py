@@ -10,6 +10,9 @@
   host tests: none of them may reach a launch or trip a sanitizer.
 - The length predicates the kernels apply to device metadata run on the host
   at the int32 limits (tests/native/host_predicates.cpp).
+- The balanced schedule's split of positions among workgroups and XCDs
+  (tests/native/host_shares.cpp) is checked for every grid up to 300
+  workgroups and the grids the kernels launch.
 
 Each sanitized build is loaded into a child Python process with the
 sanitizer runtime preloaded."""
@@ -84,3 +87,14 @@ def test_length_predicates_at_int32_limits(tmp_path):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1")
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=60)
     assert r.returncode == 0 and "host predicates ok" in r.stdout, r.stdout + r.stderr
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir(HIP_INCLUDE), reason="needs g++ and HIP headers")
+def test_balanced_shares(tmp_path):
+    exe = tmp_path / "host_shares"
+    subprocess.run(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", HIP_INCLUDE, "-I",
+                    os.path.join(ROOT, "include"), "-I", CSRC] + SAN +
+                   [os.path.join(NATIVE, "host_shares.cpp"), "-o", str(exe)], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "host shares ok" in r.stdout, r.stdout + r.stderr
