@@ -97,6 +97,10 @@ def _declare(L):
     L.kvo_recompute_ratio.argtypes = [_D, _D, _I, _D]
     L.kvo_recompute_count.restype = _I
     L.kvo_recompute_count.argtypes = [_D, _I]
+    L.kvo_layer_window.restype = _I
+    L.kvo_layer_window.argtypes = [ctypes.c_void_p, _I, _I]
+    L.kvo_window_released.restype = None
+    L.kvo_window_released.argtypes = [ctypes.c_void_p, _I, _I, ctypes.c_void_p]
     L.kvo_set_threads.restype = None
     L.kvo_set_threads.argtypes = [_I]
     L.kvo_max_threads.restype = _I
@@ -361,6 +365,20 @@ def recompute_ratio(load_time: float, token_time: float, num_tokens: int, floor_
 
 def recompute_count(ratio: float, num_tokens: int) -> int:
     return lib().kvo_recompute_count(float(ratio), int(num_tokens))
+
+
+def layer_window(windows, layer: int) -> int:
+    """Window of a 0-based layer from a per-layer list repeated cyclically."""
+    w = np.ascontiguousarray(windows, dtype=np.int32)
+    return lib().kvo_layer_window(_ptr(w), len(w), int(layer))
+
+
+def window_released(lens, window: int) -> np.ndarray:
+    """Per sequence, the leading blocks no later query attends (-1: negative length)."""
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    out = np.zeros(len(ln), dtype=np.int32)
+    lib().kvo_window_released(_ptr(ln), len(ln), int(window), _ptr(out))
+    return out
 
 
 def set_threads(n: int) -> None:

@@ -785,3 +785,40 @@ int kvo_recompute_count(double ratio, int num_tokens)
     if (c > (double)num_tokens) c = (double)num_tokens;
     return (int)c;
 }
+
+/* [KVSYS, "어텐션 윈도우 크기"]: the maximum attention window is given per
+ * layer as a list, and a list shorter than the number of layers is repeated
+ * as often as needed. Layer `layer` (0-based) gets the entry that the list,
+ * written out again and again, holds at that place. */
+int kvo_layer_window(const int *windows, int n_windows, int layer)
+{
+    int i, pos = 0;
+    if (n_windows <= 0 || layer < 0) return -1;
+    for (;;) {  /* walk the repeated list up to the layer */
+        for (i = 0; i < n_windows; ++i, ++pos)
+            if (pos == layer) return windows[i];
+    }
+}
+
+/* [KVSYS, "제한된 어텐션 윈도우 크기"]: blocks outside a layer's limited
+ * attention window are released for reuse. A sequence holding L tokens gets
+ * its next query at position L, and that query attends the last `window`
+ * tokens up to and including itself (a window of 0 attends every token);
+ * every later query starts later still. A block is released once its last
+ * token lies before the first position the next query attends: count the
+ * leading blocks for which that holds. A negative length gives -1. */
+void kvo_window_released(const int *lens, int batch, int window, int *out)
+{
+    int b;
+    for (b = 0; b < batch; ++b) {
+        const long long L = lens[b];
+        long long first = 0, n = 0;  /* first attended position, released blocks */
+        if (L < 0) {
+            out[b] = -1;
+            continue;
+        }
+        if (window > 0 && L + 1 - window > 0) first = L + 1 - window;
+        while (n * 16 + 15 < first) ++n;  /* block n ends before the window */
+        out[b] = (int)n;
+    }
+}

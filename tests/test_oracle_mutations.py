@@ -25,6 +25,12 @@ MUTANTS = {
              "int t = (L + 1) % BLOCK;\n        for (int h = 0; h < n_kv; ++h) {\n            size_t dst"),
     # window off by one
     "window": ("? n - window : 0;", "? n - window + 1 : 0;"),
+    # the per-layer window list indexed from the second entry
+    "layer_window_shift": ("if (pos == layer) return windows[i];", "if (pos == layer + 1) return windows[i];"),
+    # released blocks: the next query's own token left out of its window
+    "released_own_token": ("first = L + 1 - window;", "first = L - window;"),
+    # released blocks: a block released as soon as its first token leaves the window
+    "released_first_token": ("while (n * 16 + 15 < first) ++n;", "while (n * 16 < first) ++n;"),
     # INT4 rounding ties to even instead of half away from zero
     "round_even": ("c = (int)roundf(v);", "c = (int)rintf(v);"),
     # INT4 codes not clamped above 15 (fp16 rounding of s can push the quotient past 15.5)

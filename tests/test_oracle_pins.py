@@ -785,3 +785,33 @@ def test_recompute_count(orc):
     for n in range(1, 300):                                # the count never falls below ratio * n
         c = orc.recompute_count(0.15, n)
         assert c >= 0.15 * n - 1e-12 and c - 1 < 0.15 * n
+
+
+# KVSYS "어텐션 윈도우 크기": the page's own example, max_attention_window =
+# [4096, 256], makes the 1st, 3rd and 5th layers full attention and the 2nd,
+# 4th and 6th limited to 256 tokens; a one-entry list covers every layer.
+def test_layer_window_page_example(orc):
+    assert [orc.layer_window([4096, 256], layer) for layer in range(6)] == [4096, 256, 4096, 256, 4096, 256]
+    assert [orc.layer_window([4096], layer) for layer in range(5)] == [4096] * 5
+    assert [orc.layer_window([7, 8, 9], layer) for layer in range(8)] == [7, 8, 9, 7, 8, 9, 7, 8]
+
+
+# KVSYS "제한된 어텐션 윈도우 크기": blocks that no later query can attend are
+# released. Brute force: the later queries of a sequence holding L tokens sit
+# at positions L, L + 1, ...; each attends the last `window` tokens up to
+# itself (all tokens for window 0). The released count is the first block any
+# of them attends (every block from there on is attended by some query).
+@pytest.mark.parametrize("window", [0, 1, 2, 15, 16, 17, 31, 32, 33, 64, 100, 1000])
+def test_window_released_brute_force(orc, window):
+    rng = np.random.default_rng(77 + window)
+    lens = [int(x) for x in rng.integers(0, 300, 60)] + [0, 1, 15, 16, 17, 31, 32, 33, 999, -1, -500]
+    got = orc.window_released(lens, window)
+    for L, g in zip(lens, got):
+        if L < 0:
+            assert g == -1
+            continue
+        attended = set()
+        for p in range(L, L + 40):
+            lo = 0 if window == 0 else max(0, p + 1 - window)
+            attended |= {t // 16 for t in range(lo, p + 1)}
+        assert g == min(attended), (L, window)
