@@ -390,6 +390,32 @@ kv_status rope_rerotate(kv_pool_t pool, const int32_t *chunk_blocks, int32_t fir
  * a packed block. 0 for a NULL pool. */
 size_t kv_block_bytes(kv_pool_t pool);
 
+/* Window of a layer [KVSYS, "어텐션 윈도우 크기": the maximum attention window
+ * is given per layer as a list, repeated when it is shorter than the number
+ * of layers]: *window_out = windows[layer % n_windows], to be passed as
+ * kv_attn_opts.window for that layer.
+ *   windows     host int32 [n_windows], each > 0 (tokens)
+ *   layer       0-based layer index
+ * Host only; touches no device. KV_ERR_INVALID_ARG for a NULL pointer,
+ * n_windows <= 0, layer < 0 or a chosen entry <= 0. */
+kv_status kv_layer_window(const int32_t *windows, int32_t n_windows, int32_t layer, int32_t *window_out);
+
+/* Blocks that have left a limited attention window [KVSYS, "제한된 어텐션
+ * 윈도우 크기": blocks outside the window are released for reuse].
+ * released[b] = the number of leading table entries of sequence b that no
+ * later query can attend. A later query sits at position >= seq_lens[b] and
+ * attends the last `window` tokens up to and including itself, so every
+ * token before seq_lens[b] + 1 - window is dead, and the count is
+ * floor(max(0, seq_lens[b] + 1 - window) / 16). window 0 (all tokens)
+ * releases nothing; a negative length gives -1. The caller frees those
+ * blocks; the pool and the tables are not touched.
+ *   seq_lens    device int32 [batch]: tokens now held by each sequence
+ *   released    device int32 [batch], written
+ * Asynchronous on `stream`. KV_ERR_INVALID_ARG for batch < 0, window < 0,
+ * or a NULL array when batch > 0. */
+kv_status kv_window_released_blocks(const int32_t *seq_lens, int32_t batch, int32_t window, int32_t *released,
+                                    void *stream);
+
 /* Copy whole blocks inside a pool [KVSYS, "부분 재사용": a partially matching
  * block is copied before a request that reuses it writes into it]:
  * block dst_blocks[i] <- block src_blocks[i] in every per-block region, i < n.

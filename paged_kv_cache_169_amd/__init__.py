@@ -117,6 +117,8 @@ _kv_quantize_int4 = _decl("kv_quantize_int4", _I32, [_P, _P, _P, _I32, _P, _P, _
 _rope_rerotate = _decl("rope_rerotate", _I32, [_P, _P, _I32, _I32, _I32, _F, _I32, _P])
 _kv_block_bytes = _decl("kv_block_bytes", _SZ, [_P])
 _kv_copy_blocks = _decl("kv_copy_blocks", _I32, [_P, _P, _P, _I32, _P])
+_kv_layer_window = _decl("kv_layer_window", _I32, [_P, _I32, _I32, _P])
+_kv_window_released_blocks = _decl("kv_window_released_blocks", _I32, [_P, _I32, _I32, _P, _P])
 _kv_gather_blocks = _decl("kv_gather_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
 _kv_scatter_blocks = _decl("kv_scatter_blocks", _I32, [_P, _P, _I32, _P, _SZ, _P])
 _kv_token_deviation = _decl("kv_token_deviation", _I32, [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P])
@@ -446,6 +448,29 @@ def kv_block_bytes(pool: KVPool) -> int:
     return int(_kv_block_bytes(pool.handle))
 
 
+def kv_layer_window(windows, layer: int) -> int:
+    """Window of a 0-based layer from a per-layer list repeated cyclically."""
+    w = (ctypes.c_int32 * len(windows))(*[int(x) for x in windows])
+    out = ctypes.c_int32(0)
+    _check(_kv_layer_window(ctypes.cast(w, ctypes.c_void_p) if len(windows) else None, len(windows), int(layer),
+                            ctypes.byref(out)), "kv_layer_window")
+    return int(out.value)
+
+
+def kv_window_released_blocks(seq_lens: torch.Tensor, window: int, released: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """Per sequence, the leading blocks no later query can attend (-1 for a
+    negative length), as an int32 device tensor."""
+    B = int(seq_lens.numel())
+    if released is None:
+        released = torch.empty(B, dtype=torch.int32, device=seq_lens.device)
+    if int(released.numel()) != B:
+        raise ValueError("released must hold one entry per sequence")
+    _check(_kv_window_released_blocks(_i32(seq_lens, "seq_lens"), B, int(window), _i32(released, "released"),
+                                      _stream(stream)), "kv_window_released_blocks")
+    return released
+
+
 def kv_copy_blocks(pool: KVPool, src_blocks: torch.Tensor, dst_blocks: torch.Tensor, stream=None) -> None:
     n = int(src_blocks.numel())
     if int(dst_blocks.numel()) != n:
@@ -554,4 +579,5 @@ raw = {
     "paged_decode_attention_shared_workspace_bytes": _paged_decode_attention_shared_workspace_bytes,
     "kv_validate_tables": _kv_validate_tables, "kv_read_probe": _kv_read_probe,
     "kv_decode_step_noalloc": _kv_decode_step_noalloc,
+    "kv_layer_window": _kv_layer_window, "kv_window_released_blocks": _kv_window_released_blocks,
 }

@@ -34,6 +34,7 @@ SOURCES = {
     "blend.hip": [],
     "measure.hip": [],
     "noalloc.hip": [],
+    "window.hip": [],
 }
 
 

@@ -730,6 +730,22 @@ size_t kv_block_bytes(kv_pool_t pool) {
     return (size_t)copy_params(pool).per_block * 16;
 }
 
+kv_status kv_layer_window(const int32_t *windows, int32_t n_windows, int32_t layer, int32_t *window_out) {
+    if (!windows || !window_out || n_windows <= 0 || layer < 0) return KV_ERR_INVALID_ARG;
+    const int32_t w = windows[layer % n_windows];
+    if (w <= 0) return KV_ERR_INVALID_ARG;
+    *window_out = w;
+    return KV_OK;
+}
+
+kv_status kv_window_released_blocks(const int32_t *seq_lens, int32_t batch, int32_t window, int32_t *released,
+                                    void *stream) {
+    if (batch < 0 || window < 0) return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    if (!seq_lens || !released) return KV_ERR_INVALID_ARG;
+    return hip_status(launch_window_released(seq_lens, batch, window, released, static_cast<hipStream_t>(stream)));
+}
+
 kv_status kv_copy_blocks(kv_pool_t pool, const int32_t *src_blocks, const int32_t *dst_blocks, int32_t n,
                          void *stream) {
     if (!pool || n < 0) return KV_ERR_INVALID_ARG;

@@ -1,5 +1,6 @@
 // host_predicates.cpp -- the length predicates the kernels apply to device
-// metadata (internal.h: length_after, append_fits, ctx_of, seq_range), run
+// metadata (internal.h: length_after, append_fits, ctx_of, seq_range,
+// window_released), run
 // on the host at the int32 limits, under the sanitizers
 // (tests/test_sanitizers.py): a corrupt length near INT32_MAX must read as
 // invalid, never wrap into a valid one.
@@ -53,6 +54,12 @@ int main() {
     CHECK(seq_range(-1, 4, 0, 4, 1, 1).bad);
     CHECK(!seq_range(64, 4, 0, 4, 1, 1).bad && seq_range(65, 4, 0, 4, 1, 1).bad);
     CHECK(!seq_range(mb * kBlock, mb, 0, mb, 1, 1).bad);
+    // blocks released by a limited window, at the int32 limits
+    CHECK(window_released(INT_MAX, 1) == (int)(2147483647LL / kBlock));  // tokens 0 .. INT_MAX - 1 dead
+    CHECK(window_released(INT_MAX, INT_MAX) == 0);
+    CHECK(window_released(INT_MAX, 0) == 0);
+    CHECK(window_released(-1, 16) == -1 && window_released(INT_MIN, 0) == -1);
+    CHECK(window_released(100, 16) == 5 && window_released(15, 1) == 0 && window_released(16, 1) == 1);
     if (failures) return 1;
     std::printf("host predicates ok\n");
     return 0;

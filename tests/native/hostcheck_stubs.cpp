@@ -19,6 +19,9 @@ namespace kvc {
 hipError_t launch_deviation(int, const DeviationParams &, hipStream_t) { reached("launch_deviation"); }
 hipError_t launch_topk(const TopkParams &, hipStream_t) { reached("launch_topk"); }
 hipError_t launch_copy_blocks(const CopyParams &, hipStream_t) { reached("launch_copy_blocks"); }
+hipError_t launch_window_released(const int32_t *, int, int, int32_t *, hipStream_t) {
+    reached("launch_window_released");
+}
 hipError_t launch_append(int, const AppendParams &, hipStream_t) { reached("launch_append"); }
 hipError_t launch_attention(int, int, const AttnParams &, hipStream_t, hipEvent_t, hipEvent_t) {
     reached("launch_attention");

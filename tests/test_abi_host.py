@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(kv):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 31, names
     lib = kv.lib_handle()
     for n in names:
         assert hasattr(lib, n), n
@@ -368,3 +368,28 @@ def test_library_is_built_from_the_current_sources():
     assert os.path.exists(b.DIGEST_FILE), "library built without its source digest: rebuild"
     with open(b.DIGEST_FILE) as f:
         assert f.read().strip() == b.sources_digest(), "libkvcache.so is older than its sources: the last build failed or was not run"
+
+
+def test_layer_window_matches_oracle(kv, orc):
+    for windows in ([4096, 256], [4096], [7, 8, 9], [1, 2, 3, 4, 5]):
+        for layer in range(12):
+            assert kv.kv_layer_window(windows, layer) == orc.layer_window(windows, layer)
+    f = kv.raw["kv_layer_window"]
+    out = ctypes.c_int32(0)
+    w = (ctypes.c_int32 * 2)(4096, 0)
+    assert f(ctypes.cast(w, ctypes.c_void_p), 2, -1, ctypes.byref(out)) == kv.KV_ERR_INVALID_ARG  # layer < 0
+    assert f(ctypes.cast(w, ctypes.c_void_p), 0, 0, ctypes.byref(out)) == kv.KV_ERR_INVALID_ARG   # empty list
+    assert f(ctypes.cast(w, ctypes.c_void_p), 2, 3, ctypes.byref(out)) == kv.KV_ERR_INVALID_ARG   # entry 0
+    assert f(None, 2, 0, ctypes.byref(out)) == kv.KV_ERR_INVALID_ARG
+    assert f(ctypes.cast(w, ctypes.c_void_p), 2, 0, None) == kv.KV_ERR_INVALID_ARG
+    assert f(ctypes.cast(w, ctypes.c_void_p), 2, 2, ctypes.byref(out)) == kv.KV_OK and out.value == 4096
+
+
+def test_window_released_host_checks(kv):
+    f = kv.raw["kv_window_released_blocks"]
+    dummy = ctypes.c_void_p(16)  # never dereferenced: each call returns before any launch
+    assert f(dummy, -1, 16, dummy, None) == kv.KV_ERR_INVALID_ARG
+    assert f(dummy, 4, -1, dummy, None) == kv.KV_ERR_INVALID_ARG
+    assert f(None, 4, 16, dummy, None) == kv.KV_ERR_INVALID_ARG
+    assert f(dummy, 4, 16, None, None) == kv.KV_ERR_INVALID_ARG
+    assert f(None, 0, 16, None, None) == kv.KV_OK
