@@ -12,6 +12,7 @@
 #include <utility>
 
 #include "internal.h"
+#include "window.h"
 
 using namespace kvc;
 

@@ -162,16 +162,6 @@ __host__ __device__ inline XcdShares xcd_shares_of(long total, int n) {
     return sh;
 }
 
-// Leading blocks of a sequence of L tokens that no later query can attend
-// under a window of `window` tokens (0: all tokens): a later query at
-// position >= L attends positions >= L + 1 - window. -1 for a negative L.
-__host__ __device__ inline int window_released(int L, int window) {
-    if (L < 0) return -1;
-    if (window <= 0) return 0;
-    const long long dead = (long long)L + 1 - window;  // tokens before the window
-    return dead > 0 ? (int)(dead / kBlock) : 0;
-}
-
 // Attended length of sequence b (negative: invalid).
 __host__ __device__ inline int ctx_of(const AttnParams &p, int b) {
     const int L = p.ctx_lens[b];
@@ -249,7 +239,6 @@ struct PrefixArgs {
 hipError_t launch_deviation(int dtype, const DeviationParams &p, hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
-hipError_t launch_window_released(const int32_t *lens, int batch, int window, int32_t *out, hipStream_t s);
 hipError_t launch_append(int dtype, const AppendParams &p, hipStream_t s);
 // e0 / e1 (may be null): events recorded at the start / end of the attention
 // kernel; e_end: at the end of the merge (recorded on the stream when no merge

@@ -3,7 +3,7 @@
 // outside the window are released for reuse): one thread per sequence reads
 // its length and writes how many leading table entries no later query can
 // attend (window_released in internal.h).
-#include "internal.h"
+#include "window.h"
 
 namespace kvc {
 

@@ -8,6 +8,7 @@
 #include <cstdio>
 
 #include "internal.h"
+#include "window.h"
 
 using namespace kvc;
 

@@ -8,6 +8,7 @@
 #include <cstdlib>
 
 #include "internal.h"
+#include "window.h"
 
 namespace kvc {
 
